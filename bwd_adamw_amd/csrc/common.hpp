@@ -1,0 +1,99 @@
+// Device-side building blocks shared by the liblora kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LORA_DEV __device__ __forceinline__
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// Dropout hash ("4.3. Training Guide", "Dropout"): SplitMix64's output
+// function (Steele, Lea & Flood 2014) applied to state z.  The host chains it
+// over (seed, step, ordinal, layer, proj) into `base`; a row key is
+// mix(base ^ t) and the element decision uses mix(row ^ k).
+// ---------------------------------------------------------------------------
+LORA_DEV uint64_t sm_mix(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct DropParams {
+  uint64_t base;   // chained key of (seed, step, ordinal, layer, proj)
+  uint32_t thr;    // keep iff top-24 hash bits >= thr; thr == 0: keep all
+  float keep;      // float(1/(1-p)), multiplier of kept elements
+  int on;          // 0: dropout disabled
+};
+
+LORA_DEV uint64_t drop_row(const DropParams& d, int64_t t) {
+  return sm_mix(d.base ^ (uint64_t)t);
+}
+LORA_DEV bool drop_keep(const DropParams& d, uint64_t row, int64_t k) {
+  return (uint32_t)(sm_mix(row ^ (uint64_t)k) >> 40) >= d.thr;
+}
+// Multiplier of element (row key, k): keep ? keep-scale : 0.
+LORA_DEV float drop_mul(const DropParams& d, uint64_t row, int64_t k) {
+  return drop_keep(d, row, k) ? d.keep : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32 (round to nearest even; NaN stays NaN)
+// ---------------------------------------------------------------------------
+LORA_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+LORA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+LORA_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers.  Operand/result lane layouts (wave64):
+//  32x32x2 f32 : a = A[l%32][l/32], b = B[l/32][l%32],
+//                d[v] = D[8*(v/4) + 4*(l/32) + v%4][l%32]
+//  16x16x4 f32 : a = A[l%16][l/16], b = B[l/16][l%16],
+//                d[v] = D[4*(l/16) + v][l%16]
+//  32x32x16 bf16: a = A[l%32][k-group l/32 (8 values)], b likewise,
+//                d as for 32x32x2.
+// The contraction index carried by a lane group only has to agree between
+// the two operands, so kernels permute it freely to get wide LDS reads.
+// ---------------------------------------------------------------------------
+LORA_DEV f32x16 mfma32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+LORA_DEV f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+LORA_DEV f32x16 mfma32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+LORA_DEV int row32(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+LORA_DEV int row16(int v, int lane) { return 4 * (lane >> 4) + v; }
+
+// Wave-wide sum of a double (butterfly over 64 lanes; every lane gets it).
+LORA_DEV double wave_sum(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+LORA_DEV float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+}  // namespace lora

@@ -1,0 +1,274 @@
+// Frozen-weight GEMMs with float32 W on fp32 MFMA (v_mfma_f32_32x32x2f32).
+//
+// Forward ("8. LoRA Fundamentals", "How it works"):
+//   Z[t,n] = sum_k X[t,k] W[n,k]  +  s * sum_j U[t,j] B[n,j]
+// The rank-r up-projection is a second, short contraction into the same
+// accumulators: U and B tiles are staged through LDS after the main loop.
+//
+// dX ("Training decisions"; "Backward Bug Hunts ...", "Bug #1"):
+//   dX[t,k] = sum_n g[t,n] W[n,k]  +  (s * sum_j V[t,j] A[j,k]) * mask * keep
+// W is read in its native [N,K] layout (rows of W are the contraction
+// index); nothing is transposed in memory.  The LoRA term is contracted
+// first, masked in registers, then the frozen contraction accumulates on top.
+//
+// Block: 256 threads = 2x2 waves, tile BM x BN, K-step BK = 32, LDS double
+// buffered.  Within a K-step the lane half h = lane/32 takes contraction
+// indices 16h..16h+15 so each lane reads its A (and, forward, B) operands with
+// 128-bit LDS loads.  Split-K over the contraction writes per-split partials
+// that a second kernel sums in fixed order (no atomics).
+#pragma once
+#include "common.hpp"
+
+namespace lora {
+
+struct GemmF32Args {
+  const float* A;          // [M, Kc] contraction contiguous (X or dY)
+  int64_t lda;
+  const float* acn;        // per-contraction multiplier num/den on A (DoRA g), or NULL
+  const float* acd;
+  const float* B;          // fwd: W [Nc, Kc];  dx: W [Kc, Nc]
+  int64_t ldb;
+  int64_t M, Nc, Kc;
+  const float* XA;         // LoRA operand on the A side: U (fwd) or V (dx), [M, r]
+  const float* XB;         // fwd: B_lora [Nc, r];  dx: A_lora [r, Nc]
+  int64_t r;
+  float xs;                // LoRA scale s
+  DropParams drop;         // dx only: mask of the LoRA term at (t = m, k = n)
+  int64_t ksplit;          // contraction length per split (multiple of 32)
+  int nsplit;
+  float* C;                // output (nsplit == 1): Y or dX, [M, Nc]
+  float* C2;               // fwd DoRA: Z, or NULL
+  const float* cn;         // fwd DoRA epilogue column scale cn/cd, or NULL
+  const float* cd;
+  float* part;             // [nsplit, M, Nc] partials when nsplit > 1
+};
+
+template <int BM, int BN, bool FWD>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
+  constexpr int BK = 32;
+  constexpr int LDA = BK + 4;
+  constexpr int LDB = FWD ? (BK + 4) : (BN + 4);
+  constexpr int BSZ = FWD ? BN * LDB : BK * LDB;
+  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int AF4 = BM * BK / 4 / 256;
+  constexpr int BF4 = BN * BK / 4 / 256;
+  static_assert(AF4 >= 1 && BF4 >= 1, "tile too small for 256 threads");
+
+  __shared__ __attribute__((aligned(16))) float As[2][BM * LDA];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BSZ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int split = blockIdx.z;
+  const int64_t kbeg = (int64_t)split * p.ksplit;
+  const int64_t kend = min(p.Kc, kbeg + p.ksplit);
+  const int hl = lane >> 5, l32 = lane & 31;
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  f32x4 ra[AF4], rb[BF4];
+
+  // A side: rows m, contraction contiguous.
+  auto load_a = [&](const float* src, int64_t ld, int64_t k0, int64_t klim, float mul,
+                    const float* cn, const float* cd) {
+#pragma unroll
+    for (int q = 0; q < AF4; ++q) {
+      const int f = tid + 256 * q;
+      const int row = f >> 3, c4 = f & 7;
+      const int64_t gm = m0 + row, gk = k0 + 4 * c4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (gm < p.M && gk < klim) {
+        v = *reinterpret_cast<const f32x4*>(src + gm * ld + gk);
+        if (cn) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= cn[gk + e] / cd[gk + e];
+        }
+        v *= mul;
+      }
+      ra[q] = v;
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < AF4; ++q) {
+      const int f = tid + 256 * q;
+      const int row = f >> 3, c4 = f & 7;
+      *reinterpret_cast<f32x4*>(&As[buf][row * LDA + 4 * c4]) = ra[q];
+    }
+  };
+  // B side.  fwd: rows n, contraction contiguous.  dx: rows = contraction.
+  auto load_b = [&](const float* src, int64_t ld, int64_t k0, int64_t klim) {
+#pragma unroll
+    for (int q = 0; q < BF4; ++q) {
+      const int f = tid + 256 * q;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (FWD) {
+        const int row = f >> 3, c4 = f & 7;
+        const int64_t gn = n0 + row, gk = k0 + 4 * c4;
+        if (gn < p.Nc && gk < klim) v = *reinterpret_cast<const f32x4*>(src + gn * ld + gk);
+      } else {
+        const int row = f / (BN / 4), c4 = f % (BN / 4);
+        const int64_t gk = k0 + row, gn = n0 + 4 * c4;
+        if (gk < klim && gn < p.Nc) v = *reinterpret_cast<const f32x4*>(src + gk * ld + gn);
+      }
+      rb[q] = v;
+    }
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < BF4; ++q) {
+      const int f = tid + 256 * q;
+      if (FWD) {
+        const int row = f >> 3, c4 = f & 7;
+        *reinterpret_cast<f32x4*>(&Bs[buf][row * LDB + 4 * c4]) = rb[q];
+      } else {
+        const int row = f / (BN / 4), c4 = f % (BN / 4);
+        *reinterpret_cast<f32x4*>(&Bs[buf][row * LDB + 4 * c4]) = rb[q];
+      }
+    }
+  };
+  auto compute = [&](int buf) {
+    f32x4 av[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        av[i][q] = *reinterpret_cast<const f32x4*>(
+            &As[buf][(wm0 + i * 32 + l32) * LDA + 16 * hl + 4 * q]);
+    if (FWD) {
+      f32x4 bv[NI][4];
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bv[j][q] = *reinterpret_cast<const f32x4*>(
+              &Bs[buf][(wn0 + j * 32 + l32) * LDB + 16 * hl + 4 * q]);
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = mfma32x32x2(av[i][s >> 2][s & 3], bv[j][s >> 2][s & 3], acc[i][j]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        float bv[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) bv[j] = Bs[buf][(16 * hl + s) * LDB + wn0 + j * 32 + l32];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = mfma32x32x2(av[i][s >> 2][s & 3], bv[j], acc[i][j]);
+      }
+    }
+  };
+  // Unpipelined contraction over the LoRA rank (r <= 128: at most 4 steps).
+  auto lora_contraction = [&]() {
+    for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
+      load_a(p.XA, p.r, k0, p.r, p.xs, nullptr, nullptr);
+      load_b(p.XB, FWD ? p.r : p.Nc, k0, p.r);
+      __syncthreads();
+      store_a(0);
+      store_b(0);
+      __syncthreads();
+      compute(0);
+    }
+    __syncthreads();
+  };
+
+  if (!FWD && split == 0 && p.r > 0) {
+    lora_contraction();
+    if (p.drop.on) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
+          const uint64_t rk = drop_row(p.drop, gm);
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int64_t gn = n0 + wn0 + j * 32 + l32;
+            acc[i][j][v] *= drop_mul(p.drop, rk, gn);
+          }
+        }
+    }
+  }
+
+  // Main contraction over [kbeg, kend), double buffered.
+  const int64_t nk = (kend - kbeg + BK - 1) / BK;
+  if (nk > 0) {
+    load_a(p.A, p.lda, kbeg, kend, 1.0f, p.acn, p.acd);
+    load_b(p.B, p.ldb, kbeg, kend);
+    store_a(0);
+    store_b(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const int cur = (int)(kt & 1);
+      if (kt + 1 < nk) {
+        load_a(p.A, p.lda, kbeg + (kt + 1) * BK, kend, 1.0f, p.acn, p.acd);
+        load_b(p.B, p.ldb, kbeg + (kt + 1) * BK, kend);
+      }
+      compute(cur);
+      if (kt + 1 < nk) {
+        store_a(cur ^ 1);
+        store_b(cur ^ 1);
+      }
+      __syncthreads();
+    }
+  }
+
+  if (FWD && split == 0 && p.r > 0) lora_contraction();
+
+  // Epilogue.
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t gn = n0 + wn0 + j * 32 + l32;
+      if (gn >= p.Nc) continue;
+      float c = 1.0f;
+      if (p.nsplit == 1 && p.cn) c = p.cn[gn] / p.cd[gn];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
+        if (gm >= p.M) continue;
+        const float x = acc[i][j][v];
+        if (p.nsplit == 1) {
+          p.C[gm * p.Nc + gn] = x * c;
+          if (p.C2) p.C2[gm * p.Nc + gn] = x;
+        } else {
+          p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
+        }
+      }
+    }
+}
+
+// Sum of split-K partials in split order; optional DoRA column scale.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int nsplit,
+                                                            int64_t M, int64_t Nc, float* C,
+                                                            float* C2, const float* cn,
+                                                            const float* cd) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t total = M * Nc;
+  if (i4 >= total) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + i4);
+  for (int q = 1; q < nsplit; ++q) s += *reinterpret_cast<const f32x4*>(part + q * total + i4);
+  if (C2) *reinterpret_cast<f32x4*>(C2 + i4) = s;
+  if (cn) {
+    const int64_t n = i4 % Nc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] *= cn[n + e] / cd[n + e];
+  }
+  *reinterpret_cast<f32x4*>(C + i4) = s;
+}
+
+}  // namespace lora

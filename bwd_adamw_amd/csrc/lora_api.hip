@@ -1,0 +1,503 @@
+// liblora: C-ABI entry points (include/lora.h) over the gfx950 kernels.
+//
+// Every entry point validates all arguments before enqueueing anything,
+// plans its launches from the shapes alone (so equal shapes always give the
+// same split structure and bitwise-equal results), carves split partials out
+// of the caller's workspace and enqueues on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/lora.h"
+#include "common.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_f32.hpp"
+#include "optim.hpp"
+#include "skinny.hpp"
+
+using namespace lora;
+
+namespace {
+
+// --------------------------------------------------------------- helpers ---
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline int64_t clampi(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+uint64_t host_mix(uint64_t z) {   // SplitMix64 output function (see common.hpp)
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+bool drop_valid(const lora_dropout* d) {
+  if (!d) return true;
+  return d->p >= 0.0f && d->p < 1.0f;   // rejects NaN as well
+}
+
+DropParams make_drop(const lora_dropout* d) {
+  DropParams dp;
+  dp.base = 0;
+  dp.thr = 0;
+  dp.keep = 1.0f;
+  dp.on = 0;
+  if (!d || d->p == 0.0f) return dp;
+  uint64_t h = host_mix(d->seed);
+  h = host_mix(h ^ (uint64_t)d->step);
+  h = host_mix(h ^ (uint64_t)(int64_t)d->ordinal);
+  h = host_mix(h ^ (uint64_t)(int64_t)d->layer);
+  h = host_mix(h ^ (uint64_t)(int64_t)d->proj);
+  dp.base = h;
+  dp.thr = (uint32_t)nearbyint((double)d->p * 16777216.0);   // ties to even
+  dp.keep = (float)(1.0 / (1.0 - (double)d->p));
+  dp.on = 1;
+  return dp;
+}
+
+int rank_pad(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
+
+// ------------------------------------------------------------- planning ---
+struct Split {
+  int64_t len;   // contraction (or row) length per split
+  int n;         // number of splits
+};
+
+// Split a length L into n pieces of a multiple of `q`, aiming for `want`
+// blocks in total given `other` blocks along the other axis.
+Split plan_split(int64_t L, int64_t other, int64_t want, int64_t q, int64_t min_len) {
+  int64_t n = clampi(cdiv(want, other), 1, std::max<int64_t>(1, L / min_len));
+  int64_t len = rup(cdiv(L, n), q);
+  return {len, (int)cdiv(L, len)};
+}
+
+struct GemmPlan {
+  int bm, bn;
+  Split k;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16) {
+  GemmPlan g;
+  if (bf16) {
+    g.bm = g.bn = 128;
+    const int64_t tiles = cdiv(M, 128) * cdiv(Nc, 128);
+    g.k = plan_split(Kc, tiles, 256, 64, 512);
+  } else {
+    const int64_t t128 = cdiv(M, 128) * cdiv(Nc, 128);
+    if (t128 >= 256) {
+      g.bm = g.bn = 128;
+      g.k = {rup(Kc, 32), 1};
+    } else {
+      g.bm = g.bn = 64;
+      const int64_t tiles = cdiv(M, 64) * cdiv(Nc, 64);
+      g.k = plan_split(Kc, tiles, 256, 32, 256);
+    }
+  }
+  return g;
+}
+
+// Workspace layout of one linear (forward and backward share the buffer).
+struct Layout {
+  Split down, k3, k4;
+  GemmPlan gf, gd;
+  size_t upart, xbf, gfpart;                        // forward
+  size_t vpart, v, dbpart, dmpart, gbf, gdpart, dapart;  // backward
+  size_t fwd_bytes, bwd_bytes;
+};
+
+size_t carve(size_t& off, size_t bytes) {
+  const size_t at = off;
+  off += (bytes + 255) & ~size_t(255);
+  return at;
+}
+
+Layout make_layout(const lora_linear* L) {
+  Layout y;
+  const int64_t T = L->tokens, K = L->in_dim, N = L->out_dim, r = L->rank;
+  const bool bf = L->w_dtype == LORA_BF16;
+  y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, 256);
+  y.k3 = plan_split(T, cdiv(N, SK_C), 512, SK_T, SK_T);
+  y.k4 = plan_split(T, cdiv(K, SK_C), 512, SK_T, SK_T);
+  y.gf = plan_gemm(T, N, K, bf);
+  y.gd = plan_gemm(T, K, N, bf);
+  size_t off = 0;
+  y.upart = carve(off, sizeof(float) * y.down.n * T * r);
+  y.xbf = carve(off, bf ? sizeof(uint16_t) * T * K : 0);
+  y.gfpart = carve(off, y.gf.k.n > 1 ? sizeof(float) * y.gf.k.n * T * N : 0);
+  y.fwd_bytes = off;
+  off = 0;
+  y.vpart = carve(off, sizeof(float) * cdiv(N, SK_C) * T * r);
+  y.v = carve(off, sizeof(float) * T * r);
+  y.dbpart = carve(off, sizeof(float) * y.k3.n * N * r);
+  y.dmpart = carve(off, (L->dora_mag ? sizeof(float) * y.k3.n * N : 0));
+  y.gbf = carve(off, bf ? sizeof(uint16_t) * T * N : 0);
+  y.gdpart = carve(off, y.gd.k.n > 1 ? sizeof(float) * y.gd.k.n * T * K : 0);
+  y.dapart = carve(off, sizeof(float) * y.k4.n * r * K);
+  y.bwd_bytes = off;
+  return y;
+}
+
+int check_linear(const lora_linear* L) {
+  if (!L) return LORA_E_INVALID;
+  if (L->tokens <= 0 || L->in_dim <= 0 || L->out_dim <= 0 || L->rank <= 0) return LORA_E_SHAPE;
+  if (L->rank > 128 || L->rank > L->in_dim || L->rank > L->out_dim) return LORA_E_SHAPE;
+  if (L->w_dtype != LORA_F32 && L->w_dtype != LORA_BF16) return LORA_E_DTYPE;
+  const int64_t q = L->w_dtype == LORA_BF16 ? 8 : 4;
+  if (L->in_dim % q || L->out_dim % q || L->rank % 4) return LORA_E_ALIGN;
+  if (!L->W || !L->A || !L->B) return LORA_E_INVALID;
+  if (!al16(L->W) || !al16(L->A) || !al16(L->B)) return LORA_E_ALIGN;
+  if ((L->dora_mag == nullptr) != (L->dora_norm == nullptr)) return LORA_E_INVALID;
+  if (!std::isfinite(L->scale)) return LORA_E_INVALID;
+  return LORA_OK;
+}
+
+int hip_status() { return hipGetLastError() == hipSuccess ? LORA_OK : LORA_E_HIP; }
+
+// ----------------------------------------------------------- launchers ---
+template <int RP>
+void launch_down(const float* X, int64_t T, int64_t K, const float* A, int64_t r,
+                 const DropParams& d, Split s, float* Upart, uint16_t* Xbf, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)s.n);
+  down_kernel<RP><<<grid, 256, 0, st>>>(X, T, K, A, r, d, s.len, Upart, Xbf);
+}
+template <int RP>
+void launch_k3(const float* dY, int64_t T, int64_t N, const float* B, const float* U, int64_t r,
+               const float* mag, const float* nrm, const float* Z, Split s, float* Vpart,
+               float* dBpart, float* dmpart, uint16_t* gbf, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(N, SK_C), (unsigned)s.n);
+  k3_kernel<RP><<<grid, 256, 0, st>>>(dY, T, N, B, U, r, mag, nrm, Z, s.len, Vpart, dBpart,
+                                      dmpart, gbf);
+}
+template <int RP>
+void launch_k4(const float* X, int64_t T, int64_t K, const float* V, int64_t r,
+               const DropParams& d, Split s, float* dApart, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)s.n);
+  k4_kernel<RP><<<grid, 256, 0, st>>>(X, T, K, V, r, d, s.len, dApart);
+}
+
+#define LORA_RP_DISPATCH(rp, call)      \
+  switch (rp) {                         \
+    case 16: { constexpr int RP = 16; call; } break;  \
+    case 32: { constexpr int RP = 32; call; } break;  \
+    case 64: { constexpr int RP = 64; call; } break;  \
+    default: { constexpr int RP = 128; call; } break; \
+  }
+
+void launch_reduce(const RedJob* jobs, int n, hipStream_t st) {
+  RedJobs J;
+  memset(&J, 0, sizeof(J));
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    J.job[i] = jobs[i];
+    J.blk[i] = blocks;
+    blocks += cdiv(jobs[i].n, 256);
+  }
+  J.blk[n] = blocks;
+  J.njobs = n;
+  if (blocks > 0) reduce_kernel<<<(unsigned)blocks, 256, 0, st>>>(J);
+}
+
+void launch_gemm_f32(const GemmPlan& g, bool fwd, GemmF32Args a, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
+  if (g.bm == 128) {
+    if (fwd) gemm_f32_kernel<128, 128, true><<<grid, 256, 0, st>>>(a);
+    else gemm_f32_kernel<128, 128, false><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (fwd) gemm_f32_kernel<64, 64, true><<<grid, 256, 0, st>>>(a);
+    else gemm_f32_kernel<64, 64, false><<<grid, 256, 0, st>>>(a);
+  }
+}
+
+void launch_gemm_bf16(const GemmPlan& g, bool fwd, GemmBf16Args a, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
+  if (fwd) gemm_bf16_kernel<128, 128, true><<<grid, 256, 0, st>>>(a);
+  else gemm_bf16_kernel<128, 128, false><<<grid, 256, 0, st>>>(a);
+}
+
+void launch_splitk_reduce(const float* part, int nsplit, int64_t M, int64_t Nc, float* C,
+                          float* C2, const float* cn, const float* cd, hipStream_t st) {
+  const int64_t n4 = cdiv(M * Nc, 4);
+  splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(part, nsplit, M, Nc, C, C2, cn, cd);
+}
+
+}  // namespace
+
+// =========================================================================
+extern "C" {
+
+const char* lora_status_string(int s) {
+  switch (s) {
+    case LORA_OK: return "ok";
+    case LORA_E_INVALID: return "invalid argument";
+    case LORA_E_SHAPE: return "invalid shape";
+    case LORA_E_DTYPE: return "unsupported dtype";
+    case LORA_E_ALIGN: return "misaligned pointer or dimension";
+    case LORA_E_WORKSPACE: return "workspace missing or too small";
+    case LORA_E_NONFINITE: return "non-finite gradient: update vetoed";
+    case LORA_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+double lora_scaling(double alpha, int64_t rank, int rslora) {
+  if (rank <= 0) return NAN;
+  return rslora ? alpha / sqrt((double)rank) : alpha / (double)rank;
+}
+
+double lora_lr_at(int64_t k, double lr, int schedule, int64_t warmup, int64_t total,
+                  double lr_min) {
+  if (schedule == 0) return lr;
+  if (schedule != 1 || k < 0) return NAN;
+  if (k < warmup) return lr * (double)(k + 1) / (double)warmup;
+  const int64_t span = total - warmup > 1 ? total - warmup : 1;
+  double prog = (double)(k - warmup) / (double)span;
+  if (prog > 1.0) prog = 1.0;
+  return lr_min + 0.5 * (lr - lr_min) * (1.0 + cos(M_PI * prog));
+}
+
+size_t lora_workspace_bytes(const lora_linear* lin) {
+  if (check_linear(lin) != LORA_OK) return 0;
+  const Layout y = make_layout(lin);
+  return y.fwd_bytes > y.bwd_bytes ? y.fwd_bytes : y.bwd_bytes;
+}
+
+int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U, float* Z,
+                 const lora_dropout* drop, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_linear(lin);
+  if (rc) return rc;
+  if (!X || !Y || !U) return LORA_E_INVALID;
+  if (!al16(X) || !al16(Y) || !al16(U) || (Z && !al16(Z))) return LORA_E_ALIGN;
+  if (!drop_valid(drop)) return LORA_E_INVALID;
+  const Layout y = make_layout(lin);
+  if (!ws || ws_bytes < y.fwd_bytes || !al16(ws)) return LORA_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
+  const bool bf = lin->w_dtype == LORA_BF16;
+  char* w = (char*)ws;
+  float* Upart = (float*)(w + y.upart);
+  uint16_t* Xbf = bf ? (uint16_t*)(w + y.xbf) : nullptr;
+  const DropParams d = make_drop(drop);
+
+  // U = X~ A^T (split over K), then the fixed-order sum into U.
+  LORA_RP_DISPATCH(rank_pad(r), launch_down<RP>(X, T, K, lin->A, r, d, y.down, Upart, Xbf, st));
+  RedJob ju = {Upart, U, nullptr, T * r, 1, y.down.n, 0, 1.0f};
+  launch_reduce(&ju, 1, st);
+
+  // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
+  float* gpart = y.gf.k.n > 1 ? (float*)(w + y.gfpart) : nullptr;
+  float* C2 = Z;   // Z is written whenever the caller passes it
+  if (bf) {
+    GemmBf16Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = Xbf; a.lda = K; a.B = (const uint16_t*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = N; a.Kc = K;
+    a.XA = U; a.XB = lin->B; a.r = r; a.xs = lin->scale;
+    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
+    a.C = Y; a.C2 = C2; a.cn = lin->dora_mag; a.cd = lin->dora_norm; a.part = gpart;
+    launch_gemm_bf16(y.gf, true, a, st);
+  } else {
+    GemmF32Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = N; a.Kc = K;
+    a.XA = U; a.XB = lin->B; a.r = r; a.xs = lin->scale;
+    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
+    a.C = Y; a.C2 = C2; a.cn = lin->dora_mag; a.cd = lin->dora_norm; a.part = gpart;
+    launch_gemm_f32(y.gf, true, a, st);
+  }
+  if (y.gf.k.n > 1)
+    launch_splitk_reduce(gpart, y.gf.k.n, T, N, Y, C2, lin->dora_mag, lin->dora_norm, st);
+  return hip_status();
+}
+
+int lora_backward(const lora_linear* lin, const float* X, const float* dY, const float* U,
+                  const float* Z, float* dX, float* dA, float* dB, float* dMag,
+                  int accumulate, const lora_dropout* drop, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int rc = check_linear(lin);
+  if (rc) return rc;
+  if (!X || !dY || !U || !dA || !dB) return LORA_E_INVALID;
+  if (!al16(X) || !al16(dY) || !al16(U) || !al16(dA) || !al16(dB)) return LORA_E_ALIGN;
+  if ((dX && !al16(dX)) || (Z && !al16(Z)) || (dMag && !al16(dMag))) return LORA_E_ALIGN;
+  const bool dora = lin->dora_mag != nullptr;
+  if (dMag && (!dora || !Z)) return LORA_E_INVALID;
+  if (!drop_valid(drop)) return LORA_E_INVALID;
+  const Layout y = make_layout(lin);
+  if (!ws || ws_bytes < y.bwd_bytes || !al16(ws)) return LORA_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
+  const bool bf = lin->w_dtype == LORA_BF16;
+  char* w = (char*)ws;
+  float* Vpart = (float*)(w + y.vpart);
+  float* V = (float*)(w + y.v);
+  float* dBpart = (float*)(w + y.dbpart);
+  float* dmpart = dMag ? (float*)(w + y.dmpart) : nullptr;
+  uint16_t* gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
+  float* dApart = (float*)(w + y.dapart);
+  const DropParams d = make_drop(drop);
+  const int rp = rank_pad(r);
+
+  // One pass over dY: V partials, dB partials, DoRA dm partials, bf16 g.
+  LORA_RP_DISPATCH(rp, launch_k3<RP>(dY, T, N, lin->B, U, r, lin->dora_mag, lin->dora_norm,
+                                     dMag ? Z : nullptr, y.k3, Vpart, dBpart, dmpart, gbf, st));
+  RedJob jv = {Vpart, V, nullptr, T * r, 1, (int)cdiv(N, SK_C), 0, 1.0f};
+  launch_reduce(&jv, 1, st);
+
+  if (dX) {
+    float* gpart = y.gd.k.n > 1 ? (float*)(w + y.gdpart) : nullptr;
+    if (bf) {
+      GemmBf16Args a;
+      memset(&a, 0, sizeof(a));
+      a.A = gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
+      a.M = T; a.Nc = K; a.Kc = N;
+      a.XA = V; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
+      a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
+      a.C = dX; a.part = gpart;
+      launch_gemm_bf16(y.gd, false, a, st);
+    } else {
+      GemmF32Args a;
+      memset(&a, 0, sizeof(a));
+      a.A = dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
+      a.B = (const float*)lin->W; a.ldb = K;
+      a.M = T; a.Nc = K; a.Kc = N;
+      a.XA = V; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
+      a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
+      a.C = dX; a.part = gpart;
+      launch_gemm_f32(y.gd, false, a, st);
+    }
+    if (y.gd.k.n > 1) launch_splitk_reduce(gpart, y.gd.k.n, T, K, dX, nullptr, nullptr, nullptr, st);
+  }
+
+  LORA_RP_DISPATCH(rp, launch_k4<RP>(X, T, K, V, r, d, y.k4, dApart, st));
+
+  RedJob jobs[3];
+  int nj = 0;
+  const int acc = accumulate ? 1 : 0;
+  jobs[nj++] = {dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
+  jobs[nj++] = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
+  if (dMag) jobs[nj++] = {dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
+  launch_reduce(jobs, nj, st);
+  return hip_status();
+}
+
+size_t lora_grad_prepare_workspace_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  return 4096 + 1024 * (sizeof(double) + sizeof(int)) + 256;
+}
+
+int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, float max_norm,
+                      float* d_scale, double* d_stats, double* h_norm, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!grads || !d_scale || n <= 0 || n_pred_tokens <= 0) return LORA_E_INVALID;
+  if (!(max_norm >= 0.0f) || !std::isfinite(max_norm)) return LORA_E_INVALID;
+  if (!al16(grads)) return LORA_E_ALIGN;
+  if (!ws || !al16(ws) || ws_bytes < lora_grad_prepare_workspace_bytes(n)) return LORA_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nb0 = clampi(cdiv(n, 8192), 1, 1024);
+  const int64_t per = rup(cdiv(n, nb0), 1024);
+  const int nb = (int)cdiv(n, per);
+  char* w = (char*)ws;
+  double* norm_out = (double*)w;                // {norm, clip}
+  double* part = (double*)(w + 256);
+  int* flags = (int*)(w + 256 + 1024 * sizeof(double));
+  gradnorm_pass1<<<nb, 256, 0, st>>>(grads, n, per, part, flags);
+  gradnorm_pass2<<<1, 256, 0, st>>>(part, flags, nb, n_pred_tokens, max_norm, d_scale, d_stats,
+                                    norm_out);
+  if (hip_status()) return LORA_E_HIP;
+  if (h_norm) {
+    double host[2];
+    if (hipMemcpyAsync(host, norm_out, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess)
+      return LORA_E_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LORA_E_HIP;
+    *h_norm = host[0];
+    if (std::isnan(host[0])) return LORA_E_NONFINITE;
+  }
+  return LORA_OK;
+}
+
+int lora_adamw_step(float* params, const float* grads, float* m, float* v,
+                    const lora_segment* segs, int n_seg, const lora_adamw_hparams* hp,
+                    const float* d_scale, void* stream) {
+  if (!params || !grads || !m || !v || !segs || !hp || !d_scale) return LORA_E_INVALID;
+  if (n_seg < 1 || n_seg > ADAM_MAX_SEG) return LORA_E_INVALID;
+  if (!al16(params) || !al16(grads) || !al16(m) || !al16(v)) return LORA_E_ALIGN;
+  if (!(hp->lr >= 0.0f) || !std::isfinite(hp->lr) || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) ||
+      !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !(hp->eps > 0.0f) ||
+      !std::isfinite(hp->weight_decay) || !std::isfinite(hp->plus_ratio) || hp->t < 1)
+    return LORA_E_INVALID;
+  AdamSegs S;
+  memset(&S, 0, sizeof(S));
+  int64_t blocks = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const lora_segment& g = segs[i];
+    if (g.offset < 0 || g.count < 0 || g.kind < 0 || g.kind > 2) return LORA_E_INVALID;
+    if (g.offset % 4 || g.count % 4) return LORA_E_ALIGN;
+    S.off[i] = g.offset;
+    S.cnt[i] = g.count;
+    S.kind[i] = g.kind;
+    S.blk[i] = blocks;
+    blocks += cdiv(g.count, 1024);
+  }
+  S.blk[n_seg] = blocks;
+  S.n = n_seg;
+  AdamHp H;
+  H.lr = hp->lr;
+  H.b1 = hp->beta1;
+  H.b2 = hp->beta2;
+  H.one_m_b1 = (float)(1.0 - (double)hp->beta1);
+  H.one_m_b2 = (float)(1.0 - (double)hp->beta2);
+  H.eps = hp->eps;
+  H.wd = hp->weight_decay;
+  H.ratio = hp->plus_ratio;
+  H.bc1 = (float)(1.0 - pow((double)hp->beta1, (double)hp->t));
+  H.bc2 = (float)(1.0 - pow((double)hp->beta2, (double)hp->t));
+  if (blocks == 0) return LORA_OK;
+  adamw_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(params, grads, m, v, S, H,
+                                                                   d_scale);
+  return hip_status();
+}
+
+int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim, uint8_t* mask,
+                      void* stream) {
+  if (!mask || tokens <= 0 || in_dim <= 0) return LORA_E_INVALID;
+  if (!drop_valid(drop)) return LORA_E_INVALID;
+  const DropParams d = make_drop(drop);
+  const int64_t n = tokens * in_dim;
+  dropout_mask_kernel<<<(unsigned)cdiv(n, 256), 256, 0, (hipStream_t)stream>>>(d, tokens, in_dim,
+                                                                               mask);
+  return hip_status();
+}
+
+int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream) {
+  if (!lin || !out_norm) return LORA_E_INVALID;
+  if (lin->in_dim <= 0 || lin->out_dim <= 0) return LORA_E_SHAPE;
+  if (lin->w_dtype != LORA_F32 && lin->w_dtype != LORA_BF16) return LORA_E_DTYPE;
+  if (!lin->W) return LORA_E_INVALID;
+  if ((lin->A == nullptr) != (lin->B == nullptr)) return LORA_E_INVALID;
+  const bool lora_on = lin->A != nullptr;
+  if (lora_on && (lin->rank <= 0 || lin->rank > 128)) return LORA_E_SHAPE;
+  if (!std::isfinite(lin->scale)) return LORA_E_INVALID;
+  const int64_t N = lin->out_dim, K = lin->in_dim, r = lora_on ? lin->rank : 0;
+  const float* A = lin->A;
+  const float* B = lin->B;
+  const float s = lin->scale;
+  constexpr int ROWS = 8;
+  const unsigned grid = (unsigned)cdiv(N, ROWS);
+  hipStream_t st = (hipStream_t)stream;
+  const int rp = lora_on ? rank_pad(r) : 16;
+  if (lin->w_dtype == LORA_BF16) {
+    const uint16_t* W = (const uint16_t*)lin->W;
+    LORA_RP_DISPATCH(rp, (dora_rownorm_kernel<uint16_t, RP, ROWS><<<grid, 256, 0, st>>>(
+                             W, N, K, A, B, r, s, out_norm)));
+  } else {
+    const float* W = (const float*)lin->W;
+    LORA_RP_DISPATCH(rp, (dora_rownorm_kernel<float, RP, ROWS><<<grid, 256, 0, st>>>(
+                             W, N, K, A, B, r, s, out_norm)));
+  }
+  return hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,215 @@
+// Gradient preparation, AdamW and DoRA row norms.
+//
+// gradnorm_pass1/2 ("4.3. Training Guide", "Gradient clipping"): the sum of
+// squares of the slot's summed gradient in double with a non-finite flag,
+// then one block combines the per-block partials in fixed order and emits
+// the single combined normalisation-and-clip scale.
+//
+// adamw ("4.3. Training Guide", "Optimizer"): decoupled AdamW, weight decay on
+// A only from the pre-update value at the uncorrected rate, B at lr*ratio.
+//
+// dora_rownorm ("8. LoRA Fundamentals", "How it works"): ||W_i + s (B A)_i||.
+#pragma once
+#include "common.hpp"
+
+namespace lora {
+
+LORA_DEV bool finite_bits(float x) { return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u; }
+
+// Pass 1: block b sums squares of g[b*per .. min(n, (b+1)*per)) in double.
+__global__ __launch_bounds__(256) void gradnorm_pass1(const float* __restrict__ g, int64_t n,
+                                                      int64_t per, double* __restrict__ part,
+                                                      int* __restrict__ flags) {
+  __shared__ double ws[4];
+  __shared__ int wf[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = min(n, b0 + per);
+  double s = 0.0;
+  int bad = 0;
+  // per is a multiple of 1024, so b0 is 16-byte aligned.
+  const int64_t full = b0 + ((b1 - b0) / 4) * 4;
+  for (int64_t i = b0 + 4 * tid; i < full; i += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(g + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bad |= !finite_bits(v[e]);
+      s += (double)v[e] * (double)v[e];
+    }
+  }
+  for (int64_t i = full + tid; i < b1; i += 256) {
+    const float x = g[i];
+    bad |= !finite_bits(x);
+    s += (double)x * (double)x;
+  }
+  s = wave_sum(s);
+  bad = __any(bad) ? 1 : 0;
+  if (lane == 0) {
+    ws[wave] = s;
+    wf[wave] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    part[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    flags[blockIdx.x] = wf[0] | wf[1] | wf[2] | wf[3];
+  }
+}
+
+// Pass 2: one block.  norm = sqrt(ss)/npred; clip; scale = float(clip/npred).
+__global__ __launch_bounds__(256) void gradnorm_pass2(const double* __restrict__ part,
+                                                      const int* __restrict__ flags, int nb,
+                                                      int64_t npred, float max_norm,
+                                                      float* __restrict__ d_scale,
+                                                      double* __restrict__ d_stats,
+                                                      double* __restrict__ ws_norm) {
+  __shared__ double ws[4];
+  __shared__ int wf[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double s = 0.0;
+  int bad = 0;
+  for (int i = tid; i < nb; i += 256) {
+    s += part[i];
+    bad |= flags[i];
+  }
+  s = wave_sum(s);
+  bad = __any(bad) ? 1 : 0;
+  if (lane == 0) {
+    ws[wave] = s;
+    wf[wave] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double ss = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    const int nonfinite = wf[0] | wf[1] | wf[2] | wf[3];
+    double norm = sqrt(ss) / (double)npred;
+    double clip = 1.0;
+    const double mn = (double)max_norm;
+    if (mn > 0.0 && norm > mn) clip = mn / norm;
+    float scale = (float)(clip / (double)npred);
+    if (nonfinite) {
+      norm = __builtin_nan("");
+      clip = __builtin_nan("");
+      scale = __builtin_nanf("");
+    }
+    *d_scale = scale;
+    ws_norm[0] = norm;
+    ws_norm[1] = clip;
+    if (d_stats) {
+      d_stats[0] = norm;
+      d_stats[1] = clip;
+    }
+  }
+}
+
+// AdamW over up to 64 segments; block b belongs to the segment whose block
+// range holds b; each thread updates one float4.
+constexpr int ADAM_MAX_SEG = 64;
+struct AdamSegs {
+  int64_t off[ADAM_MAX_SEG];
+  int64_t cnt[ADAM_MAX_SEG];
+  int64_t blk[ADAM_MAX_SEG + 1];
+  int32_t kind[ADAM_MAX_SEG];
+  int n;
+};
+struct AdamHp {
+  float lr, one_m_b1, b1, one_m_b2, b2, eps, wd, ratio, bc1, bc2;
+};
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ P,
+                                                    const float* __restrict__ G,
+                                                    float* __restrict__ Mo, float* __restrict__ Vo,
+                                                    AdamSegs segs, AdamHp hp,
+                                                    const float* __restrict__ d_scale) {
+  const float sc = *d_scale;
+  if (!finite_bits(sc)) return;   // vetoed update: touch nothing
+  const int64_t b = blockIdx.x;
+  int lo = 0, hi = segs.n - 1;
+  while (lo < hi) {   // last segment with blk[s] <= b
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs.blk[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const int64_t e = ((b - segs.blk[s]) * 256 + threadIdx.x) * 4;
+  if (e >= segs.cnt[s]) return;
+  const int64_t i = segs.off[s] + e;
+  const int kind = segs.kind[s];
+  const float rate = kind == 1 ? hp.lr * hp.ratio : hp.lr;
+  const float decay = kind == 0 ? hp.lr * hp.wd : 0.0f;
+  f32x4 p = *reinterpret_cast<const f32x4*>(P + i);
+  const f32x4 g = *reinterpret_cast<const f32x4*>(G + i);
+  f32x4 m = *reinterpret_cast<const f32x4*>(Mo + i);
+  f32x4 v = *reinterpret_cast<const f32x4*>(Vo + i);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float gp = g[q] * sc;
+    m[q] = hp.b1 * m[q] + hp.one_m_b1 * gp;
+    v[q] = hp.b2 * v[q] + hp.one_m_b2 * (gp * gp);
+    const float mh = m[q] / hp.bc1;
+    const float vh = v[q] / hp.bc2;
+    const float upd = mh / (sqrtf(vh) + hp.eps);
+    p[q] = (p[q] - rate * upd) - decay * p[q];
+  }
+  *reinterpret_cast<f32x4*>(P + i) = p;
+  *reinterpret_cast<f32x4*>(Mo + i) = m;
+  *reinterpret_cast<f32x4*>(Vo + i) = v;
+}
+
+// DoRA row norms: block handles ROWS rows; B rows staged in LDS; each thread
+// walks columns k = tid, tid+256, ...; the rank contraction runs in chunks of
+// 16; squares accumulate in float per thread and combine in double per row.
+template <typename WT, int RP, int ROWS>
+__global__ __launch_bounds__(256) void dora_rownorm_kernel(const WT* __restrict__ W, int64_t N,
+                                                           int64_t K, const float* __restrict__ A,
+                                                           const float* __restrict__ B, int64_t r,
+                                                           float s, float* __restrict__ out) {
+  __shared__ float Bsh[ROWS * RP];
+  __shared__ double red[4][ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = (int64_t)blockIdx.x * ROWS;
+  const bool lora = A != nullptr;
+  if (lora)
+    for (int i = tid; i < ROWS * RP; i += 256) {
+      const int row = i / RP, j = i % RP;
+      Bsh[i] = (j < r && i0 + row < N) ? B[(i0 + row) * r + j] : 0.f;
+    }
+  __syncthreads();
+  float sq[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) sq[i] = 0.f;
+  for (int64_t k = tid; k < K; k += 256) {
+    float d[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) d[i] = 0.f;
+    if (lora) {
+#pragma unroll 1
+      for (int jc = 0; jc < RP; jc += 16) {
+        float a[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) a[jj] = (jc + jj) < r ? A[(int64_t)(jc + jj) * K + k] : 0.f;
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) d[i] += Bsh[i * RP + jc + jj] * a[jj];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      if (i0 + i >= N) continue;
+      float w;
+      if constexpr (sizeof(WT) == 2) w = bf16_bits_to_f32(W[(i0 + i) * K + k]);
+      else w = W[(i0 + i) * K + k];
+      w += s * d[i];
+      sq[i] += w * w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const double t = wave_sum((double)sq[i]);
+    if (lane == 0) red[wave][i] = t;
+  }
+  __syncthreads();
+  if (tid < ROWS && i0 + tid < N)
+    out[i0 + tid] = (float)sqrt(((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
+}
+
+}  // namespace lora

@@ -1,0 +1,224 @@
+"""Thin ctypes binding of liblora (include/lora.h).
+
+Argument marshalling only: every function here checks tensor placement and
+dtype, turns tensors into device pointers and calls the C entry point of the
+same name.  All computation happens in the HIP kernels behind the C ABI.
+There is no fallback: if liblora.so is missing or the device is not a GPU,
+the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "LoraError", "lib", "LoraLinear", "LoraDropout", "LoraSegment", "LoraAdamwHparams",
+    "F32", "BF16", "KIND_A", "KIND_B", "KIND_MAG",
+    "lora_workspace_bytes", "lora_forward", "lora_backward",
+    "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
+    "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
+    "lora_status_string", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
+
+F32, BF16 = 0, 1
+KIND_A, KIND_B, KIND_MAG = 0, 1, 2
+LORA_E_NONFINITE = -6
+
+# Every symbol include/lora.h declares.
+EXPORTS = (
+    "lora_workspace_bytes", "lora_forward", "lora_backward",
+    "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
+    "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
+    "lora_status_string",
+)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lora_status_string(status)} (status {status})")
+
+
+class LoraDropout(C.Structure):
+    _fields_ = [("seed", C.c_uint64), ("step", C.c_int64), ("ordinal", C.c_int32),
+                ("layer", C.c_int32), ("proj", C.c_int32), ("p", C.c_float)]
+
+
+class LoraLinear(C.Structure):
+    _fields_ = [("tokens", C.c_int64), ("in_dim", C.c_int64), ("out_dim", C.c_int64),
+                ("rank", C.c_int64), ("w_dtype", C.c_int32), ("scale", C.c_float),
+                ("W", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p),
+                ("dora_mag", C.c_void_p), ("dora_norm", C.c_void_p)]
+
+
+class LoraSegment(C.Structure):
+    _fields_ = [("offset", C.c_int64), ("count", C.c_int64), ("kind", C.c_int32)]
+
+
+class LoraAdamwHparams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float),
+                ("eps", C.c_float), ("weight_decay", C.c_float), ("plus_ratio", C.c_float),
+                ("t", C.c_int64)]
+
+
+_LIB = None
+
+
+def lib() -> C.CDLL:
+    """Load liblora.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bwd_adamw_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I64, I32, F, SZ = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t
+        sig = {
+            "lora_workspace_bytes": (SZ, [P]),
+            "lora_forward": (I32, [P, P, P, P, P, P, P, SZ, P]),
+            "lora_backward": (I32, [P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
+            "lora_grad_prepare_workspace_bytes": (SZ, [I64]),
+            "lora_grad_prepare": (I32, [P, I64, I64, F, P, P, P, P, SZ, P]),
+            "lora_adamw_step": (I32, [P, P, P, P, P, I32, P, P, P]),
+            "lora_dropout_mask": (I32, [P, I64, I64, P, P]),
+            "lora_dora_row_norms": (I32, [P, P, P]),
+            "lora_scaling": (C.c_double, [C.c_double, I64, I32]),
+            "lora_lr_at": (C.c_double, [I64, C.c_double, I32, I64, I64, C.c_double]),
+            "lora_status_string": (C.c_char_p, [I32]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t, name, dtype=torch.float32):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise LoraError(fn, rc)
+
+
+def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None) -> LoraLinear:
+    """Descriptor of one adapted linear: W [N,K] (float32 or bfloat16),
+    A [r,K], B [N,r] float32, optional DoRA magnitude and norm [N]."""
+    if W.dtype == torch.float32:
+        wd = F32
+    elif W.dtype == torch.bfloat16:
+        wd = BF16
+    else:
+        raise TypeError(f"W must be float32 or bfloat16, got {W.dtype}")
+    N, K = W.shape
+    r = A.shape[0] if A is not None else 0
+    return LoraLinear(int(tokens), int(K), int(N), int(r), wd, float(scale),
+                      _ptr(W, "W", None), _ptr(A, "A"), _ptr(B, "B"),
+                      _ptr(dora_mag, "dora_mag"), _ptr(dora_norm, "dora_norm"))
+
+
+def make_dropout(seed, step, ordinal, layer, proj, p) -> LoraDropout:
+    return LoraDropout(int(seed), int(step), int(ordinal), int(layer), int(proj), float(p))
+
+
+def _ref(s):
+    return None if s is None else C.byref(s)
+
+
+# ------------------------------------------------------------ entry points
+def lora_status_string(status: int) -> str:
+    return lib().lora_status_string(int(status)).decode()
+
+
+def lora_scaling(alpha: float, rank: int, rslora: bool = False) -> float:
+    return lib().lora_scaling(float(alpha), int(rank), 1 if rslora else 0)
+
+
+def lora_lr_at(k: int, lr: float, schedule: int = 0, warmup: int = 0, total: int = 100,
+               lr_min: float = 0.0) -> float:
+    return lib().lora_lr_at(int(k), float(lr), int(schedule), int(warmup), int(total), float(lr_min))
+
+
+def lora_workspace_bytes(lin: LoraLinear) -> int:
+    return int(lib().lora_workspace_bytes(C.byref(lin)))
+
+
+def lora_forward(lin, X, Y, U, Z=None, drop=None, ws=None, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_forward(C.byref(lin), _ptr(X, "X"), _ptr(Y, "Y"), _ptr(U, "U"), _ptr(Z, "Z"),
+                            _ref(drop), _ptr(ws, "ws", None), ws_bytes, _stream(stream))
+    _check("lora_forward", rc)
+
+
+def lora_backward(lin, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=False, drop=None,
+                  ws=None, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_backward(C.byref(lin), _ptr(X, "X"), _ptr(dY, "dY"), _ptr(U, "U"),
+                             _ptr(Z, "Z"), _ptr(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
+                             _ptr(dMag, "dMag"), 1 if accumulate else 0, _ref(drop),
+                             _ptr(ws, "ws", None), ws_bytes, _stream(stream))
+    _check("lora_backward", rc)
+
+
+def lora_grad_prepare_workspace_bytes(n: int) -> int:
+    return int(lib().lora_grad_prepare_workspace_bytes(int(n)))
+
+
+def lora_grad_prepare(grads, n_pred_tokens, max_norm, d_scale, d_stats=None, sync=True,
+                      ws=None, stream=None):
+    """Returns the norm (host float) when sync is True, else None.  A vetoed
+    (non-finite) update raises LoraError with status LORA_E_NONFINITE when
+    sync is True; otherwise the veto travels in d_scale (NaN)."""
+    n = grads.numel()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    h = C.c_double(0.0)
+    rc = lib().lora_grad_prepare(_ptr(grads, "grads"), n, int(n_pred_tokens), float(max_norm),
+                                 _ptr(d_scale, "d_scale"), _ptr(d_stats, "d_stats", torch.float64),
+                                 C.byref(h) if sync else None, _ptr(ws, "ws", None), ws_bytes,
+                                 _stream(stream))
+    _check("lora_grad_prepare", rc)
+    return h.value if sync else None
+
+
+def lora_adamw_step(params, grads, m, v, segments, hp: LoraAdamwHparams, d_scale, stream=None):
+    segs = (LoraSegment * len(segments))(*[LoraSegment(int(o), int(c), int(k)) for o, c, k in segments])
+    rc = lib().lora_adamw_step(_ptr(params, "params"), _ptr(grads, "grads"), _ptr(m, "m"),
+                               _ptr(v, "v"), segs, len(segments), C.byref(hp),
+                               _ptr(d_scale, "d_scale"), _stream(stream))
+    _check("lora_adamw_step", rc)
+
+
+def lora_dropout_mask(drop: LoraDropout, tokens, in_dim, mask, stream=None):
+    rc = lib().lora_dropout_mask(C.byref(drop), int(tokens), int(in_dim),
+                                 _ptr(mask, "mask", torch.uint8), _stream(stream))
+    _check("lora_dropout_mask", rc)
+
+
+def lora_dora_row_norms(lin: LoraLinear, out_norm, stream=None):
+    rc = lib().lora_dora_row_norms(C.byref(lin), _ptr(out_norm, "out_norm"), _stream(stream))
+    _check("lora_dora_row_norms", rc)

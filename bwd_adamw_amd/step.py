@@ -1,0 +1,199 @@
+"""One optimizer update of LoRA adapter slots, sequenced through liblora.
+
+Order of one update of a slot ("4.3. Training Guide", "Gradient
+accumulation"; "8. LoRA Fundamentals", "The training loop"):
+
+  for each accumulation chunk g:
+      forward of every adapted linear, layers 0..L-1
+      backward of every adapted linear, layers L-1..0 (gradients summed
+      into the slot's arena; chunk 0 overwrites, later chunks add)
+  prepare: global norm in double, non-finite veto, one combined scale
+  AdamW over the arena (A decayed, B at lr*ratio, DoRA magnitude)
+  DoRA: refresh the detached row norms with the updated A, B
+
+Each slot ("Multi-LoRA Training Example (fully-async)", "Design") owns its
+arena, moments, update counter and dropout seed; slots share only W.
+
+Memory layout of a slot: one float32 arena per role (params, grads, Adam m,
+Adam v), each laid out as [all A | all B | all DoRA magnitudes] in the
+linears' (layer, projection) order, so AdamW sees three segments.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import lora as L
+from .workloads import LoraConfig
+
+__all__ = ["FrozenModel", "Slot", "Trainer"]
+
+
+class FrozenModel:
+    """The frozen weights of every adapted linear, keyed (layer, proj ordinal)."""
+
+    def __init__(self, cfg: LoraConfig, weights: dict):
+        self.cfg = cfg
+        self.W = weights
+        self.keys = sorted(weights)
+        self.shape = {}
+        for key in self.keys:
+            N, K = weights[key].shape
+            self.shape[key] = (int(K), int(N))
+
+
+class Slot:
+    """Trainable state of one adapter slot (params, grads, moments, counters)."""
+
+    def __init__(self, cfg: LoraConfig, model: FrozenModel, A: dict, B: dict, seed: int,
+                 device="cuda"):
+        self.cfg = cfg
+        self.seed = int(seed)
+        self.keys = model.keys
+        r = cfg.rank
+        sizes_a = [r * model.shape[k][0] for k in self.keys]
+        sizes_b = [model.shape[k][1] * r for k in self.keys]
+        sizes_m = [model.shape[k][1] for k in self.keys] if cfg.dora else []
+        na, nb, nm = sum(sizes_a), sum(sizes_b), sum(sizes_m)
+        self.n = na + nb + nm
+        self.segments = [(0, na, L.KIND_A), (na, nb, L.KIND_B)]
+        if cfg.dora:
+            self.segments.append((na + nb, nm, L.KIND_MAG))
+        f32 = dict(device=device, dtype=torch.float32)
+        self.params = torch.zeros(self.n, **f32)
+        self.grads = torch.zeros(self.n, **f32)
+        self.m = torch.zeros(self.n, **f32)
+        self.v = torch.zeros(self.n, **f32)
+        self.A, self.B, self.mag, self.gA, self.gB, self.gmag = {}, {}, {}, {}, {}, {}
+        oa, ob, om = 0, na, na + nb
+        for i, key in enumerate(self.keys):
+            K, N = model.shape[key]
+            self.A[key] = self.params[oa:oa + r * K].view(r, K)
+            self.gA[key] = self.grads[oa:oa + r * K].view(r, K)
+            self.B[key] = self.params[ob:ob + N * r].view(N, r)
+            self.gB[key] = self.grads[ob:ob + N * r].view(N, r)
+            self.A[key].copy_(A[key])
+            self.B[key].copy_(B[key])
+            oa += r * K
+            ob += N * r
+            if cfg.dora:
+                self.mag[key] = self.params[om:om + N]
+                self.gmag[key] = self.grads[om:om + N]
+                om += N
+        self.norm = {}
+        self.t = 0   # applied updates
+        self.k = 0   # 0-based index of the next update (schedule, dropout step)
+
+
+@dataclass
+class StepStats:
+    norm: float
+    vetoed: bool
+    lr: float
+
+
+class Trainer:
+    """Runs optimizer updates of slots over one frozen model on one stream."""
+
+    def __init__(self, cfg: LoraConfig, model: FrozenModel, tokens=None, device="cuda"):
+        self.cfg = cfg
+        self.model = model
+        self.T = cfg.tokens if tokens is None else int(tokens)
+        self.scale = L.lora_scaling(cfg.alpha, cfg.rank, cfg.scaling == "rslora")
+        self.device = device
+        f32 = dict(device=device, dtype=torch.float32)
+        r = cfg.rank
+        ws = 0
+        self.U, self.Z, self.Y, self.dX = {}, {}, {}, {}
+        for key in model.keys:
+            K, N = model.shape[key]
+            lin = self._linear(key, None, dora=cfg.dora)
+            ws = max(ws, L.lora_workspace_bytes(lin))
+            self.U[key] = torch.empty(self.T, r, **f32)
+            self.Y[key] = torch.empty(self.T, N, **f32)
+            self.dX[key] = torch.empty(self.T, K, **f32)
+            if cfg.dora:
+                self.Z[key] = torch.empty(self.T, N, **f32)
+        self.ws = torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
+        self.d_scale = torch.zeros(1, **f32)
+        self.d_stats = torch.zeros(2, device=device, dtype=torch.float64)
+        self.prep_ws = None
+
+    # ------------------------------------------------------------------
+    def _linear(self, key, slot, dora=False, norms_only=False):
+        W = self.model.W[key]
+        K, N = self.model.shape[key]
+        r = self.cfg.rank
+        if slot is None:   # shape-only descriptor for workspace sizing (never launched)
+            aligned = 256
+            return L.LoraLinear(self.T, K, N, r, L.BF16 if W.dtype == torch.bfloat16 else L.F32,
+                                float(self.scale), W.data_ptr(), aligned, aligned,
+                                aligned if dora else None, aligned if dora else None)
+        mag = slot.mag.get(key) if dora else None
+        nrm = slot.norm.get(key) if dora else None
+        return L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T, mag, nrm)
+
+    def init_dora(self, slot: Slot):
+        """Magnitude = ||W_i|| rows, then the detached norms of W + s B A."""
+        for key in self.model.keys:
+            W = self.model.W[key]
+            K, N = self.model.shape[key]
+            wd = L.BF16 if W.dtype == torch.bfloat16 else L.F32
+            bare = L.LoraLinear(self.T, K, N, 0, wd, float(self.scale), W.data_ptr(),
+                                None, None, None, None)
+            L.lora_dora_row_norms(bare, slot.mag[key])
+            slot.norm[key] = torch.empty(N, device=self.device, dtype=torch.float32)
+        self.refresh_dora(slot)
+
+    def refresh_dora(self, slot: Slot):
+        for key in self.model.keys:
+            W = self.model.W[key]
+            lin = L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T)
+            L.lora_dora_row_norms(lin, slot.norm[key])
+
+    # ------------------------------------------------------------------
+    def forward_backward(self, slot: Slot, chunks: list):
+        cfg = self.cfg
+        keys = self.model.keys
+        p = float(cfg.dropout)
+        for g, chunk in enumerate(chunks):
+            lins = {}
+            for key in keys:   # layers 0..L-1
+                X, _ = chunk[key]
+                lin = self._linear(key, slot, dora=cfg.dora)
+                lins[key] = lin
+                drop = L.make_dropout(slot.seed, slot.k, g, key[0], key[1], p) if p > 0 else None
+                L.lora_forward(lin, X, self.Y[key], self.U[key], self.Z.get(key), drop, self.ws)
+            for key in reversed(keys):   # layers L-1..0
+                X, dY = chunk[key]
+                drop = L.make_dropout(slot.seed, slot.k, g, key[0], key[1], p) if p > 0 else None
+                L.lora_backward(lins[key], X, dY, self.U[key], self.Z.get(key), self.dX[key],
+                                slot.gA[key], slot.gB[key], slot.gmag.get(key),
+                                accumulate=g > 0, drop=drop, ws=self.ws)
+
+    def step(self, slot: Slot, chunks: list, sync: bool = True) -> StepStats:
+        cfg = self.cfg
+        self.forward_backward(slot, chunks)
+        if self.prep_ws is None or self.prep_ws.numel() < L.lora_grad_prepare_workspace_bytes(slot.n):
+            self.prep_ws = torch.empty(L.lora_grad_prepare_workspace_bytes(slot.n),
+                                       device=self.device, dtype=torch.uint8)
+        n_pred = self.T * len(chunks)
+        lr = L.lora_lr_at(slot.k, cfg.lr, 1 if cfg.schedule == "cosine" else 0, cfg.warmup,
+                          cfg.total_updates, cfg.lr_min)
+        try:
+            norm = L.lora_grad_prepare(slot.grads, n_pred, cfg.max_norm, self.d_scale,
+                                       self.d_stats, sync=sync, ws=self.prep_ws)
+        except L.LoraError as e:
+            if e.status == L.LORA_E_NONFINITE:
+                return StepStats(float("nan"), True, lr)
+            raise
+        hp = L.LoraAdamwHparams(lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay,
+                                cfg.plus_ratio, slot.t + 1)
+        L.lora_adamw_step(slot.params, slot.grads, slot.m, slot.v, slot.segments, hp, self.d_scale)
+        if cfg.dora:
+            self.refresh_dora(slot)
+        slot.t += 1
+        slot.k += 1
+        return StepStats(norm if norm is not None else float("nan"), False, lr)

@@ -1,0 +1,203 @@
+/*
+ * lora.h -- C ABI of liblora: the LoRA-linear training hot path on one
+ * MI355X (gfx950) GPU.
+ *
+ * The adapted linear, its backward and its optimizer step follow
+ *   - "8. LoRA Fundamentals: The Math and the Architecture Support Matrix"
+ *     (Juno documentation), sections "How it works", "The training loop" and
+ *     "Training decisions";
+ *   - "4.3. Training Guide" (Juno documentation), sections "Gradient
+ *     accumulation", "Optimizer", "Schedules", "Dropout", "Gradient clipping";
+ *   - "Backward Bug Hunts and Vulkan Tiled GEMM: Pi-Train LoRA SFT
+ *     Hardening", section "Bug #1" (the frozen weight is read in its native
+ *     layout; no transposed copy is ever made);
+ *   - "Multi-LoRA Training Example (fully-async)", section "Design (decoupled
+ *     per-adapter optimizers)" (one independent optimizer state per slot).
+ *
+ * Conventions for every entry point
+ *   - Layout is row-major and contiguous: X [T,K], W [N,K] (out x in, the
+ *     native layout), A [r,K], B [N,r], U = X~ A^T [T,r], Y, Z, dY [T,N],
+ *     dX [T,K].  T = tokens of one chunk, K = in_dim, N = out_dim, r = rank.
+ *   - Every pointer except those documented as host pointers is a device
+ *     pointer, 16-byte aligned, owned by the caller.  The library never
+ *     allocates or frees memory; scratch comes from a caller workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; the one host synchronisation in the library is in
+ *     lora_grad_prepare when `h_norm` is not NULL.
+ *   - Every argument is validated before anything is enqueued.  On a negative
+ *     status no buffer has been touched.  HIP launch failures return
+ *     LORA_E_HIP.  No exceptions cross the ABI; there is no global mutable
+ *     state, so calls on different streams may run concurrently as long as
+ *     their buffers do not overlap.
+ *   - Results are deterministic: every reduction runs in a fixed order (no
+ *     floating-point atomics), so equal inputs give bitwise equal outputs.
+ */
+#ifndef LORA_H
+#define LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_E_INVALID = -1,    /* NULL pointer, bad enum, out-of-range scalar   */
+  LORA_E_SHAPE = -2,      /* non-positive dim, rank > min(K,N) or > 128     */
+  LORA_E_DTYPE = -3,      /* unsupported frozen-weight dtype                */
+  LORA_E_ALIGN = -4,      /* pointer not 16-byte aligned, or K/N/r/segment
+                             sizes not multiples of 4 (K/N of 8 for bf16)  */
+  LORA_E_WORKSPACE = -5,  /* workspace NULL or smaller than required        */
+  LORA_E_NONFINITE = -6,  /* NaN/Inf gradient: the update is vetoed         */
+  LORA_E_HIP = -7         /* a HIP runtime call failed                      */
+} lora_status;
+
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* Train-only inverted dropout on the LoRA-branch input ("4.3. Training
+ * Guide", "Dropout"): a stateless hash of (seed, optimizer step,
+ * accumulation ordinal, layer, projection, token row, feature column).
+ * Element (t,k) is kept when the top 24 bits of the hash are
+ * >= round(p * 2^24); kept values are multiplied by float(1/(1-p)).
+ * The hash is SplitMix64's output function chained over the keys in the
+ * order seed, step, ordinal, layer, proj, t, k.  p == 0 (or a NULL
+ * descriptor) turns dropout off.  Requires 0 <= p < 1. */
+typedef struct lora_dropout {
+  uint64_t seed;
+  int64_t step;      /* 0-based index of the optimizer update being built  */
+  int32_t ordinal;   /* accumulation chunk index within the update         */
+  int32_t layer;
+  int32_t proj;      /* projection ordinal: wq..wdown = 0..6               */
+  float p;
+} lora_dropout;
+
+/* One adapted linear ("8. LoRA Fundamentals", "How it works"):
+ *   Y = X W^T + scale * (X~ A^T) B^T,   X~ = X masked by dropout.
+ * DoRA (same section): when dora_mag and dora_norm are both non-NULL, the
+ * output column n is multiplied by dora_mag[n] / dora_norm[n]; the norm is a
+ * detached input (see lora_dora_row_norms).
+ * Constraints: tokens, in_dim, out_dim > 0; in_dim and out_dim multiples of 4
+ * (of 8 for bf16 W); rank a multiple of 4 with rank <= min(in_dim, out_dim,
+ * 128).  W is float32 or bf16.  Any T is accepted (ragged tails are masked). */
+typedef struct lora_linear {
+  int64_t tokens, in_dim, out_dim, rank;
+  int32_t w_dtype;          /* lora_dtype                                  */
+  float scale;              /* alpha/rank or alpha/sqrt(rank)              */
+  const void* W;            /* [N,K] float32 or bf16                       */
+  const float* A;           /* [r,K]                                       */
+  const float* B;           /* [N,r]                                       */
+  const float* dora_mag;    /* [N] or NULL                                 */
+  const float* dora_norm;   /* [N] or NULL                                 */
+} lora_linear;
+
+/* A run of parameters in the optimizer arena. kind 0 = LoRA A (decayed,
+ * rate lr), 1 = LoRA B (never decayed, rate lr * plus_ratio), 2 = DoRA
+ * magnitude (never decayed, rate lr). */
+typedef struct lora_segment {
+  int64_t offset, count;
+  int32_t kind;
+} lora_segment;
+
+/* AdamW hyper-parameters of one update ("4.3. Training Guide", "Optimizer").
+ * lr is the already-scheduled rate of this update; t is the 1-based count of
+ * applied updates of the slot including this one. */
+typedef struct lora_adamw_hparams {
+  float lr, beta1, beta2, eps, weight_decay, plus_ratio;
+  int64_t t;
+} lora_adamw_hparams;
+
+/* Bytes of workspace that lora_forward and lora_backward need for `lin`
+ * (split-contraction partials).  Returns 0 when `lin` is invalid. */
+size_t lora_workspace_bytes(const lora_linear* lin);
+
+/* Forward of one chunk ("8. LoRA Fundamentals", "How it works"):
+ *   U = X~ A^T  [T,r]  (saved for the backward)
+ *   Z = X W^T + scale * U B^T  [T,N]
+ *   Y = Z, or Y = (dora_mag/dora_norm) * Z per column for DoRA.
+ * Z may be NULL; DoRA callers pass it (the backward needs it).  Y and U are
+ * overwritten.  `drop` may be NULL.  ws must hold lora_workspace_bytes(lin). */
+int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U,
+                 float* Z, const lora_dropout* drop, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Backward of one chunk ("8. LoRA Fundamentals", "Training decisions" and
+ * "The training loop"; "Backward Bug Hunts ...", "Bug #1").  With g = dY, or
+ * for DoRA g = dY * dora_mag/dora_norm (the norm is detached):
+ *   V   = g B                                   [T,r]
+ *   dX  = g W + scale * (V A) * mask * keep     [T,K]  overwritten
+ *   dB (+)= scale * g^T U                       [N,r]
+ *   dA (+)= scale * V^T X~                      [r,K]
+ *   dMag (+)= sum_t dY * Z / dora_norm          [N]    (DoRA, may be NULL)
+ * accumulate != 0 adds into dA/dB/dMag (gradient accumulation over the
+ * chunks of one update); accumulate == 0 overwrites them (first chunk).
+ * W is read in its native [N,K] layout.  dX may be NULL (not computed).
+ * U is the forward's U of the same chunk; Z is required when dMag is given.
+ * The mask is recomputed from `drop`, which must equal the forward's. */
+int lora_backward(const lora_linear* lin, const float* X, const float* dY,
+                  const float* U, const float* Z, float* dX, float* dA,
+                  float* dB, float* dMag, int accumulate,
+                  const lora_dropout* drop, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Workspace bytes lora_grad_prepare needs for n gradient elements. */
+size_t lora_grad_prepare_workspace_bytes(int64_t n);
+
+/* Prepare the summed gradients of one slot ("4.3. Training Guide",
+ * "Gradient clipping" and "Gradient accumulation").  Pass 1: sum of squares
+ * in double and a non-finite flag, per block.  Pass 2 (one block, fixed
+ * order): norm = sqrt(ss)/n_pred_tokens; clip = max_norm/norm when
+ * max_norm > 0 and norm > max_norm, else 1; writes the combined scale
+ * *d_scale = float(clip/n_pred_tokens), or NaN when any gradient is
+ * non-finite.  `grads` is not modified (the scale is applied on load by
+ * lora_adamw_step).  If h_norm (host) is not NULL the call waits for the
+ * stream, stores the norm (NaN on veto) and returns LORA_E_NONFINITE on a
+ * veto; with h_norm NULL nothing waits and the veto travels in *d_scale.
+ * d_stats (device, may be NULL) receives {norm, clip} as doubles. */
+int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens,
+                      float max_norm, float* d_scale, double* d_stats,
+                      double* h_norm, void* ws, size_t ws_bytes, void* stream);
+
+/* Decoupled AdamW over the arena segments ("4.3. Training Guide",
+ * "Optimizer"; "8. LoRA Fundamentals", "The training loop"):
+ *   g' = grads * (*d_scale)
+ *   m = b1 m + (1-b1) g';  v = b2 v + (1-b2) g'^2
+ *   p -= rate * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps)
+ *   A only: p -= lr * weight_decay * p_old
+ * rate = lr (A, magnitude) or lr * plus_ratio (B).  When *d_scale is not
+ * finite (a vetoed update) no element is changed.  `segs` is a host array
+ * of n_seg (1..64) non-overlapping segments. */
+int lora_adamw_step(float* params, const float* grads, float* m, float* v,
+                    const lora_segment* segs, int n_seg,
+                    const lora_adamw_hparams* hp, const float* d_scale,
+                    void* stream);
+
+/* Writes the dropout keep mask [tokens, in_dim] (1 = keep) of `drop`: the
+ * same decisions lora_forward and lora_backward take inline. */
+int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim,
+                      uint8_t* mask, void* stream);
+
+/* DoRA row norms ("8. LoRA Fundamentals", "How it works"):
+ * out_norm[i] = || W_i + scale * (B A)_i ||_2 over the K inputs.  With
+ * lin->A == lin->B == NULL it gives ||W_i|| (the magnitude initialisation).
+ * lin->tokens is ignored. */
+int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream);
+
+/* Host helpers. */
+/* alpha/rank, or alpha/sqrt(rank) when rslora != 0 ("How it works"). */
+double lora_scaling(double alpha, int64_t rank, int rslora);
+/* Learning rate of the 0-based update k ("4.3. Training Guide",
+ * "Schedules"): schedule 0 = constant lr; 1 = warmup-cosine: lr*(k+1)/warmup
+ * for k < warmup, then lr_min + (lr-lr_min)(1+cos(pi*min(1,(k-warmup)/
+ * max(1,total-warmup))))/2. */
+double lora_lr_at(int64_t k, double lr, int schedule, int64_t warmup,
+                  int64_t total, double lr_min);
+/* Static message for a status code. */
+const char* lora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_H */

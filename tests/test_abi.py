@@ -1,0 +1,111 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/lora.h declares, rejects invalid arguments before touching a device,
+and its host helpers agree with the oracle."""
+
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import oracle as O
+from bwd_adamw_amd import lora as L
+
+# The validation tests below pass placeholder pointers; they must only ever
+# run where no GPU exists, so that a validation bug cannot launch a kernel.
+no_device = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="placeholder-pointer tests run only on GPU-less hosts")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lora.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    declared = _declared()
+    assert len(declared) >= 11
+    assert sorted(L.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert L.lora_status_string(0) == "ok"
+    assert "vetoed" in L.lora_status_string(-6)
+    assert L.lora_status_string(12345) == "unknown status"
+
+
+def test_scaling_matches_oracle():
+    for alpha, r, mode in ((8, 4, "standard"), (16, 8, "standard"), (32, 32, "rslora"), (64, 64, "standard")):
+        assert L.lora_scaling(alpha, r, mode == "rslora") == pytest.approx(O.scaling(alpha, r, mode), rel=1e-15)
+
+
+@pytest.mark.parametrize("k", list(range(0, 12)) + [40, 55, 99, 100, 150])
+def test_lr_schedule_matches_oracle(k):
+    got = L.lora_lr_at(k, 1e-4, 1, 10, 100, 1e-6)
+    ref = O.lr_at(k, 1e-4, "cosine", 10, 100, 1e-6)
+    assert got == pytest.approx(ref, rel=1e-14, abs=1e-20)
+    assert L.lora_lr_at(k, 3e-4, 0) == 3e-4
+
+
+def _lin(**kw):
+    d = dict(tokens=8, in_dim=16, out_dim=16, rank=4, w_dtype=L.F32, scale=2.0, W=256, A=256, B=256,
+             dora_mag=None, dora_norm=None)
+    d.update(kw)
+    return L.LoraLinear(**d)
+
+
+@no_device
+@pytest.mark.parametrize("kw,status", [
+    (dict(tokens=0), -2), (dict(in_dim=-4), -2), (dict(rank=0), -2), (dict(rank=132), -2),
+    (dict(rank=32), -2), (dict(w_dtype=7), -3), (dict(in_dim=18), -4), (dict(rank=6), -4),
+    (dict(W=None), -1), (dict(A=264), -4), (dict(dora_mag=256), -1),
+    (dict(w_dtype=L.BF16, in_dim=20), -4),
+])
+def test_invalid_descriptor_is_rejected_before_any_launch(kw, status):
+    lin = _lin(**kw)
+    assert L.lib().lora_workspace_bytes(C.byref(lin)) == 0
+    rc = L.lib().lora_forward(C.byref(lin), 256, 256, 256, None, None, 256, 1 << 20, None)
+    assert rc == status
+
+
+@no_device
+def test_workspace_and_dropout_validation():
+    lin = _lin()
+    need = L.lib().lora_workspace_bytes(C.byref(lin))
+    assert need > 0
+    assert L.lib().lora_forward(C.byref(lin), 256, 256, 256, None, None, 256, 16, None) == -5
+    assert L.lib().lora_forward(C.byref(lin), 256, 256, 256, None, None, None, need, None) == -5
+    bad = L.make_dropout(1, 0, 0, 0, 0, 1.0)
+    assert L.lib().lora_forward(C.byref(lin), 256, 256, 256, None, C.byref(bad), 256, need, None) == -1
+    nan = L.make_dropout(1, 0, 0, 0, 0, math.nan)
+    assert L.lib().lora_dropout_mask(C.byref(nan), 4, 4, 256, None) == -1
+    # backward: dMag without DoRA, misaligned outputs
+    assert L.lib().lora_backward(C.byref(lin), 256, 256, 256, 256, 256, 256, 256, 256, 0, None,
+                                 256, need, None) == -1
+    assert L.lib().lora_backward(C.byref(lin), 256, 256, 256, None, 260, 256, 256, None, 0, None,
+                                 256, need, None) == -4
+
+
+@no_device
+def test_optimizer_entry_validation():
+    lib = L.lib()
+    hp = L.LoraAdamwHparams(1e-4, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    seg = (L.LoraSegment * 1)(L.LoraSegment(0, 6, 0))
+    assert lib.lora_adamw_step(256, 256, 256, 256, seg, 1, C.byref(hp), 256, None) == -4
+    seg = (L.LoraSegment * 1)(L.LoraSegment(0, 8, 5))
+    assert lib.lora_adamw_step(256, 256, 256, 256, seg, 1, C.byref(hp), 256, None) == -1
+    assert lib.lora_adamw_step(256, 256, 256, 256, seg, 0, C.byref(hp), 256, None) == -1
+    hp0 = L.LoraAdamwHparams(1e-4, 0.9, 0.999, 1e-8, 0.01, 1.0, 0)
+    seg = (L.LoraSegment * 1)(L.LoraSegment(0, 8, 0))
+    assert lib.lora_adamw_step(256, 256, 256, 256, seg, 1, C.byref(hp0), 256, None) == -1
+    assert lib.lora_grad_prepare(256, 10, 0, 1.0, 256, None, None, 256, 1 << 16, None) == -1
+    assert lib.lora_grad_prepare(256, 10, 4, -1.0, 256, None, None, 256, 1 << 16, None) == -1
+    assert lib.lora_grad_prepare(256, 10, 4, 1.0, 256, None, None, 256, 16, None) == -5

@@ -1,0 +1,438 @@
+"""GPU parity: every C-ABI entry point against the float64 CPU oracle on the
+same seeded inputs.
+
+Bars: dropout masks bit-exact; float32-W paths max|gpu-ref|/max|ref| <= 1e-4;
+bf16-W paths <= 2e-2 (the frozen products round X and dY to bf16 for MFMA).
+"""
+
+import hashlib
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bwd_adamw_amd import lora as L
+from bwd_adamw_amd import step as S
+from bwd_adamw_amd import workloads as WL
+from tests.helpers import np64, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------- inputs ----
+def _linear_case(T, K, N, r, w_dtype="f32", seed=0, x_std=1.0, dy_std=1.0, b_std=0.01,
+                 device="cpu"):
+    key = lambda kind, c=0: (900 + seed, 0, 0, 0, c, kind)
+    W = WL.draw((N, K), key("W"), "normal", 0.02, device)
+    out = {}
+    if w_dtype == "bf16":
+        out["Wq"] = W.to(torch.bfloat16)
+        W = out["Wq"].float()
+    else:
+        out["Wq"] = W
+    out["W"] = W
+    out["A"] = WL.draw((r, K), key("A"), "uniform", 1 / math.sqrt(K), device)
+    out["B"] = WL.draw((N, r), key("B"), "normal", b_std, device)
+    out["X"] = WL.draw((T, K), key("X"), "normal", x_std, device)
+    out["dY"] = WL.draw((T, N), key("dY"), "normal", dy_std, device)
+    return out
+
+
+def _gpu(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+def _run_gpu(c, s, p=0.0, dkeys=(1234, 0, 0, 0, 0), dora=False, accumulate=False):
+    g = _gpu(c)
+    T, K = g["X"].shape
+    N = g["W"].shape[0]
+    r = g["A"].shape[0]
+    mag = nrm = None
+    if dora:
+        mag = torch.empty(N, device=DEV)
+        nrm = torch.empty(N, device=DEV)
+        bare = L.make_linear(g["Wq"], None, None, s, T)
+        L.lora_dora_row_norms(bare, mag)
+        L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], s, T), nrm)
+    lin = L.make_linear(g["Wq"], g["A"], g["B"], s, T, mag, nrm)
+    ws = torch.empty(L.lora_workspace_bytes(lin), device=DEV, dtype=torch.uint8)
+    drop = L.make_dropout(*dkeys, p) if p > 0 else None
+    nanf = float("nan")
+    Y = torch.full((T, N), nanf, device=DEV)
+    U = torch.full((T, r), nanf, device=DEV)
+    Z = torch.full((T, N), nanf, device=DEV) if dora else None
+    L.lora_forward(lin, g["X"], Y, U, Z, drop, ws)
+    dX = torch.full((T, K), nanf, device=DEV)
+    dA = torch.full((r, K), nanf, device=DEV)
+    dB = torch.full((N, r), nanf, device=DEV)
+    dm = torch.full((N,), nanf, device=DEV) if dora else None
+    L.lora_backward(lin, g["X"], g["dY"], U, Z, dX, dA, dB, dm, False, drop, ws)
+    torch.cuda.synchronize()
+    return dict(Y=Y, U=U, Z=Z, dX=dX, dA=dA, dB=dB, dmag=dm, mag=mag, norm=nrm, lin=lin, ws=ws, g=g)
+
+
+def _oracle(c, s, p=0.0, dkeys=(1234, 0, 0, 0, 0), mag=None, nrm=None):
+    X, W, A, B, dY = (np64(c[k]) for k in ("X", "W", "A", "B", "dY"))
+    T, K = X.shape
+    keep, ks = None, 1.0
+    if p > 0:
+        keep = O.dropout_keep(*dkeys, T, K, p)
+        ks = O.dropout_scale(p)
+    Y, U, Z = O.forward(X, W, A, B, s, keep, ks, mag, nrm)
+    gr = O.backward(X, dY, W, A, B, s, U, keep, ks, mag, nrm, Z)
+    return dict(Y=Y, U=U, Z=Z, **gr)
+
+
+# ------------------------------------------------------------- dropout -----
+@pytest.mark.parametrize("T,K,p,keys", [
+    (33, 72, 0.05, (1234, 0, 0, 0, 0)),
+    (128, 2048, 0.05, (1234, 3, 2, 21, 2)),
+    (64, 2560, 0.1, (1235, 7, 1, 35, 6)),
+    (1, 4, 0.5, (0, 0, 0, 0, 0)),
+    (17, 9728, 0.1, (2**63 + 11, 2**40, 1, 5, 4)),
+])
+def test_dropout_mask_bit_exact(T, K, p, keys):
+    _say("dropout", T, K, p, keys)
+    mask = torch.full((T, K), 7, device=DEV, dtype=torch.uint8)
+    L.lora_dropout_mask(L.make_dropout(*keys, p), T, K, mask)
+    got = mask.cpu().numpy().astype(bool)
+    ref = O.dropout_keep(*keys, T, K, p)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------- per-linear fwd / bwd ----
+LINEAR_CASES = [
+    # name, T, K, N, r, w dtype, scale, dropout p, dora, x_std, dy_std
+    ("single-64x64", 32, 64, 64, 4, "f32", 2.0, 0.0, False, 1.0, 1.0),
+    ("ragged-f32", 37, 84, 100, 8, "f32", 2.0, 0.1, False, 1.0, 1.0),
+    ("ragged-f32-dora", 37, 84, 100, 8, "f32", 1.5, 0.1, True, 1.0, 1.0),
+    ("ragged-f32-r128", 70, 132, 136, 128, "f32", 0.5, 0.0, False, 1.0, 1.0),
+    ("tinyllama-wq", 128, 2048, 2048, 8, "f32", 2.0, 0.05, False, 1.0, 1e-2),
+    ("tinyllama-wv", 128, 2048, 256, 8, "f32", 2.0, 0.05, False, 1.0, 1e-2),
+    ("wide-4096", 1536, 4096, 4096, 16, "f32", 2.0, 0.0, False, 1.0, 1.0),
+    ("ragged-bf16", 70, 136, 264, 32, "bf16", math.sqrt(32), 0.1, False, 1.0, 1e-2),
+    ("ragged-bf16-dora", 129, 264, 136, 64, "bf16", 1.0, 0.1, True, 1.0, 1e-2),
+    ("qwen-wq-slice", 256, 2560, 4096, 32, "bf16", math.sqrt(32), 0.0, False, 1.0, 1e-2),
+    ("qwen-wdown-slice", 256, 9728, 2560, 32, "bf16", math.sqrt(32), 0.0, False, 1.0, 1e-2),
+    ("qwen-dora-wgate-slice", 256, 2560, 9728, 64, "bf16", 1.0, 0.1, True, 1.0, 1e-2),
+]
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=[c[0] for c in LINEAR_CASES])
+def test_linear_forward_backward_parity(case):
+    name, T, K, N, r, wd, s, p, dora, xs, dys = case
+    _say("linear", name)
+    c = _linear_case(T, K, N, r, wd, seed=zlib.crc32(name.encode()) % 1000, x_std=xs, dy_std=dys)
+    dk = (1234, 2, 1, 3, 4)
+    got = _run_gpu(c, s, p, dk, dora)
+    mag = np64(got["mag"]) if dora else None
+    nrm = np64(got["norm"]) if dora else None
+    ref = _oracle(c, s, p, dk, mag, nrm)
+    tol = TOL[wd]
+    names = ["Y", "U", "dX", "dA", "dB"] + (["Z", "dmag"] if dora else [])
+    for n in names:
+        e = rel_err(got[n], ref[n])
+        _say(f"  {n}: rel err {e:.3e}")
+        assert torch.isfinite(got[n]).all(), f"{n} has unwritten (NaN) elements"
+        assert e <= tol, (n, e)
+
+
+def test_backward_accumulates_over_chunks():
+    T, K, N, r = 64, 128, 96, 8
+    c1 = _linear_case(T, K, N, r, seed=1)
+    c2 = dict(c1)
+    c2["X"] = WL.draw((T, K), (77, 0, 0, 0, 1, "X"), "normal", 1.0)
+    c2["dY"] = WL.draw((T, N), (77, 0, 0, 0, 1, "dY"), "normal", 1.0)
+    g1, g2 = _gpu(c1), _gpu(c2)
+    lin = L.make_linear(g1["Wq"], g1["A"], g1["B"], 2.0, T)
+    ws = torch.empty(L.lora_workspace_bytes(lin), device=DEV, dtype=torch.uint8)
+    dA = torch.full((r, K), float("nan"), device=DEV)
+    dB = torch.full((N, r), float("nan"), device=DEV)
+    for i, g in enumerate((g1, g2)):
+        Y = torch.empty(T, N, device=DEV)
+        U = torch.empty(T, r, device=DEV)
+        L.lora_forward(lin, g["X"], Y, U, None, None, ws)
+        L.lora_backward(lin, g["X"], g["dY"], U, None, None, dA, dB, None, i > 0, None, ws)
+    r1, r2 = _oracle(c1, 2.0), _oracle(c2, 2.0)
+    assert rel_err(dA, r1["dA"] + r2["dA"]) <= 1e-4
+    assert rel_err(dB, r1["dB"] + r2["dB"]) <= 1e-4
+
+
+def test_zero_adapter_gives_exact_zero_dA_and_frozen_output():
+    T, K, N, r = 96, 256, 192, 16
+    c = _linear_case(T, K, N, r, seed=5)
+    c["B"] = torch.zeros_like(c["B"])
+    got = _run_gpu(c, 2.0, 0.1)
+    assert torch.count_nonzero(got["dA"]).item() == 0
+    frozen = np64(c["X"]) @ np64(c["W"]).T
+    assert rel_err(got["Y"], frozen) <= 1e-5
+
+
+def test_adjointness_of_frozen_products_on_gpu():
+    """<X W^T, V> == <X, V W>: pins the native-layout dX GEMM to the forward."""
+    T, K, N, r = 160, 384, 320, 8
+    c = _linear_case(T, K, N, r, seed=6)
+    c["B"] = torch.zeros_like(c["B"])
+    got = _run_gpu(c, 1.0)
+    lhs = float((np64(got["Y"]) * np64(c["dY"])).sum())
+    rhs = float((np64(c["X"]) * np64(got["dX"])).sum())
+    assert abs(lhs - rhs) <= 1e-5 * (np.abs(np64(got["Y"])).sum() + 1.0)
+
+
+def test_linear_outputs_are_deterministic():
+    c = _linear_case(200, 512, 384, 16, seed=7)
+    a = _run_gpu(c, 2.0, 0.1)
+    b = _run_gpu(c, 2.0, 0.1)
+    for n in ("Y", "U", "dX", "dA", "dB"):
+        assert torch.equal(a[n], b[n]), n
+
+
+# --------------------------------------------- full-size, sampled outputs --
+FULL_CASES = [
+    # workload, projection index, rows sampled
+    (4, 0, 48), (4, 6, 48), (5, 4, 32),
+]
+
+
+@pytest.mark.parametrize("wl,pi,rows", FULL_CASES, ids=[f"wl{a}-p{b}" for a, b, _ in FULL_CASES])
+def test_full_size_linear_sampled(wl, pi, rows):
+    """Full workload shape in the launch plan the bench uses; Y and dX are
+    checked on sampled rows, U, dA, dB (and dm) in full."""
+    cfg = WL.get_config(wl)
+    proj = cfg.projections[pi]
+    _say("full-size", cfg.name, proj.name)
+    inp = WL.linear_inputs(cfg, 0, proj, device=DEV, chunks=1)
+    s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
+    c = {"Wq": inp.get("W_bf16", inp["W"]), "W": inp["W"], "A": inp["A"], "B": inp["B"],
+         "X": inp["X"][0], "dY": inp["dY"][0]}
+    p = cfg.dropout
+    dk = (cfg.seeds[0], 0, 0, 0, proj.ordinal)
+    got = _run_gpu(c, s, p, dk, cfg.dora)
+    T = cfg.tokens
+    idx = np.sort(np.random.default_rng(wl * 10 + pi).choice(T, rows, replace=False))
+    X, W, A, B, dY = (np64(c[k]) for k in ("X", "W", "A", "B", "dY"))
+    keep, ks = (O.dropout_keep(*dk, T, proj.in_dim, p), O.dropout_scale(p)) if p > 0 else (None, 1.0)
+    mag = np64(got["mag"]) if cfg.dora else None
+    nrm = np64(got["norm"]) if cfg.dora else None
+    Yr, Ur, Zr = O.forward(X[idx], W, A, B, s, None if keep is None else keep[idx], ks, mag, nrm)
+    tol = TOL[cfg.w_dtype]
+    assert rel_err(np64(got["Y"])[idx], Yr) <= tol
+    # U in full (cheap), then the rank-side gradients in full
+    Xt = X if keep is None else np.where(keep, X * ks, 0.0)
+    U_full = Xt @ A.T
+    assert rel_err(got["U"], U_full) <= 1e-4
+    g = dY * (mag / nrm)[None, :] if cfg.dora else dY
+    V = g @ B
+    assert rel_err(got["dB"], s * (g.T @ U_full)) <= 1e-4
+    assert rel_err(got["dA"], s * (V.T @ Xt)) <= 1e-4
+    lora_rows = s * (V[idx] @ A)
+    if keep is not None:
+        lora_rows = np.where(keep[idx], lora_rows * ks, 0.0)
+    dXr = g[idx] @ W + lora_rows
+    assert rel_err(np64(got["dX"])[idx], dXr) <= tol
+    if cfg.dora:
+        Zfull = np64(got["Z"])
+        assert rel_err(Zfull[idx], Zr) <= tol
+        assert rel_err(got["dmag"], (dY * Zfull).sum(0) / nrm) <= 1e-4
+
+
+# --------------------------------------------------- prepare and AdamW -----
+@pytest.mark.parametrize("n,scale,max_norm,n_pred", [
+    (1, 3.0, 1.0, 1), (1003, 10.0, 1.0, 4), (131072, 1e-3, 1.0, 1536), (1126400, 1.0, 0.0, 512),
+    (5_000_001, 0.5, 2.0, 8),
+])
+def test_grad_prepare_parity(n, scale, max_norm, n_pred):
+    g = WL.draw((n,), (500, 0, 0, 0, n % 97, "dY"), "normal", scale)
+    gd = g.to(DEV)
+    d_scale = torch.zeros(1, device=DEV)
+    stats = torch.zeros(2, device=DEV, dtype=torch.float64)
+    ws = torch.empty(L.lora_grad_prepare_workspace_bytes(n), device=DEV, dtype=torch.uint8)
+    norm = L.lora_grad_prepare(gd, n_pred, max_norm, d_scale, stats, True, ws)
+    ref = O.grad_prepare([np64(g)], n_pred, max_norm)
+    assert norm == pytest.approx(ref["norm"], rel=1e-12)
+    assert d_scale.item() == pytest.approx(ref["scale"], rel=1e-6)
+    assert stats[1].item() == pytest.approx(ref["clip"], rel=1e-12)
+    if ref["clip"] < 1.0:   # clipped: the prepared gradient has norm max_norm
+        assert np.linalg.norm(np64(g) * d_scale.item()) == pytest.approx(max_norm, rel=1e-6)
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), -float("inf")])
+def test_grad_prepare_vetoes_non_finite(bad):
+    g = torch.randn(10000, device=DEV)
+    g[1234] = bad
+    d_scale = torch.zeros(1, device=DEV)
+    ws = torch.empty(L.lora_grad_prepare_workspace_bytes(g.numel()), device=DEV, dtype=torch.uint8)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_grad_prepare(g, 4, 1.0, d_scale, None, True, ws)
+    assert e.value.status == L.LORA_E_NONFINITE
+    assert math.isnan(d_scale.item())
+    # AdamW on a vetoed scale changes nothing
+    p = torch.randn(10000, device=DEV)
+    m = torch.randn(10000, device=DEV)
+    v = torch.rand(10000, device=DEV)
+    before = [x.clone() for x in (p, m, v)]
+    L.lora_adamw_step(p, torch.nan_to_num(g), m, v, [(0, 10000, 0)],
+                      L.LoraAdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.1, 1.0, 3), d_scale)
+    for x, y in zip((p, m, v), before):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("t", [1, 2, 7])
+def test_adamw_parity_on_shared_inputs(t):
+    segs = [(0, 4096, 0), (4096, 1000, 1), (5096, 2000, 2), (7096, 4, 0)]
+    n = 7100
+    p0 = WL.draw((n,), (501, t, 0, 0, 0, "A"), "normal", 0.05)
+    g0 = WL.draw((n,), (501, t, 0, 0, 0, "dY"), "normal", 1.0)
+    m0 = WL.draw((n,), (501, t, 0, 0, 0, "X"), "normal", 0.01) * (t > 1)
+    v0 = WL.draw((n,), (501, t, 0, 0, 0, "B"), "uniform", 1e-4).abs() * (t > 1)
+    c = float(np.float32(0.125))
+    lr, wd, ratio = 2e-4, 0.1, 16.0
+    P, G, M, V = (x.to(DEV) for x in (p0, g0, m0, v0))
+    d_scale = torch.tensor([c], device=DEV)
+    L.lora_adamw_step(P, G, M, V, segs, L.LoraAdamwHparams(lr, 0.9, 0.999, 1e-8, wd, ratio, t), d_scale)
+    kinds = {0: "A", 1: "B", 2: "mag"}
+    for off, cnt, kind in segs:
+        sl = slice(off, off + cnt)
+        pr, mr, vr = O.adamw_update(np64(p0[sl]), np64(g0[sl]), np64(m0[sl]), np64(v0[sl]),
+                                    kinds[kind], lr, t, c, weight_decay=wd, plus_ratio=ratio)
+        assert rel_err(np64(P[sl]) - np64(p0[sl]), pr - np64(p0[sl])) <= 1e-4
+        assert rel_err(M[sl], mr) <= 1e-5
+        assert rel_err(V[sl], vr) <= 1e-5
+
+
+@pytest.mark.parametrize("wd_,N,K,r", [("f32", 100, 84, 8), ("bf16", 264, 136, 64), ("bf16", 2560, 9728, 32)])
+def test_dora_row_norms_parity(wd_, N, K, r):
+    c = _linear_case(8, K, N, r, wd_, seed=11, b_std=0.05)
+    g = _gpu(c)
+    out = torch.empty(N, device=DEV)
+    L.lora_dora_row_norms(L.make_linear(g["Wq"], None, None, 1.0, 8), out)
+    assert rel_err(out, O.dora_row_norms(np64(c["W"]))) <= 1e-5
+    L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], 1.7, 8), out)
+    assert rel_err(out, O.dora_row_norms(np64(c["W"]), np64(c["A"]), np64(c["B"]), 1.7)) <= 1e-5
+
+
+# ------------------------------------------------------ end-to-end steps ---
+def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None):
+    """Run `steps` updates on the GPU and in the oracle from equal inputs;
+    return both states and gradients."""
+    layers = cfg.layers if layers is None else layers
+    T = cfg.tokens if tokens is None else tokens
+    nslots = cfg.slots if slots is None else slots
+    s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
+    W, Wq = {}, {}
+    for l in range(layers):
+        for pj in cfg.projections:
+            inp = WL.linear_inputs(cfg, l, pj, chunks=0, tokens=T)
+            W[(l, pj.ordinal)] = inp["W"]
+            Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"])
+    model = S.FrozenModel(cfg, {k: v.to(DEV) for k, v in Wq.items()})
+    trainer = S.Trainer(cfg, model, tokens=T)
+    results = []
+    for si in range(nslots):
+        A, B, chunks = {}, {}, [dict() for _ in range(cfg.chunks)]
+        for l in range(layers):
+            for pj in cfg.projections:
+                inp = WL.linear_inputs(cfg, l, pj, slot=si, tokens=T)
+                key = (l, pj.ordinal)
+                A[key], B[key] = inp["A"], inp["B"]
+                for g in range(cfg.chunks):
+                    chunks[g][key] = (inp["X"][g], inp["dY"][g])
+        slot = S.Slot(cfg, model, {k: v.to(DEV) for k, v in A.items()},
+                      {k: v.to(DEV) for k, v in B.items()}, cfg.seeds[si])
+        if cfg.dora:
+            trainer.init_dora(slot)
+        ost = O.SlotState(params={k: {"A": np64(A[k]), "B": np64(B[k])} for k in A})
+        if cfg.dora:
+            for k in A:
+                ost.params[k]["mag"] = np64(slot.mag[k])   # ||W_i|| from the shared bf16/f32 W
+                ost.norms[k] = O.dora_row_norms(np64(W[k]), ost.params[k]["A"], ost.params[k]["B"], s)
+        gchunks = [{k: (x.to(DEV), d.to(DEV)) for k, (x, d) in ch.items()} for ch in chunks]
+        ochunks = [{k: (np64(x), np64(d)) for k, (x, d) in ch.items()} for ch in chunks]
+        lin64 = {k: np64(v) for k, v in W.items()}
+        hist = []
+        for it in range(steps):
+            p_before = slot.params.clone()
+            o_before = {k: {n: a.copy() for n, a in v.items()} for k, v in ost.params.items()}
+            st = trainer.step(slot, gchunks)
+            hp = dict(s=s, p=cfg.dropout, seed=cfg.seeds[si], n_pred=T * cfg.chunks,
+                      max_norm=cfg.max_norm,
+                      lr=O.lr_at(ost.k, cfg.lr, cfg.schedule, cfg.warmup, cfg.total_updates, cfg.lr_min),
+                      weight_decay=cfg.weight_decay, plus_ratio=cfg.plus_ratio, dora=cfg.dora)
+            res = O.train_step(ost, lin64, ochunks, hp)
+            hist.append((p_before, o_before, st, res, slot.grads.clone()))
+        results.append((slot, ost, hist))
+    torch.cuda.synchronize()
+    return results
+
+
+def _flat(slot, per_key, order=("A", "B", "mag")):
+    """Oracle per-linear dict -> the slot arena order [A..., B..., mag...]."""
+    parts = []
+    for n in order:
+        for k in slot.keys:
+            if n in per_key[k]:
+                parts.append(np.asarray(per_key[k][n], dtype=np.float64).ravel())
+    return np.concatenate(parts)
+
+
+E2E = [
+    ("wl1", 1, None, None, 3),
+    ("wl2", 2, None, None, 1),
+    ("wl3", 3, None, None, 1),
+    ("wl4-1layer-T512", 4, 1, 512, 2),
+    ("wl5-1layer-T256", 5, 1, 256, 2),
+]
+
+
+@pytest.mark.parametrize("name,wl,layers,tokens,steps", E2E, ids=[e[0] for e in E2E])
+def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
+    cfg = WL.get_config(wl)
+    _say("e2e", name)
+    for slot, ost, hist in _e2e(cfg, layers, tokens, steps):
+        for it, (p_before, o_before, st, res, grads) in enumerate(hist):
+            assert not st.vetoed and not res["vetoed"]
+            assert st.norm == pytest.approx(res["prep"]["norm"], rel=1e-4)
+            g_ref = _flat(slot, res["grads"])
+            e = rel_err(grads, g_ref)
+            _say(f"  step {it}: grad rel err {e:.3e}, norm {st.norm:.6g} vs {res['prep']['norm']:.6g}")
+            assert e <= 1e-4
+        # update of the last step, excluding elements whose gradient is
+        # within rounding of zero (where the sign of g decides the step)
+        p_before, o_before, st, res, grads = hist[-1]
+        d_ref = _flat(slot, {k: {n: ost.params[k][n] - o_before[k][n] for n in ost.params[k]}
+                             for k in ost.params})
+        d_gpu = np64(slot.params) - np64(p_before)
+        g_ref = _flat(slot, res["grads"])
+        keep = np.abs(g_ref) >= 1e-3 * np.abs(g_ref).max()
+        e = rel_err(d_gpu[keep], d_ref[keep])
+        _say(f"  update rel err {e:.3e} over {keep.sum()} of {keep.size} (excluded {(~keep).sum()})")
+        assert e <= 1e-3
+
+
+def test_seeded_runs_give_identical_adapters():
+    cfg = WL.get_config(2)
+    digests = []
+    for _ in range(2):
+        (slot, _, _), = _e2e(cfg, layers=2, tokens=64, steps=2)
+        digests.append(hashlib.sha256(slot.params.cpu().numpy().tobytes()).hexdigest())
+    assert digests[0] == digests[1]
+
+
+def test_invalid_arguments_raise_before_work():
+    c = _gpu(_linear_case(16, 64, 64, 4))
+    lin = L.make_linear(c["Wq"], c["A"], c["B"], 2.0, 16)
+    Y = torch.zeros(16, 64, device=DEV)
+    U = torch.zeros(16, 4, device=DEV)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_forward(lin, c["X"], Y, U, None, None, torch.empty(16, device=DEV, dtype=torch.uint8))
+    assert e.value.status == -5
+    assert torch.count_nonzero(Y).item() == 0
