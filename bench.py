@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the LoRA-linear training step on one MI355X.
+
+One step = one optimizer update of every adapter slot: for each of the G
+accumulation chunks, forward and backward of every adapted linear (all
+layers, all projections), then gradient preparation, AdamW and (DoRA) the
+row-norm refresh.  Inputs are seeded synthetic tensors already resident in
+HBM; the timed region contains exactly `--steps` updates.
+
+Prints one JSON line: tokens/s for the whole job, the roofline position of
+the kernel that takes most of the time (its average duration measured with
+HIP events on its launch stream during a second, instrumented pass of the
+same steps), a per-kernel breakdown, and the CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LoRA-linear fwd+bwd+step tokens/sec; % MFMA peak (GEMM), % HBM peak (rest)"
+PEAK = {"hbm": 8000.0, "f32": 157.3, "bf16": 2516.6}   # GB/s; TFLOP/s dense MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
+    """Frozen model, slots and per-slot chunk inputs, all seeded."""
+    import torch
+    from bwd_adamw_amd import step as S
+    from bwd_adamw_amd import workloads as WL
+
+    layers = cfg.layers if layers is None else layers
+    T = cfg.tokens if tokens is None else tokens
+    G = cfg.chunks if chunks is None else chunks
+    Wq = {}
+    for l in range(layers):
+        for pj in cfg.projections:
+            inp = WL.linear_inputs(cfg, l, pj, chunks=0, tokens=T, device=device)
+            Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"])
+    model = S.FrozenModel(cfg, Wq)
+    trainer = S.Trainer(cfg, model, tokens=T, device=device)
+    slots, inputs = [], []
+    for si in range(cfg.slots):
+        A, B = {}, {}
+        chunk_list = [dict() for _ in range(G)]
+        xcache = {}
+        for l in range(layers):
+            for pj in cfg.projections:
+                key = (l, pj.ordinal)
+                n = cfg.number
+                A[key] = WL.draw((cfg.rank, pj.in_dim), (n, si, l, pj.ordinal, 0, "A"), "uniform",
+                                 1.0 / pj.in_dim ** 0.5, device)
+                B[key] = WL.draw((pj.out_dim, cfg.rank), (n, si, l, pj.ordinal, 0, "B"), "normal",
+                                 cfg.b_std, device)
+                for g in range(G):
+                    xk = (l, pj.x_group, g)
+                    if xk not in xcache:
+                        xcache[xk] = WL.draw((T, pj.in_dim), (n, si, l, 100 + pj.x_group, g, "X"),
+                                             "normal", cfg.x_std, device)
+                    dY = WL.draw((T, pj.out_dim), (n, si, l, pj.ordinal, g, "dY"), "normal",
+                                 cfg.dy_std, device)
+                    chunk_list[g][key] = (xcache[xk], dY)
+        slot = S.Slot(cfg, model, A, B, cfg.seeds[si], device=device)
+        if cfg.dora:
+            trainer.init_dora(slot)
+        slots.append(slot)
+        inputs.append(chunk_list)
+    return model, trainer, slots, inputs
+
+
+def run_steps(trainer, slots, inputs, n):
+    for _ in range(n):
+        for slot, chunks in zip(slots, inputs):
+            st = trainer.step(slot, chunks)
+            if st.vetoed:
+                raise RuntimeError("non-finite gradient in a synthetic run")
+
+
+def roofline_of(entries, cfg):
+    """Dominant kernel (largest summed time) and its place on the roofline."""
+    dom = max(entries, key=lambda e: e["total_ms"])
+    sec = dom["avg_ms"] / 1e3
+    if dom["kernel"].startswith("gemm"):
+        peak = PEAK["bf16" if "bf16" in dom["kernel"] else "f32"]
+        achieved = dom["flops"] / sec / 1e12
+        rl = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    else:
+        achieved = dom["bytes"] / sec / 1e9
+        rl = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm"], "unit": "GB/s"}
+    rl["frac"] = rl["achieved"] / rl["peak"]
+    rl["traffic"] = None
+    rl["kernel"] = dom["kernel"]
+    rl["shape"] = [dom["M"], dom["N"], dom["K"]]
+    rl["avg_us"] = dom["avg_ms"] * 1e3
+    rl["launches"] = dom["launches"]
+    return rl
+
+
+def kernel_table(entries, total_ms):
+    rows = []
+    for e in sorted(entries, key=lambda e: -e["total_ms"])[:16]:
+        sec = e["avg_ms"] / 1e3
+        row = {"kernel": e["kernel"], "shape": [e["M"], e["N"], e["K"]], "launches": e["launches"],
+               "avg_us": round(e["avg_ms"] * 1e3, 3), "share": round(e["total_ms"] / total_ms, 4)}
+        if e["kernel"].startswith("gemm"):
+            peak = PEAK["bf16" if "bf16" in e["kernel"] else "f32"]
+            row["tflops"] = round(e["flops"] / sec / 1e12, 2)
+            row["frac_mfma"] = round(e["flops"] / sec / 1e12 / peak, 4)
+        else:
+            row["gbps"] = round(e["bytes"] / sec / 1e9, 1)
+            row["frac_hbm"] = round(e["bytes"] / sec / 1e9 / PEAK["hbm"], 4)
+        rows.append(row)
+    return rows
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle's whole step on a bounded sample: the first L_s layers of
+    one slot with all G chunks; L_s grows until about `budget_s` of work."""
+    import numpy as np
+    import oracle as O
+    from bwd_adamw_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
+    f64 = lambda t: t.double().numpy()
+    elapsed_total, layers_done, tokens = 0.0, 0, 0
+    per_layer = []
+    for l in range(cfg.layers):
+        lin, params, chunks = {}, {}, [dict() for _ in range(cfg.chunks)]
+        for pj in cfg.projections:
+            inp = WL.linear_inputs(cfg, l, pj)
+            key = (l, pj.ordinal)
+            lin[key] = f64(inp["W"])
+            params[key] = {"A": f64(inp["A"]), "B": f64(inp["B"])}
+            if cfg.dora:
+                params[key]["mag"] = O.dora_row_norms(lin[key])
+            for g in range(cfg.chunks):
+                chunks[g][key] = (f64(inp["X"][g]), f64(inp["dY"][g]))
+        st = O.SlotState(params=params)
+        if cfg.dora:
+            for key in lin:
+                st.norms[key] = O.dora_row_norms(lin[key], params[key]["A"], params[key]["B"], s)
+        hp = dict(s=s, p=cfg.dropout, seed=cfg.seeds[0], n_pred=cfg.tokens * cfg.chunks,
+                  max_norm=cfg.max_norm, lr=cfg.lr, weight_decay=cfg.weight_decay,
+                  plus_ratio=cfg.plus_ratio, dora=cfg.dora)
+        t0 = time.perf_counter()
+        O.train_step(st, lin, chunks, hp)
+        dt = time.perf_counter() - t0
+        per_layer.append(dt)
+        elapsed_total += dt
+        layers_done += 1
+        if elapsed_total >= budget_s:
+            break
+    # whole-step time of the full workload, scaled from the sampled layers
+    step_s = elapsed_total / layers_done * cfg.layers * cfg.slots
+    value = cfg.tokens_per_step / step_s
+    sample = (f"oracle train_step of {layers_done} of {cfg.layers} layers (all projections, "
+              f"{cfg.chunks} chunk(s) of {cfg.tokens} tokens, slot 0), {elapsed_total:.1f} s, "
+              f"scaled to the full {cfg.layers}-layer x {cfg.slots}-slot step")
+    return {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload number (default: the TinyLlama-shaped wq+wv workload)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: only --gpus 1 is supported (the path is built and measured on one GPU)")
+        sys.exit(2)
+
+    import torch
+    from bwd_adamw_amd import lora as L
+    from bwd_adamw_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        sys.exit(1)
+    L.lib()
+    cfg = WL.get_config(args.config)
+    dev = "cuda"
+    t0 = time.perf_counter()
+    model, trainer, slots, inputs = build_workload(cfg, dev)
+    torch.cuda.synchronize()
+    log(f"setup {cfg.name}: {time.perf_counter() - t0:.1f} s")
+
+    run_steps(trainer, slots, inputs, args.warmup)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(trainer, slots, inputs, args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    value = cfg.tokens_per_step * args.steps / elapsed
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value:.1f} tokens/s")
+
+    # instrumented pass over the same number of steps: per-kernel HIP events
+    L.lora_profile_begin(200000)
+    t1 = time.perf_counter()
+    run_steps(trainer, slots, inputs, args.steps)
+    entries = L.lora_profile_end()
+    prof_ms = (time.perf_counter() - t1) / args.steps * 1e3
+    kernel_ms = sum(e["total_ms"] for e in entries) / args.steps
+    log(f"profiled pass: {prof_ms:.3f} ms/step, kernel time {kernel_ms:.3f} ms/step")
+
+    rl = roofline_of(entries, cfg)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.w_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {
+            "workload": cfg.name, "layers": cfg.layers,
+            "projections": [f"{p.name} {p.in_dim}->{p.out_dim}" for p in cfg.projections],
+            "tokens_per_chunk": cfg.tokens, "chunks": cfg.chunks, "slots": cfg.slots,
+            "tokens_per_step": cfg.tokens_per_step, "rank": cfg.rank, "w_dtype": cfg.w_dtype,
+            "dropout": cfg.dropout, "dora": cfg.dora, "parallelism": "single GPU",
+        },
+        "roofline": rl,
+        "kernels": {"sum_kernel_ms_per_step": kernel_ms, "table": kernel_table(entries, kernel_ms * args.steps)},
+    }
+    if args.cpu_budget > 0:
+        t2 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        log(f"cpu baseline: {time.perf_counter() - t2:.1f} s")
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "optim.hpp"
+#include "profile.hpp"
 #include "skinny.hpp"
 
 using namespace lora;
@@ -161,6 +162,8 @@ template <int RP>
 void launch_down(const float* X, int64_t T, int64_t K, const float* A, int64_t r,
                  const DropParams& d, Split s, float* Upart, uint16_t* Xbf, hipStream_t st) {
   dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)s.n);
+  prof::Scope ps(st, "down_u", T, r, K, 2.0 * T * K * r,
+                 4.0 * (T * K + r * K + T * r) + (Xbf ? 2.0 * T * K : 0.0));
   down_kernel<RP><<<grid, 256, 0, st>>>(X, T, K, A, r, d, s.len, Upart, Xbf);
 }
 template <int RP>
@@ -168,6 +171,9 @@ void launch_k3(const float* dY, int64_t T, int64_t N, const float* B, const floa
                const float* mag, const float* nrm, const float* Z, Split s, float* Vpart,
                float* dBpart, float* dmpart, uint16_t* gbf, hipStream_t st) {
   dim3 grid((unsigned)cdiv(N, SK_C), (unsigned)s.n);
+  prof::Scope ps(st, "k3_v_db", T, N, r, 4.0 * T * N * r,
+                 4.0 * (T * N + T * r + 2 * N * r) + (Z ? 4.0 * T * N : 0.0) +
+                     (gbf ? 2.0 * T * N : 0.0));
   k3_kernel<RP><<<grid, 256, 0, st>>>(dY, T, N, B, U, r, mag, nrm, Z, s.len, Vpart, dBpart,
                                       dmpart, gbf);
 }
@@ -175,6 +181,7 @@ template <int RP>
 void launch_k4(const float* X, int64_t T, int64_t K, const float* V, int64_t r,
                const DropParams& d, Split s, float* dApart, hipStream_t st) {
   dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)s.n);
+  prof::Scope ps(st, "k4_da", T, r, K, 2.0 * T * K * r, 4.0 * (T * K + T * r + 2 * r * K));
   k4_kernel<RP><<<grid, 256, 0, st>>>(X, T, K, V, r, d, s.len, dApart);
 }
 
@@ -197,11 +204,17 @@ void launch_reduce(const RedJob* jobs, int n, hipStream_t st) {
   }
   J.blk[n] = blocks;
   J.njobs = n;
+  double bytes = 0.0;
+  for (int i = 0; i < n; ++i) bytes += 4.0 * (double)jobs[i].n * (jobs[i].nparts + 1 + jobs[i].accumulate);
+  prof::Scope ps(st, "reduce", jobs[0].n, n, jobs[0].nparts, 0.0, bytes);
   if (blocks > 0) reduce_kernel<<<(unsigned)blocks, 256, 0, st>>>(J);
 }
 
 void launch_gemm_f32(const GemmPlan& g, bool fwd, GemmF32Args a, hipStream_t st) {
   dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
+  prof::Scope ps(st, fwd ? "gemm_f32_fwd" : "gemm_f32_dx", a.M, a.Nc, a.Kc,
+                 2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
+                 4.0 * (a.M * a.Kc + a.Nc * a.Kc + a.M * a.Nc * (a.C2 ? 2 : 1)));
   if (g.bm == 128) {
     if (fwd) gemm_f32_kernel<128, 128, true><<<grid, 256, 0, st>>>(a);
     else gemm_f32_kernel<128, 128, false><<<grid, 256, 0, st>>>(a);
@@ -213,6 +226,9 @@ void launch_gemm_f32(const GemmPlan& g, bool fwd, GemmF32Args a, hipStream_t st)
 
 void launch_gemm_bf16(const GemmPlan& g, bool fwd, GemmBf16Args a, hipStream_t st) {
   dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
+  prof::Scope ps(st, fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
+                 2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
+                 2.0 * (a.M * a.Kc + a.Nc * a.Kc) + 4.0 * a.M * a.Nc * (a.C2 ? 2 : 1));
   if (fwd) gemm_bf16_kernel<128, 128, true><<<grid, 256, 0, st>>>(a);
   else gemm_bf16_kernel<128, 128, false><<<grid, 256, 0, st>>>(a);
 }
@@ -220,6 +236,7 @@ void launch_gemm_bf16(const GemmPlan& g, bool fwd, GemmBf16Args a, hipStream_t s
 void launch_splitk_reduce(const float* part, int nsplit, int64_t M, int64_t Nc, float* C,
                           float* C2, const float* cn, const float* cd, hipStream_t st) {
   const int64_t n4 = cdiv(M * Nc, 4);
+  prof::Scope ps(st, "splitk_reduce", M, Nc, nsplit, 0.0, 4.0 * M * Nc * (nsplit + (C2 ? 2 : 1)));
   splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(part, nsplit, M, Nc, C, C2, cn, cd);
 }
 
@@ -403,9 +420,15 @@ int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, floa
   double* norm_out = (double*)w;                // {norm, clip}
   double* part = (double*)(w + 256);
   int* flags = (int*)(w + 256 + 1024 * sizeof(double));
-  gradnorm_pass1<<<nb, 256, 0, st>>>(grads, n, per, part, flags);
-  gradnorm_pass2<<<1, 256, 0, st>>>(part, flags, nb, n_pred_tokens, max_norm, d_scale, d_stats,
-                                    norm_out);
+  {
+    prof::Scope ps(st, "gradnorm_pass1", n, nb, 0, 2.0 * n, 4.0 * n);
+    gradnorm_pass1<<<nb, 256, 0, st>>>(grads, n, per, part, flags);
+  }
+  {
+    prof::Scope ps(st, "gradnorm_pass2", nb, 1, 0, 0.0, 12.0 * nb);
+    gradnorm_pass2<<<1, 256, 0, st>>>(part, flags, nb, n_pred_tokens, max_norm, d_scale, d_stats,
+                                      norm_out);
+  }
   if (hip_status()) return LORA_E_HIP;
   if (h_norm) {
     double host[2];
@@ -424,8 +447,8 @@ int lora_adamw_step(float* params, const float* grads, float* m, float* v,
   if (!params || !grads || !m || !v || !segs || !hp || !d_scale) return LORA_E_INVALID;
   if (n_seg < 1 || n_seg > ADAM_MAX_SEG) return LORA_E_INVALID;
   if (!al16(params) || !al16(grads) || !al16(m) || !al16(v)) return LORA_E_ALIGN;
-  if (!(hp->lr >= 0.0f) || !std::isfinite(hp->lr) || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) ||
-      !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !(hp->eps > 0.0f) ||
+  if (!(hp->lr >= 0.0) || !std::isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+      !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) ||
       !std::isfinite(hp->weight_decay) || !std::isfinite(hp->plus_ratio) || hp->t < 1)
     return LORA_E_INVALID;
   AdamSegs S;
@@ -444,17 +467,23 @@ int lora_adamw_step(float* params, const float* grads, float* m, float* v,
   S.blk[n_seg] = blocks;
   S.n = n_seg;
   AdamHp H;
-  H.lr = hp->lr;
-  H.b1 = hp->beta1;
-  H.b2 = hp->beta2;
-  H.one_m_b1 = (float)(1.0 - (double)hp->beta1);
-  H.one_m_b2 = (float)(1.0 - (double)hp->beta2);
-  H.eps = hp->eps;
-  H.wd = hp->weight_decay;
-  H.ratio = hp->plus_ratio;
-  H.bc1 = (float)(1.0 - pow((double)hp->beta1, (double)hp->t));
-  H.bc2 = (float)(1.0 - pow((double)hp->beta2, (double)hp->t));
+  H.b1 = (float)hp->beta1;
+  H.b2 = (float)hp->beta2;
+  H.one_m_b1 = (float)(1.0 - hp->beta1);
+  H.one_m_b2 = (float)(1.0 - hp->beta2);
+  H.eps = (float)hp->eps;
+  H.bc1 = (float)(1.0 - pow(hp->beta1, (double)hp->t));
+  H.bc2 = (float)(1.0 - pow(hp->beta2, (double)hp->t));
+  H.rate[0] = (float)hp->lr;
+  H.rate[1] = (float)(hp->lr * hp->plus_ratio);
+  H.rate[2] = (float)hp->lr;
+  H.decay[0] = (float)(hp->lr * hp->weight_decay);
+  H.decay[1] = 0.0f;
+  H.decay[2] = 0.0f;
   if (blocks == 0) return LORA_OK;
+  int64_t total = 0;
+  for (int i = 0; i < n_seg; ++i) total += segs[i].count;
+  prof::Scope ps((hipStream_t)stream, "adamw", total, n_seg, 0, 0.0, 28.0 * total);
   adamw_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(params, grads, m, v, S, H,
                                                                    d_scale);
   return hip_status();
@@ -466,6 +495,7 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim, 
   if (!drop_valid(drop)) return LORA_E_INVALID;
   const DropParams d = make_drop(drop);
   const int64_t n = tokens * in_dim;
+  prof::Scope ps((hipStream_t)stream, "dropout_mask", tokens, in_dim, 0, 0.0, (double)n);
   dropout_mask_kernel<<<(unsigned)cdiv(n, 256), 256, 0, (hipStream_t)stream>>>(d, tokens, in_dim,
                                                                                mask);
   return hip_status();
@@ -488,6 +518,8 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream) {
   const unsigned grid = (unsigned)cdiv(N, ROWS);
   hipStream_t st = (hipStream_t)stream;
   const int rp = lora_on ? rank_pad(r) : 16;
+  prof::Scope ps(st, "dora_rownorm", N, K, r, 2.0 * N * K * (r + 1),
+                 (lin->w_dtype == LORA_BF16 ? 2.0 : 4.0) * N * K + 4.0 * r * (N + K) + 4.0 * N);
   if (lin->w_dtype == LORA_BF16) {
     const uint16_t* W = (const uint16_t*)lin->W;
     LORA_RP_DISPATCH(rp, (dora_rownorm_kernel<uint16_t, RP, ROWS><<<grid, 256, 0, st>>>(
@@ -498,6 +530,48 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream) {
                              W, N, K, A, B, r, s, out_norm)));
   }
   return hip_status();
+}
+
+// ------------------------------------------------------------ profiling ---
+int lora_profile_begin(int max_launches) {
+  if (max_launches <= 0) return LORA_E_INVALID;
+  prof::State& s = prof::state();
+  const size_t need = 2 * (size_t)max_launches;
+  while (s.events.size() < need) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return LORA_E_HIP;
+    s.events.push_back(e);
+  }
+  s.recs.clear();
+  s.used = 0;
+  s.on = true;
+  return LORA_OK;
+}
+
+int lora_profile_end(lora_profile_entry* out, int max_entries) {
+  prof::State& s = prof::state();
+  if (!s.on) return LORA_E_INVALID;
+  s.on = false;
+  if (hipDeviceSynchronize() != hipSuccess) return LORA_E_HIP;
+  int n = 0;
+  for (const prof::Rec& r : s.recs) {
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, s.events[r.ev], s.events[r.ev + 1]) != hipSuccess) return LORA_E_HIP;
+    int j = 0;
+    while (j < n && !(out[j].kernel == r.name && out[j].M == r.M && out[j].N == r.N &&
+                      out[j].K == r.K))
+      ++j;
+    if (j == n) {
+      if (n == max_entries || !out) continue;
+      out[n] = {r.name, r.M, r.N, r.K, 0, 0.0, r.flops, r.bytes};
+      ++n;
+    }
+    out[j].launches += 1;
+    out[j].total_ms += (double)ms;
+  }
+  s.recs.clear();
+  s.used = 0;
+  return n;
 }
 
 }  // extern "C"

@@ -112,7 +112,9 @@ struct AdamSegs {
   int n;
 };
 struct AdamHp {
-  float lr, one_m_b1, b1, one_m_b2, b2, eps, wd, ratio, bc1, bc2;
+  float b1, one_m_b1, b2, one_m_b2, eps, bc1, bc2;
+  float rate[3];    // per kind: lr (A), lr*plus_ratio (B), lr (magnitude)
+  float decay[3];   // per kind: lr*weight_decay (A), 0, 0
 };
 
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ P,
@@ -133,8 +135,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ P,
   if (e >= segs.cnt[s]) return;
   const int64_t i = segs.off[s] + e;
   const int kind = segs.kind[s];
-  const float rate = kind == 1 ? hp.lr * hp.ratio : hp.lr;
-  const float decay = kind == 0 ? hp.lr * hp.wd : 0.0f;
+  const float rate = hp.rate[kind];
+  const float decay = hp.decay[kind];
   f32x4 p = *reinterpret_cast<const f32x4*>(P + i);
   const f32x4 g = *reinterpret_cast<const f32x4*>(G + i);
   f32x4 m = *reinterpret_cast<const f32x4*>(Mo + i);

@@ -20,7 +20,7 @@ __all__ = [
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
-    "lora_status_string", "EXPORTS",
+    "lora_status_string", "lora_profile_begin", "lora_profile_end", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
@@ -34,7 +34,7 @@ EXPORTS = (
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
-    "lora_status_string",
+    "lora_status_string", "lora_profile_begin", "lora_profile_end",
 )
 
 
@@ -56,13 +56,19 @@ class LoraLinear(C.Structure):
                 ("dora_mag", C.c_void_p), ("dora_norm", C.c_void_p)]
 
 
+class LoraProfileEntry(C.Structure):
+    _fields_ = [("kernel", C.c_char_p), ("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64),
+                ("launches", C.c_int64), ("total_ms", C.c_double), ("flops", C.c_double),
+                ("bytes", C.c_double)]
+
+
 class LoraSegment(C.Structure):
     _fields_ = [("offset", C.c_int64), ("count", C.c_int64), ("kind", C.c_int32)]
 
 
 class LoraAdamwHparams(C.Structure):
-    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float),
-                ("eps", C.c_float), ("weight_decay", C.c_float), ("plus_ratio", C.c_float),
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("plus_ratio", C.c_double),
                 ("t", C.c_int64)]
 
 
@@ -89,6 +95,8 @@ def lib() -> C.CDLL:
             "lora_scaling": (C.c_double, [C.c_double, I64, I32]),
             "lora_lr_at": (C.c_double, [I64, C.c_double, I32, I64, I64, C.c_double]),
             "lora_status_string": (C.c_char_p, [I32]),
+            "lora_profile_begin": (I32, [I32]),
+            "lora_profile_end": (I32, [P, I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -222,3 +230,22 @@ def lora_dropout_mask(drop: LoraDropout, tokens, in_dim, mask, stream=None):
 def lora_dora_row_norms(lin: LoraLinear, out_norm, stream=None):
     rc = lib().lora_dora_row_norms(C.byref(lin), _ptr(out_norm, "out_norm"), _stream(stream))
     _check("lora_dora_row_norms", rc)
+
+
+def lora_profile_begin(max_launches: int = 100000):
+    _check("lora_profile_begin", lib().lora_profile_begin(int(max_launches)))
+
+
+def lora_profile_end(max_entries: int = 512) -> list:
+    """Close the profile; returns dicts with kernel, M, N, K, launches,
+    total_ms, avg_ms, flops and bytes (per launch)."""
+    buf = (LoraProfileEntry * max_entries)()
+    n = lib().lora_profile_end(buf, max_entries)
+    if n < 0:
+        raise LoraError("lora_profile_end", n)
+    out = []
+    for e in buf[:n]:
+        out.append(dict(kernel=e.kernel.decode(), M=e.M, N=e.N, K=e.K, launches=e.launches,
+                        total_ms=e.total_ms, avg_ms=e.total_ms / max(1, e.launches),
+                        flops=e.flops, bytes=e.bytes))
+    return out

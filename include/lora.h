@@ -102,9 +102,11 @@ typedef struct lora_segment {
 
 /* AdamW hyper-parameters of one update ("4.3. Training Guide", "Optimizer").
  * lr is the already-scheduled rate of this update; t is the 1-based count of
- * applied updates of the slot including this one. */
+ * applied updates of the slot including this one.  Host doubles: the derived
+ * constants (1-beta, bias corrections, rates) are formed in double and
+ * rounded once to float for the kernel. */
 typedef struct lora_adamw_hparams {
-  float lr, beta1, beta2, eps, weight_decay, plus_ratio;
+  double lr, beta1, beta2, eps, weight_decay, plus_ratio;
   int64_t t;
 } lora_adamw_hparams;
 
@@ -183,6 +185,25 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim,
  * lin->A == lin->B == NULL it gives ||W_i|| (the magnitude initialisation).
  * lin->tokens is ignored. */
 int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream);
+
+/* Diagnostics: launch timing.  lora_profile_begin opens a profile that can
+ * hold max_launches launches (it creates that many HIP event pairs once and
+ * keeps them); until lora_profile_end, each kernel launch of the library is
+ * bracketed by two events recorded on its own stream.  lora_profile_end waits
+ * for the device, writes up to max_entries aggregates (one per kernel name and
+ * shape, in first-launch order) and returns their count, or a negative status.
+ * `kernel` points to a static string.  flops and bytes are the algorithmic
+ * work of one launch (bytes: each operand read once, each result written
+ * once).  Not thread-safe; meant for benchmarks, not production paths. */
+typedef struct lora_profile_entry {
+  const char* kernel;
+  int64_t M, N, K;        /* shape the kernel name documents                  */
+  int64_t launches;
+  double total_ms;        /* summed event-to-event time over the launches      */
+  double flops, bytes;    /* algorithmic work of one launch                    */
+} lora_profile_entry;
+int lora_profile_begin(int max_launches);
+int lora_profile_end(lora_profile_entry* out, int max_entries);
 
 /* Host helpers. */
 /* alpha/rank, or alpha/sqrt(rank) when rslora != 0 ("How it works"). */

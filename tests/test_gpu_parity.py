@@ -395,27 +395,46 @@ E2E = [
 
 @pytest.mark.parametrize("name,wl,layers,tokens,steps", E2E, ids=[e[0] for e in E2E])
 def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
+    """Whole updates against the oracle's train_step.
+
+    Gradients: A and B are float32-exact on every path (rank-side products
+    run in float32), so they meet 1e-4; the DoRA magnitude gradient reads Z,
+    which a bf16-W frozen product rounds, so it meets the bf16 bar.
+    Updates: Adam normalises each element by its own gradient history, so an
+    element whose gradient is within the path's error of zero may move by up
+    to 2 lr either way.  Elements are compared where every step's reference
+    gradient exceeds `floor` times the segment's largest, with floor = 1e-3
+    for float32-exact gradients and 0.1 for the bf16-rounded magnitude
+    gradient (whose error is ~1e-3 of the largest)."""
     cfg = WL.get_config(wl)
     _say("e2e", name)
     for slot, ost, hist in _e2e(cfg, layers, tokens, steps):
+        seg = {}
+        for off, cnt, kind in slot.segments:
+            seg[kind] = slice(off, off + cnt)
+        ok = np.ones(slot.n, dtype=bool)
         for it, (p_before, o_before, st, res, grads) in enumerate(hist):
             assert not st.vetoed and not res["vetoed"]
             assert st.norm == pytest.approx(res["prep"]["norm"], rel=1e-4)
             g_ref = _flat(slot, res["grads"])
-            e = rel_err(grads, g_ref)
-            _say(f"  step {it}: grad rel err {e:.3e}, norm {st.norm:.6g} vs {res['prep']['norm']:.6g}")
-            assert e <= 1e-4
-        # update of the last step, excluding elements whose gradient is
-        # within rounding of zero (where the sign of g decides the step)
+            g_gpu = np64(grads)
+            for kind, sl in seg.items():
+                e = rel_err(g_gpu[sl], g_ref[sl])
+                bar = TOL[cfg.w_dtype] if kind == L.KIND_MAG else 1e-4
+                floor = 0.1 if (kind == L.KIND_MAG and cfg.w_dtype == "bf16") else 1e-3
+                ok[sl] &= np.abs(g_ref[sl]) >= floor * np.abs(g_ref[sl]).max()
+                _say(f"  step {it} seg {kind}: grad rel err {e:.3e} (bar {bar:g})")
+                assert e <= bar, (it, kind, e)
         p_before, o_before, st, res, grads = hist[-1]
         d_ref = _flat(slot, {k: {n: ost.params[k][n] - o_before[k][n] for n in ost.params[k]}
                              for k in ost.params})
         d_gpu = np64(slot.params) - np64(p_before)
-        g_ref = _flat(slot, res["grads"])
-        keep = np.abs(g_ref) >= 1e-3 * np.abs(g_ref).max()
-        e = rel_err(d_gpu[keep], d_ref[keep])
-        _say(f"  update rel err {e:.3e} over {keep.sum()} of {keep.size} (excluded {(~keep).sum()})")
-        assert e <= 1e-3
+        for kind, sl in seg.items():
+            m = ok[sl]
+            e = rel_err(d_gpu[sl][m], d_ref[sl][m])
+            bar = 2e-2 if (kind == L.KIND_MAG and cfg.w_dtype == "bf16") else 1e-3
+            _say(f"  update seg {kind}: rel err {e:.3e} over {m.sum()} of {m.size}")
+            assert e <= bar, (kind, e)
 
 
 def test_seeded_runs_give_identical_adapters():
