@@ -96,4 +96,18 @@ LORA_DEV float wave_sum(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------------------
+// Split reductions run in a fixed order; no floating-point atomics anywhere.
+// ---------------------------------------------------------------------------
+// Fixed-order sum of nparts partials of one element: (sum_p part[p*stride+i])
+// * alpha (/ div), added to or stored into out[i].
+LORA_DEV void sum_partials(const float* part, int64_t stride, int nparts, int64_t i, float alpha,
+                           const float* div, int64_t divi, float* out, int accumulate) {
+  float s = part[i];
+  for (int q = 1; q < nparts; ++q) s += part[(int64_t)q * stride + i];
+  s *= alpha;
+  if (div) s /= div[divi];
+  out[i] = accumulate ? out[i] + s : s;
+}
+
 }  // namespace lora

@@ -1,17 +1,25 @@
 // Frozen-weight GEMMs with bf16 W on bf16 MFMA (v_mfma_f32_32x32x16_bf16),
 // float32 accumulation.  Same contractions as gemm_f32.hpp:
-//   forward: Z = Xb W^T + s U B^T            (Xb = bf16(X), written by down)
-//   dX     : dX = gb W + (s V A) * mask * keep   (gb = bf16(g), written by k3)
-// The LoRA operands (U, B, V, A: float32) are rounded to bf16 while staging.
+//   forward: Z = Xb W^T + s U B^T                 (Xb = bf16(X), written by down)
+//   dX     : dX = gb W + (s V A) * mask * keep    (gb = bf16(g), written by k3)
+// The LoRA operands (U, B, V, A: float32) are rounded to bf16 while staging;
+// U and V may arrive as split partials, summed in split order while staging.
 //
-// LDS holds both operands as [row][contraction] bf16 with a 16-byte pad, so
-// every MFMA operand is one 128-bit LDS read: lane half h takes contraction
-// indices 32h..32h+31 of each 64-wide K-step.  For dX the W tile arrives with
-// the contraction index as its row (W's native [N,K] layout); each thread
-// loads an 8-row x 4-column block and transposes it in registers before the
-// LDS write.
+// Block: 512 threads = 2 x 4 waves over a BM x BN tile (256x256, 256x128 or
+// 128x128), K-step 64, LDS double buffered.  LDS holds both operands as
+// [row][contraction] bf16 with a 16-byte pad, so every MFMA operand is one
+// 128-bit LDS read: lane half h takes contraction indices 32h..32h+31 of the
+// K-step.  For dX the W tile arrives with the contraction index as its row
+// (W's native [N,K] layout); each thread loads an 8-row x 4-column block and
+// transposes it in registers before the LDS write.
+//
+// The grid is one-dimensional.  Workgroups are dealt to the 8 XCDs round
+// robin, so block b runs on XCD b % 8; the tile order is remapped so that
+// each XCD works through one contiguous band of row-major tiles and keeps the
+// band's A panels in its own L2.
 #pragma once
 #include "common.hpp"
+#include "gemm_f32.hpp"   // LoraOperand
 
 namespace lora {
 
@@ -21,43 +29,54 @@ struct GemmBf16Args {
   const uint16_t* B;       // fwd: W [Nc, Kc];  dx: W [Kc, Nc]   (bf16)
   int64_t ldb;
   int64_t M, Nc, Kc;
-  const float* XA;         // U (fwd) or V (dx), float32 [M, r]
+  LoraOperand xa;          // U (fwd) or V (dx), float32 [M, r], possibly as partials
   const float* XB;         // fwd: B_lora [Nc, r];  dx: A_lora [r, Nc]  (float32)
   int64_t r;
   float xs;
   DropParams drop;
-  int64_t ksplit;
-  int nsplit;
   float* C;
   float* C2;
   const float* cn;
   const float* cd;
-  float* part;
 };
 
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
-template <int BM, int BN, bool FWD>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
-  constexpr int BK = 64;
-  constexpr int LDS_ROW = BK + 8;               // bf16 elements per LDS row (144 B)
-  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
-  constexpr int ACH = BM * (BK / 8) / 256;      // 16-byte A chunks per thread
-  constexpr int BCH = BN * (BK / 8) / 256;      // 16-byte B chunks per thread (fwd)
-  constexpr int BIT = (BK / 8) * (BN / 4) / 256;  // transposed 8x4 items per thread (dx)
-  static_assert(ACH >= 1 && BCH >= 1 && BIT >= 1, "tile too small");
+// Tile of linear block b with the XCD-banded order (a bijection on [0, T)).
+LORA_DEV int64_t xcd_tile(int64_t b, int64_t T) {
+  const int64_t q = T / 8, rem = T % 8;
+  const int64_t x = b % 8, idx = b / 8;
+  const int64_t start = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
+  return start + idx;
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_ROW];
+template <int BM, int BN, bool FWD>
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
+  constexpr int NT = 512;
+  constexpr int BK = 64;
+  constexpr int LDS_ROW = BK + 8;                   // bf16 elements per LDS row (144 B)
+  constexpr int WGM = 2, WGN = 4;
+  constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
+  constexpr int ACH = BM * (BK / 8) / NT;           // 16-byte A chunks per thread
+  constexpr int BCH = BN * (BK / 8) / NT;           // 16-byte B chunks per thread (fwd)
+  constexpr int BITEMS = (BK / 8) * (BN / 4);       // transposed 8x4 blocks (dx)
+  constexpr int BIT = (BITEMS + NT - 1) / NT;
+  static_assert(ACH >= 1 && BCH >= 1 && MI >= 1 && NI >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDS_ROW];
+  auto As = [&](int b) -> uint16_t* { return smem + b * (BM * LDS_ROW); };
+  auto Bs = [&](int b) -> uint16_t* { return smem + 2 * BM * LDS_ROW + b * (BN * LDS_ROW); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int split = blockIdx.z;
-  const int64_t kbeg = (int64_t)split * p.ksplit;
-  const int64_t kend = min(p.Kc, kbeg + p.ksplit);
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  const int64_t ntn = (p.Nc + BN - 1) / BN;
+  const int64_t ntiles = ntn * ((p.M + BM - 1) / BM);
+  const int64_t tile = xcd_tile(blockIdx.x, ntiles);
+  const int64_t m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+  const int64_t kend = p.Kc;
   const int hl = lane >> 5, l32 = lane & 31;
+  const bool store_xa = p.xa.out != nullptr && n0 == 0;
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -81,35 +100,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
   auto load_a = [&](int64_t k0) {
 #pragma unroll
     for (int q = 0; q < ACH; ++q) {
-      const int f = tid + 256 * q;
+      const int f = tid + NT * q;
       ra[q] = ld8(p.A, m0 + (f >> 3), p.M, p.lda, k0 + 8 * (f & 7), kend);
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < ACH; ++q) {
-      const int f = tid + 256 * q;
-      *reinterpret_cast<u32x4*>(&As[buf][(f >> 3) * LDS_ROW + 8 * (f & 7)]) = ra[q];
+      const int f = tid + NT * q;
+      *reinterpret_cast<u32x4*>(&As(buf)[(f >> 3) * LDS_ROW + 8 * (f & 7)]) = ra[q];
     }
   };
   auto load_b = [&](int64_t k0) {
     if constexpr (FWD) {
 #pragma unroll
       for (int q = 0; q < BCH; ++q) {
-        const int f = tid + 256 * q;
+        const int f = tid + NT * q;
         rbf[q] = ld8(p.B, n0 + (f >> 3), p.Nc, p.ldb, k0 + 8 * (f & 7), kend);
       }
     } else {
 #pragma unroll
       for (int q = 0; q < BIT; ++q) {
-        const int f = tid + 256 * q;
+        const int f = tid + NT * q;
         const int cq = f % (BN / 4), kg = f / (BN / 4);
         const int64_t gn = n0 + 4 * cq;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int64_t gk = k0 + 8 * kg + i;
           u32x2 v = {0u, 0u};
-          if (gk < kend && gn < p.Nc) v = *reinterpret_cast<const u32x2*>(p.B + gk * p.ldb + gn);
+          if (f < BITEMS && gk < kend && gn < p.Nc)
+            v = *reinterpret_cast<const u32x2*>(p.B + gk * p.ldb + gn);
           rbt[q][i] = v;
         }
       }
@@ -117,7 +137,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
   };
   // Transposed write: column e of the 8x4 block becomes 8 contraction values.
   auto store_bt = [&](int buf, int q, const u32x2 (&w)[8]) {
-    const int f = tid + 256 * q;
+    const int f = tid + NT * q;
+    if (f >= BITEMS) return;
     const int cq = f % (BN / 4), kg = f / (BN / 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -128,15 +149,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
         const uint32_t x1 = (e < 2) ? w[2 * d + 1].x : w[2 * d + 1].y;
         o[d] = (e & 1) ? (hi16(x0) | (hi16(x1) << 16)) : (lo16(x0) | (lo16(x1) << 16));
       }
-      *reinterpret_cast<u32x4*>(&Bs[buf][(4 * cq + e) * LDS_ROW + 8 * kg]) = o;
+      *reinterpret_cast<u32x4*>(&Bs(buf)[(4 * cq + e) * LDS_ROW + 8 * kg]) = o;
     }
   };
   auto store_b = [&](int buf) {
     if constexpr (FWD) {
 #pragma unroll
       for (int q = 0; q < BCH; ++q) {
-        const int f = tid + 256 * q;
-        *reinterpret_cast<u32x4*>(&Bs[buf][(f >> 3) * LDS_ROW + 8 * (f & 7)]) = rbf[q];
+        const int f = tid + NT * q;
+        *reinterpret_cast<u32x4*>(&Bs(buf)[(f >> 3) * LDS_ROW + 8 * (f & 7)]) = rbf[q];
       }
     } else {
 #pragma unroll
@@ -150,11 +171,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         av[i] = *reinterpret_cast<const u32x4*>(
-            &As[buf][(wm0 + i * 32 + l32) * LDS_ROW + 32 * hl + 8 * s]);
+            &As(buf)[(wm0 + i * 32 + l32) * LDS_ROW + 32 * hl + 8 * s]);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
         bv[j] = *reinterpret_cast<const u32x4*>(
-            &Bs[buf][(wn0 + j * 32 + l32) * LDS_ROW + 32 * hl + 8 * s]);
+            &Bs(buf)[(wn0 + j * 32 + l32) * LDS_ROW + 32 * hl + 8 * s]);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -165,33 +186,40 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
   auto lora_contraction = [&]() {
     for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
       __syncthreads();
-      // A side: XA [M, r] rows m, scaled by s.
-      for (int f = tid; f < BM * (BK / 4); f += 256) {
+      // A side: XA [M, r] rows m (split partials summed), scaled by s.
+      for (int f = tid; f < BM * (BK / 4); f += NT) {
         const int row = f / (BK / 4), c4 = f % (BK / 4);
         const int64_t gm = m0 + row, gk = k0 + 4 * c4;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gm < p.M && gk < p.r) v = *reinterpret_cast<const f32x4*>(p.XA + gm * p.r + gk) * p.xs;
+        if (gm < p.M && gk < p.r) {
+          const int64_t i = gm * p.r + gk;
+          v = *reinterpret_cast<const f32x4*>(p.xa.p + i);
+          for (int part = 1; part < p.xa.nparts; ++part)
+            v += *reinterpret_cast<const f32x4*>(p.xa.p + part * p.xa.stride + i);
+          if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
+          v *= p.xs;
+        }
         u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(&As[0][row * LDS_ROW + 4 * c4]) = b;
+        *reinterpret_cast<u32x2*>(&As(0)[row * LDS_ROW + 4 * c4]) = b;
       }
       if constexpr (FWD) {
         // B_lora [Nc, r]: rows n, rank contiguous.
-        for (int f = tid; f < BN * (BK / 4); f += 256) {
+        for (int f = tid; f < BN * (BK / 4); f += NT) {
           const int row = f / (BK / 4), c4 = f % (BK / 4);
           const int64_t gn = n0 + row, gk = k0 + 4 * c4;
           f32x4 v = {0.f, 0.f, 0.f, 0.f};
           if (gn < p.Nc && gk < p.r) v = *reinterpret_cast<const f32x4*>(p.XB + gn * p.r + gk);
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(&Bs[0][row * LDS_ROW + 4 * c4]) = b;
+          *reinterpret_cast<u32x2*>(&Bs(0)[row * LDS_ROW + 4 * c4]) = b;
         }
       } else {
         // A_lora [r, Nc]: rows are the contraction index; transpose on store.
-        for (int f = tid; f < BN * BK; f += 256) {
+        for (int f = tid; f < BN * BK; f += NT) {
           const int n = f % BN, kk = f / BN;
           const int64_t gn = n0 + n, gk = k0 + kk;
           float v = 0.f;
           if (gn < p.Nc && gk < p.r) v = p.XB[gk * p.Nc + gn];
-          Bs[0][n * LDS_ROW + kk] = (uint16_t)f32_to_bf16_bits(v);
+          Bs(0)[n * LDS_ROW + kk] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
       __syncthreads();
@@ -200,7 +228,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
     __syncthreads();
   };
 
-  if (!FWD && split == 0 && p.r > 0) {
+  if (!FWD && p.r > 0) {
     lora_contraction();
     if (p.drop.on) {
 #pragma unroll
@@ -218,29 +246,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
     }
   }
 
-  const int64_t nk = (kend - kbeg + BK - 1) / BK;
-  if (nk > 0) {
-    load_a(kbeg);
-    load_b(kbeg);
-    store_a(0);
-    store_b(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int cur = (int)(kt & 1);
-      if (kt + 1 < nk) {
-        load_a(kbeg + (kt + 1) * BK);
-        load_b(kbeg + (kt + 1) * BK);
-      }
-      compute(cur);
-      if (kt + 1 < nk) {
-        store_a(cur ^ 1);
-        store_b(cur ^ 1);
-      }
-      __syncthreads();
+  const int64_t nk = (kend + BK - 1) / BK;
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  store_b(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt & 1);
+    if (kt + 1 < nk) {
+      load_a((kt + 1) * BK);
+      load_b((kt + 1) * BK);
     }
+    compute(cur);
+    if (kt + 1 < nk) {
+      store_a(cur ^ 1);
+      store_b(cur ^ 1);
+    }
+    __syncthreads();
   }
 
-  if (FWD && split == 0 && p.r > 0) lora_contraction();
+  if (FWD && p.r > 0) lora_contraction();
 
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -248,19 +274,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmBf16Args p) {
     for (int j = 0; j < NI; ++j) {
       const int64_t gn = n0 + wn0 + j * 32 + l32;
       if (gn >= p.Nc) continue;
-      float c = 1.0f;
-      if (p.nsplit == 1 && p.cn) c = p.cn[gn] / p.cd[gn];
+      const float c = p.cn ? p.cn[gn] / p.cd[gn] : 1.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
         if (gm >= p.M) continue;
         const float x = acc[i][j][v];
-        if (p.nsplit == 1) {
-          p.C[gm * p.Nc + gn] = x * c;
-          if (p.C2) p.C2[gm * p.Nc + gn] = x;
-        } else {
-          p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
-        }
+        p.C[gm * p.Nc + gn] = x * c;
+        if (p.C2) p.C2[gm * p.Nc + gn] = x;
       }
     }
 }

@@ -3,7 +3,7 @@
 // Forward ("8. LoRA Fundamentals", "How it works"):
 //   Z[t,n] = sum_k X[t,k] W[n,k]  +  s * sum_j U[t,j] B[n,j]
 // The rank-r up-projection is a second, short contraction into the same
-// accumulators: U and B tiles are staged through LDS after the main loop.
+// accumulators, staged through LDS after the main loop.
 //
 // dX ("Training decisions"; "Backward Bug Hunts ...", "Bug #1"):
 //   dX[t,k] = sum_n g[t,n] W[n,k]  +  (s * sum_j V[t,j] A[j,k]) * mask * keep
@@ -11,15 +11,29 @@
 // index); nothing is transposed in memory.  The LoRA term is contracted
 // first, masked in registers, then the frozen contraction accumulates on top.
 //
-// Block: 256 threads = 2x2 waves, tile BM x BN, K-step BK = 32, LDS double
-// buffered.  Within a K-step the lane half h = lane/32 takes contraction
-// indices 16h..16h+15 so each lane reads its A (and, forward, B) operands with
-// 128-bit LDS loads.  Split-K over the contraction writes per-split partials
-// that a second kernel sums in fixed order (no atomics).
+// The LoRA operand U (forward) or V (dX) may arrive as split partials from
+// the rank-side kernels; they are summed in split order while staging, and
+// the forward stores the summed U once (blocks of column tile 0).
+//
+// Block: 256 threads = 2x2 waves, tile BM x BN, K-step 32, LDS double
+// buffered.  Within a K-step lane half h takes contraction indices
+// 16h..16h+15 so A (and, forward, B) operands are 128-bit LDS reads.
+// Short-M shapes split the contraction across blocks (grid z): each split
+// writes a partial tile and splitk_reduce_kernel sums them in split order and
+// applies the epilogue.  The LoRA contraction belongs to split 0.
 #pragma once
 #include "common.hpp"
 
 namespace lora {
+
+// LoRA operand of the A side: nparts partials [nparts][M][r] summed in order
+// (nparts == 1: the operand itself).  `out`, when set, receives the sum.
+struct LoraOperand {
+  const float* p;
+  int64_t stride;
+  int nparts;
+  float* out;
+};
 
 struct GemmF32Args {
   const float* A;          // [M, Kc] contraction contiguous (X or dY)
@@ -29,14 +43,14 @@ struct GemmF32Args {
   const float* B;          // fwd: W [Nc, Kc];  dx: W [Kc, Nc]
   int64_t ldb;
   int64_t M, Nc, Kc;
-  const float* XA;         // LoRA operand on the A side: U (fwd) or V (dx), [M, r]
+  LoraOperand xa;          // U (fwd) or V (dx), [M, r]
   const float* XB;         // fwd: B_lora [Nc, r];  dx: A_lora [r, Nc]
   int64_t r;
   float xs;                // LoRA scale s
   DropParams drop;         // dx only: mask of the LoRA term at (t = m, k = n)
   int64_t ksplit;          // contraction length per split (multiple of 32)
   int nsplit;
-  float* C;                // output (nsplit == 1): Y or dX, [M, Nc]
+  float* C;                // Y or dX, [M, Nc] (nsplit == 1)
   float* C2;               // fwd DoRA: Z, or NULL
   const float* cn;         // fwd DoRA epilogue column scale cn/cd, or NULL
   const float* cd;
@@ -46,16 +60,22 @@ struct GemmF32Args {
 template <int BM, int BN, bool FWD>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   constexpr int BK = 32;
+  constexpr int KW = BK;                // contraction indices per wave per K-step
+  constexpr int KH = KW / 2;            // per lane half
   constexpr int LDA = BK + 4;
   constexpr int LDB = FWD ? (BK + 4) : (BN + 4);
   constexpr int BSZ = FWD ? BN * LDB : BK * LDB;
-  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int AF4 = BM * BK / 4 / 256;
   constexpr int BF4 = BN * BK / 4 / 256;
-  static_assert(AF4 >= 1 && BF4 >= 1, "tile too small for 256 threads");
+  constexpr int AC4 = BK / 4;           // float4 per A row of a K-step
+  static_assert(AF4 >= 1 && BF4 >= 1 && MI >= 1 && NI >= 1, "tile shape");
+  static_assert(KH % 4 == 0, "lane-half slice must be whole float4s");
 
-  __shared__ __attribute__((aligned(16))) float As[2][BM * LDA];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BSZ];
+  __shared__ __attribute__((aligned(16))) float smem[2 * BM * LDA + 2 * BSZ];
+  auto As = [&](int b) -> float* { return smem + b * (BM * LDA); };
+  auto Bs = [&](int b) -> float* { return smem + 2 * BM * LDA + b * BSZ; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
@@ -64,6 +84,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   const int64_t kbeg = (int64_t)split * p.ksplit;
   const int64_t kend = min(p.Kc, kbeg + p.ksplit);
   const int hl = lane >> 5, l32 = lane & 31;
+  const bool store_xa = p.xa.out != nullptr && blockIdx.x == 0 && split == 0;
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -75,22 +96,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
 
   f32x4 ra[AF4], rb[BF4];
 
-  // A side: rows m, contraction contiguous.
-  auto load_a = [&](const float* src, int64_t ld, int64_t k0, int64_t klim, float mul,
-                    const float* cn, const float* cd) {
+  // A side (main operand): rows m, contraction contiguous.
+  auto load_a = [&](int64_t k0) {
 #pragma unroll
     for (int q = 0; q < AF4; ++q) {
       const int f = tid + 256 * q;
-      const int row = f >> 3, c4 = f & 7;
+      const int row = f / AC4, c4 = f % AC4;
       const int64_t gm = m0 + row, gk = k0 + 4 * c4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (gm < p.M && gk < klim) {
-        v = *reinterpret_cast<const f32x4*>(src + gm * ld + gk);
-        if (cn) {
+      if (gm < p.M && gk < kend) {
+        v = *reinterpret_cast<const f32x4*>(p.A + gm * p.lda + gk);
+        if (p.acn) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= cn[gk + e] / cd[gk + e];
+          for (int e = 0; e < 4; ++e) v[e] *= p.acn[gk + e] / p.acd[gk + e];
         }
-        v *= mul;
+      }
+      ra[q] = v;
+    }
+  };
+  // A side (LoRA operand): rows m, rank contiguous, partials summed, times s.
+  auto load_xa = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < AF4; ++q) {
+      const int f = tid + 256 * q;
+      const int row = f / AC4, c4 = f % AC4;
+      const int64_t gm = m0 + row, gk = k0 + 4 * c4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (gm < p.M && gk < p.r) {
+        const int64_t i = gm * p.r + gk;
+        v = *reinterpret_cast<const f32x4*>(p.xa.p + i);
+        for (int part = 1; part < p.xa.nparts; ++part)
+          v += *reinterpret_cast<const f32x4*>(p.xa.p + part * p.xa.stride + i);
+        if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
+        v *= p.xs;
       }
       ra[q] = v;
     }
@@ -99,8 +137,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
 #pragma unroll
     for (int q = 0; q < AF4; ++q) {
       const int f = tid + 256 * q;
-      const int row = f >> 3, c4 = f & 7;
-      *reinterpret_cast<f32x4*>(&As[buf][row * LDA + 4 * c4]) = ra[q];
+      const int row = f / AC4, c4 = f % AC4;
+      *reinterpret_cast<f32x4*>(&As(buf)[row * LDA + 4 * c4]) = ra[q];
     }
   };
   // B side.  fwd: rows n, contraction contiguous.  dx: rows = contraction.
@@ -110,7 +148,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
       const int f = tid + 256 * q;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (FWD) {
-        const int row = f >> 3, c4 = f & 7;
+        const int row = f / AC4, c4 = f % AC4;
         const int64_t gn = n0 + row, gk = k0 + 4 * c4;
         if (gn < p.Nc && gk < klim) v = *reinterpret_cast<const f32x4*>(src + gn * ld + gk);
       } else {
@@ -126,32 +164,31 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
     for (int q = 0; q < BF4; ++q) {
       const int f = tid + 256 * q;
       if (FWD) {
-        const int row = f >> 3, c4 = f & 7;
-        *reinterpret_cast<f32x4*>(&Bs[buf][row * LDB + 4 * c4]) = rb[q];
+        const int row = f / AC4, c4 = f % AC4;
+        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = rb[q];
       } else {
         const int row = f / (BN / 4), c4 = f % (BN / 4);
-        *reinterpret_cast<f32x4*>(&Bs[buf][row * LDB + 4 * c4]) = rb[q];
+        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = rb[q];
       }
     }
   };
   auto compute = [&](int buf) {
-    f32x4 av[MI][4];
+    const int kb = KH * hl;
+    f32x4 av[MI][KH / 4];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        av[i][q] = *reinterpret_cast<const f32x4*>(
-            &As[buf][(wm0 + i * 32 + l32) * LDA + 16 * hl + 4 * q]);
+      for (int q = 0; q < KH / 4; ++q)
+        av[i][q] = *reinterpret_cast<const f32x4*>(&As(buf)[(wm0 + i * 32 + l32) * LDA + kb + 4 * q]);
     if (FWD) {
-      f32x4 bv[NI][4];
+      f32x4 bv[NI][KH / 4];
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          bv[j][q] = *reinterpret_cast<const f32x4*>(
-              &Bs[buf][(wn0 + j * 32 + l32) * LDB + 16 * hl + 4 * q]);
+        for (int q = 0; q < KH / 4; ++q)
+          bv[j][q] = *reinterpret_cast<const f32x4*>(&Bs(buf)[(wn0 + j * 32 + l32) * LDB + kb + 4 * q]);
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
+      for (int s = 0; s < KH; ++s)
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -159,10 +196,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
             acc[i][j] = mfma32x32x2(av[i][s >> 2][s & 3], bv[j][s >> 2][s & 3], acc[i][j]);
     } else {
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
+      for (int s = 0; s < KH; ++s) {
         float bv[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) bv[j] = Bs[buf][(16 * hl + s) * LDB + wn0 + j * 32 + l32];
+        for (int j = 0; j < NI; ++j) bv[j] = Bs(buf)[(kb + s) * LDB + wn0 + j * 32 + l32];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -171,10 +208,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
       }
     }
   };
-  // Unpipelined contraction over the LoRA rank (r <= 128: at most 4 steps).
+  // Unpipelined contraction over the LoRA rank (r <= 128).
   auto lora_contraction = [&]() {
     for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
-      load_a(p.XA, p.r, k0, p.r, p.xs, nullptr, nullptr);
+      load_xa(k0);
       load_b(p.XB, FWD ? p.r : p.Nc, k0, p.r);
       __syncthreads();
       store_a(0);
@@ -206,7 +243,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   // Main contraction over [kbeg, kend), double buffered.
   const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
-    load_a(p.A, p.lda, kbeg, kend, 1.0f, p.acn, p.acd);
+    load_a(kbeg);
     load_b(p.B, p.ldb, kbeg, kend);
     store_a(0);
     store_b(0);
@@ -214,7 +251,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
     for (int64_t kt = 0; kt < nk; ++kt) {
       const int cur = (int)(kt & 1);
       if (kt + 1 < nk) {
-        load_a(p.A, p.lda, kbeg + (kt + 1) * BK, kend, 1.0f, p.acn, p.acd);
+        load_a(kbeg + (kt + 1) * BK);
         load_b(p.B, p.ldb, kbeg + (kt + 1) * BK, kend);
       }
       compute(cur);
@@ -235,8 +272,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
     for (int j = 0; j < NI; ++j) {
       const int64_t gn = n0 + wn0 + j * 32 + l32;
       if (gn >= p.Nc) continue;
-      float c = 1.0f;
-      if (p.nsplit == 1 && p.cn) c = p.cn[gn] / p.cd[gn];
+      const float c = (p.nsplit == 1 && p.cn) ? p.cn[gn] / p.cd[gn] : 1.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
@@ -252,7 +288,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
     }
 }
 
-// Sum of split-K partials in split order; optional DoRA column scale.
+// Sum of the split partials in split order, then the epilogue of the unsplit
+// kernel (Z = sum; Y = sum * cn/cd per column).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int nsplit,
                                                             int64_t M, int64_t Nc, float* C,
                                                             float* C2, const float* cn,

@@ -75,37 +75,46 @@ Split plan_split(int64_t L, int64_t other, int64_t want, int64_t q, int64_t min_
   return {len, (int)cdiv(L, len)};
 }
 
-struct GemmPlan {
-  int bm, bn;
-  Split k;
-};
-
-GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16) {
-  GemmPlan g;
-  if (bf16) {
-    g.bm = g.bn = 128;
-    const int64_t tiles = cdiv(M, 128) * cdiv(Nc, 128);
-    g.k = plan_split(Kc, tiles, 256, 64, 512);
-  } else {
-    const int64_t t128 = cdiv(M, 128) * cdiv(Nc, 128);
-    if (t128 >= 256) {
-      g.bm = g.bn = 128;
-      g.k = {rup(Kc, 32), 1};
-    } else {
-      g.bm = g.bn = 64;
-      const int64_t tiles = cdiv(M, 64) * cdiv(Nc, 64);
-      g.k = plan_split(Kc, tiles, 256, 32, 256);
-    }
-  }
-  return g;
+// Row range of the rank-side backward kernels: whole T (results written
+// directly, no reduction launch) when T is short or the column strips alone
+// fill the chip; otherwise split to about 512 blocks.
+Split plan_rows(int64_t T, int64_t strips) {
+  if (T <= 256 || strips >= 256) return {rup(T, SK_T), 1};
+  return plan_split(T, strips, 512, SK_T, SK_T);
 }
 
-// Workspace layout of one linear (forward and backward share the buffer).
+struct GemmPlan {
+  int bm, bn;
+  Split k;           // contraction split across blocks (fp32 only)
+};
+
+// bf16: the largest tile whose grid still covers most of the 256 CUs.
+// fp32: 128x128 when that fills the chip, else 64x64 with the contraction
+// split across blocks until about 256 blocks run.
+GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16) {
+  if (bf16) {
+    const int shapes[3][2] = {{256, 256}, {256, 128}, {128, 128}};
+    for (const auto& t : shapes)
+      if (cdiv(M, t[0]) * cdiv(Nc, t[1]) >= 200) return {t[0], t[1], {Kc, 1}};
+    return {128, 128, {Kc, 1}};
+  }
+  if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}};
+  const int64_t tiles = cdiv(M, 64) * cdiv(Nc, 64);
+  return {64, 64, plan_split(Kc, tiles, 256, 32, 256)};
+}
+
+// The consumers of the V partials (dX GEMM head, k4) sum them while staging
+// when the repeated reads stay small; otherwise a separate launch sums them.
+constexpr double kPartialRereadBytes = 64.0 * 1024 * 1024;
+
+// Workspace layout of one linear.  Forward and backward share the buffer.
 struct Layout {
   Split down, k3, k4;
   GemmPlan gf, gd;
-  size_t upart, xbf, gfpart;                        // forward
-  size_t vpart, v, dbpart, dmpart, gbf, gdpart, dapart;  // backward
+  int64_t strips;      // 64-column strips of dY (k3 grid x): V partial count
+  bool vreduce;        // V partials summed by a separate launch
+  size_t upart, xbf, gfpart;                          // forward
+  size_t vpart, v, dbpart, dmpart, gbf, gdpart, dapart;   // backward
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -119,24 +128,27 @@ Layout make_layout(const lora_linear* L) {
   Layout y;
   const int64_t T = L->tokens, K = L->in_dim, N = L->out_dim, r = L->rank;
   const bool bf = L->w_dtype == LORA_BF16;
-  y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, 256);
-  y.k3 = plan_split(T, cdiv(N, SK_C), 512, SK_T, SK_T);
-  y.k4 = plan_split(T, cdiv(K, SK_C), 512, SK_T, SK_T);
+  y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, SK_C);
+  y.strips = cdiv(N, SK_C);
+  y.k3 = plan_rows(T, y.strips);
+  y.k4 = plan_rows(T, cdiv(K, SK_C));
   y.gf = plan_gemm(T, N, K, bf);
   y.gd = plan_gemm(T, K, N, bf);
+  const double vbytes = 4.0 * y.strips * T * r;
+  y.vreduce = y.strips > 1 && vbytes * (cdiv(K, y.gd.bn) + cdiv(K, SK_C)) > kPartialRereadBytes;
   size_t off = 0;
-  y.upart = carve(off, sizeof(float) * y.down.n * T * r);
+  y.upart = carve(off, y.down.n > 1 ? sizeof(float) * y.down.n * T * r : 0);
   y.xbf = carve(off, bf ? sizeof(uint16_t) * T * K : 0);
   y.gfpart = carve(off, y.gf.k.n > 1 ? sizeof(float) * y.gf.k.n * T * N : 0);
   y.fwd_bytes = off;
   off = 0;
-  y.vpart = carve(off, sizeof(float) * cdiv(N, SK_C) * T * r);
-  y.v = carve(off, sizeof(float) * T * r);
-  y.dbpart = carve(off, sizeof(float) * y.k3.n * N * r);
-  y.dmpart = carve(off, (L->dora_mag ? sizeof(float) * y.k3.n * N : 0));
+  y.vpart = carve(off, y.strips > 1 ? sizeof(float) * y.strips * T * r : 0);
+  y.v = carve(off, (y.strips == 1 || y.vreduce) ? sizeof(float) * T * r : 0);
+  y.dbpart = carve(off, y.k3.n > 1 ? sizeof(float) * y.k3.n * N * r : 0);
+  y.dmpart = carve(off, (L->dora_mag && y.k3.n > 1) ? sizeof(float) * y.k3.n * N : 0);
   y.gbf = carve(off, bf ? sizeof(uint16_t) * T * N : 0);
   y.gdpart = carve(off, y.gd.k.n > 1 ? sizeof(float) * y.gd.k.n * T * K : 0);
-  y.dapart = carve(off, sizeof(float) * y.k4.n * r * K);
+  y.dapart = carve(off, y.k4.n > 1 ? sizeof(float) * y.k4.n * r * K : 0);
   y.bwd_bytes = off;
   return y;
 }
@@ -158,35 +170,20 @@ int check_linear(const lora_linear* L) {
 int hip_status() { return hipGetLastError() == hipSuccess ? LORA_OK : LORA_E_HIP; }
 
 // ----------------------------------------------------------- launchers ---
-template <int RP>
-void launch_down(const float* X, int64_t T, int64_t K, const float* A, int64_t r,
-                 const DropParams& d, Split s, float* Upart, uint16_t* Xbf, hipStream_t st) {
-  dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)s.n);
-  prof::Scope ps(st, "down_u", T, r, K, 2.0 * T * K * r,
-                 4.0 * (T * K + r * K + T * r) + (Xbf ? 2.0 * T * K : 0.0));
-  down_kernel<RP><<<grid, 256, 0, st>>>(X, T, K, A, r, d, s.len, Upart, Xbf);
+// Every kernel goes through here: 256 threads per block, on the caller's
+// stream, with the profile's packet-timestamp events when one is open.
+template <typename F, typename... Args>
+void launch_n(F kern, dim3 grid, unsigned threads, hipStream_t st, const prof::Scope& ps,
+              Args... args) {
+  hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, st, ps.start(), ps.stop(), 0, args...);
 }
-template <int RP>
-void launch_k3(const float* dY, int64_t T, int64_t N, const float* B, const float* U, int64_t r,
-               const float* mag, const float* nrm, const float* Z, Split s, float* Vpart,
-               float* dBpart, float* dmpart, uint16_t* gbf, hipStream_t st) {
-  dim3 grid((unsigned)cdiv(N, SK_C), (unsigned)s.n);
-  prof::Scope ps(st, "k3_v_db", T, N, r, 4.0 * T * N * r,
-                 4.0 * (T * N + T * r + 2 * N * r) + (Z ? 4.0 * T * N : 0.0) +
-                     (gbf ? 2.0 * T * N : 0.0));
-  k3_kernel<RP><<<grid, 256, 0, st>>>(dY, T, N, B, U, r, mag, nrm, Z, s.len, Vpart, dBpart,
-                                      dmpart, gbf);
-}
-template <int RP>
-void launch_k4(const float* X, int64_t T, int64_t K, const float* V, int64_t r,
-               const DropParams& d, Split s, float* dApart, hipStream_t st) {
-  dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)s.n);
-  prof::Scope ps(st, "k4_da", T, r, K, 2.0 * T * K * r, 4.0 * (T * K + T * r + 2 * r * K));
-  k4_kernel<RP><<<grid, 256, 0, st>>>(X, T, K, V, r, d, s.len, dApart);
+template <typename F, typename... Args>
+void launch(F kern, dim3 grid, hipStream_t st, const prof::Scope& ps, Args... args) {
+  launch_n(kern, grid, 256u, st, ps, args...);
 }
 
-#define LORA_RP_DISPATCH(rp, call)      \
-  switch (rp) {                         \
+#define LORA_RP_DISPATCH(rp, call)                    \
+  switch (rp) {                                       \
     case 16: { constexpr int RP = 16; call; } break;  \
     case 32: { constexpr int RP = 32; call; } break;  \
     case 64: { constexpr int RP = 64; call; } break;  \
@@ -197,47 +194,58 @@ void launch_reduce(const RedJob* jobs, int n, hipStream_t st) {
   RedJobs J;
   memset(&J, 0, sizeof(J));
   int64_t blocks = 0;
+  double bytes = 0.0;
   for (int i = 0; i < n; ++i) {
     J.job[i] = jobs[i];
     J.blk[i] = blocks;
     blocks += cdiv(jobs[i].n, 256);
+    bytes += 4.0 * (double)jobs[i].n * (jobs[i].nparts + 1 + jobs[i].accumulate);
   }
   J.blk[n] = blocks;
   J.njobs = n;
-  double bytes = 0.0;
-  for (int i = 0; i < n; ++i) bytes += 4.0 * (double)jobs[i].n * (jobs[i].nparts + 1 + jobs[i].accumulate);
-  prof::Scope ps(st, "reduce", jobs[0].n, n, jobs[0].nparts, 0.0, bytes);
-  if (blocks > 0) reduce_kernel<<<(unsigned)blocks, 256, 0, st>>>(J);
+  if (blocks == 0) return;
+  prof::Scope ps("reduce", jobs[0].n, n, jobs[0].nparts, 0.0, bytes);
+  launch(reduce_kernel, dim3((unsigned)blocks), st, ps, J);
 }
 
-void launch_gemm_f32(const GemmPlan& g, bool fwd, GemmF32Args a, hipStream_t st) {
+void launch_gemm_f32(const GemmPlan& g, bool fwd, const GemmF32Args& a, hipStream_t st) {
   dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
-  prof::Scope ps(st, fwd ? "gemm_f32_fwd" : "gemm_f32_dx", a.M, a.Nc, a.Kc,
-                 2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
-                 4.0 * (a.M * a.Kc + a.Nc * a.Kc + a.M * a.Nc * (a.C2 ? 2 : 1)));
-  if (g.bm == 128) {
-    if (fwd) gemm_f32_kernel<128, 128, true><<<grid, 256, 0, st>>>(a);
-    else gemm_f32_kernel<128, 128, false><<<grid, 256, 0, st>>>(a);
-  } else {
-    if (fwd) gemm_f32_kernel<64, 64, true><<<grid, 256, 0, st>>>(a);
-    else gemm_f32_kernel<64, 64, false><<<grid, 256, 0, st>>>(a);
+  {
+    prof::Scope ps(fwd ? "gemm_f32_fwd" : "gemm_f32_dx", a.M, a.Nc, a.Kc,
+                   2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
+                   4.0 * (a.M * a.Kc + a.Nc * a.Kc + a.M * a.Nc * (a.C2 ? 2 : 1)));
+    if (g.bm == 128) {
+      if (fwd) launch(gemm_f32_kernel<128, 128, true>, grid, st, ps, a);
+      else launch(gemm_f32_kernel<128, 128, false>, grid, st, ps, a);
+    } else {
+      if (fwd) launch(gemm_f32_kernel<64, 64, true>, grid, st, ps, a);
+      else launch(gemm_f32_kernel<64, 64, false>, grid, st, ps, a);
+    }
+  }
+  if (g.k.n > 1) {
+    const int64_t n4 = cdiv(a.M * a.Nc, 4);
+    prof::Scope ps("splitk_reduce", a.M, a.Nc, g.k.n, 0.0,
+                   4.0 * a.M * a.Nc * (g.k.n + (a.C2 ? 2 : 1)));
+    launch(splitk_reduce_kernel, dim3((unsigned)cdiv(n4, 256)), st, ps, (const float*)a.part,
+           g.k.n, a.M, a.Nc, a.C, a.C2, a.cn, a.cd);
   }
 }
 
-void launch_gemm_bf16(const GemmPlan& g, bool fwd, GemmBf16Args a, hipStream_t st) {
-  dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
-  prof::Scope ps(st, fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
+void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st) {
+  const dim3 grid((unsigned)(cdiv(a.Nc, g.bn) * cdiv(a.M, g.bm)));
+  prof::Scope ps(fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
                  2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                  2.0 * (a.M * a.Kc + a.Nc * a.Kc) + 4.0 * a.M * a.Nc * (a.C2 ? 2 : 1));
-  if (fwd) gemm_bf16_kernel<128, 128, true><<<grid, 256, 0, st>>>(a);
-  else gemm_bf16_kernel<128, 128, false><<<grid, 256, 0, st>>>(a);
-}
-
-void launch_splitk_reduce(const float* part, int nsplit, int64_t M, int64_t Nc, float* C,
-                          float* C2, const float* cn, const float* cd, hipStream_t st) {
-  const int64_t n4 = cdiv(M * Nc, 4);
-  prof::Scope ps(st, "splitk_reduce", M, Nc, nsplit, 0.0, 4.0 * M * Nc * (nsplit + (C2 ? 2 : 1)));
-  splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(part, nsplit, M, Nc, C, C2, cn, cd);
+#define LORA_BF16_TILE(BM_, BN_)                                                      \
+  if (g.bm == BM_ && g.bn == BN_) {                                                   \
+    if (fwd) launch_n(gemm_bf16_kernel<BM_, BN_, true>, grid, 512u, st, ps, a);        \
+    else launch_n(gemm_bf16_kernel<BM_, BN_, false>, grid, 512u, st, ps, a);           \
+    return;                                                                           \
+  }
+  LORA_BF16_TILE(256, 256)
+  LORA_BF16_TILE(256, 128)
+  LORA_BF16_TILE(128, 128)
+#undef LORA_BF16_TILE
 }
 
 }  // namespace
@@ -289,44 +297,47 @@ int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U, flo
   if (!al16(X) || !al16(Y) || !al16(U) || (Z && !al16(Z))) return LORA_E_ALIGN;
   if (!drop_valid(drop)) return LORA_E_INVALID;
   const Layout y = make_layout(lin);
-  if (!ws || ws_bytes < y.fwd_bytes || !al16(ws)) return LORA_E_WORKSPACE;
+  if (y.fwd_bytes && (!ws || ws_bytes < y.fwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
   const bool bf = lin->w_dtype == LORA_BF16;
   char* w = (char*)ws;
-  float* Upart = (float*)(w + y.upart);
+  float* Upart = y.down.n > 1 ? (float*)(w + y.upart) : nullptr;
   uint16_t* Xbf = bf ? (uint16_t*)(w + y.xbf) : nullptr;
   const DropParams d = make_drop(drop);
 
-  // U = X~ A^T (split over K), then the fixed-order sum into U.
-  LORA_RP_DISPATCH(rank_pad(r), launch_down<RP>(X, T, K, lin->A, r, d, y.down, Upart, Xbf, st));
-  RedJob ju = {Upart, U, nullptr, T * r, 1, y.down.n, 0, 1.0f};
-  launch_reduce(&ju, 1, st);
+  // U = X~ A^T, split over K; the GEMM sums the splits while staging U and
+  // stores the summed U.
+  {
+    prof::Scope ps("down_u", T, r, K, 2.0 * T * K * r,
+                   4.0 * (T * K + r * K + T * r) + (Xbf ? 2.0 * T * K : 0.0));
+    const dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)y.down.n);
+    LORA_RP_DISPATCH(rank_pad(r), launch(down_kernel<RP>, grid, st, ps, X, T, K, lin->A, r, d,
+                                         y.down.len, Upart, U, Xbf));
+  }
+  const LoraOperand xa = y.down.n > 1 ? LoraOperand{Upart, T * r, y.down.n, U}
+                                      : LoraOperand{U, T * r, 1, nullptr};
 
   // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
-  float* gpart = y.gf.k.n > 1 ? (float*)(w + y.gfpart) : nullptr;
-  float* C2 = Z;   // Z is written whenever the caller passes it
   if (bf) {
     GemmBf16Args a;
     memset(&a, 0, sizeof(a));
     a.A = Xbf; a.lda = K; a.B = (const uint16_t*)lin->W; a.ldb = K;
     a.M = T; a.Nc = N; a.Kc = K;
-    a.XA = U; a.XB = lin->B; a.r = r; a.xs = lin->scale;
-    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
-    a.C = Y; a.C2 = C2; a.cn = lin->dora_mag; a.cd = lin->dora_norm; a.part = gpart;
+    a.xa = xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
+    a.C = Y; a.C2 = Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
     launch_gemm_bf16(y.gf, true, a, st);
   } else {
     GemmF32Args a;
     memset(&a, 0, sizeof(a));
     a.A = X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
     a.M = T; a.Nc = N; a.Kc = K;
-    a.XA = U; a.XB = lin->B; a.r = r; a.xs = lin->scale;
+    a.xa = xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
     a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
-    a.C = Y; a.C2 = C2; a.cn = lin->dora_mag; a.cd = lin->dora_norm; a.part = gpart;
+    a.C = Y; a.C2 = Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
+    a.part = y.gf.k.n > 1 ? (float*)(w + y.gfpart) : nullptr;
     launch_gemm_f32(y.gf, true, a, st);
   }
-  if (y.gf.k.n > 1)
-    launch_splitk_reduce(gpart, y.gf.k.n, T, N, Y, C2, lin->dora_mag, lin->dora_norm, st);
   return hip_status();
 }
 
@@ -343,36 +354,50 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
   if (dMag && (!dora || !Z)) return LORA_E_INVALID;
   if (!drop_valid(drop)) return LORA_E_INVALID;
   const Layout y = make_layout(lin);
-  if (!ws || ws_bytes < y.bwd_bytes || !al16(ws)) return LORA_E_WORKSPACE;
+  if (y.bwd_bytes && (!ws || ws_bytes < y.bwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
   const bool bf = lin->w_dtype == LORA_BF16;
   char* w = (char*)ws;
-  float* Vpart = (float*)(w + y.vpart);
-  float* V = (float*)(w + y.v);
-  float* dBpart = (float*)(w + y.dbpart);
-  float* dmpart = dMag ? (float*)(w + y.dmpart) : nullptr;
-  uint16_t* gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
-  float* dApart = (float*)(w + y.dapart);
   const DropParams d = make_drop(drop);
   const int rp = rank_pad(r);
+  const int acc = accumulate ? 1 : 0;
 
-  // One pass over dY: V partials, dB partials, DoRA dm partials, bf16 g.
-  LORA_RP_DISPATCH(rp, launch_k3<RP>(dY, T, N, lin->B, U, r, lin->dora_mag, lin->dora_norm,
-                                     dMag ? Z : nullptr, y.k3, Vpart, dBpart, dmpart, gbf, st));
-  RedJob jv = {Vpart, V, nullptr, T * r, 1, (int)cdiv(N, SK_C), 0, 1.0f};
-  launch_reduce(&jv, 1, st);
+  // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
+  K3Out o;
+  o.Vpart = y.strips > 1 ? (float*)(w + y.vpart) : nullptr;
+  o.V = (y.strips == 1 || y.vreduce) ? (float*)(w + y.v) : nullptr;
+  o.dBpart = y.k3.n > 1 ? (float*)(w + y.dbpart) : nullptr;
+  o.dB = dB;
+  o.dmpart = (dMag && y.k3.n > 1) ? (float*)(w + y.dmpart) : nullptr;
+  o.dm = dMag;
+  o.gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
+  o.scale = lin->scale;
+  o.accumulate = acc;
+  {
+    const float* Zin = dMag ? Z : nullptr;
+    prof::Scope ps("k3_v_db", T, N, r, 4.0 * T * N * r,
+                   4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
+                       (o.gbf ? 2.0 * T * N : 0.0));
+    const dim3 grid((unsigned)y.strips, (unsigned)y.k3.n);
+    LORA_RP_DISPATCH(rp, launch(k3_kernel<RP>, grid, st, ps, dY, T, N, lin->B, U, r,
+                                lin->dora_mag, lin->dora_norm, Zin, y.k3.len, o));
+  }
+  if (y.vreduce) {
+    RedJob jv = {o.Vpart, o.V, nullptr, T * r, 1, (int)y.strips, 0, 1.0f};
+    launch_reduce(&jv, 1, st);
+  }
+  const LoraOperand xv = (y.strips == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
+                                                      : LoraOperand{o.Vpart, T * r, (int)y.strips, nullptr};
 
   if (dX) {
-    float* gpart = y.gd.k.n > 1 ? (float*)(w + y.gdpart) : nullptr;
     if (bf) {
       GemmBf16Args a;
       memset(&a, 0, sizeof(a));
-      a.A = gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
+      a.A = o.gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
       a.M = T; a.Nc = K; a.Kc = N;
-      a.XA = V; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
-      a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
-      a.C = dX; a.part = gpart;
+      a.xa = xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
+      a.C = dX;
       launch_gemm_bf16(y.gd, false, a, st);
     } else {
       GemmF32Args a;
@@ -380,23 +405,31 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
       a.A = dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
       a.B = (const float*)lin->W; a.ldb = K;
       a.M = T; a.Nc = K; a.Kc = N;
-      a.XA = V; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
+      a.xa = xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
       a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
-      a.C = dX; a.part = gpart;
+      a.C = dX;
+      a.part = y.gd.k.n > 1 ? (float*)(w + y.gdpart) : nullptr;
       launch_gemm_f32(y.gd, false, a, st);
     }
-    if (y.gd.k.n > 1) launch_splitk_reduce(gpart, y.gd.k.n, T, K, dX, nullptr, nullptr, nullptr, st);
   }
 
-  LORA_RP_DISPATCH(rp, launch_k4<RP>(X, T, K, V, r, d, y.k4, dApart, st));
+  float* dApart = y.k4.n > 1 ? (float*)(w + y.dapart) : nullptr;
+  {
+    prof::Scope ps("k4_da", T, r, K, 2.0 * T * K * r, 4.0 * (T * K + T * r + 2 * r * K));
+    const dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)y.k4.n);
+    LORA_RP_DISPATCH(rp, launch(k4_kernel<RP>, grid, st, ps, X, T, K, xv.p, xv.nparts, r, d,
+                                y.k4.len, dApart, dA, lin->scale, acc));
+  }
 
+  // Gradient splits over token ranges: one fixed-order reduction launch.
   RedJob jobs[3];
   int nj = 0;
-  const int acc = accumulate ? 1 : 0;
-  jobs[nj++] = {dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
-  jobs[nj++] = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
-  if (dMag) jobs[nj++] = {dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
-  launch_reduce(jobs, nj, st);
+  if (y.k3.n > 1) {
+    jobs[nj++] = {o.dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
+    if (dMag) jobs[nj++] = {o.dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
+  }
+  if (y.k4.n > 1) jobs[nj++] = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
+  if (nj) launch_reduce(jobs, nj, st);
   return hip_status();
 }
 
@@ -421,13 +454,13 @@ int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, floa
   double* part = (double*)(w + 256);
   int* flags = (int*)(w + 256 + 1024 * sizeof(double));
   {
-    prof::Scope ps(st, "gradnorm_pass1", n, nb, 0, 2.0 * n, 4.0 * n);
-    gradnorm_pass1<<<nb, 256, 0, st>>>(grads, n, per, part, flags);
+    prof::Scope ps("gradnorm_pass1", n, nb, 0, 2.0 * n, 4.0 * n);
+    launch(gradnorm_pass1, dim3(nb), st, ps, grads, n, per, part, flags);
   }
   {
-    prof::Scope ps(st, "gradnorm_pass2", nb, 1, 0, 0.0, 12.0 * nb);
-    gradnorm_pass2<<<1, 256, 0, st>>>(part, flags, nb, n_pred_tokens, max_norm, d_scale, d_stats,
-                                      norm_out);
+    prof::Scope ps("gradnorm_pass2", nb, 1, 0, 0.0, 12.0 * nb);
+    launch(gradnorm_pass2, dim3(1), st, ps, (const double*)part, (const int*)flags, nb,
+           n_pred_tokens, max_norm, d_scale, d_stats, norm_out);
   }
   if (hip_status()) return LORA_E_HIP;
   if (h_norm) {
@@ -483,9 +516,9 @@ int lora_adamw_step(float* params, const float* grads, float* m, float* v,
   if (blocks == 0) return LORA_OK;
   int64_t total = 0;
   for (int i = 0; i < n_seg; ++i) total += segs[i].count;
-  prof::Scope ps((hipStream_t)stream, "adamw", total, n_seg, 0, 0.0, 28.0 * total);
-  adamw_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(params, grads, m, v, S, H,
-                                                                   d_scale);
+  prof::Scope ps("adamw", total, n_seg, 0, 0.0, 28.0 * total);
+  launch(adamw_kernel, dim3((unsigned)blocks), (hipStream_t)stream, ps, params, grads, m, v, S, H,
+         d_scale);
   return hip_status();
 }
 
@@ -495,9 +528,9 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim, 
   if (!drop_valid(drop)) return LORA_E_INVALID;
   const DropParams d = make_drop(drop);
   const int64_t n = tokens * in_dim;
-  prof::Scope ps((hipStream_t)stream, "dropout_mask", tokens, in_dim, 0, 0.0, (double)n);
-  dropout_mask_kernel<<<(unsigned)cdiv(n, 256), 256, 0, (hipStream_t)stream>>>(d, tokens, in_dim,
-                                                                               mask);
+  prof::Scope ps("dropout_mask", tokens, in_dim, 0, 0.0, (double)n);
+  launch(dropout_mask_kernel, dim3((unsigned)cdiv(n, 256)), (hipStream_t)stream, ps, d, tokens,
+         in_dim, mask);
   return hip_status();
 }
 
@@ -518,16 +551,16 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream) {
   const unsigned grid = (unsigned)cdiv(N, ROWS);
   hipStream_t st = (hipStream_t)stream;
   const int rp = lora_on ? rank_pad(r) : 16;
-  prof::Scope ps(st, "dora_rownorm", N, K, r, 2.0 * N * K * (r + 1),
+  prof::Scope ps("dora_rownorm", N, K, r, 2.0 * N * K * (r + 1),
                  (lin->w_dtype == LORA_BF16 ? 2.0 : 4.0) * N * K + 4.0 * r * (N + K) + 4.0 * N);
   if (lin->w_dtype == LORA_BF16) {
     const uint16_t* W = (const uint16_t*)lin->W;
-    LORA_RP_DISPATCH(rp, (dora_rownorm_kernel<uint16_t, RP, ROWS><<<grid, 256, 0, st>>>(
-                             W, N, K, A, B, r, s, out_norm)));
+    LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<uint16_t, RP, ROWS>, dim3(grid), st, ps, W, N,
+                                K, A, B, r, s, out_norm));
   } else {
     const float* W = (const float*)lin->W;
-    LORA_RP_DISPATCH(rp, (dora_rownorm_kernel<float, RP, ROWS><<<grid, 256, 0, st>>>(
-                             W, N, K, A, B, r, s, out_norm)));
+    LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<float, RP, ROWS>, dim3(grid), st, ps, W, N, K,
+                                A, B, r, s, out_norm));
   }
   return hip_status();
 }

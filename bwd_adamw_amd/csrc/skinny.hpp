@@ -12,10 +12,13 @@
 // "Backward Bug Hunts ...", "Bug #1" for the dA = s (B^T g) x^T factor;
 // "4.3. Training Guide", "Dropout" for the mask, recomputed inline).
 //
-// Each block streams a 64 x 64 tile of the activation per stage through LDS
-// and contracts it against the small rank-side operand with MFMA.  The long
-// axis of each contraction is split across blocks; every block writes its own
-// partial and fixed-order reducers sum them (deterministic, no atomics).
+// Each block streams 64 x 64 tiles of the activation through LDS and
+// contracts them against the small rank-side operand with MFMA.  The long
+// axis of each contraction may be split across blocks; each block then writes
+// its own partial, and the partials are summed in split order by whoever
+// reads them next (the frozen GEMM while staging U or V, k4 while staging V)
+// or by reduce_kernel into the gradient arena.  No floating-point atomics and
+// no cross-block synchronisation inside a kernel.
 #pragma once
 #include "common.hpp"
 
@@ -26,22 +29,23 @@ constexpr int SK_C = 64;      // columns per stage
 constexpr int SK_LD = SK_C + 4;
 
 // ---------------------------------------------------------------------------
-// down: Upart[split][t][j] = sum_{k in split} X~[t,k] A[j,k].  Optionally also
-// writes the unmasked bf16 copy of X (used by the bf16 frozen GEMM).
+// down: Upart[split][t][j] = sum_{k in split} X~[t,k] A[j,k]; also writes the
+// unmasked bf16 copy of X (used by the bf16 frozen GEMM) when Xbf != NULL.
 // Grid: (ceil(T/64), nsplit).  RP = rank padded to a multiple of 16.
+// With one split the block writes U itself.
 // ---------------------------------------------------------------------------
 template <int RP>
 __global__ __launch_bounds__(256) void down_kernel(const float* __restrict__ X, int64_t T,
                                                    int64_t K, const float* __restrict__ A,
                                                    int64_t r, DropParams drop, int64_t ksplit,
-                                                   float* __restrict__ Upart,
+                                                   float* __restrict__ Upart, float* __restrict__ U,
                                                    uint16_t* __restrict__ Xbf) {
   __shared__ __attribute__((aligned(16))) float Xs[SK_T * SK_LD];
   __shared__ __attribute__((aligned(16))) float As_[RP * SK_LD];
   constexpr int JG = RP / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * SK_T;
-  const int split = blockIdx.y;
+  const int split = blockIdx.y, nsplit = gridDim.y;
   const int64_t kb = (int64_t)split * ksplit, ke = min(K, kb + ksplit);
   const int l16 = lane & 15, h = lane >> 4;
 
@@ -50,7 +54,6 @@ __global__ __launch_bounds__(256) void down_kernel(const float* __restrict__ X, 
   for (int j = 0; j < JG; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t k0 = kb; k0 < ke; k0 += SK_C) {
-    // X tile: 64 rows x 64 cols = 1024 float4, 4 per thread.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int f = tid + 256 * q;
@@ -71,7 +74,6 @@ __global__ __launch_bounds__(256) void down_kernel(const float* __restrict__ X, 
       }
       *reinterpret_cast<f32x4*>(&Xs[row * SK_LD + 4 * c4]) = v;
     }
-    // A tile: RP rows x 64 cols.
 #pragma unroll
     for (int q = 0; q < RP / 16; ++q) {
       const int f = tid + 256 * q;
@@ -98,13 +100,14 @@ __global__ __launch_bounds__(256) void down_kernel(const float* __restrict__ X, 
     }
     __syncthreads();
   }
+  float* dst = nsplit == 1 ? U : Upart + (int64_t)split * T * r;
 #pragma unroll
   for (int j = 0; j < JG; ++j)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t t = t0 + 16 * wave + row16(v, lane);
       const int64_t jj = 16 * j + l16;
-      if (t < T && jj < r) Upart[((int64_t)split * T + t) * r + jj] = acc[j][v];
+      if (t < T && jj < r) dst[t * r + jj] = acc[j][v];
     }
 }
 
@@ -115,14 +118,26 @@ __global__ __launch_bounds__(256) void down_kernel(const float* __restrict__ X, 
 //   dBpart[y][n][j]  = sum_{t in range} g[t,n] U[t,j]
 //   dmpart[y][n]     = sum_{t in range} dY[t,n] Z[t,n]          (DoRA)
 //   gbf[t][n]        = bf16(g)                                   (optional)
+// With one strip V is written directly; with one row range dB (and dm) are
+// scaled and written (or added) directly.
 // ---------------------------------------------------------------------------
+struct K3Out {
+  float* Vpart;
+  float* V;
+  float* dBpart;
+  float* dB;
+  float* dmpart;
+  float* dm;
+  uint16_t* gbf;
+  float scale;
+  int accumulate;
+};
+
 template <int RP>
 __global__ __launch_bounds__(256) void k3_kernel(
     const float* __restrict__ dY, int64_t T, int64_t N, const float* __restrict__ B,
     const float* __restrict__ U, int64_t r, const float* __restrict__ mag,
-    const float* __restrict__ nrm, const float* __restrict__ Z, int64_t tsplit,
-    float* __restrict__ Vpart, float* __restrict__ dBpart, float* __restrict__ dmpart,
-    uint16_t* __restrict__ gbf) {
+    const float* __restrict__ nrm, const float* __restrict__ Z, int64_t tsplit, K3Out o) {
   __shared__ __attribute__((aligned(16))) float Gs[SK_T * SK_LD];
   __shared__ __attribute__((aligned(16))) float Bt[RP * SK_LD];        // B^T tile [j][n]
   __shared__ __attribute__((aligned(16))) float Us[SK_T * (RP + 4)];   // U tile [t][j]
@@ -135,15 +150,14 @@ __global__ __launch_bounds__(256) void k3_kernel(
   const int64_t tb = (int64_t)blockIdx.y * tsplit, te = min(T, tb + tsplit);
   const int c4 = tid & 15;               // this thread's column quad (fixed)
   const int64_t ncol = n0 + 4 * c4;
+  const int nstrip = gridDim.x, nts = gridDim.y;
 
-  // Column multipliers (DoRA c = mag/norm) of this thread's 4 columns.
   float cmul[4] = {1.f, 1.f, 1.f, 1.f};
   if (mag) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (ncol + e < N) cmul[e] = mag[ncol + e] / nrm[ncol + e];
   }
-  // B^T tile: Bt[j][n] = B[n0 + n][j]; loaded once.
   for (int i = tid; i < RP * SK_C; i += 256) {
     const int j = i / SK_C, n = i % SK_C;
     float v = 0.f;
@@ -151,10 +165,11 @@ __global__ __launch_bounds__(256) void k3_kernel(
     Bt[j * SK_LD + n] = v;
   }
 
-  f32x4 accB[JG];   // dB partial: rows n = 16*wave + ..., cols j
+  f32x4 accB[JG];
 #pragma unroll
   for (int j = 0; j < JG; ++j) accB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dm[4] = {0.f, 0.f, 0.f, 0.f};
+  float* vdst = nstrip == 1 ? o.V : o.Vpart + (int64_t)blockIdx.x * T * r;
 
   for (int64_t t0 = tb; t0 < te; t0 += SK_T) {
     __syncthreads();
@@ -172,9 +187,9 @@ __global__ __launch_bounds__(256) void k3_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] *= cmul[e];
-        if (gbf) {
+        if (o.gbf) {
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(gbf + t * N + ncol) = b;
+          *reinterpret_cast<u32x2*>(o.gbf + t * N + ncol) = b;
         }
       }
       *reinterpret_cast<f32x4*>(&Gs[row * SK_LD + 4 * c4]) = v;
@@ -188,8 +203,7 @@ __global__ __launch_bounds__(256) void k3_kernel(
     }
     __syncthreads();
 
-    // V partial for rows 16*wave.. of this stage: contraction over the strip.
-    {
+    {   // V contribution of this strip for rows 16*wave.. of the stage
       f32x4 gv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(256) void k3_kernel(
         for (int v = 0; v < 4; ++v) {
           const int64_t t = t0 + 16 * wave + row16(v, lane);
           const int64_t jj = 16 * j + l16;
-          if (t < te && jj < r) Vpart[((int64_t)blockIdx.x * T + t) * r + jj] = accV[j][v];
+          if (t < te && jj < r) vdst[t * r + jj] = accV[j][v];
         }
     }
     // dB partial: rows n = 16*wave + l16 (A operand g^T), contraction over t.
@@ -223,37 +237,55 @@ __global__ __launch_bounds__(256) void k3_kernel(
       for (int j = 0; j < JG; ++j) accB[j] = mfma16x16x4(a, Us[tt * LDU + 16 * j + l16], accB[j]);
     }
   }
-  // dB partial out: accB[j][v] = dB[n = 16*wave + 4*(l/16) + v][j = 16j + l16]
+
+  // dB (and dm) of this strip: direct when there is one row range.
+  const bool bdirect = nts == 1;
 #pragma unroll
   for (int j = 0; j < JG; ++j)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t n = n0 + 16 * wave + row16(v, lane);
       const int64_t jj = 16 * j + l16;
-      if (n < N && jj < r) dBpart[((int64_t)blockIdx.y * N + n) * r + jj] = accB[j][v];
+      if (n < N && jj < r) {
+        if (bdirect) {
+          const float x = accB[j][v] * o.scale;
+          o.dB[n * r + jj] = o.accumulate ? o.dB[n * r + jj] + x : x;
+        } else {
+          o.dBpart[((int64_t)blockIdx.y * N + n) * r + jj] = accB[j][v];
+        }
+      }
     }
-  if (dmpart) {
-    // Reduce the per-thread column sums over the 16 row groups in fixed order.
+  if (o.dm) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[tid >> 4][4 * c4 + e] = dm[e];
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 64 && n0 + tid < N) {
       float s = 0.f;
       for (int g = 0; g < 16; ++g) s += red[g][tid];
-      if (n0 + tid < N) dmpart[(int64_t)blockIdx.y * N + n0 + tid] = s;
+      if (bdirect) {
+        s /= nrm[n0 + tid];
+        o.dm[n0 + tid] = o.accumulate ? o.dm[n0 + tid] + s : s;
+      } else {
+        o.dmpart[(int64_t)blockIdx.y * N + n0 + tid] = s;
+      }
     }
   }
+
 }
 
 // ---------------------------------------------------------------------------
-// k4: dApart[y][j][k] = sum_{t in range y} V[t,j] X~[t,k].
+// k4: dApart[y][j][k] = sum_{t in range y} V[t,j] X~[t,k], V given as vparts
+// partials [vparts][T][r] summed in order while staging.
 // Grid: (ceil(K/64), nts).  Wave w owns columns 16w..16w+15 of the strip.
+// With one row range the block scales and writes (or adds) dA itself.
 // ---------------------------------------------------------------------------
 template <int RP>
 __global__ __launch_bounds__(256) void k4_kernel(const float* __restrict__ X, int64_t T,
                                                  int64_t K, const float* __restrict__ V,
-                                                 int64_t r, DropParams drop, int64_t tsplit,
-                                                 float* __restrict__ dApart) {
+                                                 int vparts, int64_t r, DropParams drop,
+                                                 int64_t tsplit, float* __restrict__ dApart,
+                                                 float* __restrict__ dA, float scale,
+                                                 int accumulate) {
   __shared__ __attribute__((aligned(16))) float Xs[SK_T * SK_LD];
   __shared__ __attribute__((aligned(16))) float Vs[SK_T * (RP + 4)];
   constexpr int JG = RP / 16;
@@ -264,6 +296,7 @@ __global__ __launch_bounds__(256) void k4_kernel(const float* __restrict__ X, in
   const int64_t tb = (int64_t)blockIdx.y * tsplit, te = min(T, tb + tsplit);
   const int c4 = tid & 15;
   const int64_t kcol = k0 + 4 * c4;
+  const int nts = gridDim.y;
 
   f32x4 acc[JG];
 #pragma unroll
@@ -290,7 +323,12 @@ __global__ __launch_bounds__(256) void k4_kernel(const float* __restrict__ X, in
       const int row = i / (RP / 4), q = i % (RP / 4);
       const int64_t t = t0 + row;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (t < te && 4 * q < r) v = *reinterpret_cast<const f32x4*>(V + t * r + 4 * q);
+      if (t < te && 4 * q < r) {
+        const int64_t i = t * r + 4 * q;
+        v = *reinterpret_cast<const f32x4*>(V + i);
+        for (int part = 1; part < vparts; ++part)
+          v += *reinterpret_cast<const f32x4*>(V + part * T * r + i);
+      }
       *reinterpret_cast<f32x4*>(&Vs[row * LDV + 4 * q]) = v;
     }
     __syncthreads();
@@ -309,13 +347,20 @@ __global__ __launch_bounds__(256) void k4_kernel(const float* __restrict__ X, in
     for (int v = 0; v < 4; ++v) {
       const int64_t jj = 16 * j + row16(v, lane);
       const int64_t k = k0 + 16 * wave + l16;
-      if (jj < r && k < K) dApart[((int64_t)blockIdx.y * r + jj) * K + k] = acc[j][v];
+      if (jj < r && k < K) {
+        if (nts == 1) {
+          const float x = acc[j][v] * scale;
+          dA[jj * K + k] = accumulate ? dA[jj * K + k] + x : x;
+        } else {
+          dApart[((int64_t)blockIdx.y * r + jj) * K + k] = acc[j][v];
+        }
+      }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Fixed-order reduction of partials: out[i] (+)= alpha * sum_p part[p][i]
-// (optionally divided by div[i % divn]).  Up to 4 independent jobs per launch.
+// (/ div[i % divn]).  Up to 4 independent jobs per launch.
 // ---------------------------------------------------------------------------
 struct RedJob {
   const float* part;
@@ -339,11 +384,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(RedJobs jobs) {
   const RedJob& J = jobs.job[j];
   const int64_t i = ((int64_t)blockIdx.x - jobs.blk[j]) * 256 + threadIdx.x;
   if (i >= J.n) return;
-  float s = J.part[i];
-  for (int q = 1; q < J.nparts; ++q) s += J.part[(int64_t)q * J.n + i];
-  s *= J.alpha;
-  if (J.div) s /= J.div[i % J.divn];
-  J.out[i] = J.accumulate ? J.out[i] + s : s;
+  sum_partials(J.part, J.n, J.nparts, i, J.alpha, J.div, J.div ? i % J.divn : 0, J.out,
+               J.accumulate);
 }
 
 // ---------------------------------------------------------------------------

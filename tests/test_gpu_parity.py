@@ -447,11 +447,46 @@ def test_seeded_runs_give_identical_adapters():
 
 
 def test_invalid_arguments_raise_before_work():
-    c = _gpu(_linear_case(16, 64, 64, 4))
-    lin = L.make_linear(c["Wq"], c["A"], c["B"], 2.0, 16)
-    Y = torch.zeros(16, 64, device=DEV)
-    U = torch.zeros(16, 4, device=DEV)
+    T, K, N, r = 128, 2048, 2048, 8          # a shape that needs split partials
+    c = _gpu(_linear_case(T, K, N, r))
+    lin = L.make_linear(c["Wq"], c["A"], c["B"], 2.0, T)
+    assert L.lora_workspace_bytes(lin) > 1024
+    Y = torch.zeros(T, N, device=DEV)
+    U = torch.zeros(T, r, device=DEV)
     with pytest.raises(L.LoraError) as e:
         L.lora_forward(lin, c["X"], Y, U, None, None, torch.empty(16, device=DEV, dtype=torch.uint8))
     assert e.value.status == -5
-    assert torch.count_nonzero(Y).item() == 0
+    bad = L.make_dropout(1, 0, 0, 0, 0, 1.5)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_forward(lin, c["X"], Y, U, None, bad, None)
+    assert e.value.status == -1
+    assert torch.count_nonzero(Y).item() == 0 and torch.count_nonzero(U).item() == 0
+
+
+@pytest.mark.parametrize("T,K,N,r", [(128, 2048, 2048, 8), (300, 520, 1096, 16)])
+def test_workspace_contents_do_not_matter(T, K, N, r):
+    """The workspace only carries split partials that each call writes before
+    reading: a garbage-filled workspace gives bitwise the results of a zeroed
+    one, and repeated calls on one workspace stay equal."""
+    c = _gpu(_linear_case(T, K, N, r, seed=12))
+    lin = L.make_linear(c["Wq"], c["A"], c["B"], 2.0, T)
+    nb = L.lora_workspace_bytes(lin)
+    outs = []
+    for fill in ("zero", "garbage", "reuse"):
+        if fill != "reuse":
+            ws = torch.zeros(nb, device=DEV, dtype=torch.uint8)
+            if fill == "garbage":
+                ws.random_(0, 256)
+        drop = L.make_dropout(7, 1, 0, 0, 2, 0.1)
+        Y = torch.empty(T, N, device=DEV)
+        U = torch.empty(T, r, device=DEV)
+        dX = torch.empty(T, K, device=DEV)
+        dA = torch.empty(r, K, device=DEV)
+        dB = torch.empty(N, r, device=DEV)
+        L.lora_forward(lin, c["X"], Y, U, None, drop, ws)
+        L.lora_backward(lin, c["X"], c["dY"], U, None, dX, dA, dB, None, False, drop, ws)
+        torch.cuda.synchronize()
+        outs.append((Y, U, dX, dA, dB))
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
