@@ -404,8 +404,9 @@ def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
     element whose gradient is within the path's error of zero may move by up
     to 2 lr either way.  Elements are compared where every step's reference
     gradient exceeds `floor` times the segment's largest, with floor = 1e-3
-    for float32-exact gradients and 0.1 for the bf16-rounded magnitude
-    gradient (whose error is ~1e-3 of the largest)."""
+    for float32-exact gradients and 0.1 for bf16-affected ones (the DoRA
+    magnitude gradient, and on bf16 DoRA slots every segment after the first
+    step), whose error is ~1e-3 of the largest."""
     cfg = WL.get_config(wl)
     _say("e2e", name)
     for slot, ost, hist in _e2e(cfg, layers, tokens, steps):
@@ -420,8 +421,13 @@ def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
             g_gpu = np64(grads)
             for kind, sl in seg.items():
                 e = rel_err(g_gpu[sl], g_ref[sl])
-                bar = TOL[cfg.w_dtype] if kind == L.KIND_MAG else 1e-4
-                floor = 0.1 if (kind == L.KIND_MAG and cfg.w_dtype == "bf16") else 1e-3
+                # After a DoRA update the magnitude (trained on the bf16-rounded
+                # gradient) scales every later gradient, so from the second step
+                # on a bf16 DoRA slot meets the bf16 bar throughout.
+                bf_dora = cfg.dora and cfg.w_dtype == "bf16"
+                bf_hit = (kind == L.KIND_MAG and cfg.w_dtype == "bf16") or (bf_dora and it > 0)
+                bar = TOL[cfg.w_dtype] if (kind == L.KIND_MAG or bf_hit) else 1e-4
+                floor = 0.1 if bf_hit else 1e-3
                 ok[sl] &= np.abs(g_ref[sl]) >= floor * np.abs(g_ref[sl]).max()
                 _say(f"  step {it} seg {kind}: grad rel err {e:.3e} (bar {bar:g})")
                 assert e <= bar, (it, kind, e)
@@ -432,7 +438,7 @@ def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
         for kind, sl in seg.items():
             m = ok[sl]
             e = rel_err(d_gpu[sl][m], d_ref[sl][m])
-            bar = 2e-2 if (kind == L.KIND_MAG and cfg.w_dtype == "bf16") else 1e-3
+            bar = 2e-2 if (cfg.w_dtype == "bf16" and (kind == L.KIND_MAG or cfg.dora)) else 1e-3
             _say(f"  update seg {kind}: rel err {e:.3e} over {m.sum()} of {m.size}")
             assert e <= bar, (kind, e)
 
