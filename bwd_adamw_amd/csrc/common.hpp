@@ -110,4 +110,21 @@ LORA_DEV void sum_partials(const float* part, int64_t stride, int nparts, int64_
   out[i] = accumulate ? out[i] + s : s;
 }
 
+// Fixed-order sum of nparts float4 partials at part[q*stride + i]: loads are
+// issued eight at a time so their latencies overlap; the additions still run
+// in index order.
+LORA_DEV f32x4 sum_parts4(const float* part, int64_t stride, int nparts, int64_t i) {
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
+  int q = 1;
+  for (; q + 8 <= nparts; q += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(part + (int64_t)(q + u) * stride + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; q < nparts; ++q) s += *reinterpret_cast<const f32x4*>(part + (int64_t)q * stride + i);
+  return s;
+}
+
 }  // namespace lora

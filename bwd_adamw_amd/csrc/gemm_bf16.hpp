@@ -14,9 +14,11 @@
 // transposes it in registers before the LDS write.
 //
 // The grid is one-dimensional.  Workgroups are dealt to the 8 XCDs round
-// robin, so block b runs on XCD b % 8; the tile order is remapped so that
-// each XCD works through one contiguous band of row-major tiles and keeps the
-// band's A panels in its own L2.
+// robin, so block b runs on XCD b % 8, and each XCD starts its blocks in
+// order.  Block b is mapped to a contiguous run of tile indices per XCD, and
+// tile indices walk the output in groups of GROUP_M tile rows, column by
+// column, so the tiles an XCD has resident at once form a compact rectangle
+// whose A and B K-slices are shared in that XCD's L2.
 #pragma once
 #include "common.hpp"
 #include "gemm_f32.hpp"   // LoraOperand
@@ -43,7 +45,7 @@ struct GemmBf16Args {
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
-// Tile of linear block b with the XCD-banded order (a bijection on [0, T)).
+// Tile index of linear block b: contiguous per XCD (a bijection on [0, T)).
 LORA_DEV int64_t xcd_tile(int64_t b, int64_t T) {
   const int64_t q = T / 8, rem = T % 8;
   const int64_t x = b % 8, idx = b / 8;
@@ -51,7 +53,20 @@ LORA_DEV int64_t xcd_tile(int64_t b, int64_t T) {
   return start + idx;
 }
 
-template <int BM, int BN, bool FWD>
+// Tile index g -> (tile row, tile col), walking groups of GROUP_M tile rows
+// column by column (a bijection onto the ntm x ntn tiles).
+constexpr int GROUP_M = 4;
+LORA_DEV void grouped_tile(int64_t g, int64_t ntm, int64_t ntn, int64_t& tm, int64_t& tn) {
+  const int64_t first = (g / (GROUP_M * ntn)) * GROUP_M;
+  const int64_t gsize = min((int64_t)GROUP_M, ntm - first);
+  const int64_t gin = g - first * ntn;
+  tm = first + gin % gsize;
+  tn = gin / gsize;
+}
+
+// EXACT: M, Nc and Kc are multiples of BM, BN and 64, so the main loop runs
+// without bounds checks (no divergent branches around its loads).
+template <int BM, int BN, bool FWD, bool EXACT>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
   constexpr int NT = 512;
   constexpr int BK = 64;
@@ -70,10 +85,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
-  const int64_t ntn = (p.Nc + BN - 1) / BN;
-  const int64_t ntiles = ntn * ((p.M + BM - 1) / BM);
-  const int64_t tile = xcd_tile(blockIdx.x, ntiles);
-  const int64_t m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+  const int64_t ntn = (p.Nc + BN - 1) / BN, ntm = (p.M + BM - 1) / BM;
+  int64_t tm, tn;
+  grouped_tile(xcd_tile(blockIdx.x, ntm * ntn), ntm, ntn, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t kend = p.Kc;
   const int hl = lane >> 5, l32 = lane & 31;
   const bool store_xa = p.xa.out != nullptr && n0 == 0;
@@ -93,6 +108,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
   // 8 contiguous bf16 at src[row*ld + k .. +8), zero beyond klim (klim % 8 == 0).
   auto ld8 = [&](const uint16_t* src, int64_t row, int64_t rows, int64_t ld, int64_t k,
                  int64_t klim) -> u32x4 {
+    if (EXACT) return *reinterpret_cast<const u32x4*>(src + row * ld + k);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (row < rows && k < klim) v = *reinterpret_cast<const u32x4*>(src + row * ld + k);
     return v;
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
         for (int i = 0; i < 8; ++i) {
           const int64_t gk = k0 + 8 * kg + i;
           u32x2 v = {0u, 0u};
-          if (f < BITEMS && gk < kend && gn < p.Nc)
+          if (EXACT ? (f < BITEMS) : (f < BITEMS && gk < kend && gn < p.Nc))
             v = *reinterpret_cast<const u32x2*>(p.B + gk * p.ldb + gn);
           rbt[q][i] = v;
         }
@@ -193,9 +209,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (gm < p.M && gk < p.r) {
           const int64_t i = gm * p.r + gk;
-          v = *reinterpret_cast<const f32x4*>(p.xa.p + i);
-          for (int part = 1; part < p.xa.nparts; ++part)
-            v += *reinterpret_cast<const f32x4*>(p.xa.p + part * p.xa.stride + i);
+          v = sum_parts4(p.xa.p, p.xa.stride, p.xa.nparts, i);
           if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
           v *= p.xs;
         }

@@ -57,7 +57,9 @@ struct GemmF32Args {
   float* part;             // [nsplit, M, Nc] partials when nsplit > 1
 };
 
-template <int BM, int BN, bool FWD>
+// EXACT: M and Nc are multiples of BM and BN and every split range a multiple
+// of 32, so the main loop runs without bounds checks.
+template <int BM, int BN, bool FWD, bool EXACT>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   constexpr int BK = 32;
   constexpr int KW = BK;                // contraction indices per wave per K-step
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
       const int row = f / AC4, c4 = f % AC4;
       const int64_t gm = m0 + row, gk = k0 + 4 * c4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (gm < p.M && gk < kend) {
+      if (EXACT || (gm < p.M && gk < kend)) {
         v = *reinterpret_cast<const f32x4*>(p.A + gm * p.lda + gk);
         if (p.acn) {
 #pragma unroll
@@ -124,9 +126,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (gm < p.M && gk < p.r) {
         const int64_t i = gm * p.r + gk;
-        v = *reinterpret_cast<const f32x4*>(p.xa.p + i);
-        for (int part = 1; part < p.xa.nparts; ++part)
-          v += *reinterpret_cast<const f32x4*>(p.xa.p + part * p.xa.stride + i);
+        v = sum_parts4(p.xa.p, p.xa.stride, p.xa.nparts, i);
         if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
         v *= p.xs;
       }
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
     }
   };
   // B side.  fwd: rows n, contraction contiguous.  dx: rows = contraction.
-  auto load_b = [&](const float* src, int64_t ld, int64_t k0, int64_t klim) {
+  auto load_b = [&](const float* src, int64_t ld, int64_t k0, int64_t klim, bool exact) {
 #pragma unroll
     for (int q = 0; q < BF4; ++q) {
       const int f = tid + 256 * q;
@@ -150,11 +150,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
       if (FWD) {
         const int row = f / AC4, c4 = f % AC4;
         const int64_t gn = n0 + row, gk = k0 + 4 * c4;
-        if (gn < p.Nc && gk < klim) v = *reinterpret_cast<const f32x4*>(src + gn * ld + gk);
+        if (exact || (gn < p.Nc && gk < klim)) v = *reinterpret_cast<const f32x4*>(src + gn * ld + gk);
       } else {
         const int row = f / (BN / 4), c4 = f % (BN / 4);
         const int64_t gk = k0 + row, gn = n0 + 4 * c4;
-        if (gk < klim && gn < p.Nc) v = *reinterpret_cast<const f32x4*>(src + gk * ld + gn);
+        if (exact || (gk < klim && gn < p.Nc)) v = *reinterpret_cast<const f32x4*>(src + gk * ld + gn);
       }
       rb[q] = v;
     }
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   auto lora_contraction = [&]() {
     for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
       load_xa(k0);
-      load_b(p.XB, FWD ? p.r : p.Nc, k0, p.r);
+      load_b(p.XB, FWD ? p.r : p.Nc, k0, p.r, false);
       __syncthreads();
       store_a(0);
       store_b(0);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
     load_a(kbeg);
-    load_b(p.B, p.ldb, kbeg, kend);
+    load_b(p.B, p.ldb, kbeg, kend, EXACT);
     store_a(0);
     store_b(0);
     __syncthreads();
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
       const int cur = (int)(kt & 1);
       if (kt + 1 < nk) {
         load_a(kbeg + (kt + 1) * BK);
-        load_b(p.B, p.ldb, kbeg + (kt + 1) * BK, kend);
+        load_b(p.B, p.ldb, kbeg + (kt + 1) * BK, kend, EXACT);
       }
       compute(cur);
       if (kt + 1 < nk) {

@@ -210,17 +210,23 @@ void launch_reduce(const RedJob* jobs, int n, hipStream_t st) {
 
 void launch_gemm_f32(const GemmPlan& g, bool fwd, const GemmF32Args& a, hipStream_t st) {
   dim3 grid((unsigned)cdiv(a.Nc, g.bn), (unsigned)cdiv(a.M, g.bm), (unsigned)g.k.n);
+  const bool exact = a.M % g.bm == 0 && a.Nc % g.bn == 0 && a.Kc % g.k.len == 0 && g.k.len % 32 == 0;
   {
     prof::Scope ps(fwd ? "gemm_f32_fwd" : "gemm_f32_dx", a.M, a.Nc, a.Kc,
                    2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                    4.0 * (a.M * a.Kc + a.Nc * a.Kc + a.M * a.Nc * (a.C2 ? 2 : 1)));
-    if (g.bm == 128) {
-      if (fwd) launch(gemm_f32_kernel<128, 128, true>, grid, st, ps, a);
-      else launch(gemm_f32_kernel<128, 128, false>, grid, st, ps, a);
-    } else {
-      if (fwd) launch(gemm_f32_kernel<64, 64, true>, grid, st, ps, a);
-      else launch(gemm_f32_kernel<64, 64, false>, grid, st, ps, a);
-    }
+#define LORA_F32_TILE(BM_)                                                              \
+  if (g.bm == BM_) {                                                                    \
+    if (fwd) {                                                                          \
+      if (exact) launch(gemm_f32_kernel<BM_, BM_, true, true>, grid, st, ps, a);        \
+      else launch(gemm_f32_kernel<BM_, BM_, true, false>, grid, st, ps, a);             \
+    } else {                                                                            \
+      if (exact) launch(gemm_f32_kernel<BM_, BM_, false, true>, grid, st, ps, a);       \
+      else launch(gemm_f32_kernel<BM_, BM_, false, false>, grid, st, ps, a);            \
+    }                                                                                   \
+  }
+    LORA_F32_TILE(128) else LORA_F32_TILE(64)
+#undef LORA_F32_TILE
   }
   if (g.k.n > 1) {
     const int64_t n4 = cdiv(a.M * a.Nc, 4);
@@ -236,10 +242,16 @@ void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStr
   prof::Scope ps(fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
                  2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                  2.0 * (a.M * a.Kc + a.Nc * a.Kc) + 4.0 * a.M * a.Nc * (a.C2 ? 2 : 1));
+  const bool exact = a.M % g.bm == 0 && a.Nc % g.bn == 0 && a.Kc % 64 == 0;
 #define LORA_BF16_TILE(BM_, BN_)                                                      \
   if (g.bm == BM_ && g.bn == BN_) {                                                   \
-    if (fwd) launch_n(gemm_bf16_kernel<BM_, BN_, true>, grid, 512u, st, ps, a);        \
-    else launch_n(gemm_bf16_kernel<BM_, BN_, false>, grid, 512u, st, ps, a);           \
+    if (fwd) {                                                                        \
+      if (exact) launch_n(gemm_bf16_kernel<BM_, BN_, true, true>, grid, 512u, st, ps, a); \
+      else launch_n(gemm_bf16_kernel<BM_, BN_, true, false>, grid, 512u, st, ps, a);   \
+    } else {                                                                          \
+      if (exact) launch_n(gemm_bf16_kernel<BM_, BN_, false, true>, grid, 512u, st, ps, a); \
+      else launch_n(gemm_bf16_kernel<BM_, BN_, false, false>, grid, 512u, st, ps, a);  \
+    }                                                                                 \
     return;                                                                           \
   }
   LORA_BF16_TILE(256, 256)

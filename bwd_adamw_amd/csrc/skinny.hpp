@@ -325,9 +325,7 @@ __global__ __launch_bounds__(256) void k4_kernel(const float* __restrict__ X, in
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (t < te && 4 * q < r) {
         const int64_t i = t * r + 4 * q;
-        v = *reinterpret_cast<const f32x4*>(V + i);
-        for (int part = 1; part < vparts; ++part)
-          v += *reinterpret_cast<const f32x4*>(V + part * T * r + i);
+        v = sum_parts4(V, T * r, vparts, i);
       }
       *reinterpret_cast<f32x4*>(&Vs[row * LDV + 4 * q]) = v;
     }
