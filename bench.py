@@ -86,6 +86,54 @@ def run_steps(trainer, slots, inputs, n):
                 raise RuntimeError("non-finite gradient in a synthetic run")
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "bwd_adamw_amd", "traffic.json")
+
+
+def kernel_source_digest():
+    """SHA-256 over the HIP sources; stored counter readings are valid only
+    for the kernels they were taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "bwd_adamw_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(src, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, shape):
+    """HBM bytes per launch of (kernel, shape) from the stored FETCH_SIZE and
+    WRITE_SIZE readings, each scaled by the factor a plain copy of known size
+    gave for the same counter; None when absent or taken on other sources."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(f"{kernel} {shape[0]}x{shape[1]}x{shape[2]}")
+    if not k:
+        return None
+    return k["fetch_kib"] * 1024.0 * rec["copy_factor_fetch"] + \
+        k["write_kib"] * 1024.0 * rec["copy_factor_write"]
+
+
+def copy_calibration(mib):
+    """A plain device copy of `mib` MiB, five times: the reference dispatch
+    whose FETCH_SIZE / WRITE_SIZE readings convert the counters to bytes."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n,
+                                           "dispatches": 5}}), flush=True)
+
+
 def roofline_of(entries, cfg):
     """Dominant kernel (largest summed time) and its place on the roofline."""
     dom = max(entries, key=lambda e: e["total_ms"])
@@ -98,7 +146,7 @@ def roofline_of(entries, cfg):
         achieved = dom["bytes"] / sec / 1e9
         rl = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm"], "unit": "GB/s"}
     rl["frac"] = rl["achieved"] / rl["peak"]
-    rl["traffic"] = None
+    rl["traffic"] = measured_traffic(dom["kernel"], [dom["M"], dom["N"], dom["K"]])
     rl["kernel"] = dom["kernel"]
     rl["shape"] = [dom["M"], dom["N"], dom["K"]]
     rl["avg_us"] = dom["avg_ms"] * 1e3
@@ -124,8 +172,10 @@ def kernel_table(entries, total_ms):
 
 
 def cpu_baseline(cfg, budget_s):
-    """The oracle's whole step on a bounded sample: the first L_s layers of
-    one slot with all G chunks; L_s grows until about `budget_s` of work."""
+    """The oracle's whole step on a bounded sample: the full per-layer step
+    (all projections, all G chunks, one slot) layer after layer, wrapping
+    round to layer 0 again, until about `budget_s` of work; the per-layer
+    time is scaled to the whole workload."""
     import numpy as np
     import oracle as O
     from bwd_adamw_amd import workloads as WL
@@ -136,9 +186,7 @@ def cpu_baseline(cfg, budget_s):
         cores = os.cpu_count() or 1
     s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
     f64 = lambda t: t.double().numpy()
-    elapsed_total, layers_done, tokens = 0.0, 0, 0
-    per_layer = []
-    for l in range(cfg.layers):
+    def layer_inputs(l):
         lin, params, chunks = {}, {}, [dict() for _ in range(cfg.chunks)]
         for pj in cfg.projections:
             inp = WL.linear_inputs(cfg, l, pj)
@@ -149,6 +197,24 @@ def cpu_baseline(cfg, budget_s):
                 params[key]["mag"] = O.dora_row_norms(lin[key])
             for g in range(cfg.chunks):
                 chunks[g][key] = (f64(inp["X"][g]), f64(inp["dY"][g]))
+        return lin, params, chunks
+
+    # Layers are generated once and kept while they fit in about 2 GB; the
+    # timed loop then cycles over the kept layers.
+    cache, cache_bytes = [], 0
+    elapsed_total, layers_done = 0.0, 0
+    while elapsed_total < budget_s:
+        l = layers_done % cfg.layers
+        if l < len(cache):
+            lin, params0, chunks = cache[l]
+        elif cache_bytes < 2e9 or not cache:
+            lin, params0, chunks = layer_inputs(l)
+            cache.append((lin, params0, chunks))
+            cache_bytes += sum(w.nbytes for w in lin.values()) + \
+                sum(x.nbytes + d.nbytes for c in chunks for x, d in c.values())
+        else:
+            lin, params0, chunks = cache[layers_done % len(cache)]
+        params = {k: {n: a.copy() for n, a in v.items()} for k, v in params0.items()}
         st = O.SlotState(params=params)
         if cfg.dora:
             for key in lin:
@@ -158,18 +224,15 @@ def cpu_baseline(cfg, budget_s):
                   plus_ratio=cfg.plus_ratio, dora=cfg.dora)
         t0 = time.perf_counter()
         O.train_step(st, lin, chunks, hp)
-        dt = time.perf_counter() - t0
-        per_layer.append(dt)
-        elapsed_total += dt
+        elapsed_total += time.perf_counter() - t0
         layers_done += 1
-        if elapsed_total >= budget_s:
-            break
     # whole-step time of the full workload, scaled from the sampled layers
     step_s = elapsed_total / layers_done * cfg.layers * cfg.slots
     value = cfg.tokens_per_step / step_s
-    sample = (f"oracle train_step of {layers_done} of {cfg.layers} layers (all projections, "
-              f"{cfg.chunks} chunk(s) of {cfg.tokens} tokens, slot 0), {elapsed_total:.1f} s, "
-              f"scaled to the full {cfg.layers}-layer x {cfg.slots}-slot step")
+    sample = (f"oracle train_step, one layer at a time (all projections, {cfg.chunks} chunk(s) of "
+              f"{cfg.tokens} tokens, slot 0): {layers_done} layer-steps over the {cfg.layers} "
+              f"layers in {elapsed_total:.1f} s, scaled to the full {cfg.layers}-layer x "
+              f"{cfg.slots}-slot step")
     return {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": sample}
 
@@ -183,6 +246,8 @@ def main():
                     help="workload number (default: the TinyLlama-shaped wq+wv workload)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -197,6 +262,9 @@ def main():
     if not torch.cuda.is_available():
         log("bench.py: no GPU visible")
         sys.exit(1)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     L.lib()
     cfg = WL.get_config(args.config)
     dev = "cuda"
