@@ -111,20 +111,59 @@ LORA_DEV void sum_partials(const float* part, int64_t stride, int nparts, int64_
 }
 
 // Fixed-order sum of nparts float4 partials at part[q*stride + i]: loads are
-// issued eight at a time so their latencies overlap; the additions still run
-// in index order.
+// issued sixteen at a time so their latencies overlap (one round trip for up
+// to 17 partials); the additions still run in index order.
 LORA_DEV f32x4 sum_parts4(const float* part, int64_t stride, int nparts, int64_t i) {
   f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
-  int q = 1;
-  for (; q + 8 <= nparts; q += 8) {
-    f32x4 v[8];
+  for (int q = 1; q < nparts; q += 16) {
+    f32x4 v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(part + (int64_t)(q + u) * stride + i);
+    for (int u = 0; u < 16; ++u)
+      if (q + u < nparts) v[u] = *reinterpret_cast<const f32x4*>(part + (int64_t)(q + u) * stride + i);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+    for (int u = 0; u < 16; ++u)
+      if (q + u < nparts) s += v[u];
   }
-  for (; q < nparts; ++q) s += *reinterpret_cast<const f32x4*>(part + (int64_t)q * stride + i);
   return s;
+}
+
+// The same for one float.
+LORA_DEV float sum_parts1(const float* part, int64_t stride, int nparts, int64_t i) {
+  float s = part[i];
+  for (int q = 1; q < nparts; q += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (q + u < nparts) v[u] = part[(int64_t)(q + u) * stride + i];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (q + u < nparts) s += v[u];
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Block -> tile order.  Workgroups of a launch are dealt to the 8 XCDs round
+// robin (block b runs on XCD b % 8), so tiles that share operands are given
+// to blocks of one XCD, where they share its L2.
+// ---------------------------------------------------------------------------
+// Tile index of linear block b: contiguous per XCD (a bijection on [0, T)).
+LORA_DEV int64_t xcd_tile(int64_t b, int64_t T) {
+  const int64_t q = T / 8, rem = T % 8;
+  const int64_t x = b % 8, idx = b / 8;
+  const int64_t start = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
+  return start + idx;
+}
+
+// Tile index g -> (tile row, tile col), walking groups of GROUP_M tile rows
+// column by column (a bijection onto the ntm x ntn tiles).
+constexpr int GROUP_M = 4;
+LORA_DEV void grouped_tile(int64_t g, int64_t ntm, int64_t ntn, int64_t& tm, int64_t& tn) {
+  const int64_t first = (g / (GROUP_M * ntn)) * GROUP_M;
+  const int64_t gsize = min((int64_t)GROUP_M, ntm - first);
+  const int64_t gin = g - first * ntn;
+  tm = first + gin % gsize;
+  tn = gin / gsize;
 }
 
 }  // namespace lora

@@ -1,0 +1,204 @@
+// Short-chunk path (fp32 W, contraction split across blocks): each linear's
+// forward and backward in two launches apiece.
+//
+// When the token count T is small the frozen GEMM only fills the chip with
+// its contraction split across blocks, and every launch costs a few
+// microseconds of latency however little it does.  So the rank-side work
+// runs beside the GEMM instead of before it:
+//
+//   forward  1: split GEMM partials of X W^T    |  down: U = X~ A^T (partials)
+//            2: Y = sum of partials + s U B^T   (U summed once per row and
+//               stored; DoRA: Z = that, Y = Z * mag/norm)
+//   backward 1: split GEMM partials of g W  |  k3: V (few partials), dB (, dm)
+//            2: dX = sum + (s V A) * mask * keep  |  k4: dA  |  dB/dm reduce
+//
+// ("8. LoRA Fundamentals", "How it works" for the forward; "Backward Bug
+// Hunts ...", "Bug #1" for dX, dA and dB; "4.3. Training Guide", "Dropout"
+// for the mask on the LoRA branch only.)  The LoRA terms are rank-r outer
+// products that need the finished U or V, so they move out of the GEMM into
+// the launch that sums its partials.  All sums run in a fixed order.
+//
+// Roles of one launch share a single LDS array (the largest role's size), so
+// a role's blocks co-reside with the GEMM's on a CU.
+#pragma once
+#include "common.hpp"
+#include "gemm_f32.hpp"
+#include "skinny.hpp"
+
+namespace lora {
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Split GEMM blocks first, then `side_blocks` blocks of the side role on a
+// (side_x, *) grid.
+struct SplitGrid {
+  int64_t ntn, ntm;       // 64 x 64 output tiles
+  int nsplit;
+  int64_t gemm_blocks;    // ntn * ntm * nsplit
+  int64_t side_x;
+  int64_t side_blocks;
+};
+
+// GEMM block b -> (tile col, tile row, split).  Consecutive tile indices on
+// one XCD walk the M tiles of one W slice first: the blocks that read the
+// same W slice share an L2.
+LORA_DEV void split_tile(const SplitGrid& f, int64_t b, int64_t& tn, int64_t& tm, int& split) {
+  const int64_t g = xcd_tile(b, f.gemm_blocks);
+  tm = g % f.ntm;
+  const int64_t rest = g / f.ntm;
+  tn = rest % f.ntn;
+  split = (int)(rest / f.ntn);
+}
+
+template <bool EXACT, int RP>
+__global__ __launch_bounds__(256) void fwd_main_kernel(GemmF32Args g, DownArgs d, SplitGrid f) {
+  constexpr int L = cmax(gemm_f32_lds_floats<64, 64, true>(), down_lds_floats<RP>());
+  __shared__ __attribute__((aligned(16))) float smem[L];
+  const int64_t b = blockIdx.x;
+  if (b < f.gemm_blocks) {
+    int64_t tn, tm;
+    int split;
+    split_tile(f, b, tn, tm, split);
+    gemm_f32_block<64, 64, true, EXACT, gemm_f32_depth<64, 64>()>(g, smem, tn, tm, split);
+  } else {
+    const int64_t sb = b - f.gemm_blocks;
+    down_block<RP>(d, smem, sb % f.side_x, (int)(sb / f.side_x));
+  }
+}
+
+template <bool EXACT, int RP>
+__global__ __launch_bounds__(256) void bwd_main_kernel(GemmF32Args g, K3Args k, SplitGrid f) {
+  constexpr int L = cmax(gemm_f32_lds_floats<64, 64, false>(), k3_lds_floats<RP>());
+  __shared__ __attribute__((aligned(16))) float smem[L];
+  const int64_t b = blockIdx.x;
+  if (b < f.gemm_blocks) {
+    int64_t tn, tm;
+    int split;
+    split_tile(f, b, tn, tm, split);
+    gemm_f32_block<64, 64, false, EXACT, gemm_f32_depth<64, 64>()>(g, smem, tn, tm, split);
+  } else {
+    const int64_t sb = b - f.gemm_blocks;
+    k3_block<RP>(k, smem, sb % f.side_x, (int)(sb / f.side_x));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue of a split GEMM: C[m, n] = sum_q part[q][m][n] + LoRA term.
+//   forward: + sum_j (s U[m,j]) B[n,j]                     XB = B_lora [Nc, r]
+//   dx     : + (sum_j (s V[m,j]) A[j,n]) * mask(m,n)*keep  XB = A_lora [r, Nc]
+// A block covers `rows` rows x `cols` columns (rows * cols <= 1024, each
+// thread 4 consecutive columns); the U or V rows it needs are summed from
+// their partials once, into LDS.
+// ---------------------------------------------------------------------------
+constexpr int EPI_MAX_ROWS = 16;
+constexpr int EPI_MAX_RANK = 32;
+
+struct EpiArgs {
+  const float* part;      // [nsplit, M, Nc]
+  int nsplit;
+  int64_t M, Nc;
+  LoraOperand xa;         // U or V [M, r] (partials); out: store the summed U
+  const float* XB;
+  int64_t r;
+  float s;
+  DropParams drop;        // dx only
+  float* C;
+  float* C2;              // forward DoRA: Z
+  const float* cn;        // forward DoRA: column scale cn / cd
+  const float* cd;
+  int cols, rows;
+  int64_t ncb;            // column blocks per row block
+  int64_t blocks;
+};
+
+template <bool FWD>
+LORA_DEV void epi_block(const EpiArgs& e, float* smem, int64_t b) {
+  const int64_t rb = b / e.ncb, cb = b % e.ncb;
+  const int64_t m0 = rb * e.rows, c0 = cb * e.cols;
+  const int tid = threadIdx.x;
+  const int r = (int)e.r;
+  float* xs = smem;   // [rows][r], already times s
+  for (int i = tid; i < e.rows * r; i += 256) {
+    const int lr = i / r, j = i % r;
+    const int64_t m = m0 + lr;
+    float v = 0.f;
+    if (m < e.M) {
+      const int64_t idx = m * e.r + j;
+      v = sum_parts1(e.xa.p, e.xa.stride, e.xa.nparts, idx);
+      if (FWD && e.xa.out && cb == 0) e.xa.out[idx] = v;
+    }
+    xs[i] = v * e.s;
+  }
+  __syncthreads();
+  const int t4 = 4 * tid;
+  const int lr = t4 / e.cols, lc = t4 % e.cols;
+  const int64_t m = m0 + lr, n = c0 + lc;
+  if (lr >= e.rows || m >= e.M || n >= e.Nc) return;
+  const int64_t i4 = m * e.Nc + n;
+  const f32x4 acc = sum_parts4(e.part, e.M * e.Nc, e.nsplit, i4);
+  const float* xr = xs + lr * r;
+  f32x4 lo = {0.f, 0.f, 0.f, 0.f};
+  if (FWD) {
+    for (int j4 = 0; j4 < r; j4 += 4) {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(xr + j4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(e.XB + (n + q) * e.r + j4);
+        lo[q] += u[0] * bq[0] + u[1] * bq[1] + u[2] * bq[2] + u[3] * bq[3];
+      }
+    }
+  } else {
+    for (int j = 0; j < r; ++j) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(e.XB + j * e.Nc + n);
+      lo += xr[j] * a;
+    }
+    if (e.drop.on) {
+      const uint64_t rk = drop_row(e.drop, m);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lo[q] *= drop_mul(e.drop, rk, n + q);
+    }
+  }
+  f32x4 z = acc + lo;
+  if (FWD) {
+    if (e.C2) *reinterpret_cast<f32x4*>(e.C2 + i4) = z;
+    if (e.cn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) z[q] *= e.cn[n + q] / e.cd[n + q];
+    }
+  }
+  *reinterpret_cast<f32x4*>(e.C + i4) = z;
+}
+
+__global__ __launch_bounds__(256) void fwd_epi_kernel(EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) float smem[EPI_MAX_ROWS * EPI_MAX_RANK];
+  epi_block<true>(e, smem, blockIdx.x);
+}
+
+// k4 blocks first (the longest), then the dX epilogue, then reduction jobs
+// (dB and dm when k3 split its token range).
+struct BwdEpiGrid {
+  int64_t k4_x, k4_blocks, epi_blocks;
+  int narrow;   // k4 as k4n_block (16 columns per block over all T)
+};
+
+template <int RP>
+__global__ __launch_bounds__(256) void bwd_epi_kernel(EpiArgs e, K4Args k, RedJobs jobs,
+                                                      BwdEpiGrid f) {
+  constexpr int L = cmax(cmax(k4_lds_floats<RP>(), k4n_lds_floats<RP>()),
+                         EPI_MAX_ROWS * EPI_MAX_RANK);
+  __shared__ __attribute__((aligned(16))) float smem[L];
+  int64_t b = blockIdx.x;
+  if (b < f.k4_blocks) {
+    if (f.narrow) k4n_block<RP>(k, smem, b);
+    else k4_block<RP>(k, smem, b % f.k4_x, (int)(b / f.k4_x));
+    return;
+  }
+  b -= f.k4_blocks;
+  if (b < f.epi_blocks) {
+    epi_block<false>(e, smem, b);
+    return;
+  }
+  reduce_block(jobs, b - f.epi_blocks);
+}
+
+}  // namespace lora

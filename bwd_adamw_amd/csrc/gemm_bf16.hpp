@@ -45,25 +45,6 @@ struct GemmBf16Args {
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
-// Tile index of linear block b: contiguous per XCD (a bijection on [0, T)).
-LORA_DEV int64_t xcd_tile(int64_t b, int64_t T) {
-  const int64_t q = T / 8, rem = T % 8;
-  const int64_t x = b % 8, idx = b / 8;
-  const int64_t start = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
-  return start + idx;
-}
-
-// Tile index g -> (tile row, tile col), walking groups of GROUP_M tile rows
-// column by column (a bijection onto the ntm x ntn tiles).
-constexpr int GROUP_M = 4;
-LORA_DEV void grouped_tile(int64_t g, int64_t ntm, int64_t ntn, int64_t& tm, int64_t& tn) {
-  const int64_t first = (g / (GROUP_M * ntn)) * GROUP_M;
-  const int64_t gsize = min((int64_t)GROUP_M, ntm - first);
-  const int64_t gin = g - first * ntn;
-  tm = first + gin % gsize;
-  tn = gin / gsize;
-}
-
 // EXACT: M, Nc and Kc are multiples of BM, BN and 64, so the main loop runs
 // without bounds checks (no divergent branches around its loads).
 template <int BM, int BN, bool FWD, bool EXACT>

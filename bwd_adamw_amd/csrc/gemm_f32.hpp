@@ -57,10 +57,28 @@ struct GemmF32Args {
   float* part;             // [nsplit, M, Nc] partials when nsplit > 1
 };
 
+// LDS floats of one block (double-buffered A and B stages).
+template <int BM, int BN, bool FWD>
+constexpr int gemm_f32_lds_floats() {
+  return 2 * BM * (32 + 4) + 2 * (FWD ? BN * (32 + 4) : 32 * (BN + 4));
+}
+
+// One output tile (tm, tn) of split `split`, in LDS `smem`
+// (gemm_f32_lds_floats<BM, BN, FWD>() floats).
+//
+// The main loop keeps DEPTH K-steps of global loads in flight in registers:
+// a K-step's operands take longer to arrive than one K-step of MFMA work, so
+// the load for step k + DEPTH is issued while step k is computed.  At step k
+// LDS buffer k%2 holds step k, register stage (k+1)%DEPTH holds step k+1 and
+// is stored to the other buffer after the MFMAs, and stage k%DEPTH (stored
+// one step earlier) is refilled.  The loop is unrolled by DEPTH so every
+// stage index is a compile-time constant.
+//
 // EXACT: M and Nc are multiples of BM and BN and every split range a multiple
 // of 32, so the main loop runs without bounds checks.
-template <int BM, int BN, bool FWD, bool EXACT>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
+template <int BM, int BN, bool FWD, bool EXACT, int DEPTH>
+LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int64_t tm,
+                             int split) {
   constexpr int BK = 32;
   constexpr int KW = BK;                // contraction indices per wave per K-step
   constexpr int KH = KW / 2;            // per lane half
@@ -74,19 +92,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   constexpr int AC4 = BK / 4;           // float4 per A row of a K-step
   static_assert(AF4 >= 1 && BF4 >= 1 && MI >= 1 && NI >= 1, "tile shape");
   static_assert(KH % 4 == 0, "lane-half slice must be whole float4s");
+  static_assert(DEPTH >= 2, "at least one K-step of loads in flight");
 
-  __shared__ __attribute__((aligned(16))) float smem[2 * BM * LDA + 2 * BSZ];
   auto As = [&](int b) -> float* { return smem + b * (BM * LDA); };
   auto Bs = [&](int b) -> float* { return smem + 2 * BM * LDA + b * BSZ; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int split = blockIdx.z;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t kbeg = (int64_t)split * p.ksplit;
   const int64_t kend = min(p.Kc, kbeg + p.ksplit);
   const int hl = lane >> 5, l32 = lane & 31;
-  const bool store_xa = p.xa.out != nullptr && blockIdx.x == 0 && split == 0;
+  const bool store_xa = p.xa.out != nullptr && tn == 0 && split == 0;
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -96,10 +113,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  f32x4 ra[AF4], rb[BF4];
+  struct Stage {
+    f32x4 a[AF4], b[BF4];
+  };
 
   // A side (main operand): rows m, contraction contiguous.
-  auto load_a = [&](int64_t k0) {
+  auto load_a = [&](Stage& S, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < AF4; ++q) {
       const int f = tid + 256 * q;
@@ -113,11 +132,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
           for (int e = 0; e < 4; ++e) v[e] *= p.acn[gk + e] / p.acd[gk + e];
         }
       }
-      ra[q] = v;
+      S.a[q] = v;
     }
   };
   // A side (LoRA operand): rows m, rank contiguous, partials summed, times s.
-  auto load_xa = [&](int64_t k0) {
+  auto load_xa = [&](Stage& S, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < AF4; ++q) {
       const int f = tid + 256 * q;
@@ -130,19 +149,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
         if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
         v *= p.xs;
       }
-      ra[q] = v;
+      S.a[q] = v;
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](const Stage& S, int buf) {
 #pragma unroll
     for (int q = 0; q < AF4; ++q) {
       const int f = tid + 256 * q;
       const int row = f / AC4, c4 = f % AC4;
-      *reinterpret_cast<f32x4*>(&As(buf)[row * LDA + 4 * c4]) = ra[q];
+      *reinterpret_cast<f32x4*>(&As(buf)[row * LDA + 4 * c4]) = S.a[q];
     }
   };
   // B side.  fwd: rows n, contraction contiguous.  dx: rows = contraction.
-  auto load_b = [&](const float* src, int64_t ld, int64_t k0, int64_t klim, bool exact) {
+  auto load_b = [&](Stage& S, const float* src, int64_t ld, int64_t k0, int64_t klim, bool exact) {
 #pragma unroll
     for (int q = 0; q < BF4; ++q) {
       const int f = tid + 256 * q;
@@ -156,19 +175,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
         const int64_t gk = k0 + row, gn = n0 + 4 * c4;
         if (exact || (gk < klim && gn < p.Nc)) v = *reinterpret_cast<const f32x4*>(src + gk * ld + gn);
       }
-      rb[q] = v;
+      S.b[q] = v;
     }
   };
-  auto store_b = [&](int buf) {
+  auto store_b = [&](const Stage& S, int buf) {
 #pragma unroll
     for (int q = 0; q < BF4; ++q) {
       const int f = tid + 256 * q;
       if (FWD) {
         const int row = f / AC4, c4 = f % AC4;
-        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = rb[q];
+        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = S.b[q];
       } else {
         const int row = f / (BN / 4), c4 = f % (BN / 4);
-        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = rb[q];
+        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = S.b[q];
       }
     }
   };
@@ -210,19 +229,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   };
   // Unpipelined contraction over the LoRA rank (r <= 128).
   auto lora_contraction = [&]() {
+    Stage S;
     for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
-      load_xa(k0);
-      load_b(p.XB, FWD ? p.r : p.Nc, k0, p.r, false);
+      load_xa(S, k0);
+      load_b(S, p.XB, FWD ? p.r : p.Nc, k0, p.r, false);
       __syncthreads();
-      store_a(0);
-      store_b(0);
+      store_a(S, 0);
+      store_b(S, 0);
       __syncthreads();
       compute(0);
     }
     __syncthreads();
   };
 
-  if (!FWD && split == 0 && p.r > 0) {
+  const bool lora = split == 0 && p.r > 0 && p.XB != nullptr;
+  if (!FWD && lora) {
     lora_contraction();
     if (p.drop.on) {
 #pragma unroll
@@ -240,30 +261,41 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
     }
   }
 
-  // Main contraction over [kbeg, kend), double buffered.
+  // Main contraction over [kbeg, kend).
   const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
-    load_a(kbeg);
-    load_b(p.B, p.ldb, kbeg, kend, EXACT);
-    store_a(0);
-    store_b(0);
+    Stage R[DEPTH];
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+      if (u < nk) {
+        load_a(R[u], kbeg + u * BK);
+        load_b(R[u], p.B, p.ldb, kbeg + u * BK, kend, EXACT);
+      }
+    store_a(R[0], 0);
+    store_b(R[0], 0);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int cur = (int)(kt & 1);
-      if (kt + 1 < nk) {
-        load_a(kbeg + (kt + 1) * BK);
-        load_b(p.B, p.ldb, kbeg + (kt + 1) * BK, kend, EXACT);
+    for (int64_t kt = 0; kt < nk; kt += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int64_t k = kt + u;
+        if (k < nk) {
+          if (k + DEPTH < nk) {
+            load_a(R[u], kbeg + (k + DEPTH) * BK);
+            load_b(R[u], p.B, p.ldb, kbeg + (k + DEPTH) * BK, kend, EXACT);
+          }
+          const int buf = (int)(k & 1);
+          compute(buf);
+          if (k + 1 < nk) {
+            store_a(R[(u + 1) % DEPTH], buf ^ 1);
+            store_b(R[(u + 1) % DEPTH], buf ^ 1);
+          }
+          __syncthreads();
+        }
       }
-      compute(cur);
-      if (kt + 1 < nk) {
-        store_a(cur ^ 1);
-        store_b(cur ^ 1);
-      }
-      __syncthreads();
     }
   }
 
-  if (FWD && split == 0 && p.r > 0) lora_contraction();
+  if (FWD && lora) lora_contraction();
 
   // Epilogue.
 #pragma unroll
@@ -286,6 +318,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
         }
       }
     }
+}
+
+// K-steps of loads in flight per tile size (register budget of a stage).
+template <int BM, int BN>
+constexpr int gemm_f32_depth() {
+  return BM * BN <= 64 * 64 ? 4 : 2;
+}
+
+// Grid (Nc/BN, M/BM, nsplit).
+template <int BM, int BN, bool FWD, bool EXACT>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
+  __shared__ __attribute__((aligned(16))) float smem[gemm_f32_lds_floats<BM, BN, FWD>()];
+  gemm_f32_block<BM, BN, FWD, EXACT, gemm_f32_depth<BM, BN>()>(p, smem, blockIdx.x, blockIdx.y,
+                                                                 blockIdx.z);
 }
 
 // Sum of the split partials in split order, then the epilogue of the unsplit

@@ -12,6 +12,7 @@
 
 #include "../../include/lora.h"
 #include "common.hpp"
+#include "fused.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "optim.hpp"
@@ -100,7 +101,37 @@ GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16) {
   }
   if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}};
   const int64_t tiles = cdiv(M, 64) * cdiv(Nc, 64);
-  return {64, 64, plan_split(Kc, tiles, 256, 32, 256)};
+  return {64, 64, plan_split(Kc, tiles, 256, 32, 128)};
+}
+
+// Short chunks: the contraction is split across blocks, and each linear runs
+// as two launches per direction with the rank-side kernels beside the GEMM
+// (fused.hpp).  The epilogue keeps U or V rows in LDS, hence the rank limit.
+bool use_split_path(const GemmPlan& g, int64_t r, bool bf16) {
+  return !bf16 && g.k.n > 1 && g.bm == 64 && r <= EPI_MAX_RANK;
+}
+
+EpiArgs epi_shape(int64_t M, int64_t Nc) {
+  EpiArgs e;
+  memset(&e, 0, sizeof(e));
+  e.M = M;
+  e.Nc = Nc;
+  e.cols = (int)std::min<int64_t>(1024, rup(Nc, 4));
+  e.rows = (int)std::min<int64_t>(EPI_MAX_ROWS, 1024 / e.cols);
+  e.ncb = cdiv(Nc, e.cols);
+  e.blocks = cdiv(M, e.rows) * e.ncb;
+  return e;
+}
+
+SplitGrid split_grid(int64_t M, int64_t Nc, int nsplit, int64_t side_x, int64_t side_y) {
+  SplitGrid f;
+  f.ntn = cdiv(Nc, 64);
+  f.ntm = cdiv(M, 64);
+  f.nsplit = nsplit;
+  f.gemm_blocks = f.ntn * f.ntm * nsplit;
+  f.side_x = side_x;
+  f.side_blocks = side_x * side_y;
+  return f;
 }
 
 // The consumers of the V partials (dX GEMM head, k4) sum them while staging
@@ -134,6 +165,12 @@ Layout make_layout(const lora_linear* L) {
   y.k4 = plan_rows(T, cdiv(K, SK_C));
   y.gf = plan_gemm(T, N, K, bf);
   y.gd = plan_gemm(T, K, N, bf);
+  // Beside the split GEMM the down projection needs no parallelism of its
+  // own: 256 columns per block keeps its partials few for the epilogue.
+  if (use_split_path(y.gf, r, bf)) {
+    const int64_t len = rup(cdiv(K, cdiv(K, 256)), SK_C);
+    y.down = {len, (int)cdiv(K, len)};
+  }
   const double vbytes = 4.0 * y.strips * T * r;
   y.vreduce = y.strips > 1 && vbytes * (cdiv(K, y.gd.bn) + cdiv(K, SK_C)) > kPartialRereadBytes;
   size_t off = 0;
@@ -143,7 +180,7 @@ Layout make_layout(const lora_linear* L) {
   y.fwd_bytes = off;
   off = 0;
   y.vpart = carve(off, y.strips > 1 ? sizeof(float) * y.strips * T * r : 0);
-  y.v = carve(off, (y.strips == 1 || y.vreduce) ? sizeof(float) * T * r : 0);
+  y.v = carve(off, sizeof(float) * T * r);
   y.dbpart = carve(off, y.k3.n > 1 ? sizeof(float) * y.k3.n * N * r : 0);
   y.dmpart = carve(off, (L->dora_mag && y.k3.n > 1) ? sizeof(float) * y.k3.n * N : 0);
   y.gbf = carve(off, bf ? sizeof(uint16_t) * T * N : 0);
@@ -181,6 +218,15 @@ template <typename F, typename... Args>
 void launch(F kern, dim3 grid, hipStream_t st, const prof::Scope& ps, Args... args) {
   launch_n(kern, grid, 256u, st, ps, args...);
 }
+
+#define LORA_RP_DISPATCH_32(rp, call)                 \
+  if (rp <= 16) {                                     \
+    constexpr int RP = 16;                            \
+    call;                                             \
+  } else {                                            \
+    constexpr int RP = 32;                            \
+    call;                                             \
+  }
 
 #define LORA_RP_DISPATCH(rp, call)                    \
   switch (rp) {                                       \
@@ -318,17 +364,51 @@ int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U, flo
   uint16_t* Xbf = bf ? (uint16_t*)(w + y.xbf) : nullptr;
   const DropParams d = make_drop(drop);
 
+  DownArgs da;
+  da.X = X; da.T = T; da.K = K; da.A = lin->A; da.r = r; da.drop = d;
+  da.ksplit = y.down.len; da.nsplit = y.down.n; da.Upart = Upart; da.U = U; da.Xbf = Xbf;
+  const double down_flops = 2.0 * T * K * r;
+  const double down_bytes = 4.0 * (T * K + r * K + T * r) + (Xbf ? 2.0 * T * K : 0.0);
+  const LoraOperand xa = y.down.n > 1 ? LoraOperand{Upart, T * r, y.down.n, U}
+                                      : LoraOperand{U, T * r, 1, nullptr};
+
+  if (use_split_path(y.gf, r, bf)) {
+    // Launch 1: split GEMM partials of X W^T beside the down projection.
+    GemmF32Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = N; a.Kc = K;
+    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
+    a.part = (float*)(w + y.gfpart);
+    const SplitGrid f = split_grid(T, N, y.gf.k.n, cdiv(T, SK_T), y.down.n);
+    const bool exact = T % 64 == 0 && N % 64 == 0 && K % y.gf.k.len == 0 && y.gf.k.len % 32 == 0;
+    {
+      prof::Scope ps("gemm_f32_fwd+down", T, N, K, 2.0 * T * N * K + down_flops,
+                     4.0 * (T * K + N * K + y.gf.k.n * T * N) + down_bytes);
+      const dim3 grid((unsigned)(f.gemm_blocks + f.side_blocks));
+      LORA_RP_DISPATCH_32(rank_pad(r), {
+        if (exact) launch(fwd_main_kernel<true, RP>, grid, st, ps, a, da, f);
+        else launch(fwd_main_kernel<false, RP>, grid, st, ps, a, da, f);
+      });
+    }
+    // Launch 2: Y = sum of partials + s U B^T (DoRA: Z and the row scale).
+    EpiArgs e = epi_shape(T, N);
+    e.part = a.part; e.nsplit = y.gf.k.n;
+    e.xa = xa; e.XB = lin->B; e.r = r; e.s = lin->scale;
+    e.C = Y; e.C2 = Z; e.cn = lin->dora_mag; e.cd = lin->dora_norm;
+    prof::Scope ps("fwd_epilogue", T, N, y.gf.k.n, 2.0 * T * N * r,
+                   4.0 * T * N * (y.gf.k.n + (Z ? 2 : 1)) + 4.0 * (y.down.n * T * r + N * r));
+    launch(fwd_epi_kernel, dim3((unsigned)e.blocks), st, ps, e);
+    return hip_status();
+  }
+
   // U = X~ A^T, split over K; the GEMM sums the splits while staging U and
   // stores the summed U.
   {
-    prof::Scope ps("down_u", T, r, K, 2.0 * T * K * r,
-                   4.0 * (T * K + r * K + T * r) + (Xbf ? 2.0 * T * K : 0.0));
+    prof::Scope ps("down_u", T, r, K, down_flops, down_bytes);
     const dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)y.down.n);
-    LORA_RP_DISPATCH(rank_pad(r), launch(down_kernel<RP>, grid, st, ps, X, T, K, lin->A, r, d,
-                                         y.down.len, Upart, U, Xbf));
+    LORA_RP_DISPATCH(rank_pad(r), launch(down_kernel<RP>, grid, st, ps, da));
   }
-  const LoraOperand xa = y.down.n > 1 ? LoraOperand{Upart, T * r, y.down.n, U}
-                                      : LoraOperand{U, T * r, 1, nullptr};
 
   // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
   if (bf) {
@@ -378,7 +458,7 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
   // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
   K3Out o;
   o.Vpart = y.strips > 1 ? (float*)(w + y.vpart) : nullptr;
-  o.V = (y.strips == 1 || y.vreduce) ? (float*)(w + y.v) : nullptr;
+  o.V = (float*)(w + y.v);
   o.dBpart = y.k3.n > 1 ? (float*)(w + y.dbpart) : nullptr;
   o.dB = dB;
   o.dmpart = (dMag && y.k3.n > 1) ? (float*)(w + y.dmpart) : nullptr;
@@ -386,21 +466,109 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
   o.gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
   o.scale = lin->scale;
   o.accumulate = acc;
+  const float* Zin = dMag ? Z : nullptr;
+  K3Args ka;
+  ka.dY = dY; ka.T = T; ka.N = N; ka.B = lin->B; ka.U = U; ka.r = r;
+  ka.mag = lin->dora_mag; ka.nrm = lin->dora_norm; ka.Z = Zin;
+  ka.tsplit = y.k3.len; ka.nstrip = y.strips; ka.spb = 1; ka.nts = y.k3.n; ka.o = o;
+  const double k3_flops = 4.0 * T * N * r;
+  const double k3_bytes = 4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
+                          (o.gbf ? 2.0 * T * N : 0.0);
+  const LoraOperand xv = (y.strips == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
+                                                      : LoraOperand{o.Vpart, T * r, (int)y.strips, nullptr};
+  float* dApart = y.k4.n > 1 ? (float*)(w + y.dapart) : nullptr;
+  K4Args k4a;
+  k4a.X = X; k4a.T = T; k4a.K = K; k4a.V = xv.p; k4a.vparts = xv.nparts; k4a.r = r; k4a.drop = d;
+  k4a.tsplit = y.k4.len; k4a.nts = y.k4.n; k4a.dApart = dApart; k4a.dA = dA;
+  k4a.scale = lin->scale; k4a.accumulate = acc;
+  const double k4_flops = 2.0 * T * K * r;
+  const double k4_bytes = 4.0 * (T * K + T * r + 2 * r * K);
+
+  // Gradient splits over token ranges: fixed-order reduction jobs.
+  RedJob jobs[3];
+  int nj = 0;
+  if (y.k3.n > 1) {
+    jobs[nj++] = {o.dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
+    if (dMag) jobs[nj++] = {o.dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
+  }
+
+  if (dX && use_split_path(y.gd, r, bf)) {
+    // Launch 1: split GEMM partials of g W beside k3 (V partials, dB, dm).
+    GemmF32Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
+    a.B = (const float*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = K; a.Kc = N;
+    a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
+    a.part = (float*)(w + y.gdpart);
+    // k3 beside the GEMM: one strip per block (each strip is a chain of
+    // dependent loads), several only past 32 strips, so V arrives as at most
+    // 32 partials for the two consumers of launch 2.
+    K3Args kb = ka;
+    kb.spb = cdiv(y.strips, 32);
+    const int64_t nvp = cdiv(y.strips, kb.spb);
+    kb.o.V = (float*)(w + y.v);
+    kb.o.Vpart = nvp > 1 ? (float*)(w + y.vpart) : nullptr;
+    const LoraOperand vd = nvp > 1 ? LoraOperand{kb.o.Vpart, T * r, (int)nvp, nullptr}
+                                   : LoraOperand{kb.o.V, T * r, 1, nullptr};
+    const SplitGrid f = split_grid(T, K, y.gd.k.n, nvp, y.k3.n);
+    const bool exact = T % 64 == 0 && K % 64 == 0 && N % y.gd.k.len == 0 && y.gd.k.len % 32 == 0;
+    {
+      prof::Scope ps("gemm_f32_dx+k3", T, K, N, 2.0 * T * N * K + k3_flops,
+                     4.0 * (T * N + N * K + y.gd.k.n * T * K) + k3_bytes);
+      const dim3 grid((unsigned)(f.gemm_blocks + f.side_blocks));
+      LORA_RP_DISPATCH_32(rp, {
+        if (exact) launch(bwd_main_kernel<true, RP>, grid, st, ps, a, kb, f);
+        else launch(bwd_main_kernel<false, RP>, grid, st, ps, a, kb, f);
+      });
+    }
+    // Launch 2: dX = sum of partials + (s V A) * mask * keep, beside k4 and
+    // the dB / dm reductions.
+    k4a.V = vd.p;
+    k4a.vparts = vd.nparts;
+    EpiArgs e = epi_shape(T, K);
+    e.part = a.part; e.nsplit = y.gd.k.n;
+    e.xa = vd; e.XB = lin->A; e.r = r; e.s = lin->scale; e.drop = d;
+    e.C = dX;
+    RedJobs J;
+    memset(&J, 0, sizeof(J));
+    int64_t rblocks = 0;
+    for (int i = 0; i < nj; ++i) {
+      J.job[i] = jobs[i];
+      J.blk[i] = rblocks;
+      rblocks += cdiv(jobs[i].n, 256);
+    }
+    J.blk[nj] = rblocks;
+    J.njobs = nj;
+    BwdEpiGrid g;
+    g.narrow = T <= K4N_MAX_T && y.k4.n == 1;
+    g.k4_x = g.narrow ? cdiv(K, 16) : cdiv(K, SK_C);
+    g.k4_blocks = g.k4_x * y.k4.n;
+    g.epi_blocks = e.blocks;
+    {
+      prof::Scope ps("dx_epilogue+k4", T, K, y.gd.k.n, 2.0 * T * K * r + k4_flops,
+                     4.0 * T * K * (y.gd.k.n + 1) + 4.0 * (nvp * T * r + r * K) + k4_bytes);
+      LORA_RP_DISPATCH_32(rp, launch(bwd_epi_kernel<RP>,
+                                     dim3((unsigned)(g.k4_blocks + g.epi_blocks + rblocks)), st,
+                                     ps, e, k4a, J, g));
+    }
+    if (y.k4.n > 1) {
+      RedJob ja = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
+      launch_reduce(&ja, 1, st);
+    }
+    return hip_status();
+  }
+
+  // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
   {
-    const float* Zin = dMag ? Z : nullptr;
-    prof::Scope ps("k3_v_db", T, N, r, 4.0 * T * N * r,
-                   4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
-                       (o.gbf ? 2.0 * T * N : 0.0));
+    prof::Scope ps("k3_v_db", T, N, r, k3_flops, k3_bytes);
     const dim3 grid((unsigned)y.strips, (unsigned)y.k3.n);
-    LORA_RP_DISPATCH(rp, launch(k3_kernel<RP>, grid, st, ps, dY, T, N, lin->B, U, r,
-                                lin->dora_mag, lin->dora_norm, Zin, y.k3.len, o));
+    LORA_RP_DISPATCH(rp, launch(k3_kernel<RP>, grid, st, ps, ka));
   }
   if (y.vreduce) {
     RedJob jv = {o.Vpart, o.V, nullptr, T * r, 1, (int)y.strips, 0, 1.0f};
     launch_reduce(&jv, 1, st);
   }
-  const LoraOperand xv = (y.strips == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
-                                                      : LoraOperand{o.Vpart, T * r, (int)y.strips, nullptr};
 
   if (dX) {
     if (bf) {
@@ -425,21 +593,12 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
     }
   }
 
-  float* dApart = y.k4.n > 1 ? (float*)(w + y.dapart) : nullptr;
   {
-    prof::Scope ps("k4_da", T, r, K, 2.0 * T * K * r, 4.0 * (T * K + T * r + 2 * r * K));
+    prof::Scope ps("k4_da", T, r, K, k4_flops, k4_bytes);
     const dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)y.k4.n);
-    LORA_RP_DISPATCH(rp, launch(k4_kernel<RP>, grid, st, ps, X, T, K, xv.p, xv.nparts, r, d,
-                                y.k4.len, dApart, dA, lin->scale, acc));
+    LORA_RP_DISPATCH(rp, launch(k4_kernel<RP>, grid, st, ps, k4a));
   }
 
-  // Gradient splits over token ranges: one fixed-order reduction launch.
-  RedJob jobs[3];
-  int nj = 0;
-  if (y.k3.n > 1) {
-    jobs[nj++] = {o.dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
-    if (dMag) jobs[nj++] = {o.dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
-  }
   if (y.k4.n > 1) jobs[nj++] = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
   if (nj) launch_reduce(jobs, nj, st);
   return hip_status();

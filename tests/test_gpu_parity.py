@@ -124,6 +124,13 @@ LINEAR_CASES = [
     ("qwen-wq-slice", 256, 2560, 4096, 32, "bf16", math.sqrt(32), 0.0, False, 1.0, 1e-2),
     ("qwen-wdown-slice", 256, 9728, 2560, 32, "bf16", math.sqrt(32), 0.0, False, 1.0, 1e-2),
     ("qwen-dora-wgate-slice", 256, 2560, 9728, 64, "bf16", 1.0, 0.1, True, 1.0, 1e-2),
+    # short chunks: contraction split across blocks, rank-side work beside the GEMM
+    ("split-ragged-f32", 100, 1000, 600, 8, "f32", 2.0, 0.1, False, 1.0, 1.0),
+    ("split-ragged-f32-dora", 72, 1032, 520, 12, "f32", 1.5, 0.1, True, 1.0, 1.0),
+    ("split-f32-r32", 128, 1024, 768, 32, "f32", 2.0, 0.05, False, 1.0, 1e-2),
+    ("split-f32-token-ranges", 400, 1024, 512, 8, "f32", 2.0, 0.05, False, 1.0, 1.0),
+    ("split-f32-v-reduced", 128, 1088, 8192, 32, "f32", 2.0, 0.05, False, 1.0, 1e-2),
+    ("split-f32-r40", 128, 1024, 512, 40, "f32", 2.0, 0.1, False, 1.0, 1.0),
 ]
 
 
@@ -146,8 +153,8 @@ def test_linear_forward_backward_parity(case):
         assert e <= tol, (n, e)
 
 
-def test_backward_accumulates_over_chunks():
-    T, K, N, r = 64, 128, 96, 8
+@pytest.mark.parametrize("T,K,N,r", [(64, 128, 96, 8), (128, 1024, 512, 8)])
+def test_backward_accumulates_over_chunks(T, K, N, r):
     c1 = _linear_case(T, K, N, r, seed=1)
     c2 = dict(c1)
     c2["X"] = WL.draw((T, K), (77, 0, 0, 0, 1, "X"), "normal", 1.0)
