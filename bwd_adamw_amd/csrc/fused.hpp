@@ -59,14 +59,14 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(GemmF32Args g, DownArgs d
     int64_t tn, tm;
     int split;
     split_tile(f, b, tn, tm, split);
-    gemm_f32_block<64, 64, true, EXACT, gemm_f32_depth<64, 64>()>(g, smem, tn, tm, split);
+    gemm_f32_block<64, 64, true, EXACT, gemm_f32_depth<64, 64>(), false>(g, smem, tn, tm, split);
   } else {
     const int64_t sb = b - f.gemm_blocks;
     down_block<RP>(d, smem, sb % f.side_x, (int)(sb / f.side_x));
   }
 }
 
-template <bool EXACT, int RP>
+template <bool EXACT, bool SCALEA, int RP>
 __global__ __launch_bounds__(256) void bwd_main_kernel(GemmF32Args g, K3Args k, SplitGrid f) {
   constexpr int L = cmax(gemm_f32_lds_floats<64, 64, false>(), k3_lds_floats<RP>());
   __shared__ __attribute__((aligned(16))) float smem[L];
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(GemmF32Args g, K3Args k, 
     int64_t tn, tm;
     int split;
     split_tile(f, b, tn, tm, split);
-    gemm_f32_block<64, 64, false, EXACT, gemm_f32_depth<64, 64>()>(g, smem, tn, tm, split);
+    gemm_f32_block<64, 64, false, EXACT, gemm_f32_depth<64, 64>(), SCALEA>(g, smem, tn, tm, split);
   } else {
     const int64_t sb = b - f.gemm_blocks;
     k3_block<RP>(k, smem, sb % f.side_x, (int)(sb / f.side_x));

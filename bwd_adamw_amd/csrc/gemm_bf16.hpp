@@ -5,13 +5,19 @@
 // The LoRA operands (U, B, V, A: float32) are rounded to bf16 while staging;
 // U and V may arrive as split partials, summed in split order while staging.
 //
-// Block: 512 threads = 2 x 4 waves over a BM x BN tile (256x256, 256x128 or
-// 128x128), K-step 64, LDS double buffered.  LDS holds both operands as
-// [row][contraction] bf16 with a 16-byte pad, so every MFMA operand is one
-// 128-bit LDS read: lane half h takes contraction indices 32h..32h+31 of the
-// K-step.  For dX the W tile arrives with the contraction index as its row
-// (W's native [N,K] layout); each thread loads an 8-row x 4-column block and
-// transposes it in registers before the LDS write.
+// Block: NT threads = WGM x WGN waves over a BM x BN tile, K-step BK.  LDS is
+// double buffered and holds both operands as [row][contraction] bf16 with a
+// 16-byte pad, so every MFMA operand is one 128-bit LDS read: lane half h
+// takes contraction indices h*BK/2 .. (h+1)*BK/2 - 1 of the K-step.  For dX
+// the W tile arrives with the contraction index as its row (W's native [N,K]
+// layout); each thread loads an 8-row x 4-column block and transposes it in
+// registers before the LDS write.
+//
+// The main loop keeps DEPTH K-steps of global loads in flight in registers
+// (the load for step k + DEPTH is issued while step k is computed; DEPTH 1
+// is the plain double buffer) with a straight-line body: every step issues its loads (clamped to the last step
+// past the end), out-of-range elements are zeroed when stored to LDS, so the
+// compiler waits for exactly the stage it stores.
 //
 // The grid is one-dimensional.  Workgroups are dealt to the 8 XCDs round
 // robin, so block b runs on XCD b % 8, and each XCD starts its blocks in
@@ -20,6 +26,8 @@
 // column, so the tiles an XCD has resident at once form a compact rectangle
 // whose A and B K-slices are shared in that XCD's L2.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm_f32.hpp"   // LoraOperand
 
@@ -45,20 +53,25 @@ struct GemmBf16Args {
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
-// EXACT: M, Nc and Kc are multiples of BM, BN and 64, so the main loop runs
-// without bounds checks (no divergent branches around its loads).
-template <int BM, int BN, bool FWD, bool EXACT>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
-  constexpr int NT = 512;
-  constexpr int BK = 64;
-  constexpr int LDS_ROW = BK + 8;                   // bf16 elements per LDS row (144 B)
-  constexpr int WGM = 2, WGN = 4;
+// EXACT: M, Nc and Kc are multiples of BM, BN and BK: nothing is out of range.
+template <int BM, int BN, int NT, int WGM, int BK, int DEPTH, bool FWD, bool EXACT>
+__global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
+  constexpr int WGN = NT / 64 / WGM;
+  constexpr int LDS_ROW = BK + 8;                   // bf16 elements per LDS row
+  constexpr int CPR = BK / 8;                       // 16-byte chunks per row per K-step
   constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
-  constexpr int ACH = BM * (BK / 8) / NT;           // 16-byte A chunks per thread
-  constexpr int BCH = BN * (BK / 8) / NT;           // 16-byte B chunks per thread (fwd)
-  constexpr int BITEMS = (BK / 8) * (BN / 4);       // transposed 8x4 blocks (dx)
+  constexpr int ACH = BM * CPR / NT;                // 16-byte A chunks per thread
+  constexpr int BCH = BN * CPR / NT;                // 16-byte B chunks per thread (fwd)
+  constexpr int BITEMS = CPR * (BN / 4);            // transposed 8x4 blocks (dx)
   constexpr int BIT = (BITEMS + NT - 1) / NT;
+  constexpr int KS = BK / 16;                       // MFMAs per K-step per output tile
+  constexpr int LBK = 64;                           // K-step of the LoRA contraction
+  constexpr int LROW = LBK + 8;
+  static_assert(WGM * WGN * 64 == NT, "wave grid");
   static_assert(ACH >= 1 && BCH >= 1 && MI >= 1 && NI >= 1, "tile too small");
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole chunks per thread");
+  static_assert((BM + BN) * LROW <= 2 * (BM + BN) * LDS_ROW, "LoRA staging fits the LDS");
+  static_assert(DEPTH >= 1, "stages in flight");
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDS_ROW];
   auto As = [&](int b) -> uint16_t* { return smem + b * (BM * LDS_ROW); };
@@ -82,110 +95,134 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  u32x4 ra[ACH];
-  u32x4 rbf[FWD ? BCH : 1];
-  u32x2 rbt[FWD ? 1 : BIT][8];
+  struct Stage {
+    u32x4 a[ACH];
+    u32x4 bf[FWD ? BCH : 1];
+    u32x2 bt[FWD ? 1 : BIT][8];
+  };
 
-  // 8 contiguous bf16 at src[row*ld + k .. +8), zero beyond klim (klim % 8 == 0).
-  auto ld8 = [&](const uint16_t* src, int64_t row, int64_t rows, int64_t ld, int64_t k,
-                 int64_t klim) -> u32x4 {
-    if (EXACT) return *reinterpret_cast<const u32x4*>(src + row * ld + k);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < rows && k < klim) v = *reinterpret_cast<const u32x4*>(src + row * ld + k);
-    return v;
+  // Operand loads are raw buffer loads with a 32-bit byte offset (the
+  // thread's base plus a uniform step), so a stage holds no 64-bit
+  // addresses.  Each resource starts at this block's tiles and ends at its
+  // operand's end, and the hardware returns zero for offsets past that end:
+  // rows past the operand read as zero, and only the contraction edge
+  // (forward) or column edge (dX) is masked, when the stage is stored.
+  constexpr int RPQ = NT / CPR;                     // chunk rows per thread pass
+  const int64_t arows = p.M - m0;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + m0 * p.lda), (short)0, (int)(uint32_t)min<int64_t>(0xffffffffll, arows * p.lda * 2),
+      0x00020000);
+  const uint32_t voffA = (uint32_t)(((tid / CPR) * p.lda + 8 * (tid % CPR)) * 2);
+  const __amdgpu_buffer_rsrc_t rB =
+      FWD ? __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(p.B + n0 * p.ldb), (short)0,
+                (int)(uint32_t)min<int64_t>(0xffffffffll, (p.Nc - n0) * p.ldb * 2), 0x00020000)
+          : __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(p.B + n0), (short)0,
+                (int)(uint32_t)min<int64_t>(0xffffffffll, (p.Kc * p.ldb - n0) * 2), 0x00020000);
+  constexpr int CQN = BN / 4;                       // dX: 4-column quads per row
+  constexpr int KGQ = NT / CQN;                     // dX: 8-row groups per thread pass
+  static_assert(NT % CPR == 0 && (FWD || NT % CQN == 0), "uniform chunk rows");
+  const uint32_t voffB = FWD ? (uint32_t)(((tid / CPR) * p.ldb + 8 * (tid % CPR)) * 2)
+                             : (uint32_t)(((tid / CQN) * 8 * p.ldb + 4 * (tid % CQN)) * 2);
+
+  auto a_ok = [&](int64_t k0) -> bool { return EXACT || k0 + 8 * (tid % CPR) < kend; };
+  auto bt_ok = [&](int q) -> bool {
+    return (EXACT || n0 + 4 * (tid % CQN) < p.Nc) && tid + NT * q < BITEMS;
   };
-  auto load_a = [&](int64_t k0) {
+  auto load = [&](Stage& S, int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < ACH; ++q)
+      S.a[q] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rA, voffA + (uint32_t)((q * RPQ * p.lda + k0) * 2), 0, 0));
+    if constexpr (FWD) {
+#pragma unroll
+      for (int q = 0; q < BCH; ++q)
+        S.bf[q] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rB, voffB + (uint32_t)((q * RPQ * p.ldb + k0) * 2), 0, 0));
+    } else {
+#pragma unroll
+      for (int q = 0; q < BIT; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          S.bt[q][i] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                         rB, voffB + (uint32_t)(((int64_t)q * KGQ * 8 + i + k0) * p.ldb * 2), 0, 0));
+    }
+  };
+  auto store = [&](const Stage& S, int64_t k0, int buf) {
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const bool aok = a_ok(k0);
 #pragma unroll
     for (int q = 0; q < ACH; ++q) {
       const int f = tid + NT * q;
-      ra[q] = ld8(p.A, m0 + (f >> 3), p.M, p.lda, k0 + 8 * (f & 7), kend);
+      *reinterpret_cast<u32x4*>(&As(buf)[(f / CPR) * LDS_ROW + 8 * (f % CPR)]) = aok ? S.a[q] : z4;
     }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < ACH; ++q) {
-      const int f = tid + NT * q;
-      *reinterpret_cast<u32x4*>(&As(buf)[(f >> 3) * LDS_ROW + 8 * (f & 7)]) = ra[q];
-    }
-  };
-  auto load_b = [&](int64_t k0) {
     if constexpr (FWD) {
 #pragma unroll
       for (int q = 0; q < BCH; ++q) {
         const int f = tid + NT * q;
-        rbf[q] = ld8(p.B, n0 + (f >> 3), p.Nc, p.ldb, k0 + 8 * (f & 7), kend);
+        *reinterpret_cast<u32x4*>(&Bs(buf)[(f / CPR) * LDS_ROW + 8 * (f % CPR)]) = aok ? S.bf[q] : z4;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < BIT; ++q) {
         const int f = tid + NT * q;
-        const int cq = f % (BN / 4), kg = f / (BN / 4);
-        const int64_t gn = n0 + 4 * cq;
+        if (f >= BITEMS) continue;
+        const int cq = f % CQN, kg = f / CQN;
+        const bool ok = bt_ok(q);
+        u32x2 w[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t gk = k0 + 8 * kg + i;
-          u32x2 v = {0u, 0u};
-          if (EXACT ? (f < BITEMS) : (f < BITEMS && gk < kend && gn < p.Nc))
-            v = *reinterpret_cast<const u32x2*>(p.B + gk * p.ldb + gn);
-          rbt[q][i] = v;
+        for (int i = 0; i < 8; ++i) w[i] = ok ? S.bt[q][i] : u32x2{0u, 0u};
+        // column e of the 8x4 block becomes 8 contraction values
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u32x4 o;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t x0 = (e < 2) ? w[2 * d].x : w[2 * d].y;
+            const uint32_t x1 = (e < 2) ? w[2 * d + 1].x : w[2 * d + 1].y;
+            o[d] = (e & 1) ? (hi16(x0) | (hi16(x1) << 16)) : (lo16(x0) | (lo16(x1) << 16));
+          }
+          *reinterpret_cast<u32x4*>(&Bs(buf)[(4 * cq + e) * LDS_ROW + 8 * kg]) = o;
         }
       }
     }
   };
-  // Transposed write: column e of the 8x4 block becomes 8 contraction values.
-  auto store_bt = [&](int buf, int q, const u32x2 (&w)[8]) {
-    const int f = tid + NT * q;
-    if (f >= BITEMS) return;
-    const int cq = f % (BN / 4), kg = f / (BN / 4);
+  // MFMA over one staged K-step: STEPS MFMAs of 16 contraction indices per
+  // output tile, lane half hl holding indices hl*HALF .. of each LD-wide row.
+  auto compute = [&](const uint16_t* Ab, const uint16_t* Bb, auto LD, auto HALF, auto STEPS) {
+    constexpr int ld = decltype(LD)::value, half = decltype(HALF)::value;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u32x4 o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t x0 = (e < 2) ? w[2 * d].x : w[2 * d].y;
-        const uint32_t x1 = (e < 2) ? w[2 * d + 1].x : w[2 * d + 1].y;
-        o[d] = (e & 1) ? (hi16(x0) | (hi16(x1) << 16)) : (lo16(x0) | (lo16(x1) << 16));
-      }
-      *reinterpret_cast<u32x4*>(&Bs(buf)[(4 * cq + e) * LDS_ROW + 8 * kg]) = o;
-    }
-  };
-  auto store_b = [&](int buf) {
-    if constexpr (FWD) {
-#pragma unroll
-      for (int q = 0; q < BCH; ++q) {
-        const int f = tid + NT * q;
-        *reinterpret_cast<u32x4*>(&Bs(buf)[(f >> 3) * LDS_ROW + 8 * (f & 7)]) = rbf[q];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < BIT; ++q) store_bt(buf, q, rbt[q]);
-    }
-  };
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < decltype(STEPS)::value; ++s) {
       u32x4 av[MI], bv[NI];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        av[i] = *reinterpret_cast<const u32x4*>(
-            &As(buf)[(wm0 + i * 32 + l32) * LDS_ROW + 32 * hl + 8 * s]);
+        av[i] = *reinterpret_cast<const u32x4*>(&Ab[(wm0 + i * 32 + l32) * ld + half * hl + 8 * s]);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        bv[j] = *reinterpret_cast<const u32x4*>(
-            &Bs(buf)[(wn0 + j * 32 + l32) * LDS_ROW + 32 * hl + 8 * s]);
+        bv[j] = *reinterpret_cast<const u32x4*>(&Bb[(wn0 + j * 32 + l32) * ld + half * hl + 8 * s]);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j) acc[i][j] = mfma32x32x16_bf16(av[i], bv[j], acc[i][j]);
     }
   };
-  // LoRA contraction over the rank: float32 operands rounded to bf16 in LDS.
+  using MainLd = std::integral_constant<int, LDS_ROW>;
+  using MainHalf = std::integral_constant<int, BK / 2>;
+  using MainSteps = std::integral_constant<int, KS>;
+  // LoRA contraction over the rank: float32 operands rounded to bf16 in LDS,
+  // in 64-wide K-steps over the same LDS.
   auto lora_contraction = [&]() {
-    for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
+    uint16_t* La = smem;
+    uint16_t* Lb = smem + BM * LROW;
+    for (int64_t k0 = 0; k0 < p.r; k0 += LBK) {
       __syncthreads();
       // A side: XA [M, r] rows m (split partials summed), scaled by s.
-      for (int f = tid; f < BM * (BK / 4); f += NT) {
-        const int row = f / (BK / 4), c4 = f % (BK / 4);
+      for (int f = tid; f < BM * (LBK / 4); f += NT) {
+        const int row = f / (LBK / 4), c4 = f % (LBK / 4);
         const int64_t gm = m0 + row, gk = k0 + 4 * c4;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (gm < p.M && gk < p.r) {
@@ -195,30 +232,31 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
           v *= p.xs;
         }
         u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(&As(0)[row * LDS_ROW + 4 * c4]) = b;
+        *reinterpret_cast<u32x2*>(&La[row * LROW + 4 * c4]) = b;
       }
       if constexpr (FWD) {
         // B_lora [Nc, r]: rows n, rank contiguous.
-        for (int f = tid; f < BN * (BK / 4); f += NT) {
-          const int row = f / (BK / 4), c4 = f % (BK / 4);
+        for (int f = tid; f < BN * (LBK / 4); f += NT) {
+          const int row = f / (LBK / 4), c4 = f % (LBK / 4);
           const int64_t gn = n0 + row, gk = k0 + 4 * c4;
           f32x4 v = {0.f, 0.f, 0.f, 0.f};
           if (gn < p.Nc && gk < p.r) v = *reinterpret_cast<const f32x4*>(p.XB + gn * p.r + gk);
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(&Bs(0)[row * LDS_ROW + 4 * c4]) = b;
+          *reinterpret_cast<u32x2*>(&Lb[row * LROW + 4 * c4]) = b;
         }
       } else {
         // A_lora [r, Nc]: rows are the contraction index; transpose on store.
-        for (int f = tid; f < BN * BK; f += NT) {
+        for (int f = tid; f < BN * LBK; f += NT) {
           const int n = f % BN, kk = f / BN;
           const int64_t gn = n0 + n, gk = k0 + kk;
           float v = 0.f;
           if (gn < p.Nc && gk < p.r) v = p.XB[gk * p.Nc + gn];
-          Bs(0)[n * LDS_ROW + kk] = (uint16_t)f32_to_bf16_bits(v);
+          Lb[n * LROW + kk] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
       __syncthreads();
-      compute(0);
+      compute(La, Lb, std::integral_constant<int, LROW>{}, std::integral_constant<int, LBK / 2>{},
+              std::integral_constant<int, LBK / 16>{});
     }
     __syncthreads();
   };
@@ -241,24 +279,42 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmBf16Args p) {
     }
   }
 
+  // Main contraction.
   const int64_t nk = (kend + BK - 1) / BK;
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  store_b(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nk) {
-      load_a((kt + 1) * BK);
-      load_b((kt + 1) * BK);
-    }
-    compute(cur);
-    if (kt + 1 < nk) {
-      store_a(cur ^ 1);
-      store_b(cur ^ 1);
-    }
+  {
+    Stage R[DEPTH];
+    auto kstep = [&](int64_t k) { return min(k, nk - 1) * BK; };
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) load(R[u], kstep(u));
+    store(R[0], 0, 0);
     __syncthreads();
+    int64_t k = 0;
+    for (; k + DEPTH <= nk; k += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int64_t kk = k + u;
+        load(R[u], kstep(kk + DEPTH));
+        // Keep the loads ahead of this step's MFMAs: left to itself the
+        // scheduler sinks them next to their LDS stores to shorten register
+        // lifetimes, which exposes their whole latency.
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = (int)(kk & 1);
+        compute(As(buf), Bs(buf), MainLd{}, MainHalf{}, MainSteps{});
+        store(R[(u + 1) % DEPTH], kstep(kk + 1), buf ^ 1);
+        __syncthreads();
+      }
+    }
+    // Fewer than DEPTH steps left; their loads are already in flight.
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u) {
+      const int64_t kk = k + u;
+      if (kk < nk) {
+        const int buf = (int)(kk & 1);
+        compute(As(buf), Bs(buf), MainLd{}, MainHalf{}, MainSteps{});
+        if (kk + 1 < nk) store(R[(u + 1) % DEPTH], kstep(kk + 1), buf ^ 1);
+        __syncthreads();
+      }
+    }
   }
 
   if (FWD && p.r > 0) lora_contraction();

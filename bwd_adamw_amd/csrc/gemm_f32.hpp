@@ -72,11 +72,17 @@ constexpr int gemm_f32_lds_floats() {
 // LDS buffer k%2 holds step k, register stage (k+1)%DEPTH holds step k+1 and
 // is stored to the other buffer after the MFMAs, and stage k%DEPTH (stored
 // one step earlier) is refilled.  The loop is unrolled by DEPTH so every
-// stage index is a compile-time constant.
+// stage index is a compile-time constant, and its body has no branches:
+// every step issues its loads (past the last step they repeat the last
+// step's addresses and are never stored), out-of-range elements are read
+// from a valid address and zeroed when stored to LDS.  Straight-line code
+// lets the compiler wait for exactly the stage it stores, with the newer
+// stages still in flight.
 //
 // EXACT: M and Nc are multiples of BM and BN and every split range a multiple
-// of 32, so the main loop runs without bounds checks.
-template <int BM, int BN, bool FWD, bool EXACT, int DEPTH>
+// of 32, so nothing is out of range.  SCALEA: the A operand is multiplied per
+// contraction index by acn/acd (DoRA g = dY * mag/norm in dX).
+template <int BM, int BN, bool FWD, bool EXACT, int DEPTH, bool SCALEA>
 LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int64_t tm,
                              int split) {
   constexpr int BK = 32;
@@ -90,6 +96,7 @@ LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int6
   constexpr int AF4 = BM * BK / 4 / 256;
   constexpr int BF4 = BN * BK / 4 / 256;
   constexpr int AC4 = BK / 4;           // float4 per A row of a K-step
+  constexpr int NS = SCALEA ? AF4 : 1;
   static_assert(AF4 >= 1 && BF4 >= 1 && MI >= 1 && NI >= 1, "tile shape");
   static_assert(KH % 4 == 0, "lane-half slice must be whole float4s");
   static_assert(DEPTH >= 2, "at least one K-step of loads in flight");
@@ -115,80 +122,71 @@ LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int6
 
   struct Stage {
     f32x4 a[AF4], b[BF4];
+    f32x4 an[NS], ad[NS];
   };
 
-  // A side (main operand): rows m, contraction contiguous.
-  auto load_a = [&](Stage& S, int64_t k0) {
+  // Element coordinates of this thread's q-th float4 of a K-step at k0.
+  auto a_at = [&](int q, int64_t k0, int64_t& gm, int64_t& gk) -> bool {
+    const int f = tid + 256 * q;
+    gm = m0 + f / AC4;
+    gk = k0 + 4 * (f % AC4);
+    return EXACT || (gm < p.M && gk < kend);
+  };
+  auto b_at = [&](int q, int64_t k0, int64_t& gr, int64_t& gc) -> bool {
+    const int f = tid + 256 * q;
+    if (FWD) {   // rows n, contraction contiguous
+      gr = n0 + f / AC4;
+      gc = k0 + 4 * (f % AC4);
+      return EXACT || (gr < p.Nc && gc < kend);
+    } else {     // rows = contraction, columns n
+      gr = k0 + f / (BN / 4);
+      gc = n0 + 4 * (f % (BN / 4));
+      return EXACT || (gr < kend && gc < p.Nc);
+    }
+  };
+  auto load = [&](Stage& S, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < AF4; ++q) {
-      const int f = tid + 256 * q;
-      const int row = f / AC4, c4 = f % AC4;
-      const int64_t gm = m0 + row, gk = k0 + 4 * c4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (EXACT || (gm < p.M && gk < kend)) {
-        v = *reinterpret_cast<const f32x4*>(p.A + gm * p.lda + gk);
-        if (p.acn) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= p.acn[gk + e] / p.acd[gk + e];
-        }
+      int64_t gm, gk;
+      const bool ok = a_at(q, k0, gm, gk);
+      S.a[q] = *reinterpret_cast<const f32x4*>(ok ? p.A + gm * p.lda + gk : p.A);
+      if constexpr (SCALEA) {
+        const int64_t kk = ok ? gk : 0;
+        S.an[q] = *reinterpret_cast<const f32x4*>(p.acn + kk);
+        S.ad[q] = *reinterpret_cast<const f32x4*>(p.acd + kk);
       }
-      S.a[q] = v;
     }
-  };
-  // A side (LoRA operand): rows m, rank contiguous, partials summed, times s.
-  auto load_xa = [&](Stage& S, int64_t k0) {
-#pragma unroll
-    for (int q = 0; q < AF4; ++q) {
-      const int f = tid + 256 * q;
-      const int row = f / AC4, c4 = f % AC4;
-      const int64_t gm = m0 + row, gk = k0 + 4 * c4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (gm < p.M && gk < p.r) {
-        const int64_t i = gm * p.r + gk;
-        v = sum_parts4(p.xa.p, p.xa.stride, p.xa.nparts, i);
-        if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
-        v *= p.xs;
-      }
-      S.a[q] = v;
-    }
-  };
-  auto store_a = [&](const Stage& S, int buf) {
-#pragma unroll
-    for (int q = 0; q < AF4; ++q) {
-      const int f = tid + 256 * q;
-      const int row = f / AC4, c4 = f % AC4;
-      *reinterpret_cast<f32x4*>(&As(buf)[row * LDA + 4 * c4]) = S.a[q];
-    }
-  };
-  // B side.  fwd: rows n, contraction contiguous.  dx: rows = contraction.
-  auto load_b = [&](Stage& S, const float* src, int64_t ld, int64_t k0, int64_t klim, bool exact) {
 #pragma unroll
     for (int q = 0; q < BF4; ++q) {
-      const int f = tid + 256 * q;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (FWD) {
-        const int row = f / AC4, c4 = f % AC4;
-        const int64_t gn = n0 + row, gk = k0 + 4 * c4;
-        if (exact || (gn < p.Nc && gk < klim)) v = *reinterpret_cast<const f32x4*>(src + gn * ld + gk);
-      } else {
-        const int row = f / (BN / 4), c4 = f % (BN / 4);
-        const int64_t gk = k0 + row, gn = n0 + 4 * c4;
-        if (exact || (gk < klim && gn < p.Nc)) v = *reinterpret_cast<const f32x4*>(src + gk * ld + gn);
-      }
-      S.b[q] = v;
+      int64_t gr, gc;
+      const bool ok = b_at(q, k0, gr, gc);
+      S.b[q] = *reinterpret_cast<const f32x4*>(ok ? p.B + gr * p.ldb + gc : p.B);
     }
   };
-  auto store_b = [&](const Stage& S, int buf) {
+  auto store = [&](const Stage& S, int64_t k0, int buf) {
+#pragma unroll
+    for (int q = 0; q < AF4; ++q) {
+      int64_t gm, gk;
+      const bool ok = a_at(q, k0, gm, gk);
+      f32x4 v = S.a[q];
+      if constexpr (SCALEA) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= S.an[q][e] / S.ad[q][e];
+      }
+      if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int f = tid + 256 * q;
+      *reinterpret_cast<f32x4*>(&As(buf)[(f / AC4) * LDA + 4 * (f % AC4)]) = v;
+    }
 #pragma unroll
     for (int q = 0; q < BF4; ++q) {
+      int64_t gr, gc;
+      const bool ok = b_at(q, k0, gr, gc);
+      const f32x4 v = ok ? S.b[q] : f32x4{0.f, 0.f, 0.f, 0.f};
       const int f = tid + 256 * q;
-      if (FWD) {
-        const int row = f / AC4, c4 = f % AC4;
-        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = S.b[q];
-      } else {
-        const int row = f / (BN / 4), c4 = f % (BN / 4);
-        *reinterpret_cast<f32x4*>(&Bs(buf)[row * LDB + 4 * c4]) = S.b[q];
-      }
+      if (FWD)
+        *reinterpret_cast<f32x4*>(&Bs(buf)[(f / AC4) * LDB + 4 * (f % AC4)]) = v;
+      else
+        *reinterpret_cast<f32x4*>(&Bs(buf)[(f / (BN / 4)) * LDB + 4 * (f % (BN / 4))]) = v;
     }
   };
   auto compute = [&](int buf) {
@@ -227,15 +225,52 @@ LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int6
       }
     }
   };
-  // Unpipelined contraction over the LoRA rank (r <= 128).
+  // Unpipelined contraction over the LoRA rank (r <= 128): the A side is
+  // U or V (split partials summed, times s), the B side B_lora (forward,
+  // [Nc, r]) or A_lora (dX, [r, Nc]); both masked while loading.
   auto lora_contraction = [&]() {
-    Stage S;
     for (int64_t k0 = 0; k0 < p.r; k0 += BK) {
-      load_xa(S, k0);
-      load_b(S, p.XB, FWD ? p.r : p.Nc, k0, p.r, false);
+      f32x4 ra[AF4], rb[BF4];
+#pragma unroll
+      for (int q = 0; q < AF4; ++q) {
+        const int f = tid + 256 * q;
+        const int64_t gm = m0 + f / AC4, gk = k0 + 4 * (f % AC4);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (gm < p.M && gk < p.r) {
+          const int64_t i = gm * p.r + gk;
+          v = sum_parts4(p.xa.p, p.xa.stride, p.xa.nparts, i);
+          if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
+          v *= p.xs;
+        }
+        ra[q] = v;
+      }
+#pragma unroll
+      for (int q = 0; q < BF4; ++q) {
+        const int f = tid + 256 * q;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (FWD) {
+          const int64_t gn = n0 + f / AC4, gk = k0 + 4 * (f % AC4);
+          if (gn < p.Nc && gk < p.r) v = *reinterpret_cast<const f32x4*>(p.XB + gn * p.r + gk);
+        } else {
+          const int64_t gk = k0 + f / (BN / 4), gn = n0 + 4 * (f % (BN / 4));
+          if (gk < p.r && gn < p.Nc) v = *reinterpret_cast<const f32x4*>(p.XB + gk * p.Nc + gn);
+        }
+        rb[q] = v;
+      }
       __syncthreads();
-      store_a(S, 0);
-      store_b(S, 0);
+#pragma unroll
+      for (int q = 0; q < AF4; ++q) {
+        const int f = tid + 256 * q;
+        *reinterpret_cast<f32x4*>(&As(0)[(f / AC4) * LDA + 4 * (f % AC4)]) = ra[q];
+      }
+#pragma unroll
+      for (int q = 0; q < BF4; ++q) {
+        const int f = tid + 256 * q;
+        if (FWD)
+          *reinterpret_cast<f32x4*>(&Bs(0)[(f / AC4) * LDB + 4 * (f % AC4)]) = rb[q];
+        else
+          *reinterpret_cast<f32x4*>(&Bs(0)[(f / (BN / 4)) * LDB + 4 * (f % (BN / 4))]) = rb[q];
+      }
       __syncthreads();
       compute(0);
     }
@@ -265,32 +300,36 @@ LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int6
   const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
     Stage R[DEPTH];
+    auto kstep = [&](int64_t k) { return kbeg + min(k, nk - 1) * BK; };
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u)
-      if (u < nk) {
-        load_a(R[u], kbeg + u * BK);
-        load_b(R[u], p.B, p.ldb, kbeg + u * BK, kend, EXACT);
-      }
-    store_a(R[0], 0);
-    store_b(R[0], 0);
+    for (int u = 0; u < DEPTH; ++u) load(R[u], kstep(u));
+    store(R[0], kbeg, 0);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; kt += DEPTH) {
+    int64_t k = 0;
+    for (; k + DEPTH <= nk; k += DEPTH) {
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
-        const int64_t k = kt + u;
-        if (k < nk) {
-          if (k + DEPTH < nk) {
-            load_a(R[u], kbeg + (k + DEPTH) * BK);
-            load_b(R[u], p.B, p.ldb, kbeg + (k + DEPTH) * BK, kend, EXACT);
-          }
-          const int buf = (int)(k & 1);
-          compute(buf);
-          if (k + 1 < nk) {
-            store_a(R[(u + 1) % DEPTH], buf ^ 1);
-            store_b(R[(u + 1) % DEPTH], buf ^ 1);
-          }
-          __syncthreads();
-        }
+        const int64_t kk = k + u;
+        load(R[u], kstep(kk + DEPTH));
+        // Keep the loads ahead of this step's MFMAs: left to itself the
+        // scheduler sinks them next to their LDS stores to shorten register
+        // lifetimes, which exposes their whole latency.
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = (int)(kk & 1);
+        compute(buf);
+        store(R[(u + 1) % DEPTH], kstep(kk + 1), buf ^ 1);
+        __syncthreads();
+      }
+    }
+    // Fewer than DEPTH steps left; their loads are already in flight.
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u) {
+      const int64_t kk = k + u;
+      if (kk < nk) {
+        const int buf = (int)(kk & 1);
+        compute(buf);
+        if (kk + 1 < nk) store(R[(u + 1) % DEPTH], kstep(kk + 1), buf ^ 1);
+        __syncthreads();
       }
     }
   }
@@ -327,11 +366,11 @@ constexpr int gemm_f32_depth() {
 }
 
 // Grid (Nc/BN, M/BM, nsplit).
-template <int BM, int BN, bool FWD, bool EXACT>
+template <int BM, int BN, bool FWD, bool EXACT, bool SCALEA>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
   __shared__ __attribute__((aligned(16))) float smem[gemm_f32_lds_floats<BM, BN, FWD>()];
-  gemm_f32_block<BM, BN, FWD, EXACT, gemm_f32_depth<BM, BN>()>(p, smem, blockIdx.x, blockIdx.y,
-                                                                 blockIdx.z);
+  gemm_f32_block<BM, BN, FWD, EXACT, gemm_f32_depth<BM, BN>(), SCALEA>(p, smem, blockIdx.x,
+                                                                         blockIdx.y, blockIdx.z);
 }
 
 // Sum of the split partials in split order, then the epilogue of the unsplit

@@ -87,21 +87,45 @@ Split plan_rows(int64_t T, int64_t strips) {
 struct GemmPlan {
   int bm, bn;
   Split k;           // contraction split across blocks (fp32 only)
+  int cfg;           // bf16 kernel configuration (kBf16Cfg)
 };
 
-// bf16: the largest tile whose grid still covers most of the 256 CUs.
-// fp32: 128x128 when that fills the chip, else 64x64 with the contraction
-// split across blocks until about 256 blocks run.
-GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16) {
+// bf16 kernel configurations, in order of preference per direction: tile,
+// threads, wave rows, K-step, stages in flight, and the directions (1
+// forward, 2 dX) that use it.  dX's transposing loads take more registers
+// per stage, so its wide tiles keep a single stage (chosen by measurement on
+// the Qwen3-4B-shaped projections).
+struct Bf16Cfg {
+  int bm, bn, nt, wgm, bk, depth, dirs;
+};
+#define LORA_BF16_CFGS(X)             \
+  X(0, 256, 256, 512, 2, 32, 3, 1)    \
+  X(1, 256, 256, 512, 2, 64, 1, 2)    \
+  X(2, 256, 128, 512, 2, 64, 2, 1)    \
+  X(3, 256, 128, 512, 2, 64, 1, 2)    \
+  X(4, 128, 128, 512, 2, 64, 2, 3)
+constexpr Bf16Cfg kBf16Cfg[] = {
+#define LORA_CFG_ROW(i, bm, bn, nt, wgm, bk, d, dirs) {bm, bn, nt, wgm, bk, d, dirs},
+    LORA_BF16_CFGS(LORA_CFG_ROW)
+#undef LORA_CFG_ROW
+};
+constexpr int kBf16NCfg = sizeof(kBf16Cfg) / sizeof(kBf16Cfg[0]);
+
+// bf16: the first configuration whose grid still covers most of the 256
+// CUs.  fp32: 128x128 when that fills the chip, else 64x64 with the
+// contraction split across blocks until about 256 blocks run.
+GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx) {
   if (bf16) {
-    const int shapes[3][2] = {{256, 256}, {256, 128}, {128, 128}};
-    for (const auto& t : shapes)
-      if (cdiv(M, t[0]) * cdiv(Nc, t[1]) >= 200) return {t[0], t[1], {Kc, 1}};
-    return {128, 128, {Kc, 1}};
+    for (int i = 0; i < kBf16NCfg; ++i) {
+      const Bf16Cfg& c = kBf16Cfg[i];
+      if (!(c.dirs & (dx ? 2 : 1))) continue;
+      if (cdiv(M, c.bm) * cdiv(Nc, c.bn) >= 200 || i == kBf16NCfg - 1)
+        return {c.bm, c.bn, {Kc, 1}, i};
+    }
   }
-  if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}};
+  if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}, 0};
   const int64_t tiles = cdiv(M, 64) * cdiv(Nc, 64);
-  return {64, 64, plan_split(Kc, tiles, 256, 32, 128)};
+  return {64, 64, plan_split(Kc, tiles, 256, 32, 128), 0};
 }
 
 // Short chunks: the contraction is split across blocks, and each linear runs
@@ -163,8 +187,8 @@ Layout make_layout(const lora_linear* L) {
   y.strips = cdiv(N, SK_C);
   y.k3 = plan_rows(T, y.strips);
   y.k4 = plan_rows(T, cdiv(K, SK_C));
-  y.gf = plan_gemm(T, N, K, bf);
-  y.gd = plan_gemm(T, K, N, bf);
+  y.gf = plan_gemm(T, N, K, bf, false);
+  y.gd = plan_gemm(T, K, N, bf, true);
   // Beside the split GEMM the down projection needs no parallelism of its
   // own: 256 columns per block keeps its partials few for the epilogue.
   if (use_split_path(y.gf, r, bf)) {
@@ -195,11 +219,18 @@ int check_linear(const lora_linear* L) {
   if (L->tokens <= 0 || L->in_dim <= 0 || L->out_dim <= 0 || L->rank <= 0) return LORA_E_SHAPE;
   if (L->rank > 128 || L->rank > L->in_dim || L->rank > L->out_dim) return LORA_E_SHAPE;
   if (L->w_dtype != LORA_F32 && L->w_dtype != LORA_BF16) return LORA_E_DTYPE;
+  // bf16 operands are read with 32-bit byte offsets.
+  if (L->w_dtype == LORA_BF16 &&
+      (L->in_dim * L->out_dim >= (1ll << 30) || L->tokens * L->in_dim >= (1ll << 30) ||
+       L->tokens * L->out_dim >= (1ll << 30)))
+    return LORA_E_SHAPE;
   const int64_t q = L->w_dtype == LORA_BF16 ? 8 : 4;
   if (L->in_dim % q || L->out_dim % q || L->rank % 4) return LORA_E_ALIGN;
   if (!L->W || !L->A || !L->B) return LORA_E_INVALID;
   if (!al16(L->W) || !al16(L->A) || !al16(L->B)) return LORA_E_ALIGN;
   if ((L->dora_mag == nullptr) != (L->dora_norm == nullptr)) return LORA_E_INVALID;
+  if ((L->dora_mag && !al16(L->dora_mag)) || (L->dora_norm && !al16(L->dora_norm)))
+    return LORA_E_ALIGN;
   if (!std::isfinite(L->scale)) return LORA_E_INVALID;
   return LORA_OK;
 }
@@ -261,15 +292,18 @@ void launch_gemm_f32(const GemmPlan& g, bool fwd, const GemmF32Args& a, hipStrea
     prof::Scope ps(fwd ? "gemm_f32_fwd" : "gemm_f32_dx", a.M, a.Nc, a.Kc,
                    2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                    4.0 * (a.M * a.Kc + a.Nc * a.Kc + a.M * a.Nc * (a.C2 ? 2 : 1)));
-#define LORA_F32_TILE(BM_)                                                              \
-  if (g.bm == BM_) {                                                                    \
-    if (fwd) {                                                                          \
-      if (exact) launch(gemm_f32_kernel<BM_, BM_, true, true>, grid, st, ps, a);        \
-      else launch(gemm_f32_kernel<BM_, BM_, true, false>, grid, st, ps, a);             \
-    } else {                                                                            \
-      if (exact) launch(gemm_f32_kernel<BM_, BM_, false, true>, grid, st, ps, a);       \
-      else launch(gemm_f32_kernel<BM_, BM_, false, false>, grid, st, ps, a);            \
-    }                                                                                   \
+#define LORA_F32_TILE(BM_)                                                                   \
+  if (g.bm == BM_) {                                                                         \
+    if (fwd) {                                                                               \
+      if (exact) launch(gemm_f32_kernel<BM_, BM_, true, true, false>, grid, st, ps, a);      \
+      else launch(gemm_f32_kernel<BM_, BM_, true, false, false>, grid, st, ps, a);           \
+    } else if (a.acn) {                                                                      \
+      if (exact) launch(gemm_f32_kernel<BM_, BM_, false, true, true>, grid, st, ps, a);      \
+      else launch(gemm_f32_kernel<BM_, BM_, false, false, true>, grid, st, ps, a);           \
+    } else {                                                                                 \
+      if (exact) launch(gemm_f32_kernel<BM_, BM_, false, true, false>, grid, st, ps, a);     \
+      else launch(gemm_f32_kernel<BM_, BM_, false, false, false>, grid, st, ps, a);          \
+    }                                                                                        \
   }
     LORA_F32_TILE(128) else LORA_F32_TILE(64)
 #undef LORA_F32_TILE
@@ -288,21 +322,28 @@ void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStr
   prof::Scope ps(fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
                  2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                  2.0 * (a.M * a.Kc + a.Nc * a.Kc) + 4.0 * a.M * a.Nc * (a.C2 ? 2 : 1));
-  const bool exact = a.M % g.bm == 0 && a.Nc % g.bn == 0 && a.Kc % 64 == 0;
-#define LORA_BF16_TILE(BM_, BN_)                                                      \
-  if (g.bm == BM_ && g.bn == BN_) {                                                   \
-    if (fwd) {                                                                        \
-      if (exact) launch_n(gemm_bf16_kernel<BM_, BN_, true, true>, grid, 512u, st, ps, a); \
-      else launch_n(gemm_bf16_kernel<BM_, BN_, true, false>, grid, 512u, st, ps, a);   \
-    } else {                                                                          \
-      if (exact) launch_n(gemm_bf16_kernel<BM_, BN_, false, true>, grid, 512u, st, ps, a); \
-      else launch_n(gemm_bf16_kernel<BM_, BN_, false, false>, grid, 512u, st, ps, a);  \
-    }                                                                                 \
-    return;                                                                           \
+  const Bf16Cfg& c = kBf16Cfg[g.cfg];
+  const bool exact = a.M % c.bm == 0 && a.Nc % c.bn == 0 && a.Kc % c.bk == 0;
+#define LORA_BF16_TILE(i, BM_, BN_, NT_, WGM_, BK_, D_, DIRS_)                              \
+  if (g.cfg == i) {                                                                        \
+    if (fwd) {                                                                             \
+      if constexpr ((DIRS_)&1) {                                                           \
+        if (exact) launch_n(gemm_bf16_kernel<BM_, BN_, NT_, WGM_, BK_, D_, true, true>, grid, \
+                            (unsigned)NT_, st, ps, a);                                     \
+        else launch_n(gemm_bf16_kernel<BM_, BN_, NT_, WGM_, BK_, D_, true, false>, grid,      \
+                      (unsigned)NT_, st, ps, a);                                           \
+      }                                                                                    \
+    } else {                                                                               \
+      if constexpr ((DIRS_)&2) {                                                           \
+        if (exact) launch_n(gemm_bf16_kernel<BM_, BN_, NT_, WGM_, BK_, D_, false, true>, grid, \
+                            (unsigned)NT_, st, ps, a);                                     \
+        else launch_n(gemm_bf16_kernel<BM_, BN_, NT_, WGM_, BK_, D_, false, false>, grid,     \
+                      (unsigned)NT_, st, ps, a);                                           \
+      }                                                                                    \
+    }                                                                                      \
+    return;                                                                                \
   }
-  LORA_BF16_TILE(256, 256)
-  LORA_BF16_TILE(256, 128)
-  LORA_BF16_TILE(128, 128)
+  LORA_BF16_CFGS(LORA_BF16_TILE)
 #undef LORA_BF16_TILE
 }
 
@@ -518,8 +559,13 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
                      4.0 * (T * N + N * K + y.gd.k.n * T * K) + k3_bytes);
       const dim3 grid((unsigned)(f.gemm_blocks + f.side_blocks));
       LORA_RP_DISPATCH_32(rp, {
-        if (exact) launch(bwd_main_kernel<true, RP>, grid, st, ps, a, kb, f);
-        else launch(bwd_main_kernel<false, RP>, grid, st, ps, a, kb, f);
+        if (a.acn) {
+          if (exact) launch(bwd_main_kernel<true, true, RP>, grid, st, ps, a, kb, f);
+          else launch(bwd_main_kernel<false, true, RP>, grid, st, ps, a, kb, f);
+        } else {
+          if (exact) launch(bwd_main_kernel<true, false, RP>, grid, st, ps, a, kb, f);
+          else launch(bwd_main_kernel<false, false, RP>, grid, st, ps, a, kb, f);
+        }
       });
     }
     // Launch 2: dX = sum of partials + (s V A) * mask * keep, beside k4 and
