@@ -20,6 +20,12 @@
 //
 // Roles of one launch share a single LDS array (the largest role's size), so
 // a role's blocks co-reside with the GEMM's on a CU.
+//
+// A launch may carry NG linears that read the same X (the projections of one
+// layer that share their input): each linear keeps its own arguments, blocks
+// and workspace, and the launch count per direction stays two for the whole
+// group.  Per-linear arguments live in fixed-size arrays indexed inside
+// unrolled loops, so every access is a compile-time kernel-argument offset.
 #pragma once
 #include "common.hpp"
 #include "gemm_f32.hpp"
@@ -50,35 +56,79 @@ LORA_DEV void split_tile(const SplitGrid& f, int64_t b, int64_t& tn, int64_t& tm
   split = (int)(rest / f.ntn);
 }
 
-template <bool EXACT, int RP>
-__global__ __launch_bounds__(256) void fwd_main_kernel(GemmF32Args g, DownArgs d, SplitGrid f) {
+// Launch 1 of the forward: the split GEMM blocks of every linear (linear i
+// owns blocks [gstart[i], gstart[i+1])), then their down blocks (linear i:
+// [sstart[i], sstart[i+1]) on its side grid).
+template <int NG>
+struct FwdMain {
+  GemmF32Args g[NG];
+  DownArgs d[NG];
+  SplitGrid f[NG];
+  int64_t gstart[NG + 1];
+  int64_t sstart[NG + 1];
+};
+
+template <int NG, bool EXACT, int RP>
+__global__ __launch_bounds__(256) void fwd_main_kernel(FwdMain<NG> p) {
   constexpr int L = cmax(gemm_f32_lds_floats<64, 64, true>(), down_lds_floats<RP>());
   __shared__ __attribute__((aligned(16))) float smem[L];
   const int64_t b = blockIdx.x;
-  if (b < f.gemm_blocks) {
-    int64_t tn, tm;
-    int split;
-    split_tile(f, b, tn, tm, split);
-    gemm_f32_block<64, 64, true, EXACT, gemm_f32_depth<64, 64>(), false>(g, smem, tn, tm, split);
+  if (b < p.gstart[NG]) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.gstart[i + 1]) {
+        int64_t tn, tm;
+        int split;
+        split_tile(p.f[i], b - p.gstart[i], tn, tm, split);
+        gemm_f32_block<64, 64, true, EXACT, gemm_f32_depth<64, 64>(), false>(p.g[i], smem, tn, tm,
+                                                                           split);
+        return;
+      }
   } else {
-    const int64_t sb = b - f.gemm_blocks;
-    down_block<RP>(d, smem, sb % f.side_x, (int)(sb / f.side_x));
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.sstart[i + 1]) {
+        const int64_t sb = b - p.sstart[i];
+        down_block<RP>(p.d[i], smem, sb % p.f[i].side_x, (int)(sb / p.f[i].side_x));
+        return;
+      }
   }
 }
 
-template <bool EXACT, bool SCALEA, int RP>
-__global__ __launch_bounds__(256) void bwd_main_kernel(GemmF32Args g, K3Args k, SplitGrid f) {
+// Launch 1 of the backward: split GEMM blocks of g W, then k3 blocks.
+template <int NG>
+struct BwdMain {
+  GemmF32Args g[NG];
+  K3Args k[NG];
+  SplitGrid f[NG];
+  int64_t gstart[NG + 1];
+  int64_t sstart[NG + 1];
+};
+
+template <int NG, bool EXACT, bool SCALEA, int RP>
+__global__ __launch_bounds__(256) void bwd_main_kernel(BwdMain<NG> p) {
   constexpr int L = cmax(gemm_f32_lds_floats<64, 64, false>(), k3_lds_floats<RP>());
   __shared__ __attribute__((aligned(16))) float smem[L];
   const int64_t b = blockIdx.x;
-  if (b < f.gemm_blocks) {
-    int64_t tn, tm;
-    int split;
-    split_tile(f, b, tn, tm, split);
-    gemm_f32_block<64, 64, false, EXACT, gemm_f32_depth<64, 64>(), SCALEA>(g, smem, tn, tm, split);
+  if (b < p.gstart[NG]) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.gstart[i + 1]) {
+        int64_t tn, tm;
+        int split;
+        split_tile(p.f[i], b - p.gstart[i], tn, tm, split);
+        gemm_f32_block<64, 64, false, EXACT, gemm_f32_depth<64, 64>(), SCALEA>(p.g[i], smem, tn,
+                                                                             tm, split);
+        return;
+      }
   } else {
-    const int64_t sb = b - f.gemm_blocks;
-    k3_block<RP>(k, smem, sb % f.side_x, (int)(sb / f.side_x));
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.sstart[i + 1]) {
+        const int64_t sb = b - p.sstart[i];
+        k3_block<RP>(p.k[i], smem, sb % p.f[i].side_x, (int)(sb / p.f[i].side_x));
+        return;
+      }
   }
 }
 
@@ -169,36 +219,75 @@ LORA_DEV void epi_block(const EpiArgs& e, float* smem, int64_t b) {
   *reinterpret_cast<f32x4*>(e.C + i4) = z;
 }
 
-__global__ __launch_bounds__(256) void fwd_epi_kernel(EpiArgs e) {
+// Launch 2 of the forward: linear i's epilogue blocks are [start[i], start[i+1]).
+template <int NG>
+struct FwdEpi {
+  EpiArgs e[NG];
+  int64_t start[NG + 1];
+};
+
+template <int NG>
+__global__ __launch_bounds__(256) void fwd_epi_kernel(FwdEpi<NG> p) {
   __shared__ __attribute__((aligned(16))) float smem[EPI_MAX_ROWS * EPI_MAX_RANK];
-  epi_block<true>(e, smem, blockIdx.x);
+  const int64_t b = blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+    if (b < p.start[i + 1]) {
+      epi_block<true>(p.e[i], smem, b - p.start[i]);
+      return;
+    }
 }
 
-// k4 blocks first (the longest), then the dX epilogue, then reduction jobs
-// (dB and dm when k3 split its token range).
+// Launch 2 of the backward.  Per linear: k4 blocks (the longest) first, then
+// the dX epilogue, then reduction jobs (dB and dm when k3 split its token
+// range).  All linears' k4 blocks come first, then all epilogues, then all
+// reductions.
 struct BwdEpiGrid {
-  int64_t k4_x, k4_blocks, epi_blocks;
+  int64_t k4_x, k4_blocks, epi_blocks, red_blocks;
   int narrow;   // k4 as k4n_block (16 columns per block over all T)
 };
 
-template <int RP>
-__global__ __launch_bounds__(256) void bwd_epi_kernel(EpiArgs e, K4Args k, RedJobs jobs,
-                                                      BwdEpiGrid f) {
+template <int NG>
+struct BwdEpi {
+  EpiArgs e[NG];
+  K4Args k[NG];
+  RedJobs jobs[NG];
+  BwdEpiGrid f[NG];
+  int64_t kstart[NG + 1];   // k4 blocks of linear i
+  int64_t estart[NG + 1];   // epilogue blocks of linear i
+  int64_t rstart[NG + 1];   // reduction blocks of linear i
+};
+
+template <int NG, int RP>
+__global__ __launch_bounds__(256) void bwd_epi_kernel(BwdEpi<NG> p) {
   constexpr int L = cmax(cmax(k4_lds_floats<RP>(), k4n_lds_floats<RP>()),
                          EPI_MAX_ROWS * EPI_MAX_RANK);
   __shared__ __attribute__((aligned(16))) float smem[L];
-  int64_t b = blockIdx.x;
-  if (b < f.k4_blocks) {
-    if (f.narrow) k4n_block<RP>(k, smem, b);
-    else k4_block<RP>(k, smem, b % f.k4_x, (int)(b / f.k4_x));
-    return;
+  const int64_t b = blockIdx.x;
+  if (b < p.kstart[NG]) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.kstart[i + 1]) {
+        const int64_t kb = b - p.kstart[i];
+        if (p.f[i].narrow) k4n_block<RP>(p.k[i], smem, kb);
+        else k4_block<RP>(p.k[i], smem, kb % p.f[i].k4_x, (int)(kb / p.f[i].k4_x));
+        return;
+      }
+  } else if (b < p.estart[NG]) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.estart[i + 1]) {
+        epi_block<false>(p.e[i], smem, b - p.estart[i]);
+        return;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (b < p.rstart[i + 1]) {
+        reduce_block(p.jobs[i], b - p.rstart[i]);
+        return;
+      }
   }
-  b -= f.k4_blocks;
-  if (b < f.epi_blocks) {
-    epi_block<false>(e, smem, b);
-    return;
-  }
-  reduce_block(jobs, b - f.epi_blocks);
 }
 
 }  // namespace lora

@@ -347,6 +347,436 @@ void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStr
 #undef LORA_BF16_TILE
 }
 
+
+// ------------------------------------------------------- linear jobs ---
+// One linear's forward or backward, validated and planned: either the
+// short-chunk split path (fused.hpp; several linears can share its two
+// launches per direction) or the plain path.
+
+struct FwdJob {
+  bool split;
+  const lora_linear* lin;
+  int64_t T, K, N, r;
+  GemmPlan gf;
+  DownArgs da;
+  double down_flops, down_bytes;
+  LoraOperand xa;
+  // split path
+  GemmF32Args g;
+  SplitGrid f;
+  EpiArgs e;
+  bool exact;
+  int rp;
+  // plain path
+  uint16_t* Xbf;
+  const float* X;
+  float *Y, *Z, *gfpart;
+};
+
+int prepare_fwd(const lora_linear* lin, const float* X, float* Y, float* U, float* Z,
+                const lora_dropout* drop, void* ws, size_t ws_bytes, FwdJob& j) {
+  int rc = check_linear(lin);
+  if (rc) return rc;
+  if (!X || !Y || !U) return LORA_E_INVALID;
+  if (!al16(X) || !al16(Y) || !al16(U) || (Z && !al16(Z))) return LORA_E_ALIGN;
+  if (!drop_valid(drop)) return LORA_E_INVALID;
+  const Layout y = make_layout(lin);
+  if (y.fwd_bytes && (!ws || ws_bytes < y.fwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
+  const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
+  const bool bf = lin->w_dtype == LORA_BF16;
+  char* w = (char*)ws;
+  float* Upart = y.down.n > 1 ? (float*)(w + y.upart) : nullptr;
+  j.lin = lin;
+  j.T = T; j.K = K; j.N = N; j.r = r;
+  j.gf = y.gf;
+  j.X = X; j.Y = Y; j.Z = Z;
+  j.Xbf = bf ? (uint16_t*)(w + y.xbf) : nullptr;
+  j.gfpart = y.gf.k.n > 1 ? (float*)(w + y.gfpart) : nullptr;
+  DownArgs& da = j.da;
+  da.X = X; da.T = T; da.K = K; da.A = lin->A; da.r = r; da.drop = make_drop(drop);
+  da.ksplit = y.down.len; da.nsplit = y.down.n; da.Upart = Upart; da.U = U; da.Xbf = j.Xbf;
+  j.down_flops = 2.0 * T * K * r;
+  j.down_bytes = 4.0 * (T * K + r * K + T * r) + (j.Xbf ? 2.0 * T * K : 0.0);
+  j.xa = y.down.n > 1 ? LoraOperand{Upart, T * r, y.down.n, U} : LoraOperand{U, T * r, 1, nullptr};
+  j.split = use_split_path(y.gf, r, bf);
+  if (j.split) {
+    GemmF32Args& a = j.g;
+    memset(&a, 0, sizeof(a));
+    a.A = X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = N; a.Kc = K;
+    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
+    a.part = j.gfpart;
+    j.f = split_grid(T, N, y.gf.k.n, cdiv(T, SK_T), y.down.n);
+    j.exact = T % 64 == 0 && N % 64 == 0 && K % y.gf.k.len == 0 && y.gf.k.len % 32 == 0;
+    j.rp = rank_pad(r);
+    EpiArgs e = epi_shape(T, N);
+    e.part = a.part; e.nsplit = y.gf.k.n;
+    e.xa = j.xa; e.XB = lin->B; e.r = r; e.s = lin->scale;
+    e.C = Y; e.C2 = Z; e.cn = lin->dora_mag; e.cd = lin->dora_norm;
+    j.e = e;
+  }
+  return LORA_OK;
+}
+
+// Launch 1: split GEMM partials of X W^T beside the down projection; launch
+// 2: Y = sum of partials + s U B^T (DoRA: Z and the row scale).  NG linears
+// of one X share both launches.
+template <int NG>
+void launch_fwd_split(const FwdJob* J, hipStream_t st) {
+  FwdMain<NG> m;
+  FwdEpi<NG> ep;
+  int64_t b = 0, Nsum = 0;
+  double fl = 0, by = 0, efl = 0, eby = 0;
+  bool exact = true;
+  int rp = 16;
+  for (int i = 0; i < NG; ++i) {
+    m.g[i] = J[i].g;
+    m.d[i] = J[i].da;
+    m.f[i] = J[i].f;
+    m.gstart[i] = b;
+    b += J[i].f.gemm_blocks;
+    exact = exact && J[i].exact;
+    rp = std::max(rp, J[i].rp);
+    const int64_t T = J[i].T, N = J[i].N, K = J[i].K, r = J[i].r, ns = J[i].gf.k.n;
+    Nsum += N;
+    fl += 2.0 * T * N * K + J[i].down_flops;
+    by += 4.0 * (T * K + N * K + ns * T * N) + J[i].down_bytes;
+    efl += 2.0 * T * N * r;
+    eby += 4.0 * T * N * (ns + (J[i].Z ? 2 : 1)) + 4.0 * (J[i].da.nsplit * T * r + N * r);
+  }
+  m.gstart[NG] = b;
+  for (int i = 0; i < NG; ++i) {
+    m.sstart[i] = b;
+    b += J[i].f.side_blocks;
+  }
+  m.sstart[NG] = b;
+  {
+    prof::Scope ps("gemm_f32_fwd+down", J[0].T, Nsum, J[0].K, fl, by);
+    LORA_RP_DISPATCH_32(rp, {
+      if (exact) launch(fwd_main_kernel<NG, true, RP>, dim3((unsigned)b), st, ps, m);
+      else launch(fwd_main_kernel<NG, false, RP>, dim3((unsigned)b), st, ps, m);
+    });
+  }
+  b = 0;
+  for (int i = 0; i < NG; ++i) {
+    ep.e[i] = J[i].e;
+    ep.start[i] = b;
+    b += J[i].e.blocks;
+  }
+  ep.start[NG] = b;
+  prof::Scope ps("fwd_epilogue", J[0].T, Nsum, J[0].gf.k.n, efl, eby);
+  launch(fwd_epi_kernel<NG>, dim3((unsigned)b), st, ps, ep);
+}
+
+void launch_fwd_plain(const FwdJob& j, hipStream_t st) {
+  const lora_linear* lin = j.lin;
+  const int64_t T = j.T, K = j.K, N = j.N, r = j.r;
+  // U = X~ A^T, split over K; the GEMM sums the splits while staging U and
+  // stores the summed U.
+  {
+    prof::Scope ps("down_u", T, r, K, j.down_flops, j.down_bytes);
+    const dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)j.da.nsplit);
+    LORA_RP_DISPATCH(rank_pad(r), launch(down_kernel<RP>, grid, st, ps, j.da));
+  }
+  // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
+  if (lin->w_dtype == LORA_BF16) {
+    GemmBf16Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = j.Xbf; a.lda = K; a.B = (const uint16_t*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = N; a.Kc = K;
+    a.xa = j.xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
+    a.C = j.Y; a.C2 = j.Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
+    launch_gemm_bf16(j.gf, true, a, st);
+  } else {
+    GemmF32Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = j.X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
+    a.M = T; a.Nc = N; a.Kc = K;
+    a.xa = j.xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
+    a.ksplit = j.gf.k.len; a.nsplit = j.gf.k.n;
+    a.C = j.Y; a.C2 = j.Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
+    a.part = j.gfpart;
+    launch_gemm_f32(j.gf, true, a, st);
+  }
+}
+
+struct BwdJob {
+  bool split;
+  const lora_linear* lin;
+  int64_t T, K, N, r;
+  Layout y;
+  K3Out o;
+  K3Args ka;
+  K4Args k4a;
+  double k3_flops, k3_bytes, k4_flops, k4_bytes;
+  LoraOperand xv;
+  DropParams d;
+  RedJob jobs[3];
+  int nj;
+  RedJob ja;        // dA partials (k4 split over token ranges), if any
+  bool has_ja;
+  const float* dY;
+  float* dX;
+  char* w;
+  // split path
+  GemmF32Args g;
+  K3Args kb;
+  SplitGrid f;
+  EpiArgs e;
+  RedJobs J;
+  BwdEpiGrid eg;
+  int64_t nvp;
+  bool exact;
+  int rp;
+};
+
+int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const float* U,
+                const float* Z, float* dX, float* dA, float* dB, float* dMag, int accumulate,
+                const lora_dropout* drop, void* ws, size_t ws_bytes, BwdJob& j) {
+  int rc = check_linear(lin);
+  if (rc) return rc;
+  if (!X || !dY || !U || !dA || !dB) return LORA_E_INVALID;
+  if (!al16(X) || !al16(dY) || !al16(U) || !al16(dA) || !al16(dB)) return LORA_E_ALIGN;
+  if ((dX && !al16(dX)) || (Z && !al16(Z)) || (dMag && !al16(dMag))) return LORA_E_ALIGN;
+  const bool dora = lin->dora_mag != nullptr;
+  if (dMag && (!dora || !Z)) return LORA_E_INVALID;
+  if (!drop_valid(drop)) return LORA_E_INVALID;
+  const Layout y = make_layout(lin);
+  if (y.bwd_bytes && (!ws || ws_bytes < y.bwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
+  const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
+  const bool bf = lin->w_dtype == LORA_BF16;
+  char* w = (char*)ws;
+  const int acc = accumulate ? 1 : 0;
+  j.lin = lin;
+  j.T = T; j.K = K; j.N = N; j.r = r;
+  j.y = y;
+  j.w = w;
+  j.dY = dY;
+  j.dX = dX;
+  j.d = make_drop(drop);
+  j.rp = rank_pad(r);
+
+  // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
+  K3Out& o = j.o;
+  o.Vpart = y.strips > 1 ? (float*)(w + y.vpart) : nullptr;
+  o.V = (float*)(w + y.v);
+  o.dBpart = y.k3.n > 1 ? (float*)(w + y.dbpart) : nullptr;
+  o.dB = dB;
+  o.dmpart = (dMag && y.k3.n > 1) ? (float*)(w + y.dmpart) : nullptr;
+  o.dm = dMag;
+  o.gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
+  o.scale = lin->scale;
+  o.accumulate = acc;
+  const float* Zin = dMag ? Z : nullptr;
+  K3Args& ka = j.ka;
+  ka.dY = dY; ka.T = T; ka.N = N; ka.B = lin->B; ka.U = U; ka.r = r;
+  ka.mag = lin->dora_mag; ka.nrm = lin->dora_norm; ka.Z = Zin;
+  ka.tsplit = y.k3.len; ka.nstrip = y.strips; ka.spb = 1; ka.nts = y.k3.n; ka.o = o;
+  j.k3_flops = 4.0 * T * N * r;
+  j.k3_bytes = 4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
+               (o.gbf ? 2.0 * T * N : 0.0);
+  j.xv = (y.strips == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
+                                       : LoraOperand{o.Vpart, T * r, (int)y.strips, nullptr};
+  float* dApart = y.k4.n > 1 ? (float*)(w + y.dapart) : nullptr;
+  K4Args& k4a = j.k4a;
+  k4a.X = X; k4a.T = T; k4a.K = K; k4a.V = j.xv.p; k4a.vparts = j.xv.nparts; k4a.r = r;
+  k4a.drop = j.d; k4a.tsplit = y.k4.len; k4a.nts = y.k4.n; k4a.dApart = dApart; k4a.dA = dA;
+  k4a.scale = lin->scale; k4a.accumulate = acc;
+  j.k4_flops = 2.0 * T * K * r;
+  j.k4_bytes = 4.0 * (T * K + T * r + 2 * r * K);
+  // Gradient splits over token ranges: fixed-order reduction jobs.
+  j.nj = 0;
+  if (y.k3.n > 1) {
+    j.jobs[j.nj++] = {o.dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
+    if (dMag) j.jobs[j.nj++] = {o.dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
+  }
+  j.has_ja = y.k4.n > 1;
+  if (j.has_ja) j.ja = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
+
+  j.split = dX != nullptr && use_split_path(y.gd, r, bf);
+  if (!j.split) return LORA_OK;
+  GemmF32Args& a = j.g;
+  memset(&a, 0, sizeof(a));
+  a.A = dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
+  a.B = (const float*)lin->W; a.ldb = K;
+  a.M = T; a.Nc = K; a.Kc = N;
+  a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
+  a.part = (float*)(w + y.gdpart);
+  // k3 beside the GEMM: one strip per block (each strip is a chain of
+  // dependent loads), several only past 32 strips, so V arrives as at most
+  // 32 partials for the two consumers of launch 2.
+  K3Args& kb = j.kb;
+  kb = ka;
+  kb.spb = cdiv(y.strips, 32);
+  j.nvp = cdiv(y.strips, kb.spb);
+  kb.o.V = (float*)(w + y.v);
+  kb.o.Vpart = j.nvp > 1 ? (float*)(w + y.vpart) : nullptr;
+  const LoraOperand vd = j.nvp > 1 ? LoraOperand{kb.o.Vpart, T * r, (int)j.nvp, nullptr}
+                                   : LoraOperand{kb.o.V, T * r, 1, nullptr};
+  j.f = split_grid(T, K, y.gd.k.n, j.nvp, y.k3.n);
+  j.exact = T % 64 == 0 && K % 64 == 0 && N % y.gd.k.len == 0 && y.gd.k.len % 32 == 0;
+  k4a.V = vd.p;
+  k4a.vparts = vd.nparts;
+  EpiArgs e = epi_shape(T, K);
+  e.part = a.part; e.nsplit = y.gd.k.n;
+  e.xa = vd; e.XB = lin->A; e.r = r; e.s = lin->scale; e.drop = j.d;
+  e.C = dX;
+  j.e = e;
+  memset(&j.J, 0, sizeof(j.J));
+  int64_t rblocks = 0;
+  for (int i = 0; i < j.nj; ++i) {
+    j.J.job[i] = j.jobs[i];
+    j.J.blk[i] = rblocks;
+    rblocks += cdiv(j.jobs[i].n, 256);
+  }
+  j.J.blk[j.nj] = rblocks;
+  j.J.njobs = j.nj;
+  BwdEpiGrid& g = j.eg;
+  g.narrow = T <= K4N_MAX_T && y.k4.n == 1;
+  g.k4_x = g.narrow ? cdiv(K, 16) : cdiv(K, SK_C);
+  g.k4_blocks = g.k4_x * y.k4.n;
+  g.epi_blocks = e.blocks;
+  g.red_blocks = rblocks;
+  return LORA_OK;
+}
+
+// Launch 1: split GEMM partials of g W beside k3 (V partials, dB, dm);
+// launch 2: dX = sum of partials + (s V A) * mask * keep beside k4 and the
+// dB / dm reductions; then the dA reduction when k4 split its token range.
+template <int NG>
+void launch_bwd_split(const BwdJob* J, hipStream_t st) {
+  BwdMain<NG> m;
+  int64_t b = 0, Ksum = 0;
+  double fl = 0, by = 0, efl = 0, eby = 0;
+  bool exact = true, scalea = false;
+  int rp = 16;
+  for (int i = 0; i < NG; ++i) {
+    m.g[i] = J[i].g;
+    m.k[i] = J[i].kb;
+    m.f[i] = J[i].f;
+    m.gstart[i] = b;
+    b += J[i].f.gemm_blocks;
+    exact = exact && J[i].exact;
+    scalea = scalea || J[i].g.acn != nullptr;
+    rp = std::max(rp, J[i].rp);
+    const int64_t T = J[i].T, N = J[i].N, K = J[i].K, r = J[i].r, ns = J[i].y.gd.k.n;
+    Ksum += K;
+    fl += 2.0 * T * N * K + J[i].k3_flops;
+    by += 4.0 * (T * N + N * K + ns * T * K) + J[i].k3_bytes;
+    efl += 2.0 * T * K * r + J[i].k4_flops;
+    eby += 4.0 * T * K * (ns + 1) + 4.0 * (J[i].nvp * T * r + r * K) + J[i].k4_bytes;
+  }
+  m.gstart[NG] = b;
+  for (int i = 0; i < NG; ++i) {
+    m.sstart[i] = b;
+    b += J[i].f.side_blocks;
+  }
+  m.sstart[NG] = b;
+  {
+    prof::Scope ps("gemm_f32_dx+k3", J[0].T, Ksum, J[0].N, fl, by);
+    const dim3 grid((unsigned)b);
+    LORA_RP_DISPATCH_32(rp, {
+      if (scalea) {
+        if (exact) launch(bwd_main_kernel<NG, true, true, RP>, grid, st, ps, m);
+        else launch(bwd_main_kernel<NG, false, true, RP>, grid, st, ps, m);
+      } else {
+        if (exact) launch(bwd_main_kernel<NG, true, false, RP>, grid, st, ps, m);
+        else launch(bwd_main_kernel<NG, false, false, RP>, grid, st, ps, m);
+      }
+    });
+  }
+  BwdEpi<NG> ep;
+  b = 0;
+  for (int i = 0; i < NG; ++i) {
+    ep.e[i] = J[i].e;
+    ep.k[i] = J[i].k4a;
+    ep.jobs[i] = J[i].J;
+    ep.f[i] = J[i].eg;
+    ep.kstart[i] = b;
+    b += J[i].eg.k4_blocks;
+  }
+  ep.kstart[NG] = b;
+  for (int i = 0; i < NG; ++i) {
+    ep.estart[i] = b;
+    b += J[i].eg.epi_blocks;
+  }
+  ep.estart[NG] = b;
+  for (int i = 0; i < NG; ++i) {
+    ep.rstart[i] = b;
+    b += J[i].eg.red_blocks;
+  }
+  ep.rstart[NG] = b;
+  {
+    prof::Scope ps("dx_epilogue+k4", J[0].T, Ksum, J[0].y.gd.k.n, efl, eby);
+    LORA_RP_DISPATCH_32(rp, launch(bwd_epi_kernel<NG, RP>, dim3((unsigned)b), st, ps, ep));
+  }
+  RedJob ja[NG];
+  int na = 0;
+  for (int i = 0; i < NG; ++i)
+    if (J[i].has_ja) ja[na++] = J[i].ja;
+  if (na) launch_reduce(ja, na, st);
+}
+
+void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
+  const lora_linear* lin = jb.lin;
+  const Layout& y = jb.y;
+  const int64_t T = jb.T, K = jb.K, N = jb.N, r = jb.r;
+  const bool bf = lin->w_dtype == LORA_BF16;
+  const int rp = jb.rp;
+  {
+    prof::Scope ps("k3_v_db", T, N, r, jb.k3_flops, jb.k3_bytes);
+    const dim3 grid((unsigned)y.strips, (unsigned)y.k3.n);
+    LORA_RP_DISPATCH(rp, launch(k3_kernel<RP>, grid, st, ps, jb.ka));
+  }
+  if (y.vreduce) {
+    RedJob jv = {jb.o.Vpart, jb.o.V, nullptr, T * r, 1, (int)y.strips, 0, 1.0f};
+    launch_reduce(&jv, 1, st);
+  }
+  if (jb.dX) {
+    if (bf) {
+      GemmBf16Args a;
+      memset(&a, 0, sizeof(a));
+      a.A = jb.o.gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
+      a.M = T; a.Nc = K; a.Kc = N;
+      a.xa = jb.xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = jb.d;
+      a.C = jb.dX;
+      launch_gemm_bf16(y.gd, false, a, st);
+    } else {
+      GemmF32Args a;
+      memset(&a, 0, sizeof(a));
+      a.A = jb.dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
+      a.B = (const float*)lin->W; a.ldb = K;
+      a.M = T; a.Nc = K; a.Kc = N;
+      a.xa = jb.xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = jb.d;
+      a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
+      a.C = jb.dX;
+      a.part = y.gd.k.n > 1 ? (float*)(jb.w + y.gdpart) : nullptr;
+      launch_gemm_f32(y.gd, false, a, st);
+    }
+  }
+  {
+    prof::Scope ps("k4_da", T, r, K, jb.k4_flops, jb.k4_bytes);
+    const dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)y.k4.n);
+    LORA_RP_DISPATCH(rp, launch(k4_kernel<RP>, grid, st, ps, jb.k4a));
+  }
+  RedJob jobs[4];
+  int nj = 0;
+  for (int i = 0; i < jb.nj; ++i) jobs[nj++] = jb.jobs[i];
+  if (jb.has_ja) jobs[nj++] = jb.ja;
+  if (nj) launch_reduce(jobs, nj, st);
+}
+
+// Linears of a group read one X: equal token count, input width and dtype.
+int check_group(int n, const lora_linear* lins) {
+  for (int i = 0; i < n; ++i) {
+    const int rc = check_linear(&lins[i]);
+    if (rc) return rc;
+    if (lins[i].tokens != lins[0].tokens || lins[i].in_dim != lins[0].in_dim) return LORA_E_SHAPE;
+    if (lins[i].w_dtype != lins[0].w_dtype) return LORA_E_DTYPE;
+  }
+  return LORA_OK;
+}
+
 }  // namespace
 
 // =========================================================================
@@ -390,87 +820,12 @@ size_t lora_workspace_bytes(const lora_linear* lin) {
 
 int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U, float* Z,
                  const lora_dropout* drop, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_linear(lin);
+  FwdJob j;
+  const int rc = prepare_fwd(lin, X, Y, U, Z, drop, ws, ws_bytes, j);
   if (rc) return rc;
-  if (!X || !Y || !U) return LORA_E_INVALID;
-  if (!al16(X) || !al16(Y) || !al16(U) || (Z && !al16(Z))) return LORA_E_ALIGN;
-  if (!drop_valid(drop)) return LORA_E_INVALID;
-  const Layout y = make_layout(lin);
-  if (y.fwd_bytes && (!ws || ws_bytes < y.fwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
-  const bool bf = lin->w_dtype == LORA_BF16;
-  char* w = (char*)ws;
-  float* Upart = y.down.n > 1 ? (float*)(w + y.upart) : nullptr;
-  uint16_t* Xbf = bf ? (uint16_t*)(w + y.xbf) : nullptr;
-  const DropParams d = make_drop(drop);
-
-  DownArgs da;
-  da.X = X; da.T = T; da.K = K; da.A = lin->A; da.r = r; da.drop = d;
-  da.ksplit = y.down.len; da.nsplit = y.down.n; da.Upart = Upart; da.U = U; da.Xbf = Xbf;
-  const double down_flops = 2.0 * T * K * r;
-  const double down_bytes = 4.0 * (T * K + r * K + T * r) + (Xbf ? 2.0 * T * K : 0.0);
-  const LoraOperand xa = y.down.n > 1 ? LoraOperand{Upart, T * r, y.down.n, U}
-                                      : LoraOperand{U, T * r, 1, nullptr};
-
-  if (use_split_path(y.gf, r, bf)) {
-    // Launch 1: split GEMM partials of X W^T beside the down projection.
-    GemmF32Args a;
-    memset(&a, 0, sizeof(a));
-    a.A = X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
-    a.M = T; a.Nc = N; a.Kc = K;
-    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
-    a.part = (float*)(w + y.gfpart);
-    const SplitGrid f = split_grid(T, N, y.gf.k.n, cdiv(T, SK_T), y.down.n);
-    const bool exact = T % 64 == 0 && N % 64 == 0 && K % y.gf.k.len == 0 && y.gf.k.len % 32 == 0;
-    {
-      prof::Scope ps("gemm_f32_fwd+down", T, N, K, 2.0 * T * N * K + down_flops,
-                     4.0 * (T * K + N * K + y.gf.k.n * T * N) + down_bytes);
-      const dim3 grid((unsigned)(f.gemm_blocks + f.side_blocks));
-      LORA_RP_DISPATCH_32(rank_pad(r), {
-        if (exact) launch(fwd_main_kernel<true, RP>, grid, st, ps, a, da, f);
-        else launch(fwd_main_kernel<false, RP>, grid, st, ps, a, da, f);
-      });
-    }
-    // Launch 2: Y = sum of partials + s U B^T (DoRA: Z and the row scale).
-    EpiArgs e = epi_shape(T, N);
-    e.part = a.part; e.nsplit = y.gf.k.n;
-    e.xa = xa; e.XB = lin->B; e.r = r; e.s = lin->scale;
-    e.C = Y; e.C2 = Z; e.cn = lin->dora_mag; e.cd = lin->dora_norm;
-    prof::Scope ps("fwd_epilogue", T, N, y.gf.k.n, 2.0 * T * N * r,
-                   4.0 * T * N * (y.gf.k.n + (Z ? 2 : 1)) + 4.0 * (y.down.n * T * r + N * r));
-    launch(fwd_epi_kernel, dim3((unsigned)e.blocks), st, ps, e);
-    return hip_status();
-  }
-
-  // U = X~ A^T, split over K; the GEMM sums the splits while staging U and
-  // stores the summed U.
-  {
-    prof::Scope ps("down_u", T, r, K, down_flops, down_bytes);
-    const dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)y.down.n);
-    LORA_RP_DISPATCH(rank_pad(r), launch(down_kernel<RP>, grid, st, ps, da));
-  }
-
-  // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
-  if (bf) {
-    GemmBf16Args a;
-    memset(&a, 0, sizeof(a));
-    a.A = Xbf; a.lda = K; a.B = (const uint16_t*)lin->W; a.ldb = K;
-    a.M = T; a.Nc = N; a.Kc = K;
-    a.xa = xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
-    a.C = Y; a.C2 = Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
-    launch_gemm_bf16(y.gf, true, a, st);
-  } else {
-    GemmF32Args a;
-    memset(&a, 0, sizeof(a));
-    a.A = X; a.lda = K; a.B = (const float*)lin->W; a.ldb = K;
-    a.M = T; a.Nc = N; a.Kc = K;
-    a.xa = xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
-    a.ksplit = y.gf.k.len; a.nsplit = y.gf.k.n;
-    a.C = Y; a.C2 = Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
-    a.part = y.gf.k.n > 1 ? (float*)(w + y.gfpart) : nullptr;
-    launch_gemm_f32(y.gf, true, a, st);
-  }
+  if (j.split) launch_fwd_split<1>(&j, st);
+  else launch_fwd_plain(j, st);
   return hip_status();
 }
 
@@ -478,175 +833,82 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY, const
                   const float* Z, float* dX, float* dA, float* dB, float* dMag,
                   int accumulate, const lora_dropout* drop, void* ws, size_t ws_bytes,
                   void* stream) {
-  int rc = check_linear(lin);
+  BwdJob j;
+  const int rc = prepare_bwd(lin, X, dY, U, Z, dX, dA, dB, dMag, accumulate, drop, ws, ws_bytes, j);
   if (rc) return rc;
-  if (!X || !dY || !U || !dA || !dB) return LORA_E_INVALID;
-  if (!al16(X) || !al16(dY) || !al16(U) || !al16(dA) || !al16(dB)) return LORA_E_ALIGN;
-  if ((dX && !al16(dX)) || (Z && !al16(Z)) || (dMag && !al16(dMag))) return LORA_E_ALIGN;
-  const bool dora = lin->dora_mag != nullptr;
-  if (dMag && (!dora || !Z)) return LORA_E_INVALID;
-  if (!drop_valid(drop)) return LORA_E_INVALID;
-  const Layout y = make_layout(lin);
-  if (y.bwd_bytes && (!ws || ws_bytes < y.bwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
-  const bool bf = lin->w_dtype == LORA_BF16;
-  char* w = (char*)ws;
-  const DropParams d = make_drop(drop);
-  const int rp = rank_pad(r);
-  const int acc = accumulate ? 1 : 0;
+  if (j.split) launch_bwd_split<1>(&j, st);
+  else launch_bwd_plain(j, st);
+  return hip_status();
+}
 
-  // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
-  K3Out o;
-  o.Vpart = y.strips > 1 ? (float*)(w + y.vpart) : nullptr;
-  o.V = (float*)(w + y.v);
-  o.dBpart = y.k3.n > 1 ? (float*)(w + y.dbpart) : nullptr;
-  o.dB = dB;
-  o.dmpart = (dMag && y.k3.n > 1) ? (float*)(w + y.dmpart) : nullptr;
-  o.dm = dMag;
-  o.gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
-  o.scale = lin->scale;
-  o.accumulate = acc;
-  const float* Zin = dMag ? Z : nullptr;
-  K3Args ka;
-  ka.dY = dY; ka.T = T; ka.N = N; ka.B = lin->B; ka.U = U; ka.r = r;
-  ka.mag = lin->dora_mag; ka.nrm = lin->dora_norm; ka.Z = Zin;
-  ka.tsplit = y.k3.len; ka.nstrip = y.strips; ka.spb = 1; ka.nts = y.k3.n; ka.o = o;
-  const double k3_flops = 4.0 * T * N * r;
-  const double k3_bytes = 4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
-                          (o.gbf ? 2.0 * T * N : 0.0);
-  const LoraOperand xv = (y.strips == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
-                                                      : LoraOperand{o.Vpart, T * r, (int)y.strips, nullptr};
-  float* dApart = y.k4.n > 1 ? (float*)(w + y.dapart) : nullptr;
-  K4Args k4a;
-  k4a.X = X; k4a.T = T; k4a.K = K; k4a.V = xv.p; k4a.vparts = xv.nparts; k4a.r = r; k4a.drop = d;
-  k4a.tsplit = y.k4.len; k4a.nts = y.k4.n; k4a.dApart = dApart; k4a.dA = dA;
-  k4a.scale = lin->scale; k4a.accumulate = acc;
-  const double k4_flops = 2.0 * T * K * r;
-  const double k4_bytes = 4.0 * (T * K + T * r + 2 * r * K);
-
-  // Gradient splits over token ranges: fixed-order reduction jobs.
-  RedJob jobs[3];
-  int nj = 0;
-  if (y.k3.n > 1) {
-    jobs[nj++] = {o.dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
-    if (dMag) jobs[nj++] = {o.dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
+size_t lora_group_workspace_bytes(int n, const lora_linear* lins) {
+  if (n < 1 || n > LORA_MAX_GROUP || !lins) return 0;
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (check_linear(&lins[i]) != LORA_OK) return 0;
+    total += rup((int64_t)lora_workspace_bytes(&lins[i]), 256);
   }
+  return total;
+}
 
-  if (dX && use_split_path(y.gd, r, bf)) {
-    // Launch 1: split GEMM partials of g W beside k3 (V partials, dB, dm).
-    GemmF32Args a;
-    memset(&a, 0, sizeof(a));
-    a.A = dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
-    a.B = (const float*)lin->W; a.ldb = K;
-    a.M = T; a.Nc = K; a.Kc = N;
-    a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
-    a.part = (float*)(w + y.gdpart);
-    // k3 beside the GEMM: one strip per block (each strip is a chain of
-    // dependent loads), several only past 32 strips, so V arrives as at most
-    // 32 partials for the two consumers of launch 2.
-    K3Args kb = ka;
-    kb.spb = cdiv(y.strips, 32);
-    const int64_t nvp = cdiv(y.strips, kb.spb);
-    kb.o.V = (float*)(w + y.v);
-    kb.o.Vpart = nvp > 1 ? (float*)(w + y.vpart) : nullptr;
-    const LoraOperand vd = nvp > 1 ? LoraOperand{kb.o.Vpart, T * r, (int)nvp, nullptr}
-                                   : LoraOperand{kb.o.V, T * r, 1, nullptr};
-    const SplitGrid f = split_grid(T, K, y.gd.k.n, nvp, y.k3.n);
-    const bool exact = T % 64 == 0 && K % 64 == 0 && N % y.gd.k.len == 0 && y.gd.k.len % 32 == 0;
-    {
-      prof::Scope ps("gemm_f32_dx+k3", T, K, N, 2.0 * T * N * K + k3_flops,
-                     4.0 * (T * N + N * K + y.gd.k.n * T * K) + k3_bytes);
-      const dim3 grid((unsigned)(f.gemm_blocks + f.side_blocks));
-      LORA_RP_DISPATCH_32(rp, {
-        if (a.acn) {
-          if (exact) launch(bwd_main_kernel<true, true, RP>, grid, st, ps, a, kb, f);
-          else launch(bwd_main_kernel<false, true, RP>, grid, st, ps, a, kb, f);
-        } else {
-          if (exact) launch(bwd_main_kernel<true, false, RP>, grid, st, ps, a, kb, f);
-          else launch(bwd_main_kernel<false, false, RP>, grid, st, ps, a, kb, f);
-        }
-      });
-    }
-    // Launch 2: dX = sum of partials + (s V A) * mask * keep, beside k4 and
-    // the dB / dm reductions.
-    k4a.V = vd.p;
-    k4a.vparts = vd.nparts;
-    EpiArgs e = epi_shape(T, K);
-    e.part = a.part; e.nsplit = y.gd.k.n;
-    e.xa = vd; e.XB = lin->A; e.r = r; e.s = lin->scale; e.drop = d;
-    e.C = dX;
-    RedJobs J;
-    memset(&J, 0, sizeof(J));
-    int64_t rblocks = 0;
-    for (int i = 0; i < nj; ++i) {
-      J.job[i] = jobs[i];
-      J.blk[i] = rblocks;
-      rblocks += cdiv(jobs[i].n, 256);
-    }
-    J.blk[nj] = rblocks;
-    J.njobs = nj;
-    BwdEpiGrid g;
-    g.narrow = T <= K4N_MAX_T && y.k4.n == 1;
-    g.k4_x = g.narrow ? cdiv(K, 16) : cdiv(K, SK_C);
-    g.k4_blocks = g.k4_x * y.k4.n;
-    g.epi_blocks = e.blocks;
-    {
-      prof::Scope ps("dx_epilogue+k4", T, K, y.gd.k.n, 2.0 * T * K * r + k4_flops,
-                     4.0 * T * K * (y.gd.k.n + 1) + 4.0 * (nvp * T * r + r * K) + k4_bytes);
-      LORA_RP_DISPATCH_32(rp, launch(bwd_epi_kernel<RP>,
-                                     dim3((unsigned)(g.k4_blocks + g.epi_blocks + rblocks)), st,
-                                     ps, e, k4a, J, g));
-    }
-    if (y.k4.n > 1) {
-      RedJob ja = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
-      launch_reduce(&ja, 1, st);
-    }
-    return hip_status();
+int lora_forward_group(int n, const lora_linear* lins, const float* X, float* const* Y,
+                       float* const* U, float* const* Z, const lora_dropout* drops, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (n < 1 || n > LORA_MAX_GROUP || !lins || !Y || !U) return LORA_E_INVALID;
+  int rc = check_group(n, lins);
+  if (rc) return rc;
+  const size_t need = lora_group_workspace_bytes(n, lins);
+  if (need && (!ws || ws_bytes < need || !al16(ws))) return LORA_E_WORKSPACE;
+  FwdJob jobs[LORA_MAX_GROUP];
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t wi = rup((int64_t)lora_workspace_bytes(&lins[i]), 256);
+    rc = prepare_fwd(&lins[i], X, Y[i], U[i], Z ? Z[i] : nullptr, drops ? &drops[i] : nullptr,
+                     (char*)ws + off, wi, jobs[i]);
+    if (rc) return rc;
+    off += wi;
   }
-
-  // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
-  {
-    prof::Scope ps("k3_v_db", T, N, r, k3_flops, k3_bytes);
-    const dim3 grid((unsigned)y.strips, (unsigned)y.k3.n);
-    LORA_RP_DISPATCH(rp, launch(k3_kernel<RP>, grid, st, ps, ka));
-  }
-  if (y.vreduce) {
-    RedJob jv = {o.Vpart, o.V, nullptr, T * r, 1, (int)y.strips, 0, 1.0f};
-    launch_reduce(&jv, 1, st);
-  }
-
-  if (dX) {
-    if (bf) {
-      GemmBf16Args a;
-      memset(&a, 0, sizeof(a));
-      a.A = o.gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
-      a.M = T; a.Nc = K; a.Kc = N;
-      a.xa = xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
-      a.C = dX;
-      launch_gemm_bf16(y.gd, false, a, st);
-    } else {
-      GemmF32Args a;
-      memset(&a, 0, sizeof(a));
-      a.A = dY; a.lda = N; a.acn = lin->dora_mag; a.acd = lin->dora_norm;
-      a.B = (const float*)lin->W; a.ldb = K;
-      a.M = T; a.Nc = K; a.Kc = N;
-      a.xa = xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = d;
-      a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
-      a.C = dX;
-      a.part = y.gd.k.n > 1 ? (float*)(w + y.gdpart) : nullptr;
-      launch_gemm_f32(y.gd, false, a, st);
+  hipStream_t st = (hipStream_t)stream;
+  if (n == 2 && jobs[0].split && jobs[1].split) {
+    launch_fwd_split<2>(jobs, st);
+  } else {
+    for (int i = 0; i < n; ++i) {
+      if (jobs[i].split) launch_fwd_split<1>(&jobs[i], st);
+      else launch_fwd_plain(jobs[i], st);
     }
   }
+  return hip_status();
+}
 
-  {
-    prof::Scope ps("k4_da", T, r, K, k4_flops, k4_bytes);
-    const dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)y.k4.n);
-    LORA_RP_DISPATCH(rp, launch(k4_kernel<RP>, grid, st, ps, k4a));
+int lora_backward_group(int n, const lora_linear* lins, const float* X, const float* const* dY,
+                        const float* const* U, const float* const* Z, float* const* dX,
+                        float* const* dA, float* const* dB, float* const* dMag, int accumulate,
+                        const lora_dropout* drops, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 1 || n > LORA_MAX_GROUP || !lins || !dY || !U || !dA || !dB) return LORA_E_INVALID;
+  int rc = check_group(n, lins);
+  if (rc) return rc;
+  const size_t need = lora_group_workspace_bytes(n, lins);
+  if (need && (!ws || ws_bytes < need || !al16(ws))) return LORA_E_WORKSPACE;
+  BwdJob jobs[LORA_MAX_GROUP];
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t wi = rup((int64_t)lora_workspace_bytes(&lins[i]), 256);
+    rc = prepare_bwd(&lins[i], X, dY[i], U[i], Z ? Z[i] : nullptr, dX ? dX[i] : nullptr, dA[i],
+                     dB[i], dMag ? dMag[i] : nullptr, accumulate, drops ? &drops[i] : nullptr,
+                     (char*)ws + off, wi, jobs[i]);
+    if (rc) return rc;
+    off += wi;
   }
-
-  if (y.k4.n > 1) jobs[nj++] = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};
-  if (nj) launch_reduce(jobs, nj, st);
+  hipStream_t st = (hipStream_t)stream;
+  if (n == 2 && jobs[0].split && jobs[1].split) {
+    launch_bwd_split<2>(jobs, st);
+  } else {
+    for (int i = 0; i < n; ++i) {
+      if (jobs[i].split) launch_bwd_split<1>(&jobs[i], st);
+      else launch_bwd_plain(jobs[i], st);
+    }
+  }
   return hip_status();
 }
 

@@ -20,7 +20,8 @@ __all__ = [
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
-    "lora_status_string", "lora_profile_begin", "lora_profile_end", "EXPORTS",
+    "lora_status_string", "lora_profile_begin", "lora_profile_end",
+    "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
@@ -35,6 +36,7 @@ EXPORTS = (
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
+    "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
 )
 
 
@@ -97,6 +99,9 @@ def lib() -> C.CDLL:
             "lora_status_string": (C.c_char_p, [I32]),
             "lora_profile_begin": (I32, [I32]),
             "lora_profile_end": (I32, [P, I32]),
+            "lora_group_workspace_bytes": (SZ, [I32, P]),
+            "lora_forward_group": (I32, [I32, P, P, P, P, P, P, P, SZ, P]),
+            "lora_backward_group": (I32, [I32, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -191,6 +196,60 @@ def lora_backward(lin, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=False, dro
                              _ptr(dMag, "dMag"), 1 if accumulate else 0, _ref(drop),
                              _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_backward", rc)
+
+
+MAX_GROUP = 4
+
+
+def _linears(lins):
+    arr = (LoraLinear * len(lins))(*lins)
+    return arr
+
+
+def _ptrs(ts, name, optional=False):
+    """Array of device pointers, or None when every entry is None and the
+    argument is optional."""
+    if ts is None or (optional and all(t is None for t in ts)):
+        if not optional:
+            raise ValueError(f"{name} is required")
+        return None
+    return (C.c_void_p * len(ts))(*[_ptr(t, f"{name}[{i}]") for i, t in enumerate(ts)])
+
+
+def _drops(drops, n):
+    if drops is None or all(d is None for d in drops):
+        return None
+    zero = LoraDropout(0, 0, 0, 0, 0, 0.0)
+    return (LoraDropout * n)(*[zero if d is None else d for d in drops])
+
+
+def lora_group_workspace_bytes(lins) -> int:
+    return int(lib().lora_group_workspace_bytes(len(lins), _linears(lins)))
+
+
+def lora_forward_group(lins, X, Y, U, Z=None, drops=None, ws=None, stream=None):
+    """Forward of the linears `lins` that read one X; Y, U (and Z) are lists
+    with one tensor per linear."""
+    n = len(lins)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_forward_group(n, _linears(lins), _ptr(X, "X"), _ptrs(Y, "Y"), _ptrs(U, "U"),
+                                  _ptrs(Z, "Z", True), _drops(drops, n), _ptr(ws, "ws", None),
+                                  ws_bytes, _stream(stream))
+    _check("lora_forward_group", rc)
+
+
+def lora_backward_group(lins, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=False, drops=None,
+                        ws=None, stream=None):
+    """Backward of the linears `lins` that read one X; every other tensor
+    argument is a list with one entry per linear."""
+    n = len(lins)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_backward_group(n, _linears(lins), _ptr(X, "X"), _ptrs(dY, "dY"),
+                                   _ptrs(U, "U"), _ptrs(Z, "Z", True), _ptrs(dX, "dX", True),
+                                   _ptrs(dA, "dA"), _ptrs(dB, "dB"), _ptrs(dMag, "dMag", True),
+                                   1 if accumulate else 0, _drops(drops, n), _ptr(ws, "ws", None),
+                                   ws_bytes, _stream(stream))
+    _check("lora_backward_group", rc)
 
 
 def lora_grad_prepare_workspace_bytes(n: int) -> int:

@@ -105,12 +105,22 @@ class Trainer:
         self.device = device
         f32 = dict(device=device, dtype=torch.float32)
         r = cfg.rank
+        # Projections of one layer that read the same X run as one group.
+        xg = {p.ordinal: p.x_group for p in cfg.projections}
+        self.groups = []
+        for key in model.keys:
+            g = self.groups[-1] if self.groups else None
+            if g and g[0][0] == key[0] and xg[g[0][1]] == xg[key[1]] and len(g) < L.MAX_GROUP:
+                g.append(key)
+            else:
+                self.groups.append([key])
         ws = 0
+        for g in self.groups:
+            ws = max(ws, L.lora_group_workspace_bytes([self._linear(k, None, dora=cfg.dora)
+                                                       for k in g]))
         self.U, self.Z, self.Y, self.dX = {}, {}, {}, {}
         for key in model.keys:
             K, N = model.shape[key]
-            lin = self._linear(key, None, dora=cfg.dora)
-            ws = max(ws, L.lora_workspace_bytes(lin))
             self.U[key] = torch.empty(self.T, r, **f32)
             self.Y[key] = torch.empty(self.T, N, **f32)
             self.dX[key] = torch.empty(self.T, K, **f32)
@@ -155,23 +165,31 @@ class Trainer:
 
     # ------------------------------------------------------------------
     def forward_backward(self, slot: Slot, chunks: list):
+        """Every chunk: forward over the layers 0..L-1, then backward L-1..0;
+        the projections of a layer that share X go through the group calls."""
         cfg = self.cfg
-        keys = self.model.keys
         p = float(cfg.dropout)
         for g, chunk in enumerate(chunks):
-            lins = {}
-            for key in keys:   # layers 0..L-1
-                X, _ = chunk[key]
-                lin = self._linear(key, slot, dora=cfg.dora)
-                lins[key] = lin
-                drop = L.make_dropout(slot.seed, slot.k, g, key[0], key[1], p) if p > 0 else None
-                L.lora_forward(lin, X, self.Y[key], self.U[key], self.Z.get(key), drop, self.ws)
-            for key in reversed(keys):   # layers L-1..0
-                X, dY = chunk[key]
-                drop = L.make_dropout(slot.seed, slot.k, g, key[0], key[1], p) if p > 0 else None
-                L.lora_backward(lins[key], X, dY, self.U[key], self.Z.get(key), self.dX[key],
-                                slot.gA[key], slot.gB[key], slot.gmag.get(key),
-                                accumulate=g > 0, drop=drop, ws=self.ws)
+            def drops(keys):
+                if p <= 0:
+                    return None
+                return [L.make_dropout(slot.seed, slot.k, g, k[0], k[1], p) for k in keys]
+            lins = {k: self._linear(k, slot, dora=cfg.dora) for k in self.model.keys}
+            for keys in self.groups:
+                X = chunk[keys[0]][0]
+                L.lora_forward_group([lins[k] for k in keys], X, [self.Y[k] for k in keys],
+                                     [self.U[k] for k in keys],
+                                     [self.Z[k] for k in keys] if cfg.dora else None,
+                                     drops(keys), self.ws)
+            for keys in reversed(self.groups):
+                X = chunk[keys[0]][0]
+                L.lora_backward_group([lins[k] for k in keys], X, [chunk[k][1] for k in keys],
+                                      [self.U[k] for k in keys],
+                                      [self.Z[k] for k in keys] if cfg.dora else None,
+                                      [self.dX[k] for k in keys], [slot.gA[k] for k in keys],
+                                      [slot.gB[k] for k in keys],
+                                      [slot.gmag[k] for k in keys] if cfg.dora else None,
+                                      accumulate=g > 0, drops=drops(keys), ws=self.ws)
 
     def step(self, slot: Slot, chunks: list, sync: bool = True) -> StepStats:
         cfg = self.cfg

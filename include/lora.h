@@ -80,7 +80,11 @@ typedef struct lora_dropout {
  * detached input (see lora_dora_row_norms).
  * Constraints: tokens, in_dim, out_dim > 0; in_dim and out_dim multiples of 4
  * (of 8 for bf16 W); rank a multiple of 4 with rank <= min(in_dim, out_dim,
- * 128).  W is float32 or bf16.  Any T is accepted (ragged tails are masked). */
+ * 128).  W is float32 or bf16.  Any T is accepted (ragged tails are masked).
+ * Every pointer, dora_mag and dora_norm included, is 16-byte aligned
+ * (LORA_E_ALIGN otherwise).  bf16 W also needs in_dim*out_dim, tokens*in_dim
+ * and tokens*out_dim below 2^30 (its operands are addressed with 32-bit byte
+ * offsets; LORA_E_SHAPE otherwise). */
 typedef struct lora_linear {
   int64_t tokens, in_dim, out_dim, rank;
   int32_t w_dtype;          /* lora_dtype                                  */
@@ -142,6 +146,27 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY,
                   float* dB, float* dMag, int accumulate,
                   const lora_dropout* drop, void* ws, size_t ws_bytes,
                   void* stream);
+
+/* Linears that read one X (the projections of one layer that share their
+ * input, e.g. wq and wv; "8. LoRA Fundamentals", "How it works", target
+ * list) may run as a group: the same results, bitwise, as calling
+ * lora_forward / lora_backward on each in turn, with the group's launches
+ * shared where the kernels allow (short chunks with fp32 W).  All linears of
+ * a group must have equal tokens, in_dim and w_dtype (else LORA_E_SHAPE /
+ * LORA_E_DTYPE); 1 <= n <= LORA_MAX_GROUP.  Array arguments hold one entry
+ * per linear, in the order of `lins`; Z, dX, dMag and drops may be NULL as a
+ * whole (meaning NULL for every linear) or hold NULL entries.  The group
+ * workspace is the per-linear workspaces laid end to end (each rounded up to
+ * 256 bytes).  Validation of every linear precedes any launch. */
+#define LORA_MAX_GROUP 4
+size_t lora_group_workspace_bytes(int n, const lora_linear* lins);
+int lora_forward_group(int n, const lora_linear* lins, const float* X, float* const* Y,
+                       float* const* U, float* const* Z, const lora_dropout* drops, void* ws,
+                       size_t ws_bytes, void* stream);
+int lora_backward_group(int n, const lora_linear* lins, const float* X, const float* const* dY,
+                        const float* const* U, const float* const* Z, float* const* dX,
+                        float* const* dA, float* const* dB, float* const* dMag, int accumulate,
+                        const lora_dropout* drops, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes lora_grad_prepare needs for n gradient elements. */
 size_t lora_grad_prepare_workspace_bytes(int64_t n);

@@ -503,3 +503,116 @@ def test_workspace_contents_do_not_matter(T, K, N, r):
     for other in outs[1:]:
         for a, b in zip(outs[0], other):
             assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- groups -------
+def _group_case(T, K, Ns, rs, seed):
+    """Linears that read one X: per-linear W, A, B, dY; one shared X."""
+    cs = [_linear_case(T, K, N, r, seed=seed + i) for i, (N, r) in enumerate(zip(Ns, rs))]
+    for c in cs[1:]:
+        c["X"] = cs[0]["X"]
+    return cs
+
+
+def _run_linears(cs, s, p, grouped, steps=2):
+    """Forward + backward of every linear over `steps` chunks (accumulating),
+    through the group calls or one linear at a time."""
+    gs = [_gpu(c) for c in cs]
+    T, K = gs[0]["X"].shape
+    lins = [L.make_linear(g["Wq"], g["A"], g["B"], s, T) for g in gs]
+    nanf = float("nan")
+    out = {n: [] for n in ("Y", "U", "dX", "dA", "dB")}
+    for g, lin in zip(gs, lins):
+        N, r = g["W"].shape[0], g["A"].shape[0]
+        out["Y"].append(torch.full((T, N), nanf, device=DEV))
+        out["U"].append(torch.full((T, r), nanf, device=DEV))
+        out["dX"].append(torch.full((T, K), nanf, device=DEV))
+        out["dA"].append(torch.full((r, K), nanf, device=DEV))
+        out["dB"].append(torch.full((N, r), nanf, device=DEV))
+    if grouped:
+        ws = torch.empty(max(256, L.lora_group_workspace_bytes(lins)), device=DEV, dtype=torch.uint8)
+    else:
+        ws = torch.empty(max(256, max(L.lora_workspace_bytes(l) for l in lins)), device=DEV,
+                         dtype=torch.uint8)
+    for step in range(steps):
+        drops = [L.make_dropout(1234, 3, step, 5, i, p) if p > 0 else None for i in range(len(gs))]
+        X = gs[0]["X"] if step == 0 else gs[0]["X"] * 0.5
+        dYs = [g["dY"] if step == 0 else g["dY"] * -1.5 for g in gs]
+        if grouped:
+            L.lora_forward_group(lins, X, out["Y"], out["U"], None, drops, ws)
+            L.lora_backward_group(lins, X, dYs, out["U"], None, out["dX"], out["dA"], out["dB"],
+                                  None, accumulate=step > 0, drops=drops, ws=ws)
+        else:
+            for i, lin in enumerate(lins):
+                L.lora_forward(lin, X, out["Y"][i], out["U"][i], None, drops[i], ws)
+                L.lora_backward(lin, X, dYs[i], out["U"][i], None, out["dX"][i], out["dA"][i],
+                                out["dB"][i], None, accumulate=step > 0, drop=drops[i], ws=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+GROUP_CASES = [
+    # name, T, K, [N per linear], [r per linear], dropout p
+    ("tinyllama-wq-wv", 128, 2048, [2048, 256], [8, 8], 0.05),
+    ("ragged-pair", 100, 1000, [600, 264], [8, 12], 0.1),
+    ("mixed-rank-pair", 128, 1024, [512, 768], [8, 40], 0.1),     # one linear off the split path
+    ("triple", 72, 520, [264, 136, 520], [4, 8, 16], 0.1),          # more than two: one at a time
+    ("bf16-pair", 64, 264, [136, 272], [8, 8], 0.1),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=[c[0] for c in GROUP_CASES])
+def test_group_calls_equal_single_calls(case):
+    """The group calls give bitwise the results of calling each linear alone
+    (the same kernels and fixed-order sums, only sharing launches)."""
+    name, T, K, Ns, rs, p = case
+    _say("group", name)
+    cs = _group_case(T, K, Ns, rs, seed=zlib.crc32(name.encode()) % 1000)
+    if name.startswith("bf16"):
+        for c in cs:
+            c["Wq"] = c["W"].to(torch.bfloat16)
+            c["W"] = c["Wq"].float()
+    a = _run_linears(cs, 2.0, p, grouped=True)
+    b = _run_linears(cs, 2.0, p, grouped=False)
+    for n in a:
+        for i in range(len(cs)):
+            assert torch.isfinite(a[n][i]).all(), (n, i)
+            assert torch.equal(a[n][i], b[n][i]), (n, i)
+
+
+def test_group_matches_oracle():
+    """One chunk of the TinyLlama-shaped wq+wv group against the oracle."""
+    cs = _group_case(128, 2048, [2048, 256], [8, 8], seed=41)
+    gs = [_gpu(c) for c in cs]
+    lins = [L.make_linear(g["Wq"], g["A"], g["B"], 2.0, 128) for g in gs]
+    ws = torch.empty(L.lora_group_workspace_bytes(lins), device=DEV, dtype=torch.uint8)
+    dk = [(1234, 1, 0, 7, 0), (1234, 1, 0, 7, 2)]
+    drops = [L.make_dropout(*k, 0.05) for k in dk]
+    Y = [torch.empty(128, g["W"].shape[0], device=DEV) for g in gs]
+    U = [torch.empty(128, 8, device=DEV) for g in gs]
+    dX = [torch.empty(128, 2048, device=DEV) for g in gs]
+    dA = [torch.empty(8, 2048, device=DEV) for g in gs]
+    dB = [torch.empty(g["W"].shape[0], 8, device=DEV) for g in gs]
+    L.lora_forward_group(lins, gs[0]["X"], Y, U, None, drops, ws)
+    L.lora_backward_group(lins, gs[0]["X"], [g["dY"] for g in gs], U, None, dX, dA, dB, None,
+                          drops=drops, ws=ws)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cs):
+        ref = _oracle(c, 2.0, 0.05, dk[i])
+        got = dict(Y=Y[i], U=U[i], dX=dX[i], dA=dA[i], dB=dB[i])
+        for n, t in got.items():
+            e = rel_err(t, ref[n])
+            _say(f"  linear {i} {n}: rel err {e:.3e}")
+            assert e <= 1e-4, (i, n, e)
+
+
+def test_group_rejects_mismatched_linears():
+    cs = [_gpu(_linear_case(64, 128, 64, 4, seed=1)), _gpu(_linear_case(64, 256, 64, 4, seed=2))]
+    lins = [L.make_linear(c["Wq"], c["A"], c["B"], 1.0, 64) for c in cs]
+    Y = [torch.zeros(64, 64, device=DEV) for _ in cs]
+    U = [torch.zeros(64, 4, device=DEV) for _ in cs]
+    ws = torch.empty(1 << 20, device=DEV, dtype=torch.uint8)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_forward_group(lins, cs[0]["X"], Y, U, None, None, ws)
+    assert e.value.status == -2
+    assert all(torch.count_nonzero(y).item() == 0 for y in Y)
