@@ -35,10 +35,13 @@ namespace lora {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Output tile of the split GEMM.
+constexpr int SPLIT_BM = 64, SPLIT_BN = 64;
+
 // Split GEMM blocks first, then `side_blocks` blocks of the side role on a
 // (side_x, *) grid.
 struct SplitGrid {
-  int64_t ntn, ntm;       // 64 x 64 output tiles
+  int64_t ntn, ntm;       // SPLIT_BM x SPLIT_BN output tiles
   int nsplit;
   int64_t gemm_blocks;    // ntn * ntm * nsplit
   int64_t side_x;
@@ -70,7 +73,7 @@ struct FwdMain {
 
 template <int NG, bool EXACT, int RP>
 __global__ __launch_bounds__(256) void fwd_main_kernel(FwdMain<NG> p) {
-  constexpr int L = cmax(gemm_f32_lds_floats<64, 64, true>(), down_lds_floats<RP>());
+  constexpr int L = cmax(gemm_f32_lds_floats<SPLIT_BM, SPLIT_BN, true>(), down_lds_floats<RP>());
   __shared__ __attribute__((aligned(16))) float smem[L];
   const int64_t b = blockIdx.x;
   if (b < p.gstart[NG]) {
@@ -80,8 +83,8 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdMain<NG> p) {
         int64_t tn, tm;
         int split;
         split_tile(p.f[i], b - p.gstart[i], tn, tm, split);
-        gemm_f32_block<64, 64, true, EXACT, gemm_f32_depth<64, 64>(), false>(p.g[i], smem, tn, tm,
-                                                                           split);
+        gemm_f32_block<SPLIT_BM, SPLIT_BN, true, EXACT, gemm_f32_depth<SPLIT_BM, SPLIT_BN>(), false>(
+            p.g[i], smem, tn, tm, split);
         return;
       }
   } else {
@@ -107,7 +110,7 @@ struct BwdMain {
 
 template <int NG, bool EXACT, bool SCALEA, int RP>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdMain<NG> p) {
-  constexpr int L = cmax(gemm_f32_lds_floats<64, 64, false>(), k3_lds_floats<RP>());
+  constexpr int L = cmax(gemm_f32_lds_floats<SPLIT_BM, SPLIT_BN, false>(), k3_lds_floats<RP>());
   __shared__ __attribute__((aligned(16))) float smem[L];
   const int64_t b = blockIdx.x;
   if (b < p.gstart[NG]) {
@@ -117,8 +120,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdMain<NG> p) {
         int64_t tn, tm;
         int split;
         split_tile(p.f[i], b - p.gstart[i], tn, tm, split);
-        gemm_f32_block<64, 64, false, EXACT, gemm_f32_depth<64, 64>(), SCALEA>(p.g[i], smem, tn,
-                                                                             tm, split);
+        gemm_f32_block<SPLIT_BM, SPLIT_BN, false, EXACT, gemm_f32_depth<SPLIT_BM, SPLIT_BN>(),
+                       SCALEA>(p.g[i], smem, tn, tm, split);
         return;
       }
   } else {

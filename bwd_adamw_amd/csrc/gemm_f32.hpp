@@ -362,7 +362,7 @@ LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int6
 // K-steps of loads in flight per tile size (register budget of a stage).
 template <int BM, int BN>
 constexpr int gemm_f32_depth() {
-  return BM * BN <= 64 * 64 ? 4 : 2;
+  return BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 64 ? 3 : 2;
 }
 
 // Grid (Nc/BN, M/BM, nsplit).

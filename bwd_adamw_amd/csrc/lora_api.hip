@@ -112,7 +112,7 @@ constexpr Bf16Cfg kBf16Cfg[] = {
 constexpr int kBf16NCfg = sizeof(kBf16Cfg) / sizeof(kBf16Cfg[0]);
 
 // bf16: the first configuration whose grid still covers most of the 256
-// CUs.  fp32: 128x128 when that fills the chip, else 64x64 with the
+// CUs.  fp32: 128x128 when that fills the chip, else the split tile with the
 // contraction split across blocks until about 256 blocks run.
 GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx) {
   if (bf16) {
@@ -124,15 +124,15 @@ GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx) {
     }
   }
   if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}, 0};
-  const int64_t tiles = cdiv(M, 64) * cdiv(Nc, 64);
-  return {64, 64, plan_split(Kc, tiles, 256, 32, 128), 0};
+  const int64_t tiles = cdiv(M, SPLIT_BM) * cdiv(Nc, SPLIT_BN);
+  return {SPLIT_BM, SPLIT_BN, plan_split(Kc, tiles, 256, 32, 128), 0};
 }
 
 // Short chunks: the contraction is split across blocks, and each linear runs
 // as two launches per direction with the rank-side kernels beside the GEMM
 // (fused.hpp).  The epilogue keeps U or V rows in LDS, hence the rank limit.
 bool use_split_path(const GemmPlan& g, int64_t r, bool bf16) {
-  return !bf16 && g.k.n > 1 && g.bm == 64 && r <= EPI_MAX_RANK;
+  return !bf16 && g.k.n > 1 && g.bm == SPLIT_BM && g.bn == SPLIT_BN && r <= EPI_MAX_RANK;
 }
 
 EpiArgs epi_shape(int64_t M, int64_t Nc) {
@@ -149,8 +149,8 @@ EpiArgs epi_shape(int64_t M, int64_t Nc) {
 
 SplitGrid split_grid(int64_t M, int64_t Nc, int nsplit, int64_t side_x, int64_t side_y) {
   SplitGrid f;
-  f.ntn = cdiv(Nc, 64);
-  f.ntm = cdiv(M, 64);
+  f.ntn = cdiv(Nc, SPLIT_BN);
+  f.ntm = cdiv(M, SPLIT_BM);
   f.nsplit = nsplit;
   f.gemm_blocks = f.ntn * f.ntm * nsplit;
   f.side_x = side_x;
@@ -292,20 +292,20 @@ void launch_gemm_f32(const GemmPlan& g, bool fwd, const GemmF32Args& a, hipStrea
     prof::Scope ps(fwd ? "gemm_f32_fwd" : "gemm_f32_dx", a.M, a.Nc, a.Kc,
                    2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                    4.0 * (a.M * a.Kc + a.Nc * a.Kc + a.M * a.Nc * (a.C2 ? 2 : 1)));
-#define LORA_F32_TILE(BM_)                                                                   \
-  if (g.bm == BM_) {                                                                         \
+#define LORA_F32_TILE(BM_, BN_)                                                             \
+  if (g.bm == BM_ && g.bn == BN_) {                                                          \
     if (fwd) {                                                                               \
-      if (exact) launch(gemm_f32_kernel<BM_, BM_, true, true, false>, grid, st, ps, a);      \
-      else launch(gemm_f32_kernel<BM_, BM_, true, false, false>, grid, st, ps, a);           \
+      if (exact) launch(gemm_f32_kernel<BM_, BN_, true, true, false>, grid, st, ps, a);      \
+      else launch(gemm_f32_kernel<BM_, BN_, true, false, false>, grid, st, ps, a);           \
     } else if (a.acn) {                                                                      \
-      if (exact) launch(gemm_f32_kernel<BM_, BM_, false, true, true>, grid, st, ps, a);      \
-      else launch(gemm_f32_kernel<BM_, BM_, false, false, true>, grid, st, ps, a);           \
+      if (exact) launch(gemm_f32_kernel<BM_, BN_, false, true, true>, grid, st, ps, a);      \
+      else launch(gemm_f32_kernel<BM_, BN_, false, false, true>, grid, st, ps, a);           \
     } else {                                                                                 \
-      if (exact) launch(gemm_f32_kernel<BM_, BM_, false, true, false>, grid, st, ps, a);     \
-      else launch(gemm_f32_kernel<BM_, BM_, false, false, false>, grid, st, ps, a);          \
+      if (exact) launch(gemm_f32_kernel<BM_, BN_, false, true, false>, grid, st, ps, a);     \
+      else launch(gemm_f32_kernel<BM_, BN_, false, false, false>, grid, st, ps, a);          \
     }                                                                                        \
   }
-    LORA_F32_TILE(128) else LORA_F32_TILE(64)
+    LORA_F32_TILE(128, 128) else LORA_F32_TILE(SPLIT_BM, SPLIT_BN)
 #undef LORA_F32_TILE
   }
   if (g.k.n > 1) {
