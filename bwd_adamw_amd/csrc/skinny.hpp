@@ -73,15 +73,46 @@ LORA_DEV void down_block(const DownArgs& p, float* smem, int64_t bx, int split) 
 #pragma unroll
   for (int j = 0; j < JG; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = kb; k0 < ke; k0 += SK_C) {
+  // Stages of 64 columns; the next stage's loads are issued before this
+  // stage is stored and contracted (branch-free: past the end they repeat
+  // the last stage's addresses), so their latency overlaps the work.
+  struct Tile {
+    f32x4 x[4], a[RP / 16];
+  };
+  auto x_at = [&](int q, int64_t k0, int64_t& t, int64_t& k) -> bool {
+    const int f = tid + 256 * q;
+    t = t0 + (f >> 4);
+    k = k0 + 4 * (f & 15);
+    return t < T && k < ke;
+  };
+  auto a_at = [&](int q, int64_t k0, int& row, int64_t& k) -> bool {
+    const int f = tid + 256 * q;
+    row = f >> 4;
+    k = k0 + 4 * (f & 15);
+    return row < r && k < ke;
+  };
+  auto load = [&](Tile& S, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int f = tid + 256 * q;
-      const int row = f >> 4, c4 = f & 15;
-      const int64_t t = t0 + row, k = k0 + 4 * c4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (t < T && k < ke) {
-        v = *reinterpret_cast<const f32x4*>(X + t * K + k);
+      int64_t t, k;
+      const bool ok = x_at(q, k0, t, k);
+      S.x[q] = *reinterpret_cast<const f32x4*>(ok ? X + t * K + k : X);
+    }
+#pragma unroll
+    for (int q = 0; q < RP / 16; ++q) {
+      int row;
+      int64_t k;
+      const bool ok = a_at(q, k0, row, k);
+      S.a[q] = *reinterpret_cast<const f32x4*>(ok ? A + row * K + k : A);
+    }
+  };
+  auto store = [&](const Tile& S, int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t t, k;
+      const bool ok = x_at(q, k0, t, k);
+      f32x4 v = ok ? S.x[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok) {
         if (Xbf) {
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2*>(Xbf + t * K + k) = b;
@@ -92,18 +123,20 @@ LORA_DEV void down_block(const DownArgs& p, float* smem, int64_t bx, int split) 
           for (int e = 0; e < 4; ++e) v[e] *= drop_mul(drop, rk, k + e);
         }
       }
-      *reinterpret_cast<f32x4*>(&Xs[row * SK_LD + 4 * c4]) = v;
+      const int f = tid + 256 * q;
+      *reinterpret_cast<f32x4*>(&Xs[(f >> 4) * SK_LD + 4 * (f & 15)]) = v;
     }
 #pragma unroll
     for (int q = 0; q < RP / 16; ++q) {
+      int row;
+      int64_t k;
+      const bool ok = a_at(q, k0, row, k);
       const int f = tid + 256 * q;
-      const int row = f >> 4, c4 = f & 15;
-      const int64_t k = k0 + 4 * c4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (row < r && k < ke) v = *reinterpret_cast<const f32x4*>(A + row * K + k);
-      *reinterpret_cast<f32x4*>(&As_[row * SK_LD + 4 * c4]) = v;
+      *reinterpret_cast<f32x4*>(&As_[row * SK_LD + 4 * (f & 15)]) =
+          ok ? S.a[q] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
+  };
+  auto contract = [&]() {
     // wave w: rows 16w..16w+15; lane group h takes columns 16h..16h+15.
     f32x4 xv[4];
 #pragma unroll
@@ -118,8 +151,25 @@ LORA_DEV void down_block(const DownArgs& p, float* smem, int64_t bx, int split) 
 #pragma unroll
       for (int s = 0; s < 16; ++s) acc[j] = mfma16x16x4(xv[s >> 2][s & 3], av[s >> 2][s & 3], acc[j]);
     }
+  };
+  const int64_t nst = (ke - kb + SK_C - 1) / SK_C;
+  auto kst = [&](int64_t i) { return kb + min(i, nst - 1) * SK_C; };
+  Tile R[2];
+  if (nst > 0) load(R[0], kst(0));
+  auto step = [&](int64_t i, Tile& cur, Tile& nxt) {
+    load(nxt, kst(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    store(cur, kst(i));
     __syncthreads();
+    contract();
+    __syncthreads();
+  };
+  int64_t i = 0;
+  for (; i + 2 <= nst; i += 2) {
+    step(i, R[0], R[1]);
+    step(i + 1, R[1], R[0]);
   }
+  if (i < nst) step(i, R[0], R[1]);
   float* dst = nsplit == 1 ? U : Upart + (int64_t)split * T * r;
 #pragma unroll
   for (int j = 0; j < JG; ++j)
@@ -206,18 +256,84 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
   float* vdst = !want_v ? nullptr : nvp == 1 ? o.V : o.Vpart + bx * T * r;
   const int64_t sx0 = bx * p.spb, sx1 = min(p.nstrip, sx0 + p.spb);
 
-  for (int64_t sx = sx0; sx < sx1; ++sx) {
-    const int64_t n0 = sx * SK_C;
-    const int64_t ncol = n0 + 4 * c4;
-    const bool vfirst = sx == sx0;
-    __syncthreads();   // the previous strip is done with Bt and red
-
-    float cmul[4] = {1.f, 1.f, 1.f, 1.f};
-    if (mag) {
+  // The block's (strip, row stage) tiles run as one sequence, the next
+  // tile's loads in flight while this one is stored and contracted
+  // (branch-free loads; see down_block).  Per-strip set-up (column scale,
+  // B^T tile) opens a strip and its dB / dm stores close it.
+  const int64_t nst = (te - tb + SK_T - 1) / SK_T;
+  const int64_t ntot = (sx1 - sx0) * nst;
+  struct Tile {
+    f32x4 g[4], z[4], u[RP / 16];
+  };
+  auto g_ok = [&](int q, int64_t idx, int64_t& t, int64_t& ncol) -> bool {
+    const int64_t sx = sx0 + idx / nst, t0 = tb + (idx % nst) * SK_T;
+    t = t0 + (tid >> 4) + 16 * q;
+    ncol = sx * SK_C + 4 * c4;
+    return t < te && ncol < N;
+  };
+  auto u_ok = [&](int q, int64_t idx, int& row, int& q4, int64_t& t) -> bool {
+    const int64_t t0 = tb + (idx % nst) * SK_T;
+    const int i = tid + 256 * q;
+    row = i / (RP / 4);
+    q4 = i % (RP / 4);
+    t = t0 + row;
+    return t < te && 4 * q4 < r;
+  };
+  auto load = [&](Tile& S, int64_t idx) {
+    idx = min(idx, ntot - 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ncol + e < N) cmul[e] = mag[ncol + e] / nrm[ncol + e];
+    for (int q = 0; q < 4; ++q) {
+      int64_t t, ncol;
+      const bool ok = g_ok(q, idx, t, ncol);
+      S.g[q] = *reinterpret_cast<const f32x4*>(ok ? dY + t * N + ncol : dY);
+      if (Z) S.z[q] = *reinterpret_cast<const f32x4*>(ok ? Z + t * N + ncol : Z);
     }
+#pragma unroll
+    for (int q = 0; q < RP / 16; ++q) {
+      int row, q4;
+      int64_t t;
+      const bool ok = u_ok(q, idx, row, q4, t);
+      S.u[q] = *reinterpret_cast<const f32x4*>(ok ? U + t * r + 4 * q4 : U);
+    }
+  };
+
+  float cmul[4] = {1.f, 1.f, 1.f, 1.f};
+  f32x4 accB[JG];
+  float dm[4] = {0.f, 0.f, 0.f, 0.f};
+
+  auto store = [&](const Tile& S, int64_t idx) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t t, ncol;
+      const bool ok = g_ok(q, idx, t, ncol);
+      f32x4 v = ok ? S.g[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok) {
+        if (Z) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dm[e] += v[e] * S.z[q][e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= cmul[e];
+        if (o.gbf) {
+          u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(o.gbf + t * N + ncol) = b;
+        }
+      }
+      *reinterpret_cast<f32x4*>(&Gs[((tid >> 4) + 16 * q) * SK_LD + 4 * c4]) = v;
+    }
+#pragma unroll
+    for (int q = 0; q < RP / 16; ++q) {
+      int row, q4;
+      int64_t t;
+      const bool ok = u_ok(q, idx, row, q4, t);
+      *reinterpret_cast<f32x4*>(&Us[row * LDU + 4 * q4]) =
+          ok ? S.u[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto strip_begin = [&](int64_t sx) {
+    const int64_t n0 = sx * SK_C, ncol = n0 + 4 * c4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cmul[e] = (mag && ncol + e < N) ? mag[ncol + e] / nrm[ncol + e] : 1.f;
     if (want_v) {
       for (int i = tid; i < RP * SK_C; i += 256) {
         const int j = i / SK_C, n = i % SK_C;
@@ -226,84 +342,54 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
         Bt[j * SK_LD + n] = v;
       }
     }
-
-    f32x4 accB[JG];
 #pragma unroll
     for (int j = 0; j < JG; ++j) accB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dm[4] = {0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t t0 = tb; t0 < te; t0 += SK_T) {
-      __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = (tid >> 4) + 16 * q;
-        const int64_t t = t0 + row;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (t < te && ncol < N) {
-          v = *reinterpret_cast<const f32x4*>(dY + t * N + ncol);
-          if (Z) {
-            const f32x4 z = *reinterpret_cast<const f32x4*>(Z + t * N + ncol);
+    for (int e = 0; e < 4; ++e) dm[e] = 0.f;
+  };
+  auto contract = [&](int64_t sx, int64_t t0) {
+    if (want_v) {   // V contribution of this strip for rows 16*wave.. of the stage
+      f32x4 gv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dm[e] += v[e] * z[e];
-          }
+      for (int q = 0; q < 4; ++q)
+        gv[q] = *reinterpret_cast<const f32x4*>(&Gs[(16 * wave + l16) * SK_LD + 16 * h + 4 * q]);
+      f32x4 accV[JG];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= cmul[e];
-          if (o.gbf) {
-            u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            *reinterpret_cast<u32x2*>(o.gbf + t * N + ncol) = b;
-          }
-        }
-        *reinterpret_cast<f32x4*>(&Gs[row * SK_LD + 4 * c4]) = v;
-      }
-      for (int i = tid; i < SK_T * (RP / 4); i += 256) {
-        const int row = i / (RP / 4), q = i % (RP / 4);
-        const int64_t t = t0 + row;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (t < te && 4 * q < r) v = *reinterpret_cast<const f32x4*>(U + t * r + 4 * q);
-        *reinterpret_cast<f32x4*>(&Us[row * LDU + 4 * q]) = v;
-      }
-      __syncthreads();
-
-      if (want_v) {   // V contribution of this strip for rows 16*wave.. of the stage
-        f32x4 gv[4];
+      for (int j = 0; j < JG; ++j) {
+        accV[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 bv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          gv[q] = *reinterpret_cast<const f32x4*>(&Gs[(16 * wave + l16) * SK_LD + 16 * h + 4 * q]);
-        f32x4 accV[JG];
+          bv[q] = *reinterpret_cast<const f32x4*>(&Bt[(16 * j + l16) * SK_LD + 16 * h + 4 * q]);
 #pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          accV[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          f32x4 bv[4];
+        for (int s = 0; s < 16; ++s) accV[j] = mfma16x16x4(gv[s >> 2][s & 3], bv[s >> 2][s & 3], accV[j]);
+      }
+      // Each element of the block's partial is written by one thread, so
+      // later strips add to it in place.
+      const bool vfirst = sx == sx0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            bv[q] = *reinterpret_cast<const f32x4*>(&Bt[(16 * j + l16) * SK_LD + 16 * h + 4 * q]);
+      for (int j = 0; j < JG; ++j)
 #pragma unroll
-          for (int s = 0; s < 16; ++s) accV[j] = mfma16x16x4(gv[s >> 2][s & 3], bv[s >> 2][s & 3], accV[j]);
-        }
-        // Each element of the block's partial is written by one thread, so
-        // later strips add to it in place.
-#pragma unroll
-        for (int j = 0; j < JG; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t t = t0 + 16 * wave + row16(v, lane);
-            const int64_t jj = 16 * j + l16;
-            if (t < te && jj < r) {
-              float* d = vdst + t * r + jj;
-              *d = vfirst ? accV[j][v] : *d + accV[j][v];
-            }
+        for (int v = 0; v < 4; ++v) {
+          const int64_t t = t0 + 16 * wave + row16(v, lane);
+          const int64_t jj = 16 * j + l16;
+          if (t < te && jj < r) {
+            float* d = vdst + t * r + jj;
+            *d = vfirst ? accV[j][v] : *d + accV[j][v];
           }
-      }
-      // dB partial: rows n = 16*wave + l16 (A operand g^T), contraction over t.
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int tt = 4 * s + h;
-        const float a = Gs[tt * SK_LD + 16 * wave + l16];
-#pragma unroll
-        for (int j = 0; j < JG; ++j) accB[j] = mfma16x16x4(a, Us[tt * LDU + 16 * j + l16], accB[j]);
-      }
+        }
     }
-
+    // dB partial: rows n = 16*wave + l16 (A operand g^T), contraction over t.
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int tt = 4 * s + h;
+      const float a = Gs[tt * SK_LD + 16 * wave + l16];
+#pragma unroll
+      for (int j = 0; j < JG; ++j) accB[j] = mfma16x16x4(a, Us[tt * LDU + 16 * j + l16], accB[j]);
+    }
+  };
+  auto strip_end = [&](int64_t sx) {
+    const int64_t n0 = sx * SK_C;
     // dB (and dm) of this strip: direct when there is one row range.
     const bool bdirect = nts == 1;
 #pragma unroll
@@ -336,7 +422,26 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
         }
       }
     }
+  };
+  auto step = [&](int64_t idx, Tile& cur, Tile& nxt) {
+    const int64_t i = idx % nst, sx = sx0 + idx / nst, t0 = tb + i * SK_T;
+    if (i == 0) strip_begin(sx);
+    load(nxt, idx + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(cur, idx);
+    __syncthreads();
+    contract(sx, t0);
+    __syncthreads();
+    if (i == nst - 1) strip_end(sx);
+  };
+  Tile R[2];
+  if (ntot > 0) load(R[0], 0);
+  int64_t idx = 0;
+  for (; idx + 2 <= ntot; idx += 2) {
+    step(idx, R[0], R[1]);
+    step(idx + 1, R[1], R[0]);
   }
+  if (idx < ntot) step(idx, R[0], R[1]);
 }
 
 template <int RP>
@@ -397,34 +502,65 @@ LORA_DEV void k4_block(const K4Args& p, float* smem, int64_t bx, int by) {
 #pragma unroll
   for (int j = 0; j < JG; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = tb; t0 < te; t0 += SK_T) {
-    __syncthreads();
+  // Row stages of 64 tokens, the next stage's loads in flight while this one
+  // is stored and contracted (branch-free; see down_block).  V items: the
+  // 64 x RP/4 float4s of a stage, RP/16 per thread; the first partial is
+  // prefetched, further partials (if any) are added when stored.
+  struct Tile {
+    f32x4 x[4], v[RP / 16];
+  };
+  auto x_ok = [&](int q, int64_t t0, int64_t& t) -> bool {
+    t = t0 + (tid >> 4) + 16 * q;
+    return t < te && kcol < K;
+  };
+  auto v_ok = [&](int q, int64_t t0, int& row, int& q4, int64_t& t) -> bool {
+    const int i = tid + 256 * q;
+    row = i / (RP / 4);
+    q4 = i % (RP / 4);
+    t = t0 + row;
+    return t < te && 4 * q4 < r;
+  };
+  auto load = [&](Tile& S, int64_t t0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = (tid >> 4) + 16 * q;
-      const int64_t t = t0 + row;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (t < te && kcol < K) {
-        v = *reinterpret_cast<const f32x4*>(X + t * K + kcol);
-        if (drop.on) {
-          const uint64_t rk = drop_row(drop, t);
+      int64_t t;
+      const bool ok = x_ok(q, t0, t);
+      S.x[q] = *reinterpret_cast<const f32x4*>(ok ? X + t * K + kcol : X);
+    }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= drop_mul(drop, rk, kcol + e);
-        }
-      }
-      *reinterpret_cast<f32x4*>(&Xs[row * SK_LD + 4 * c4]) = v;
+    for (int q = 0; q < RP / 16; ++q) {
+      int row, q4;
+      int64_t t;
+      const bool ok = v_ok(q, t0, row, q4, t);
+      S.v[q] = *reinterpret_cast<const f32x4*>(ok ? V + t * r + 4 * q4 : V);
     }
-    for (int i = tid; i < SK_T * (RP / 4); i += 256) {
-      const int row = i / (RP / 4), q = i % (RP / 4);
-      const int64_t t = t0 + row;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (t < te && 4 * q < r) {
-        const int64_t i = t * r + 4 * q;
-        v = sum_parts4(V, T * r, vparts, i);
+  };
+  auto store = [&](const Tile& S, int64_t t0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t t;
+      const bool ok = x_ok(q, t0, t);
+      f32x4 v = ok ? S.x[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok && drop.on) {
+        const uint64_t rk = drop_row(drop, t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= drop_mul(drop, rk, kcol + e);
       }
-      *reinterpret_cast<f32x4*>(&Vs[row * LDV + 4 * q]) = v;
+      *reinterpret_cast<f32x4*>(&Xs[((tid >> 4) + 16 * q) * SK_LD + 4 * c4]) = v;
     }
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < RP / 16; ++q) {
+      int row, q4;
+      int64_t t;
+      const bool ok = v_ok(q, t0, row, q4, t);
+      f32x4 v = ok ? S.v[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok)
+        for (int pp = 1; pp < vparts; ++pp)
+          v += *reinterpret_cast<const f32x4*>(V + (int64_t)pp * T * r + t * r + 4 * q4);
+      *reinterpret_cast<f32x4*>(&Vs[row * LDV + 4 * q4]) = v;
+    }
+  };
+  auto contract = [&]() {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const int tt = 4 * s + h;
@@ -432,7 +568,25 @@ LORA_DEV void k4_block(const K4Args& p, float* smem, int64_t bx, int by) {
 #pragma unroll
       for (int j = 0; j < JG; ++j) acc[j] = mfma16x16x4(Vs[tt * LDV + 16 * j + l16], b, acc[j]);
     }
+  };
+  const int64_t nst = (te - tb + SK_T - 1) / SK_T;
+  auto tst = [&](int64_t i) { return tb + min(i, nst - 1) * SK_T; };
+  Tile R[2];
+  if (nst > 0) load(R[0], tst(0));
+  auto step = [&](int64_t i, Tile& cur, Tile& nxt) {
+    load(nxt, tst(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    store(cur, tst(i));
+    __syncthreads();
+    contract();
+    __syncthreads();
+  };
+  int64_t i = 0;
+  for (; i + 2 <= nst; i += 2) {
+    step(i, R[0], R[1]);
+    step(i + 1, R[1], R[0]);
   }
+  if (i < nst) step(i, R[0], R[1]);
   // acc[j][v] = dA[j' = 16j + 4*(l/16) + v][k = 16*wave + l16]
 #pragma unroll
   for (int j = 0; j < JG; ++j)
