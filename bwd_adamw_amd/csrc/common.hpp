@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -11,6 +12,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LORA_DEV __device__ __forceinline__
+#define LORA_HD __host__ __device__
 
 namespace lora {
 
@@ -127,11 +129,12 @@ LORA_DEV f32x4 sum_parts4(const float* part, int64_t stride, int nparts, int64_t
   return s;
 }
 
-// The same for one float.
-LORA_DEV float sum_parts1(const float* part, int64_t stride, int nparts, int64_t i) {
-  float s = part[i];
+// The same for one float or double.
+template <typename T>
+LORA_DEV T sum_parts1(const T* part, int64_t stride, int nparts, int64_t i) {
+  T s = part[i];
   for (int q = 1; q < nparts; q += 16) {
-    float v[16];
+    T v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
       if (q + u < nparts) v[u] = part[(int64_t)(q + u) * stride + i];

@@ -1013,33 +1013,98 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim, 
   return hip_status();
 }
 
-int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream) {
-  if (!lin || !out_norm) return LORA_E_INVALID;
-  if (lin->in_dim <= 0 || lin->out_dim <= 0) return LORA_E_SHAPE;
+// Row-norm grid: DN_ROWS rows per block in x (32 per wave), column splits of
+// cpw 64-column chunks in y.  The kernel holds dn_waves_per_simd(rp) waves per
+// SIMD, so a launch of W waves takes about ceil(W / slots) rounds of cpw
+// chunks each plus a start-up of about one chunk per round; cpw is the one
+// that minimises that estimate.
+struct DoraNormPlan {
+  int64_t nb, nsplit, cpw;
+};
+DoraNormPlan dora_norm_plan(int64_t N, int64_t K, int rp, bool split) {
+  DoraNormPlan q;
+  q.nb = cdiv(N, (int64_t)DN_ROWS);
+  const int64_t nch = cdiv(K, (int64_t)DN_CHUNK);
+  const int64_t waves = 4 * q.nb;
+  const int64_t slots = 1024 * (int64_t)dn_waves_per_simd(rp);
+  q.cpw = nch;
+  q.nsplit = 1;
+  if (!split) return q;
+  int64_t best = cdiv(waves, slots) * (q.cpw + 1);
+  for (int64_t cpw = nch - 1; cpw >= 1; --cpw) {
+    const int64_t s = cdiv(nch, cpw);
+    if (s > 65535) break;
+    const int64_t cost = cdiv(waves * s, slots) * (cpw + 1);
+    if (cost < best) {
+      best = cost;
+      q.cpw = cpw;
+      q.nsplit = s;
+    }
+  }
+  return q;
+}
+
+int check_row_norm_linear(const lora_linear* lin) {
+  if (!lin) return LORA_E_INVALID;
+  // in_dim <= 2^22 keeps the kernel's buffer offsets within 32 bits.
+  if (lin->in_dim <= 0 || lin->out_dim <= 0 || lin->in_dim > (1 << 22)) return LORA_E_SHAPE;
   if (lin->w_dtype != LORA_F32 && lin->w_dtype != LORA_BF16) return LORA_E_DTYPE;
   if (!lin->W) return LORA_E_INVALID;
   if ((lin->A == nullptr) != (lin->B == nullptr)) return LORA_E_INVALID;
-  const bool lora_on = lin->A != nullptr;
-  if (lora_on && (lin->rank <= 0 || lin->rank > 128)) return LORA_E_SHAPE;
+  if (lin->A && (lin->rank <= 0 || lin->rank > 128)) return LORA_E_SHAPE;
   if (!std::isfinite(lin->scale)) return LORA_E_INVALID;
+  return LORA_OK;
+}
+
+size_t lora_dora_row_norms_workspace_bytes(const lora_linear* lin) {
+  if (check_row_norm_linear(lin) != LORA_OK) return 0;
+  const DoraNormPlan q =
+      dora_norm_plan(lin->out_dim, lin->in_dim, lin->A ? rank_pad(lin->rank) : 16, true);
+  return q.nsplit > 1 ? sizeof(double) * q.nsplit * lin->out_dim : 0;
+}
+
+int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int rc = check_row_norm_linear(lin);
+  if (rc != LORA_OK) return rc;
+  if (!out_norm) return LORA_E_INVALID;
+  const bool lora_on = lin->A != nullptr;
   const int64_t N = lin->out_dim, K = lin->in_dim, r = lora_on ? lin->rank : 0;
-  const float* A = lin->A;
-  const float* B = lin->B;
-  const float s = lin->scale;
-  constexpr int ROWS = 8;
-  const unsigned grid = (unsigned)cdiv(N, ROWS);
+  const int rp = rank_pad(r);
+  const DoraNormPlan q = dora_norm_plan(N, K, lora_on ? rp : 16, workspace != nullptr);
+  if (q.nsplit > 1 && workspace_bytes < sizeof(double) * q.nsplit * N) return LORA_E_WORKSPACE;
+  const size_t wsz = lin->w_dtype == LORA_BF16 ? 2 : 4;
+  DoraNormArgs a;
+  a.W = lin->W;
+  a.N = N;
+  a.K = K;
+  a.A = lin->A;
+  a.B = lin->B;
+  a.r = (int)r;
+  a.s = lin->scale;
+  a.cpw = (int)q.cpw;
+  a.vec = al16(lin->W) && (K * wsz) % 16 == 0 && (!lora_on || (al16(lin->A) && K % 4 == 0));
+  a.part = static_cast<double*>(workspace);
+  a.out = out_norm;
   hipStream_t st = (hipStream_t)stream;
-  const int rp = lora_on ? rank_pad(r) : 16;
-  prof::Scope ps("dora_rownorm", N, K, r, 2.0 * N * K * (r + 1),
-                 (lin->w_dtype == LORA_BF16 ? 2.0 : 4.0) * N * K + 4.0 * r * (N + K) + 4.0 * N);
-  if (lin->w_dtype == LORA_BF16) {
-    const uint16_t* W = (const uint16_t*)lin->W;
-    LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<uint16_t, RP, ROWS>, dim3(grid), st, ps, W, N,
-                                K, A, B, r, s, out_norm));
-  } else {
-    const float* W = (const float*)lin->W;
-    LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<float, RP, ROWS>, dim3(grid), st, ps, W, N, K,
-                                A, B, r, s, out_norm));
+  const dim3 grid((unsigned)q.nb, (unsigned)q.nsplit);
+  {
+    prof::Scope ps("dora_rownorm", N, K, r, 2.0 * N * K * r + 3.0 * N * K,
+                   (double)wsz * N * K + 4.0 * r * (N + K) + (q.nsplit > 1 ? 8.0 : 4.0) * N);
+    if (!lora_on) {
+      if (lin->w_dtype == LORA_BF16) launch(dora_rownorm_kernel<uint16_t, 16, false>, grid, st, ps, a);
+      else launch(dora_rownorm_kernel<float, 16, false>, grid, st, ps, a);
+    } else if (lin->w_dtype == LORA_BF16) {
+      LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<uint16_t, RP, true>, grid, st, ps, a));
+    } else {
+      LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<float, RP, true>, grid, st, ps, a));
+    }
+  }
+  if (q.nsplit > 1) {
+    prof::Scope ps("dora_norm_finish", N, q.nsplit, 0, (double)N * q.nsplit,
+                   8.0 * N * q.nsplit + 4.0 * N);
+    launch(dora_norm_finish_kernel, dim3((unsigned)cdiv(N, 256)), st, ps, a.part,
+           (int)q.nsplit, N, out_norm);
   }
   return hip_status();
 }

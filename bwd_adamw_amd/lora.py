@@ -19,7 +19,8 @@ __all__ = [
     "F32", "BF16", "KIND_A", "KIND_B", "KIND_MAG",
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
-    "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
+    "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
+    "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group", "EXPORTS",
 ]
@@ -34,7 +35,8 @@ LORA_E_NONFINITE = -6
 EXPORTS = (
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
-    "lora_dropout_mask", "lora_dora_row_norms", "lora_scaling", "lora_lr_at",
+    "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
+    "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
 )
@@ -93,7 +95,8 @@ def lib() -> C.CDLL:
             "lora_grad_prepare": (I32, [P, I64, I64, F, P, P, P, P, SZ, P]),
             "lora_adamw_step": (I32, [P, P, P, P, P, I32, P, P, P]),
             "lora_dropout_mask": (I32, [P, I64, I64, P, P]),
-            "lora_dora_row_norms": (I32, [P, P, P]),
+            "lora_dora_row_norms_workspace_bytes": (SZ, [P]),
+            "lora_dora_row_norms": (I32, [P, P, P, SZ, P]),
             "lora_scaling": (C.c_double, [C.c_double, I64, I32]),
             "lora_lr_at": (C.c_double, [I64, C.c_double, I32, I64, I64, C.c_double]),
             "lora_status_string": (C.c_char_p, [I32]),
@@ -286,8 +289,21 @@ def lora_dropout_mask(drop: LoraDropout, tokens, in_dim, mask, stream=None):
     _check("lora_dropout_mask", rc)
 
 
-def lora_dora_row_norms(lin: LoraLinear, out_norm, stream=None):
-    rc = lib().lora_dora_row_norms(C.byref(lin), _ptr(out_norm, "out_norm"), _stream(stream))
+def lora_dora_row_norms_workspace_bytes(lin: LoraLinear) -> int:
+    return int(lib().lora_dora_row_norms_workspace_bytes(C.byref(lin)))
+
+
+def lora_dora_row_norms(lin: LoraLinear, out_norm, ws=None, stream=None, split=True):
+    """Row norms of W + s B A into out_norm.  `ws` is a device uint8 tensor of
+    at least lora_dora_row_norms_workspace_bytes(lin) bytes; when it is None
+    one is taken from torch's allocator (split=False passes none at all)."""
+    if ws is None and split:
+        need = lora_dora_row_norms_workspace_bytes(lin)
+        if need:
+            ws = torch.empty(need, device=out_norm.device, dtype=torch.uint8)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_dora_row_norms(C.byref(lin), _ptr(out_norm, "out_norm"),
+                                   _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_dora_row_norms", rc)
 
 

@@ -118,6 +118,9 @@ class Trainer:
         for g in self.groups:
             ws = max(ws, L.lora_group_workspace_bytes([self._linear(k, None, dora=cfg.dora)
                                                        for k in g]))
+        if cfg.dora:   # the row-norm refresh runs on the same stream between steps
+            for k in model.keys:
+                ws = max(ws, L.lora_dora_row_norms_workspace_bytes(self._linear(k, None)))
         self.U, self.Z, self.Y, self.dX = {}, {}, {}, {}
         for key in model.keys:
             K, N = model.shape[key]
@@ -153,7 +156,7 @@ class Trainer:
             wd = L.BF16 if W.dtype == torch.bfloat16 else L.F32
             bare = L.LoraLinear(self.T, K, N, 0, wd, float(self.scale), W.data_ptr(),
                                 None, None, None, None)
-            L.lora_dora_row_norms(bare, slot.mag[key])
+            L.lora_dora_row_norms(bare, slot.mag[key], self.ws)
             slot.norm[key] = torch.empty(N, device=self.device, dtype=torch.float32)
         self.refresh_dora(slot)
 
@@ -161,7 +164,7 @@ class Trainer:
         for key in self.model.keys:
             W = self.model.W[key]
             lin = L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T)
-            L.lora_dora_row_norms(lin, slot.norm[key])
+            L.lora_dora_row_norms(lin, slot.norm[key], self.ws)
 
     # ------------------------------------------------------------------
     def forward_backward(self, slot: Slot, chunks: list):

@@ -208,8 +208,19 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim,
 /* DoRA row norms ("8. LoRA Fundamentals", "How it works"):
  * out_norm[i] = || W_i + scale * (B A)_i ||_2 over the K inputs.  With
  * lin->A == lin->B == NULL it gives ||W_i|| (the magnitude initialisation).
- * lin->tokens is ignored. */
-int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* stream);
+ * lin->tokens and lin->dora_* are ignored; any out_dim > 0, 0 < in_dim <=
+ * 2^22 and 0 < rank <= 128 are accepted (LORA_E_SHAPE otherwise; unaligned
+ * rows take element loads).
+ * The contraction is split over column ranges whose double partials go to
+ * `workspace` (device, lora_dora_row_norms_workspace_bytes(lin) bytes, 0 for
+ * small K: then it may be NULL) and are summed per row in a fixed order by a
+ * second launch; with workspace == NULL one block covers all columns of its
+ * rows (fewer blocks, same result up to rounding order).  A non-NULL
+ * workspace smaller than required gives LORA_E_WORKSPACE.  out_norm is a
+ * device float[out_dim]. */
+size_t lora_dora_row_norms_workspace_bytes(const lora_linear* lin);
+int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Diagnostics: launch timing.  lora_profile_begin opens a profile that can
  * hold max_launches launches (it creates that many HIP event pairs once and

@@ -316,15 +316,36 @@ def test_adamw_parity_on_shared_inputs(t):
         assert rel_err(V[sl], vr) <= 1e-5
 
 
-@pytest.mark.parametrize("wd_,N,K,r", [("f32", 100, 84, 8), ("bf16", 264, 136, 64), ("bf16", 2560, 9728, 32)])
-def test_dora_row_norms_parity(wd_, N, K, r):
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole-rows"])
+@pytest.mark.parametrize("wd_,N,K,r", [
+    ("f32", 100, 84, 8),          # ragged rows and a partial last chunk
+    ("bf16", 264, 136, 64),
+    ("bf16", 45, 100, 12),        # rows not 16-byte aligned: element loads
+    ("f32", 33, 4097, 128),       # rank 128, odd K, many column splits
+    ("bf16", 2560, 9728, 64),     # DoRA workload shapes (wdown, wup)
+    ("bf16", 9728, 2560, 64),
+    ("f32", 2048, 2048, 8),
+])
+def test_dora_row_norms_parity(wd_, N, K, r, split):
     c = _linear_case(8, K, N, r, wd_, seed=11, b_std=0.05)
     g = _gpu(c)
-    out = torch.empty(N, device=DEV)
-    L.lora_dora_row_norms(L.make_linear(g["Wq"], None, None, 1.0, 8), out)
+    out = torch.full((N,), float("nan"), device=DEV)
+    L.lora_dora_row_norms(L.make_linear(g["Wq"], None, None, 1.0, 8), out, split=split)
     assert rel_err(out, O.dora_row_norms(np64(c["W"]))) <= 1e-5
-    L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], 1.7, 8), out)
+    out.fill_(float("nan"))
+    L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], 1.7, 8), out, split=split)
     assert rel_err(out, O.dora_row_norms(np64(c["W"]), np64(c["A"]), np64(c["B"]), 1.7)) <= 1e-5
+
+
+def test_dora_row_norms_workspace_checked():
+    c = _linear_case(8, 9728, 64, 16, "bf16", seed=3)
+    g = _gpu(c)
+    lin = L.make_linear(g["Wq"], g["A"], g["B"], 1.0, 8)
+    need = L.lora_dora_row_norms_workspace_bytes(lin)
+    assert need > 0
+    out = torch.empty(64, device=DEV)
+    with pytest.raises(L.LoraError):
+        L.lora_dora_row_norms(lin, out, torch.empty(need - 8, device=DEV, dtype=torch.uint8))
 
 
 # ------------------------------------------------------ end-to-end steps ---
