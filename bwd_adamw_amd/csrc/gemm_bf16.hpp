@@ -48,6 +48,9 @@ struct GemmBf16Args {
   float* C2;
   const float* cn;
   const float* cd;
+  int64_t ksplit;          // contraction length per split (multiple of BK)
+  int nsplit;              // splits of the contraction across blocks
+  float* part;             // [nsplit, M, Nc] partials when nsplit > 1
 };
 
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
@@ -80,12 +83,19 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int64_t ntn = (p.Nc + BN - 1) / BN, ntm = (p.M + BM - 1) / BM;
+  // Blocks are (split, tile) pairs; an XCD's contiguous run of them covers
+  // neighbouring tiles of one split, which share that split's K-slices.
+  const int64_t tiles = ntm * ntn;
+  const int64_t ts = xcd_tile(blockIdx.x, tiles * p.nsplit);
+  const int split = (int)(ts / tiles);
   int64_t tm, tn;
-  grouped_tile(xcd_tile(blockIdx.x, ntm * ntn), ntm, ntn, tm, tn);
+  grouped_tile(ts % tiles, ntm, ntn, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t kend = p.Kc;
+  const int64_t kbeg = (int64_t)split * p.ksplit;
+  const int64_t kend = min(p.Kc, kbeg + p.ksplit);
   const int hl = lane >> 5, l32 = lane & 31;
-  const bool store_xa = p.xa.out != nullptr && n0 == 0;
+  const bool lora = split == 0 && p.r > 0;
+  const bool store_xa = p.xa.out != nullptr && n0 == 0 && split == 0;
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     __syncthreads();
   };
 
-  if (!FWD && p.r > 0) {
+  if (!FWD && lora) {
     lora_contraction();
     if (p.drop.on) {
 #pragma unroll
@@ -279,14 +289,15 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     }
   }
 
-  // Main contraction.
-  const int64_t nk = (kend + BK - 1) / BK;
+  // Main contraction over [kbeg, kend); every split but the last is a whole
+  // number of K-steps, so a K-step never reaches into the next split.
+  const int64_t nk = (kend - kbeg + BK - 1) / BK;
   {
     Stage R[DEPTH];
-    auto kstep = [&](int64_t k) { return min(k, nk - 1) * BK; };
+    auto kstep = [&](int64_t k) { return kbeg + min(k, nk - 1) * BK; };
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) load(R[u], kstep(u));
-    store(R[0], 0, 0);
+    store(R[0], kbeg, 0);
     __syncthreads();
     int64_t k = 0;
     for (; k + DEPTH <= nk; k += DEPTH) {
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     }
   }
 
-  if (FWD && p.r > 0) lora_contraction();
+  if (FWD && lora) lora_contraction();
 
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -325,14 +336,18 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     for (int j = 0; j < NI; ++j) {
       const int64_t gn = n0 + wn0 + j * 32 + l32;
       if (gn >= p.Nc) continue;
-      const float c = p.cn ? p.cn[gn] / p.cd[gn] : 1.0f;
+      const float c = (p.nsplit == 1 && p.cn) ? p.cn[gn] / p.cd[gn] : 1.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
         if (gm >= p.M) continue;
         const float x = acc[i][j][v];
-        p.C[gm * p.Nc + gn] = x * c;
-        if (p.C2) p.C2[gm * p.Nc + gn] = x;
+        if (p.nsplit == 1) {
+          p.C[gm * p.Nc + gn] = x * c;
+          if (p.C2) p.C2[gm * p.Nc + gn] = x;
+        } else {
+          p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
+        }
       }
     }
 }

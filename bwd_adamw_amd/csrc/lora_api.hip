@@ -90,39 +90,68 @@ struct GemmPlan {
   int cfg;           // bf16 kernel configuration (kBf16Cfg)
 };
 
-// bf16 kernel configurations, in order of preference per direction: tile,
-// threads, wave rows, K-step, stages in flight, and the directions (1
-// forward, 2 dX) that use it.  dX's transposing loads take more registers
-// per stage, so its wide tiles keep a single stage (chosen by measurement on
-// the Qwen3-4B-shaped projections).
+// bf16 kernel configurations: tile, threads, wave rows, K-step, stages in
+// flight, the directions (1 forward, 2 dX) that use it, and the cost of one
+// round of 256 tiles (one block per CU: LDS and registers admit no second)
+// per direction: a microseconds per million (contraction length x tile area)
+// plus b microseconds.  a and b were fitted to a sweep of every configuration
+// and split on the Qwen3-4B-shaped projections at 2048 and 4096 tokens with
+// operands read from HBM (mean error 4 %; the plan it picks is within 0.1 %
+// of the sweep's best in total).  dX's transposing loads take more registers
+// per stage, so its wide tiles keep one stage.
 struct Bf16Cfg {
   int bm, bn, nt, wgm, bk, depth, dirs;
+  double a_fwd, b_fwd, a_dx, b_dx;
 };
-#define LORA_BF16_CFGS(X)             \
-  X(0, 256, 256, 512, 2, 32, 3, 1)    \
-  X(1, 256, 256, 512, 2, 64, 1, 2)    \
-  X(2, 256, 128, 512, 2, 64, 2, 1)    \
-  X(3, 256, 128, 512, 2, 64, 1, 2)    \
-  X(4, 128, 128, 512, 2, 64, 2, 3)
+#define LORA_BF16_CFGS(X)                                        \
+  X(0, 256, 256, 512, 2, 32, 3, 1, 0.409, 15.2, 0, 0)            \
+  X(1, 256, 256, 512, 2, 64, 1, 2, 0, 0, 0.479, 13.3)            \
+  X(2, 256, 128, 512, 2, 64, 2, 1, 0.482, 8.9, 0, 0)             \
+  X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.696, 7.3)             \
+  X(4, 128, 128, 512, 2, 64, 2, 3, 0.588, 5.1, 0.962, 4.6)
 constexpr Bf16Cfg kBf16Cfg[] = {
-#define LORA_CFG_ROW(i, bm, bn, nt, wgm, bk, d, dirs) {bm, bn, nt, wgm, bk, d, dirs},
+#define LORA_CFG_ROW(i, bm, bn, nt, wgm, bk, d, dirs, af, bf, ad, bd) \
+  {bm, bn, nt, wgm, bk, d, dirs, af, bf, ad, bd},
     LORA_BF16_CFGS(LORA_CFG_ROW)
 #undef LORA_CFG_ROW
 };
 constexpr int kBf16NCfg = sizeof(kBf16Cfg) / sizeof(kBf16Cfg[0]);
+constexpr int kBf16Slots = 256;  // resident tiles per round
+// Cost of a split's fp32 partials (written once, read once by the reduction
+// that also writes the result): microseconds per MB, from the same fit.
+constexpr double kSplitUsPerMB = 0.103;
 
-// bf16: the first configuration whose grid still covers most of the 256
-// CUs.  fp32: 128x128 when that fills the chip, else the split tile with the
-// contraction split across blocks until about 256 blocks run.
-GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx) {
-  if (bf16) {
-    for (int i = 0; i < kBf16NCfg; ++i) {
-      const Bf16Cfg& c = kBf16Cfg[i];
-      if (!(c.dirs & (dx ? 2 : 1))) continue;
-      if (cdiv(M, c.bm) * cdiv(Nc, c.bn) >= 200 || i == kBf16NCfg - 1)
-        return {c.bm, c.bn, {Kc, 1}, i};
+// bf16: the configuration and contraction split (whole K-steps per split,
+// at least 8 of them) with the least estimated time.
+GemmPlan plan_gemm_bf16(int64_t M, int64_t Nc, int64_t Kc, bool dx) {
+  GemmPlan best = {0, 0, {Kc, 1}, -1};
+  double tbest = 1e30;
+  for (int i = 0; i < kBf16NCfg; ++i) {
+    const Bf16Cfg& c = kBf16Cfg[i];
+    if (!(c.dirs & (dx ? 2 : 1))) continue;
+    const double a = dx ? c.a_dx : c.a_fwd, b = dx ? c.b_dx : c.b_fwd;
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(Nc, c.bn);
+    for (int s = 1; s <= 8; ++s) {
+      const int64_t len = rup(cdiv(Kc, s), c.bk);
+      if (s > 1 && len < 8 * c.bk) break;
+      const int64_t n = cdiv(Kc, len);
+      if (n != s) continue;
+      const double rounds = (double)cdiv(tiles * n, kBf16Slots);
+      double t = rounds * (a * len * c.bm * c.bn / 1e6 + b);
+      if (n > 1) t += kSplitUsPerMB * (2.0 * n + 1.0) * 4.0 * M * Nc / 1e6;
+      if (t < tbest) {
+        tbest = t;
+        best = {c.bm, c.bn, {len, (int)n}, i};
+      }
     }
   }
+  return best;
+}
+
+// fp32: 128x128 when that fills the chip, else the split tile with the
+// contraction split across blocks until about 256 blocks run.
+GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx) {
+  if (bf16) return plan_gemm_bf16(M, Nc, Kc, dx);
   if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}, 0};
   const int64_t tiles = cdiv(M, SPLIT_BM) * cdiv(Nc, SPLIT_BN);
   return {SPLIT_BM, SPLIT_BN, plan_split(Kc, tiles, 256, 32, 128), 0};
@@ -317,14 +346,30 @@ void launch_gemm_f32(const GemmPlan& g, bool fwd, const GemmF32Args& a, hipStrea
   }
 }
 
+void launch_gemm_bf16_tiles(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st);
+
+// The bf16 GEMM, then (split contraction) the fixed-order sum of its partials
+// with the unsplit kernel's epilogue.
 void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st) {
-  const dim3 grid((unsigned)(cdiv(a.Nc, g.bn) * cdiv(a.M, g.bm)));
+  launch_gemm_bf16_tiles(g, fwd, a, st);
+  if (g.k.n > 1) {
+    const int64_t n4 = cdiv(a.M * a.Nc, 4);
+    prof::Scope ps("splitk_reduce", a.M, a.Nc, g.k.n, 0.0,
+                   4.0 * a.M * a.Nc * (g.k.n + (a.C2 ? 2 : 1)));
+    launch(splitk_reduce_kernel, dim3((unsigned)cdiv(n4, 256)), st, ps, (const float*)a.part,
+           g.k.n, a.M, a.Nc, a.C, a.C2, a.cn, a.cd);
+  }
+}
+
+void launch_gemm_bf16_tiles(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st) {
+  const dim3 grid((unsigned)(cdiv(a.Nc, g.bn) * cdiv(a.M, g.bm) * g.k.n));
   prof::Scope ps(fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
                  2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
-                 2.0 * (a.M * a.Kc + a.Nc * a.Kc) + 4.0 * a.M * a.Nc * (a.C2 ? 2 : 1));
+                 2.0 * (a.M * a.Kc + a.Nc * a.Kc) +
+                     4.0 * a.M * a.Nc * (g.k.n > 1 ? g.k.n : (a.C2 ? 2 : 1)));
   const Bf16Cfg& c = kBf16Cfg[g.cfg];
   const bool exact = a.M % c.bm == 0 && a.Nc % c.bn == 0 && a.Kc % c.bk == 0;
-#define LORA_BF16_TILE(i, BM_, BN_, NT_, WGM_, BK_, D_, DIRS_)                              \
+#define LORA_BF16_TILE(i, BM_, BN_, NT_, WGM_, BK_, D_, DIRS_, AF_, BF_, AD_, BD_)            \
   if (g.cfg == i) {                                                                        \
     if (fwd) {                                                                             \
       if constexpr ((DIRS_)&1) {                                                           \
@@ -486,6 +531,7 @@ void launch_fwd_plain(const FwdJob& j, hipStream_t st) {
     a.M = T; a.Nc = N; a.Kc = K;
     a.xa = j.xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
     a.C = j.Y; a.C2 = j.Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
+    a.ksplit = j.gf.k.len; a.nsplit = j.gf.k.n; a.part = j.gfpart;
     launch_gemm_bf16(j.gf, true, a, st);
   } else {
     GemmF32Args a;
@@ -740,6 +786,8 @@ void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
       a.M = T; a.Nc = K; a.Kc = N;
       a.xa = jb.xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = jb.d;
       a.C = jb.dX;
+      a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
+      a.part = y.gd.k.n > 1 ? (float*)(jb.w + y.gdpart) : nullptr;
       launch_gemm_bf16(y.gd, false, a, st);
     } else {
       GemmF32Args a;

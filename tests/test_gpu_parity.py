@@ -205,8 +205,9 @@ def test_linear_outputs_are_deterministic():
 
 # --------------------------------------------- full-size, sampled outputs --
 FULL_CASES = [
-    # workload, projection index, rows sampled
-    (4, 0, 48), (4, 6, 48), (5, 4, 32),
+    # workload, projection index, rows sampled (the launch plans include
+    # split-contraction bf16 products in both directions)
+    (4, 0, 48), (4, 6, 48), (5, 0, 32), (5, 4, 32), (5, 6, 32),
 ]
 
 
