@@ -170,25 +170,83 @@ LORA_DEV void epi_block(const EpiArgs& e, float* smem, int64_t b) {
   const int64_t m0 = rb * e.rows, c0 = cb * e.cols;
   const int tid = threadIdx.x;
   const int r = (int)e.r;
-  float* xs = smem;   // [rows][r], already times s
-  for (int i = tid; i < e.rows * r; i += 256) {
-    const int lr = i / r, j = i % r;
-    const int64_t m = m0 + lr;
-    float v = 0.f;
-    if (m < e.M) {
-      const int64_t idx = m * e.r + j;
-      v = sum_parts1(e.xa.p, e.xa.stride, e.xa.nparts, idx);
-      if (FWD && e.xa.out && cb == 0) e.xa.out[idx] = v;
-    }
-    xs[i] = v * e.s;
-  }
-  __syncthreads();
   const int t4 = 4 * tid;
   const int lr = t4 / e.cols, lc = t4 % e.cols;
   const int64_t m = m0 + lr, n = c0 + lc;
-  if (lr >= e.rows || m >= e.M || n >= e.Nc) return;
+  const bool act = lr < e.rows && m < e.M && n < e.Nc;
   const int64_t i4 = m * e.Nc + n;
-  const f32x4 acc = sum_parts4(e.part, e.M * e.Nc, e.nsplit, i4);
+  // No barrier: each wave stages, in LDS, the rank-side rows its own lanes
+  // read (a row shared by two waves is written by both with equal values),
+  // and a wave's LDS write precedes its own reads.  Loads are issued in the
+  // order they are consumed, without loops, so their round trips overlap:
+  // first the staged rows' partials (up to UP each), then this thread's
+  // output split partials (up to PV), added in split order last.
+  constexpr int UI = 3;          // staged values per lane (5 rows x 32 ranks at 64+ columns)
+  constexpr int UP = 16, PV = 16;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wr0 = 256 * wave / e.cols;
+  const int wr1 = min((256 * wave + 252) / e.cols, e.rows - 1);
+  const int nu = wr0 <= wr1 ? (wr1 - wr0 + 1) * r : 0;
+  float uv[UI][UP];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
+    const int i = lane + 64 * it;
+    const int64_t mu = m0 + wr0 + (i < nu ? i / r : 0);
+    const int64_t idx = mu * e.r + (i < nu ? i % r : 0);
+    if (i < nu && mu < e.M) {
+#pragma unroll
+      for (int u = 0; u < UP; ++u)
+        if (u < e.xa.nparts) uv[it][u] = e.xa.p[(int64_t)u * e.xa.stride + idx];
+    }
+  }
+  f32x4 pv[PV];
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < PV; ++u)
+      if (u < e.nsplit) pv[u] = *reinterpret_cast<const f32x4*>(e.part + (int64_t)u * e.M * e.Nc + i4);
+  }
+  // An empty asm with a memory clobber emits nothing but keeps the compiler
+  // from sinking the loads above next to their first use.
+  asm volatile("" ::: "memory");
+  float* xs = smem;   // [rows][r], already times s
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
+    const int i = lane + 64 * it;
+    if (i >= nu) continue;
+    const int row = wr0 + i / r;
+    const int64_t mu = m0 + row;
+    const int64_t idx = mu * e.r + i % r;
+    float v = 0.f;
+    if (mu < e.M) {
+      v = uv[it][0];
+#pragma unroll
+      for (int u = 1; u < UP; ++u)
+        if (u < e.xa.nparts) v += uv[it][u];
+      for (int u = UP; u < e.xa.nparts; ++u) v += e.xa.p[(int64_t)u * e.xa.stride + idx];
+      if (FWD && e.xa.out && cb == 0) e.xa.out[idx] = v;
+    }
+    xs[row * r + i % r] = v * e.s;
+  }
+  // Narrow tiles (fewer than 64 columns) give a wave more rows than UI lanes'
+  // worth; the rest are staged plainly.
+  for (int i = lane + 64 * UI; i < nu; i += 64) {
+    const int row = wr0 + i / r;
+    const int64_t mu = m0 + row;
+    const int64_t idx = mu * e.r + i % r;
+    float v = 0.f;
+    if (mu < e.M) {
+      v = sum_parts1(e.xa.p, e.xa.stride, e.xa.nparts, idx);
+      if (FWD && e.xa.out && cb == 0) e.xa.out[idx] = v;
+    }
+    xs[row * r + i % r] = v * e.s;
+  }
+  if (!act) return;
+  f32x4 acc = pv[0];
+#pragma unroll
+  for (int u = 1; u < PV; ++u)
+    if (u < e.nsplit) acc += pv[u];
+  for (int u = PV; u < e.nsplit; ++u)
+    acc += *reinterpret_cast<const f32x4*>(e.part + (int64_t)u * e.M * e.Nc + i4);
   const float* xr = xs + lr * r;
   f32x4 lo = {0.f, 0.f, 0.f, 0.f};
   if (FWD) {

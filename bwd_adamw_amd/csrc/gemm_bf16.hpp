@@ -53,6 +53,8 @@ struct GemmBf16Args {
   float* part;             // [nsplit, M, Nc] partials when nsplit > 1
 };
 
+constexpr bool kBf16ReadsFirst = false;
+
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
@@ -205,6 +207,30 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // output tile, lane half hl holding indices hl*HALF .. of each LD-wide row.
   auto compute = [&](const uint16_t* Ab, const uint16_t* Bb, auto LD, auto HALF, auto STEPS) {
     constexpr int ld = decltype(LD)::value, half = decltype(HALF)::value;
+    if constexpr (kBf16ReadsFirst && decltype(STEPS)::value <= 2) {
+      // Every operand of the staged K-step is read from LDS before the
+      // first MFMA, so LDS latency overlaps the MFMAs instead of preceding
+      // each pair of them.
+      constexpr int S = decltype(STEPS)::value;
+      u32x4 av[S][MI], bv[S][NI];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          av[s][i] = *reinterpret_cast<const u32x4*>(&Ab[(wm0 + i * 32 + l32) * ld + half * hl + 8 * s]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          bv[s][j] = *reinterpret_cast<const u32x4*>(&Bb[(wn0 + j * 32 + l32) * ld + half * hl + 8 * s]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) acc[i][j] = mfma32x32x16_bf16(av[s][i], bv[s][j], acc[i][j]);
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < decltype(STEPS)::value; ++s) {
       u32x4 av[MI], bv[NI];
