@@ -58,6 +58,11 @@ other than itself):
 * ``lr_at`` -- schedule closed forms (warmup end, midpoint, end).
 * ``dora_row_norms`` -- ``numpy.linalg.norm`` of the merged weight; B = 0
   gives the plain row norms.
+* ``bf16_round`` -- hand-worked round-to-nearest-even cases (ties both ways,
+  carry into the exponent).
+* ``merge`` -- B = 0 returns W itself (RMSE 0 for bf16 W); ``X merged^T``
+  equals ``forward``'s Y (plain and DoRA); the RMSE of a matrix of ties
+  has a closed form.
 * ``train_step`` -- accumulation over G chunks equals one concatenated chunk;
   seeded reruns give identical adapters.
 """
@@ -82,6 +87,8 @@ __all__ = [
     "adamw_update",
     "lr_at",
     "dora_row_norms",
+    "bf16_round",
+    "merge",
     "SlotState",
     "train_step",
 ]
@@ -316,6 +323,38 @@ def dora_row_norms(W, A=None, B=None, s=1.0):
     else:
         M = W + F64(s) * (np.asarray(B, dtype=F64) @ np.asarray(A, dtype=F64))
     return np.sqrt((M * M).sum(axis=1))
+
+
+# --------------------------------------------------------------------------
+# Merge for export -- "8. LoRA Fundamentals", "How it works" (the effective
+# weight W + scale*B*A, merged in F32; DoRA's per-row rescale) and "Profiling
+# with --jfr" (the merge reports the RMSE of requantising the merged weight)
+# --------------------------------------------------------------------------
+def bf16_round(x):
+    """Round float32 values to bfloat16, to nearest with ties to even,
+    returned as float64.  (NaN and infinities are not handled.)"""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = (b + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
+    return r.astype(np.uint32).view(np.float32).astype(F64)
+
+
+def merge(W, A, B, s, mag=None, norm=None, out="f32"):
+    """Merged weight ``c_i (W + s B A)_i`` (``c = mag/norm`` for DoRA, else 1),
+    stored as float32 (``out="f32"``) or rounded to bfloat16 from its float32
+    value (``out="bf16"``).  Returns ``(W_out, rmse)`` where ``rmse`` is the
+    root mean square of ``W_out`` minus the float32 merged weight over all
+    elements (0 for float32 output)."""
+    M = np.asarray(W, dtype=F64) + F64(s) * (np.asarray(B, dtype=F64) @ np.asarray(A, dtype=F64))
+    if mag is not None:
+        M = M * (np.asarray(mag, dtype=F64) / np.asarray(norm, dtype=F64))[:, None]
+    m32 = M.astype(np.float32).astype(F64)
+    if out == "f32":
+        return m32, 0.0
+    if out != "bf16":
+        raise ValueError(out)
+    q = bf16_round(m32)
+    return q, float(np.sqrt(np.mean((q - m32) ** 2)))
 
 
 # --------------------------------------------------------------------------

@@ -392,3 +392,49 @@ def test_dora_step_refreshes_norms():
         pr = st.params[key]
         ref = np.linalg.norm(W + hp["s"] * pr["B"] @ pr["A"], axis=1)
         assert np.allclose(st.norms[key], ref, rtol=1e-14)
+
+
+# ------------------------------------------------------------ merge ---------
+def test_bf16_round_hand_worked_cases():
+    # bfloat16 keeps 8 significant bits: near 1 the spacing is 2**-7.
+    x = np.array([1.0 + 2.0**-8,          # tie, lower neighbour even -> 1
+                  1.0 + 3 * 2.0**-8,      # tie, upper neighbour even -> 1 + 2**-6
+                  1.0 + 2.0**-8 + 2.0**-20,   # just above the tie -> up
+                  2.0 - 2.0**-9,          # tie at the top of the binade: even is 2.0
+                  -(1.0 + 2.0**-8),       # sign is kept
+                  0.0, 3.0], dtype=np.float32)
+    want = [1.0, 1.0 + 2.0**-6, 1.0 + 2.0**-7, 2.0, -1.0, 0.0, 3.0]
+    assert O.bf16_round(x).tolist() == want
+
+
+def test_merge_with_zero_b_returns_w():
+    rng = np.random.default_rng(5)
+    W = O.bf16_round(rng.normal(0, 0.02, (12, 20)))      # bf16-representable W
+    A = rng.normal(0, 1, (4, 20))
+    W_out, rmse = O.merge(W, A, np.zeros((12, 4)), 2.0, out="bf16")
+    assert np.array_equal(W_out, W) and rmse == 0.0
+    W_out, rmse = O.merge(W, A, np.zeros((12, 4)), 2.0)
+    assert np.array_equal(W_out, W) and rmse == 0.0
+
+
+@pytest.mark.parametrize("dora", [False, True])
+def test_merged_weight_reproduces_forward(dora):
+    rng = np.random.default_rng(6)
+    T, K, N, r, s = 7, 24, 10, 4, 1.5
+    X, W = rng.normal(0, 1, (T, K)), rng.normal(0, 0.02, (N, K))
+    A, B = rng.normal(0, 0.3, (r, K)), rng.normal(0, 0.1, (N, r))
+    mag = nrm = None
+    if dora:
+        mag = rng.uniform(0.5, 2.0, N)
+        nrm = O.dora_row_norms(W, A, B, s)
+    Y, _, _ = O.forward(X, W, A, B, s, mag=mag, norm=nrm)
+    W_out, _ = O.merge(W, A, B, s, mag, nrm)
+    assert np.allclose(X @ W_out.T, Y, rtol=0, atol=1e-6 * np.abs(Y).max())
+
+
+def test_merge_rmse_of_ties_closed_form():
+    # Every merged value is a tie 1 + 2**-8 (rounds to 1) or 1 + 3*2**-8
+    # (rounds to 1 + 2**-6): each element is off by exactly 2**-8.
+    W = np.where(np.arange(6 * 8).reshape(6, 8) % 2 == 0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8)
+    _, rmse = O.merge(W, np.zeros((1, 8)), np.zeros((6, 1)), 1.0, out="bf16")
+    assert rmse == 2.0**-8
