@@ -1069,12 +1069,12 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim, 
 struct DoraNormPlan {
   int64_t nb, nsplit, cpw;
 };
-DoraNormPlan dora_norm_plan(int64_t N, int64_t K, int rp, bool split) {
+DoraNormPlan dora_norm_plan(int64_t N, int64_t K, int rp, bool split, int mode = 0) {
   DoraNormPlan q;
   q.nb = cdiv(N, (int64_t)DN_ROWS);
   const int64_t nch = cdiv(K, (int64_t)DN_CHUNK);
   const int64_t waves = 4 * q.nb;
-  const int64_t slots = 1024 * (int64_t)dn_waves_per_simd(rp);
+  const int64_t slots = 1024 * (int64_t)dn_waves_per_simd(rp, mode);
   q.cpw = nch;
   q.nsplit = 1;
   if (!split) return q;
@@ -1122,7 +1122,8 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace
   const DoraNormPlan q = dora_norm_plan(N, K, lora_on ? rp : 16, workspace != nullptr);
   if (q.nsplit > 1 && workspace_bytes < sizeof(double) * q.nsplit * N) return LORA_E_WORKSPACE;
   const size_t wsz = lin->w_dtype == LORA_BF16 ? 2 : 4;
-  DoraNormArgs a;
+  RowPassArgs a;
+  memset(&a, 0, sizeof(a));
   a.W = lin->W;
   a.N = N;
   a.K = K;
@@ -1140,12 +1141,12 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace
     prof::Scope ps("dora_rownorm", N, K, r, 2.0 * N * K * r + 3.0 * N * K,
                    (double)wsz * N * K + 4.0 * r * (N + K) + (q.nsplit > 1 ? 8.0 : 4.0) * N);
     if (!lora_on) {
-      if (lin->w_dtype == LORA_BF16) launch(dora_rownorm_kernel<uint16_t, 16, false>, grid, st, ps, a);
-      else launch(dora_rownorm_kernel<float, 16, false>, grid, st, ps, a);
+      if (lin->w_dtype == LORA_BF16) launch(row_pass_kernel<uint16_t, 16, false, 0, float>, grid, st, ps, a);
+      else launch(row_pass_kernel<float, 16, false, 0, float>, grid, st, ps, a);
     } else if (lin->w_dtype == LORA_BF16) {
-      LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<uint16_t, RP, true>, grid, st, ps, a));
+      LORA_RP_DISPATCH(rp, launch(row_pass_kernel<uint16_t, RP, true, 0, float>, grid, st, ps, a));
     } else {
-      LORA_RP_DISPATCH(rp, launch(dora_rownorm_kernel<float, RP, true>, grid, st, ps, a));
+      LORA_RP_DISPATCH(rp, launch(row_pass_kernel<float, RP, true, 0, float>, grid, st, ps, a));
     }
   }
   if (q.nsplit > 1) {
@@ -1153,6 +1154,72 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace
                    8.0 * N * q.nsplit + 4.0 * N);
     launch(dora_norm_finish_kernel, dim3((unsigned)cdiv(N, 256)), st, ps, a.part,
            (int)q.nsplit, N, out_norm);
+  }
+  return hip_status();
+}
+
+// Merge for export: the same row pass, writing c (W + s B A) instead of
+// summing its squares; the bf16 rounding error goes to per-wave partials
+// (the workspace) and one fixed-order finish.
+size_t lora_merge_workspace_bytes(const lora_linear* lin) {
+  if (check_row_norm_linear(lin) != LORA_OK) return 0;
+  const DoraNormPlan q =
+      dora_norm_plan(lin->out_dim, lin->in_dim, lin->A ? rank_pad(lin->rank) : 16, true, 1);
+  return sizeof(double) * q.nb * q.nsplit * 4;
+}
+
+int lora_merge(const lora_linear* lin, void* W_out, int out_dtype, double* rmse, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const int rc = check_row_norm_linear(lin);
+  if (rc != LORA_OK) return rc;
+  if (!W_out) return LORA_E_INVALID;
+  if (out_dtype != LORA_F32 && out_dtype != LORA_BF16) return LORA_E_DTYPE;
+  if ((lin->dora_mag == nullptr) != (lin->dora_norm == nullptr)) return LORA_E_INVALID;
+  const bool lora_on = lin->A != nullptr;
+  const int64_t N = lin->out_dim, K = lin->in_dim, r = lora_on ? lin->rank : 0;
+  const int rp = rank_pad(r);
+  const DoraNormPlan q = dora_norm_plan(N, K, lora_on ? rp : 16, true, 1);
+  const bool want_err = rmse != nullptr && out_dtype == LORA_BF16;
+  const size_t need = sizeof(double) * q.nb * q.nsplit * 4;
+  if (want_err && (!workspace || workspace_bytes < need)) return LORA_E_WORKSPACE;
+  const size_t wsz = lin->w_dtype == LORA_BF16 ? 2 : 4, osz = out_dtype == LORA_BF16 ? 2 : 4;
+  RowPassArgs a;
+  memset(&a, 0, sizeof(a));
+  a.W = lin->W;
+  a.N = N;
+  a.K = K;
+  a.A = lin->A;
+  a.B = lin->B;
+  a.r = (int)r;
+  a.s = lin->scale;
+  a.cpw = (int)q.cpw;
+  a.vec = al16(lin->W) && (K * wsz) % 16 == 0 && (!lora_on || (al16(lin->A) && K % 4 == 0));
+  a.wout = W_out;
+  a.vec_out = al16(W_out) && (K * osz) % 16 == 0;
+  a.mag = lin->dora_mag;
+  a.nrm = lin->dora_norm;
+  a.epart = want_err ? static_cast<double*>(workspace) : nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)q.nb, (unsigned)q.nsplit);
+  {
+    prof::Scope ps("merge", N, K, r, 2.0 * N * K * r + 3.0 * N * K,
+                   (double)(wsz + osz) * N * K + 4.0 * r * (N + K));
+#define LORA_MERGE_LAUNCH(WT_, OT_)                                                            \
+  if (!lora_on) launch(row_pass_kernel<WT_, 16, false, 1, OT_>, grid, st, ps, a);             \
+  else LORA_RP_DISPATCH(rp, launch(row_pass_kernel<WT_, RP, true, 1, OT_>, grid, st, ps, a));
+    if (lin->w_dtype == LORA_BF16) {
+      if (out_dtype == LORA_BF16) { LORA_MERGE_LAUNCH(uint16_t, uint16_t) }
+      else { LORA_MERGE_LAUNCH(uint16_t, float) }
+    } else {
+      if (out_dtype == LORA_BF16) { LORA_MERGE_LAUNCH(float, uint16_t) }
+      else { LORA_MERGE_LAUNCH(float, float) }
+    }
+#undef LORA_MERGE_LAUNCH
+  }
+  if (rmse) {   // float32 output: no partials, the finish writes 0
+    prof::Scope ps("merge_rmse", N, K, 0, 0.0, want_err ? (double)need : 8.0);
+    launch(rmse_finish_kernel, dim3(1), st, ps, (const double*)a.epart,
+           want_err ? (int64_t)(q.nb * q.nsplit * 4) : (int64_t)0, (double)N * (double)K, rmse);
   }
   return hip_status();
 }

@@ -173,7 +173,7 @@ constexpr int DN_ROWS = 128;  // 32 per wave
 constexpr int DN_CHUNK = 64;
 constexpr int DN_LDS_AHEAD = 4;
 
-struct DoraNormArgs {
+struct RowPassArgs {
   const void* W;
   int64_t N, K;
   const float* A;  // [r,K] or nullptr (norms of W alone)
@@ -182,12 +182,20 @@ struct DoraNormArgs {
   float s;
   int cpw;         // chunks per block (each wave walks all of them)
   int vec;         // W and A rows are 16-byte aligned: full chunks use vector loads
-  double* part;    // [gridDim.y][N] when gridDim.y > 1
-  float* out;
+  double* part;    // norms: [gridDim.y][N] when gridDim.y > 1
+  float* out;      // norms: [N]
+  // merge: W_out = c_i (W + s B A), c_i = mag[i] / nrm[i] when both are set
+  void* wout;      // [N, K] float or bf16
+  int vec_out;     // wout rows are 16-byte aligned
+  const float* mag;
+  const float* nrm;
+  double* epart;   // [gridDim.y][gridDim.x][4] squared bf16 rounding error, or nullptr
 };
 
 // Waves per SIMD the kernel is built for (registers; the host plans with it).
-LORA_HD constexpr int dn_waves_per_simd(int rp) { return rp <= 64 ? 4 : 2; }
+LORA_HD constexpr int dn_waves_per_simd(int rp, int mode = 0) {
+  return mode == 1 ? (rp <= 16 ? 4 : 2) : (rp <= 64 ? 4 : 2);   // the merge holds 32 outputs
+}
 
 template <typename WT>
 LORA_DEV float dn_w(const u32x4* w, int e) {
@@ -199,9 +207,13 @@ LORA_DEV float dn_w(const u32x4* w, int e) {
   }
 }
 
-template <typename WT, int RP, bool LORA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dn_waves_per_simd(RP))))
-void dora_rownorm_kernel(DoraNormArgs p) {
+// One pass over W's rows with (W + s B A) tiles formed on the fly.
+// MODE 0: DoRA row norms.  MODE 1: merge for export, W_out = c (W + s B A)
+// stored as OT (float, or bf16 rounded to nearest even), with the squared
+// rounding error of bf16 output summed per wave.
+template <typename WT, int RP, bool LORA, int MODE, typename OT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dn_waves_per_simd(RP, MODE))))
+void row_pass_kernel(RowPassArgs p) {
   constexpr int NS = RP / 2;                        // MFMA steps (two rank rows each)
   constexpr int WV = sizeof(WT) == 2 ? 4 : 8;       // u32x4 of W per lane and chunk
   constexpr int AQ = LORA ? RP / 16 : 1;            // A float4 per thread and chunk
@@ -299,7 +311,12 @@ void dora_rownorm_kernel(DoraNormArgs p) {
   const int64_t nch = (K + DN_CHUNK - 1) / DN_CHUNK;
   const int64_t c0 = (int64_t)blockIdx.y * p.cpw;
   const int64_t c1 = c0 + p.cpw < nch ? c0 + p.cpw : nch;
-  double sq = 0.0;
+  double sq = 0.0;  // norms: this lane's squares; merge: its rounding error
+  float crow = 1.f;
+  if constexpr (MODE == 1) {
+    if (p.mag && (lane & 31) < brows)
+      crow = p.mag[i0 + (lane & 31)] / p.nrm[i0 + (lane & 31)];
+  }
   f32x4 a[AQ];
   load_a(a, c0 * DN_CHUNK);
   store_a(a, 0);
@@ -335,24 +352,94 @@ void dora_rownorm_kernel(DoraNormArgs p) {
     }
     // acc[q][v] is column k0 + 32 (lane/32) + 2v + q of row i0 + lane%32;
     // masked columns hold W = 0 and A = 0 and add nothing.
-    float cs = 0.f;
+    if constexpr (MODE == 0) {
+      float cs = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
+      for (int v = 0; v < 16; ++v)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float x = dn_w<WT>(w, 2 * v + q) + p.s * acc[q][v];
-        cs += x * x;
+        for (int q = 0; q < 2; ++q) {
+          const float x = dn_w<WT>(w, 2 * v + q) + p.s * acc[q][v];
+          cs += x * x;
+        }
+      sq += (double)cs;
+    } else {
+      // Merged values of this lane's 32 consecutive columns.
+      float x[32];
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) x[2 * v + q] = (dn_w<WT>(w, 2 * v + q) + p.s * acc[q][v]) * crow;
+      const int64_t row = i0 + (lane & 31);
+      const int64_t kb = c * DN_CHUNK + 32 * (lane >> 5);
+      OT* dst = static_cast<OT*>(p.wout) + (row < N ? row : 0) * K + kb;
+      const bool full = p.vec_out && c * DN_CHUNK + DN_CHUNK <= K;
+      if constexpr (sizeof(OT) == 2) {
+        uint32_t pk[16];
+        float es = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t lo = f32_to_bf16_bits(x[2 * e]), hi = f32_to_bf16_bits(x[2 * e + 1]);
+          pk[e] = lo | (hi << 16);
+          const float d0 = bf16_bits_to_f32(lo) - x[2 * e], d1 = bf16_bits_to_f32(hi) - x[2 * e + 1];
+          es += d0 * d0 + d1 * d1;
+        }
+        if (row < N) {
+          if (full) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              reinterpret_cast<u32x4*>(dst)[h] = u32x4{pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+              if (kb + e < K) dst[e] = (OT)((pk[e / 2] >> (16 * (e & 1))) & 0xffffu);
+          }
+          sq += (double)es;   // masked columns are 0 on both sides
+        }
+      } else {
+        if (row < N) {
+          if (full) {
+#pragma unroll
+            for (int h = 0; h < 8; ++h)
+              reinterpret_cast<f32x4*>(dst)[h] = f32x4{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+              if (kb + e < K) dst[e] = x[e];
+          }
+        }
       }
-    sq += (double)cs;
+    }
     store_a(a, buf ^ 1);
     __syncthreads();
   }
-  // The two lanes of a row (lane/32 = 0, 1) combine.
-  sq += __shfl_xor(sq, 32, 64);
-  if (lane < brows) {
-    if (gridDim.y == 1) p.out[i0 + lane] = (float)sqrt(sq);
-    else p.part[(int64_t)blockIdx.y * N + i0 + lane] = sq;
+  if constexpr (MODE == 0) {
+    // The two lanes of a row (lane/32 = 0, 1) combine.
+    sq += __shfl_xor(sq, 32, 64);
+    if (lane < brows) {
+      if (gridDim.y == 1) p.out[i0 + lane] = (float)sqrt(sq);
+      else p.part[(int64_t)blockIdx.y * N + i0 + lane] = sq;
+    }
+  } else if (p.epart) {
+    const double t = wave_sum(sq);
+    if (lane == 0) p.epart[((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave] = t;
   }
+}
+
+// rmse = sqrt(sum of the n partials / count): each thread adds a strided
+// subset in index order, then the 256 sums combine in a fixed tree.
+__global__ __launch_bounds__(256) void rmse_finish_kernel(const double* __restrict__ part,
+                                                          int64_t n, double count,
+                                                          double* __restrict__ out) {
+  __shared__ double red[256];
+  double t = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) t += part[i];
+  red[threadIdx.x] = t;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = sqrt(red[0] / count);
 }
 
 // out[i] = sqrt of the column-split partials of row i, summed in split order.

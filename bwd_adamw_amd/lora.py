@@ -20,7 +20,7 @@ __all__ = [
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
-    "lora_scaling", "lora_lr_at",
+    "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group", "EXPORTS",
 ]
@@ -36,7 +36,7 @@ EXPORTS = (
     "lora_workspace_bytes", "lora_forward", "lora_backward",
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
-    "lora_scaling", "lora_lr_at",
+    "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
 )
@@ -97,6 +97,8 @@ def lib() -> C.CDLL:
             "lora_dropout_mask": (I32, [P, I64, I64, P, P]),
             "lora_dora_row_norms_workspace_bytes": (SZ, [P]),
             "lora_dora_row_norms": (I32, [P, P, P, SZ, P]),
+            "lora_merge_workspace_bytes": (SZ, [P]),
+            "lora_merge": (I32, [P, P, I32, P, P, SZ, P]),
             "lora_scaling": (C.c_double, [C.c_double, I64, I32]),
             "lora_lr_at": (C.c_double, [I64, C.c_double, I32, I64, I64, C.c_double]),
             "lora_status_string": (C.c_char_p, [I32]),
@@ -305,6 +307,30 @@ def lora_dora_row_norms(lin: LoraLinear, out_norm, ws=None, stream=None, split=T
     rc = lib().lora_dora_row_norms(C.byref(lin), _ptr(out_norm, "out_norm"),
                                    _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_dora_row_norms", rc)
+
+
+def lora_merge_workspace_bytes(lin: LoraLinear) -> int:
+    return int(lib().lora_merge_workspace_bytes(C.byref(lin)))
+
+
+def lora_merge(lin: LoraLinear, W_out, rmse=None, ws=None, stream=None):
+    """W_out = c (W + s B A) (c = mag/norm for DoRA) as float32 or bfloat16
+    (W_out's dtype).  `rmse` is a device float64 tensor of one element or
+    None; bf16 output needs `ws` (taken from torch's allocator when None)."""
+    if W_out.dtype == torch.float32:
+        od = F32
+    elif W_out.dtype == torch.bfloat16:
+        od = BF16
+    else:
+        raise TypeError(f"W_out must be float32 or bfloat16, got {W_out.dtype}")
+    if rmse is not None and ws is None and od == BF16:
+        ws = torch.empty(max(8, lora_merge_workspace_bytes(lin)), device=W_out.device,
+                         dtype=torch.uint8)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_merge(C.byref(lin), _ptr(W_out, "W_out", None), od,
+                          _ptr(rmse, "rmse", torch.float64), _ptr(ws, "ws", None), ws_bytes,
+                          _stream(stream))
+    _check("lora_merge", rc)
 
 
 def lora_profile_begin(max_launches: int = 100000):

@@ -222,6 +222,23 @@ size_t lora_dora_row_norms_workspace_bytes(const lora_linear* lin);
 int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Merge for export ("8. LoRA Fundamentals": "How it works" for the
+ * effective weight W + scale*B*A merged in F32 and DoRA's row rescale;
+ * "Profiling with --jfr" for the RMSE a merge reports):
+ *   W_out[i][k] = c_i * (W[i][k] + scale * (B A)[i][k]),
+ *   c_i = dora_mag[i] / dora_norm[i] when both are set (DoRA), else 1.
+ * out_dtype LORA_F32 stores the float32 values; LORA_BF16 rounds them to
+ * bfloat16, to nearest with ties to even.  W_out is a device [out_dim,
+ * in_dim] array of that type, caller-owned.  When rmse (device double[1]) is
+ * non-NULL it receives sqrt(mean((W_out - merged float32)^2)) over all
+ * elements: 0 for LORA_F32 output; for LORA_BF16 the per-wave sums go to
+ * `workspace` (lora_merge_workspace_bytes(lin) bytes, else LORA_E_WORKSPACE)
+ * and are added in a fixed order.  lin->A == lin->B == NULL merges W alone
+ * (a conversion).  Shapes as for lora_dora_row_norms. */
+size_t lora_merge_workspace_bytes(const lora_linear* lin);
+int lora_merge(const lora_linear* lin, void* W_out, int out_dtype, double* rmse, void* workspace,
+               size_t workspace_bytes, void* stream);
+
 /* Diagnostics: launch timing.  lora_profile_begin opens a profile that can
  * hold max_launches launches (it creates that many HIP event pairs once and
  * keeps them); until lora_profile_end, each kernel launch of the library is

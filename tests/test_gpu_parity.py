@@ -638,3 +638,73 @@ def test_group_rejects_mismatched_linears():
         L.lora_forward_group(lins, cs[0]["X"], Y, U, None, None, ws)
     assert e.value.status == -2
     assert all(torch.count_nonzero(y).item() == 0 for y in Y)
+
+
+# ---------------------------------------------------------- merge -----------
+MERGE_CASES = [
+    # W dtype, N, K, r, DoRA
+    ("f32", 100, 84, 8, False),       # ragged rows, partial last chunk
+    ("bf16", 45, 100, 12, True),      # rows not 16-byte aligned: element loads and stores
+    ("bf16", 264, 136, 64, False),
+    ("f32", 33, 4097, 128, True),     # rank 128, odd K
+    ("bf16", 2560, 9728, 64, True),   # DoRA workload shapes (wdown, wup)
+    ("bf16", 9728, 2560, 32, False),
+]
+
+
+@pytest.mark.parametrize("wd_,N,K,r,dora", MERGE_CASES,
+                         ids=[f"{c[0]}-{c[1]}x{c[2]}-r{c[3]}{'-dora' if c[4] else ''}" for c in MERGE_CASES])
+def test_merge_parity(wd_, N, K, r, dora):
+    c = _linear_case(8, K, N, r, wd_, seed=13, b_std=0.05)
+    g = _gpu(c)
+    s = 1.3
+    mag = nrm = None
+    if dora:
+        mag = torch.rand(N, device=DEV) + 0.5
+        nrm = torch.empty(N, device=DEV)
+        L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], s, 8), nrm)
+    lin = L.make_linear(g["Wq"], g["A"], g["B"], s, 8, mag, nrm)
+    W, A, B = np64(c["W"]), np64(c["A"]), np64(c["B"])
+    m64 = np64(mag) if dora else None
+    n64 = np64(nrm) if dora else None
+    # float32 output
+    out = torch.full((N, K), float("nan"), device=DEV)
+    rm = torch.full((1,), float("nan"), device=DEV, dtype=torch.float64)
+    L.lora_merge(lin, out, rm)
+    ref, _ = O.merge(W, A, B, s, m64, n64, "f32")
+    assert rel_err(out, ref) <= 1e-5
+    assert rm.item() == 0.0
+    # bfloat16 output: each element within one bf16 step of the oracle's
+    # rounding (the float32 sums may sit on the other side of a tie), plus
+    # the float32 sum's own error, about 2e-6 of the matrix scale (it shows
+    # where W and s B A nearly cancel); the RMSE of the rounding close to the
+    # oracle's
+    outb = torch.full((N, K), float("nan"), device=DEV, dtype=torch.bfloat16)
+    L.lora_merge(lin, outb, rm)
+    refb, rmse = O.merge(W, A, B, s, m64, n64, "bf16")
+    got = np64(outb.float())
+    step = np.abs(refb) * 2.0**-7 + 2e-6 * np.abs(ref).max()
+    assert np.all(np.abs(got - refb) <= step)
+    assert (got != refb).mean() < 1e-3
+    assert abs(rm.item() - rmse) <= 1e-3 * rmse
+
+
+def test_merge_of_zero_adapter_is_exact():
+    c = _linear_case(8, 2560, 1024, 32, "bf16", seed=14)
+    g = _gpu(c)
+    lin = L.make_linear(g["Wq"], g["A"], torch.zeros_like(g["B"]), 2.0, 8)
+    outb = torch.empty_like(g["Wq"])
+    rm = torch.full((1,), float("nan"), device=DEV, dtype=torch.float64)
+    L.lora_merge(lin, outb, rm)
+    assert torch.equal(outb, g["Wq"]) and rm.item() == 0.0
+
+
+def test_merge_checks_its_workspace():
+    c = _linear_case(8, 512, 64, 8, "bf16", seed=15)
+    g = _gpu(c)
+    lin = L.make_linear(g["Wq"], g["A"], g["B"], 1.0, 8)
+    need = L.lora_merge_workspace_bytes(lin)
+    outb = torch.empty_like(g["Wq"])
+    rm = torch.zeros(1, device=DEV, dtype=torch.float64)
+    with pytest.raises(L.LoraError):
+        L.lora_merge(lin, outb, rm, torch.empty(need - 8, device=DEV, dtype=torch.uint8))
