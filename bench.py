@@ -48,7 +48,7 @@ def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
             inp = WL.linear_inputs(cfg, l, pj, chunks=0, tokens=T, device=device)
             Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"])
     model = S.FrozenModel(cfg, Wq)
-    trainer = S.Trainer(cfg, model, tokens=T, device=device)
+    trainer = S.Trainer(cfg, model, tokens=T, device=device, slots=cfg.slots)
     slots, inputs = [], []
     for si in range(cfg.slots):
         A, B = {}, {}
@@ -80,8 +80,7 @@ def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
 
 def run_steps(trainer, slots, inputs, n):
     for _ in range(n):
-        for slot, chunks in zip(slots, inputs):
-            st = trainer.step(slot, chunks)
+        for st in trainer.step_slots(slots, inputs):
             if st.vetoed:
                 raise RuntimeError("non-finite gradient in a synthetic run")
 

@@ -33,27 +33,53 @@
 
 namespace lora {
 
+// Per-slot operands of one product.  Adapter slots that share W run as one
+// product over their stacked rows: rows [i*slot_rows, (i+1)*slot_rows) of the
+// bf16 operand and of C belong to slot i, with its own LoRA factors, dropout
+// keys and outputs.  A single linear is one slot.
+constexpr int BF16_MAX_SLOTS = 4;
+struct Bf16Slot {
+  LoraOperand xa;          // U (fwd) or V (dx), float32 [rows, r], possibly as partials
+  const float* XB;         // fwd: B_lora [Nc, r];  dx: A_lora [r, Nc]  (float32)
+  float xs;                // LoRA scale s
+  DropParams drop;         // dx: mask of the LoRA term at (slot row, n)
+  float* C;                // [rows, Nc]
+  float* C2;               // fwd DoRA: Z, or NULL
+  const float* cn;         // fwd DoRA column scale cn/cd, or NULL
+  const float* cd;
+};
+
 struct GemmBf16Args {
-  const uint16_t* A;       // [M, Kc] bf16, contraction contiguous
+  const uint16_t* A;       // [M, Kc] bf16, contraction contiguous (all slots stacked)
   int64_t lda;
   const uint16_t* B;       // fwd: W [Nc, Kc];  dx: W [Kc, Nc]   (bf16)
   int64_t ldb;
   int64_t M, Nc, Kc;
-  LoraOperand xa;          // U (fwd) or V (dx), float32 [M, r], possibly as partials
-  const float* XB;         // fwd: B_lora [Nc, r];  dx: A_lora [r, Nc]  (float32)
   int64_t r;
-  float xs;
-  DropParams drop;
-  float* C;
-  float* C2;
-  const float* cn;
-  const float* cd;
+  Bf16Slot sl[BF16_MAX_SLOTS];
+  int nslot;               // >= 1
+  int64_t slot_rows;       // rows per slot when nslot > 1 (a multiple of the tile rows)
   int64_t ksplit;          // contraction length per split (multiple of BK)
   int nsplit;              // splits of the contraction across blocks
   float* part;             // [nsplit, M, Nc] partials when nsplit > 1
 };
 
-constexpr bool kBf16ReadsFirst = false;
+// The fields of slot `slot`, chosen scalar by scalar among constant-offset
+// reads of the argument block: indexing it by a runtime value, or copying
+// one of its structs whole, makes the compiler copy the block to scratch.
+LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
+  Bf16Slot so;
+#define LORA_SEL(f)                          \
+  so.f = p.sl[0].f;                          \
+  _Pragma("unroll") for (int i = 1; i < BF16_MAX_SLOTS; ++i) \
+    if (i == slot) so.f = p.sl[i].f;
+  LORA_SEL(xa.p) LORA_SEL(xa.stride) LORA_SEL(xa.nparts) LORA_SEL(xa.out)
+  LORA_SEL(XB) LORA_SEL(xs)
+  LORA_SEL(drop.base) LORA_SEL(drop.thr) LORA_SEL(drop.keep) LORA_SEL(drop.on)
+  LORA_SEL(C) LORA_SEL(C2) LORA_SEL(cn) LORA_SEL(cd)
+#undef LORA_SEL
+  return so;
+}
 
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
@@ -96,8 +122,11 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   const int64_t kbeg = (int64_t)split * p.ksplit;
   const int64_t kend = min(p.Kc, kbeg + p.ksplit);
   const int hl = lane >> 5, l32 = lane & 31;
+  // The slot's fields are selected only where they are used (LoRA term,
+  // epilogue), so that none of them is live across the main loop.
+  const int slot = p.nslot > 1 ? (int)(m0 / p.slot_rows) : 0;
+  const int64_t moff = (int64_t)slot * p.slot_rows * (p.nslot > 1);   // slot's first row
   const bool lora = split == 0 && p.r > 0;
-  const bool store_xa = p.xa.out != nullptr && n0 == 0 && split == 0;
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -207,30 +236,6 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // output tile, lane half hl holding indices hl*HALF .. of each LD-wide row.
   auto compute = [&](const uint16_t* Ab, const uint16_t* Bb, auto LD, auto HALF, auto STEPS) {
     constexpr int ld = decltype(LD)::value, half = decltype(HALF)::value;
-    if constexpr (kBf16ReadsFirst && decltype(STEPS)::value <= 2) {
-      // Every operand of the staged K-step is read from LDS before the
-      // first MFMA, so LDS latency overlaps the MFMAs instead of preceding
-      // each pair of them.
-      constexpr int S = decltype(STEPS)::value;
-      u32x4 av[S][MI], bv[S][NI];
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-          av[s][i] = *reinterpret_cast<const u32x4*>(&Ab[(wm0 + i * 32 + l32) * ld + half * hl + 8 * s]);
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-          bv[s][j] = *reinterpret_cast<const u32x4*>(&Bb[(wn0 + j * 32 + l32) * ld + half * hl + 8 * s]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j) acc[i][j] = mfma32x32x16_bf16(av[s][i], bv[s][j], acc[i][j]);
-      return;
-    }
 #pragma unroll
     for (int s = 0; s < decltype(STEPS)::value; ++s) {
       u32x4 av[MI], bv[NI];
@@ -252,6 +257,8 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // LoRA contraction over the rank: float32 operands rounded to bf16 in LDS,
   // in 64-wide K-steps over the same LDS.
   auto lora_contraction = [&]() {
+    const Bf16Slot so = bf16_slot(p, slot);
+    const bool store_xa = so.xa.out != nullptr && n0 == 0 && split == 0;
     uint16_t* La = smem;
     uint16_t* Lb = smem + BM * LROW;
     for (int64_t k0 = 0; k0 < p.r; k0 += LBK) {
@@ -262,10 +269,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
         const int64_t gm = m0 + row, gk = k0 + 4 * c4;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (gm < p.M && gk < p.r) {
-          const int64_t i = gm * p.r + gk;
-          v = sum_parts4(p.xa.p, p.xa.stride, p.xa.nparts, i);
-          if (store_xa && p.xa.nparts > 1) *reinterpret_cast<f32x4*>(p.xa.out + i) = v;
-          v *= p.xs;
+          const int64_t i = (gm - moff) * p.r + gk;
+          v = sum_parts4(so.xa.p, so.xa.stride, so.xa.nparts, i);
+          if (store_xa && so.xa.nparts > 1) *reinterpret_cast<f32x4*>(so.xa.out + i) = v;
+          v *= so.xs;
         }
         u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2*>(&La[row * LROW + 4 * c4]) = b;
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
           const int row = f / (LBK / 4), c4 = f % (LBK / 4);
           const int64_t gn = n0 + row, gk = k0 + 4 * c4;
           f32x4 v = {0.f, 0.f, 0.f, 0.f};
-          if (gn < p.Nc && gk < p.r) v = *reinterpret_cast<const f32x4*>(p.XB + gn * p.r + gk);
+          if (gn < p.Nc && gk < p.r) v = *reinterpret_cast<const f32x4*>(so.XB + gn * p.r + gk);
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2*>(&Lb[row * LROW + 4 * c4]) = b;
         }
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
           const int n = f % BN, kk = f / BN;
           const int64_t gn = n0 + n, gk = k0 + kk;
           float v = 0.f;
-          if (gn < p.Nc && gk < p.r) v = p.XB[gk * p.Nc + gn];
+          if (gn < p.Nc && gk < p.r) v = so.XB[gk * p.Nc + gn];
           Lb[n * LROW + kk] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
@@ -299,17 +306,18 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 
   if (!FWD && lora) {
     lora_contraction();
-    if (p.drop.on) {
+    const Bf16Slot so = bf16_slot(p, slot);
+    if (so.drop.on) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
-          const uint64_t rk = drop_row(p.drop, gm);
+          const uint64_t rk = drop_row(so.drop, gm - moff);
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
             const int64_t gn = n0 + wn0 + j * 32 + l32;
-            acc[i][j][v] *= drop_mul(p.drop, rk, gn);
+            acc[i][j][v] *= drop_mul(so.drop, rk, gn);
           }
         }
     }
@@ -356,26 +364,47 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 
   if (FWD && lora) lora_contraction();
 
+  const Bf16Slot so = bf16_slot(p, slot);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int64_t gn = n0 + wn0 + j * 32 + l32;
       if (gn >= p.Nc) continue;
-      const float c = (p.nsplit == 1 && p.cn) ? p.cn[gn] / p.cd[gn] : 1.0f;
+      const float c = (p.nsplit == 1 && so.cn) ? so.cn[gn] / so.cd[gn] : 1.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
         if (gm >= p.M) continue;
         const float x = acc[i][j][v];
         if (p.nsplit == 1) {
-          p.C[gm * p.Nc + gn] = x * c;
-          if (p.C2) p.C2[gm * p.Nc + gn] = x;
+          so.C[(gm - moff) * p.Nc + gn] = x * c;
+          if (so.C2) so.C2[(gm - moff) * p.Nc + gn] = x;
         } else {
           p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
         }
       }
     }
+}
+
+// Sum of the split partials in split order, then the unsplit kernel's
+// epilogue, row by row into the row's slot (Z = sum; Y = sum * cn/cd).
+__global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(GemmBf16Args p) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t total = p.M * p.Nc;
+  if (i4 >= total) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(p.part + i4);
+  for (int q = 1; q < p.nsplit; ++q) s += *reinterpret_cast<const f32x4*>(p.part + q * total + i4);
+  const int64_t m = i4 / p.Nc, n = i4 % p.Nc;   // Nc is a multiple of 4
+  const int slot = p.nslot > 1 ? (int)(m / p.slot_rows) : 0;
+  const Bf16Slot so = bf16_slot(p, slot);
+  const int64_t o = (m - (int64_t)slot * p.slot_rows * (p.nslot > 1)) * p.Nc + n;
+  if (so.C2) *reinterpret_cast<f32x4*>(so.C2 + o) = s;
+  if (so.cn) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] *= so.cn[n + e] / so.cd[n + e];
+  }
+  *reinterpret_cast<f32x4*>(so.C + o) = s;
 }
 
 }  // namespace lora

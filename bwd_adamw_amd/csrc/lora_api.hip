@@ -208,16 +208,20 @@ size_t carve(size_t& off, size_t bytes) {
   return at;
 }
 
-Layout make_layout(const lora_linear* L) {
+// stack > 1: the linear is one of `stack` slots whose frozen products run
+// stacked; its bf16 operand copies and product partials then live in the
+// stacked region (StackLayout) instead.
+Layout make_layout(const lora_linear* L, int stack = 1) {
   Layout y;
   const int64_t T = L->tokens, K = L->in_dim, N = L->out_dim, r = L->rank;
   const bool bf = L->w_dtype == LORA_BF16;
+  const bool own = stack <= 1;
   y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, SK_C);
   y.strips = cdiv(N, SK_C);
   y.k3 = plan_rows(T, y.strips);
   y.k4 = plan_rows(T, cdiv(K, SK_C));
-  y.gf = plan_gemm(T, N, K, bf, false);
-  y.gd = plan_gemm(T, K, N, bf, true);
+  y.gf = plan_gemm(stack * T, N, K, bf, false);
+  y.gd = plan_gemm(stack * T, K, N, bf, true);
   // Beside the split GEMM the down projection needs no parallelism of its
   // own: 256 columns per block keeps its partials few for the epilogue.
   if (use_split_path(y.gf, r, bf)) {
@@ -228,19 +232,43 @@ Layout make_layout(const lora_linear* L) {
   y.vreduce = y.strips > 1 && vbytes * (cdiv(K, y.gd.bn) + cdiv(K, SK_C)) > kPartialRereadBytes;
   size_t off = 0;
   y.upart = carve(off, y.down.n > 1 ? sizeof(float) * y.down.n * T * r : 0);
-  y.xbf = carve(off, bf ? sizeof(uint16_t) * T * K : 0);
-  y.gfpart = carve(off, y.gf.k.n > 1 ? sizeof(float) * y.gf.k.n * T * N : 0);
+  y.xbf = carve(off, (bf && own) ? sizeof(uint16_t) * T * K : 0);
+  y.gfpart = carve(off, (own && y.gf.k.n > 1) ? sizeof(float) * y.gf.k.n * T * N : 0);
   y.fwd_bytes = off;
   off = 0;
   y.vpart = carve(off, y.strips > 1 ? sizeof(float) * y.strips * T * r : 0);
   y.v = carve(off, sizeof(float) * T * r);
   y.dbpart = carve(off, y.k3.n > 1 ? sizeof(float) * y.k3.n * N * r : 0);
   y.dmpart = carve(off, (L->dora_mag && y.k3.n > 1) ? sizeof(float) * y.k3.n * N : 0);
-  y.gbf = carve(off, bf ? sizeof(uint16_t) * T * N : 0);
-  y.gdpart = carve(off, y.gd.k.n > 1 ? sizeof(float) * y.gd.k.n * T * K : 0);
+  y.gbf = carve(off, (bf && own) ? sizeof(uint16_t) * T * N : 0);
+  y.gdpart = carve(off, (own && y.gd.k.n > 1) ? sizeof(float) * y.gd.k.n * T * K : 0);
   y.dapart = carve(off, y.k4.n > 1 ? sizeof(float) * y.k4.n * r * K : 0);
   y.bwd_bytes = off;
   return y;
+}
+
+// The stacked region of n bf16 slots: the slots' bf16 copies of X (forward)
+// and of g (backward), one above another, and the stacked products' split
+// partials.
+struct StackLayout {
+  GemmPlan gf, gd;
+  size_t xbf, gfpart, fwd_bytes;
+  size_t gbf, gdpart, bwd_bytes;
+};
+StackLayout make_stack_layout(const lora_linear* L, int n) {
+  StackLayout z;
+  const int64_t M = n * L->tokens, K = L->in_dim, N = L->out_dim;
+  z.gf = plan_gemm(M, N, K, true, false);
+  z.gd = plan_gemm(M, K, N, true, true);
+  size_t off = 0;
+  z.xbf = carve(off, sizeof(uint16_t) * M * K);
+  z.gfpart = carve(off, z.gf.k.n > 1 ? sizeof(float) * z.gf.k.n * M * N : 0);
+  z.fwd_bytes = off;
+  off = 0;
+  z.gbf = carve(off, sizeof(uint16_t) * M * N);
+  z.gdpart = carve(off, z.gd.k.n > 1 ? sizeof(float) * z.gd.k.n * M * K : 0);
+  z.bwd_bytes = off;
+  return z;
 }
 
 int check_linear(const lora_linear* L) {
@@ -355,9 +383,8 @@ void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStr
   if (g.k.n > 1) {
     const int64_t n4 = cdiv(a.M * a.Nc, 4);
     prof::Scope ps("splitk_reduce", a.M, a.Nc, g.k.n, 0.0,
-                   4.0 * a.M * a.Nc * (g.k.n + (a.C2 ? 2 : 1)));
-    launch(splitk_reduce_kernel, dim3((unsigned)cdiv(n4, 256)), st, ps, (const float*)a.part,
-           g.k.n, a.M, a.Nc, a.C, a.C2, a.cn, a.cd);
+                   4.0 * a.M * a.Nc * (g.k.n + (a.sl[0].C2 ? 2 : 1)));
+    launch(splitk_reduce_bf16_kernel, dim3((unsigned)cdiv(n4, 256)), st, ps, a);
   }
 }
 
@@ -366,7 +393,7 @@ void launch_gemm_bf16_tiles(const GemmPlan& g, bool fwd, const GemmBf16Args& a, 
   prof::Scope ps(fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
                  2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
                  2.0 * (a.M * a.Kc + a.Nc * a.Kc) +
-                     4.0 * a.M * a.Nc * (g.k.n > 1 ? g.k.n : (a.C2 ? 2 : 1)));
+                     4.0 * a.M * a.Nc * (g.k.n > 1 ? g.k.n : (a.sl[0].C2 ? 2 : 1)));
   const Bf16Cfg& c = kBf16Cfg[g.cfg];
   const bool exact = a.M % c.bm == 0 && a.Nc % c.bn == 0 && a.Kc % c.bk == 0;
 #define LORA_BF16_TILE(i, BM_, BN_, NT_, WGM_, BK_, D_, DIRS_, AF_, BF_, AD_, BD_)            \
@@ -418,14 +445,31 @@ struct FwdJob {
   float *Y, *Z, *gfpart;
 };
 
+// One linear's operands of the bf16 forward product.
+Bf16Slot bf16_fwd_slot(const FwdJob& j) {
+  Bf16Slot so;
+  memset(&so, 0, sizeof(so));
+  so.xa = j.xa;
+  so.XB = j.lin->B;
+  so.xs = j.lin->scale;
+  so.C = j.Y;
+  so.C2 = j.Z;
+  so.cn = j.lin->dora_mag;
+  so.cd = j.lin->dora_norm;
+  return so;
+}
+
+// stack > 1: one of `stack` stacked slots; bf is this slot's rows of the
+// stacked bf16 copy of X.
 int prepare_fwd(const lora_linear* lin, const float* X, float* Y, float* U, float* Z,
-                const lora_dropout* drop, void* ws, size_t ws_bytes, FwdJob& j) {
+                const lora_dropout* drop, void* ws, size_t ws_bytes, FwdJob& j, int stack = 1,
+                uint16_t* bf_rows = nullptr) {
   int rc = check_linear(lin);
   if (rc) return rc;
   if (!X || !Y || !U) return LORA_E_INVALID;
   if (!al16(X) || !al16(Y) || !al16(U) || (Z && !al16(Z))) return LORA_E_ALIGN;
   if (!drop_valid(drop)) return LORA_E_INVALID;
-  const Layout y = make_layout(lin);
+  const Layout y = make_layout(lin, stack);
   if (y.fwd_bytes && (!ws || ws_bytes < y.fwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
   const bool bf = lin->w_dtype == LORA_BF16;
@@ -435,8 +479,8 @@ int prepare_fwd(const lora_linear* lin, const float* X, float* Y, float* U, floa
   j.T = T; j.K = K; j.N = N; j.r = r;
   j.gf = y.gf;
   j.X = X; j.Y = Y; j.Z = Z;
-  j.Xbf = bf ? (uint16_t*)(w + y.xbf) : nullptr;
-  j.gfpart = y.gf.k.n > 1 ? (float*)(w + y.gfpart) : nullptr;
+  j.Xbf = bf ? (stack > 1 ? bf_rows : (uint16_t*)(w + y.xbf)) : nullptr;
+  j.gfpart = (stack <= 1 && y.gf.k.n > 1) ? (float*)(w + y.gfpart) : nullptr;
   DownArgs& da = j.da;
   da.X = X; da.T = T; da.K = K; da.A = lin->A; da.r = r; da.drop = make_drop(drop);
   da.ksplit = y.down.len; da.nsplit = y.down.n; da.Upart = Upart; da.U = U; da.Xbf = j.Xbf;
@@ -513,24 +557,26 @@ void launch_fwd_split(const FwdJob* J, hipStream_t st) {
   launch(fwd_epi_kernel<NG>, dim3((unsigned)b), st, ps, ep);
 }
 
+// U = X~ A^T, split over K (and the bf16 copy of X); the GEMM sums the
+// splits while staging U and stores the summed U.
+void launch_fwd_down(const FwdJob& j, hipStream_t st) {
+  prof::Scope ps("down_u", j.T, j.r, j.K, j.down_flops, j.down_bytes);
+  const dim3 grid((unsigned)cdiv(j.T, SK_T), (unsigned)j.da.nsplit);
+  LORA_RP_DISPATCH(rank_pad(j.r), launch(down_kernel<RP>, grid, st, ps, j.da));
+}
+
 void launch_fwd_plain(const FwdJob& j, hipStream_t st) {
   const lora_linear* lin = j.lin;
   const int64_t T = j.T, K = j.K, N = j.N, r = j.r;
-  // U = X~ A^T, split over K; the GEMM sums the splits while staging U and
-  // stores the summed U.
-  {
-    prof::Scope ps("down_u", T, r, K, j.down_flops, j.down_bytes);
-    const dim3 grid((unsigned)cdiv(T, SK_T), (unsigned)j.da.nsplit);
-    LORA_RP_DISPATCH(rank_pad(r), launch(down_kernel<RP>, grid, st, ps, j.da));
-  }
+  launch_fwd_down(j, st);
   // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
   if (lin->w_dtype == LORA_BF16) {
     GemmBf16Args a;
     memset(&a, 0, sizeof(a));
     a.A = j.Xbf; a.lda = K; a.B = (const uint16_t*)lin->W; a.ldb = K;
-    a.M = T; a.Nc = N; a.Kc = K;
-    a.xa = j.xa; a.XB = lin->B; a.r = r; a.xs = lin->scale;
-    a.C = j.Y; a.C2 = j.Z; a.cn = lin->dora_mag; a.cd = lin->dora_norm;
+    a.M = T; a.Nc = N; a.Kc = K; a.r = r;
+    a.nslot = 1;
+    a.sl[0] = bf16_fwd_slot(j);
     a.ksplit = j.gf.k.len; a.nsplit = j.gf.k.n; a.part = j.gfpart;
     launch_gemm_bf16(j.gf, true, a, st);
   } else {
@@ -576,9 +622,24 @@ struct BwdJob {
   int rp;
 };
 
+// One linear's operands of the bf16 dX product.
+Bf16Slot bf16_dx_slot(const BwdJob& j) {
+  Bf16Slot so;
+  memset(&so, 0, sizeof(so));
+  so.xa = j.xv;
+  so.XB = j.lin->A;
+  so.xs = j.lin->scale;
+  so.drop = j.d;
+  so.C = j.dX;
+  return so;
+}
+
+// stack > 1: one of `stack` stacked slots; bf is this slot's rows of the
+// stacked bf16 copy of g.
 int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const float* U,
                 const float* Z, float* dX, float* dA, float* dB, float* dMag, int accumulate,
-                const lora_dropout* drop, void* ws, size_t ws_bytes, BwdJob& j) {
+                const lora_dropout* drop, void* ws, size_t ws_bytes, BwdJob& j, int stack = 1,
+                uint16_t* bf_rows = nullptr) {
   int rc = check_linear(lin);
   if (rc) return rc;
   if (!X || !dY || !U || !dA || !dB) return LORA_E_INVALID;
@@ -587,7 +648,7 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   const bool dora = lin->dora_mag != nullptr;
   if (dMag && (!dora || !Z)) return LORA_E_INVALID;
   if (!drop_valid(drop)) return LORA_E_INVALID;
-  const Layout y = make_layout(lin);
+  const Layout y = make_layout(lin, stack);
   if (y.bwd_bytes && (!ws || ws_bytes < y.bwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
   const bool bf = lin->w_dtype == LORA_BF16;
@@ -610,7 +671,7 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   o.dB = dB;
   o.dmpart = (dMag && y.k3.n > 1) ? (float*)(w + y.dmpart) : nullptr;
   o.dm = dMag;
-  o.gbf = (bf && dX) ? (uint16_t*)(w + y.gbf) : nullptr;
+  o.gbf = (bf && dX) ? (stack > 1 ? bf_rows : (uint16_t*)(w + y.gbf)) : nullptr;
   o.scale = lin->scale;
   o.accumulate = acc;
   const float* Zin = dMag ? Z : nullptr;
@@ -763,29 +824,51 @@ void launch_bwd_split(const BwdJob* J, hipStream_t st) {
   if (na) launch_reduce(ja, na, st);
 }
 
-void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
-  const lora_linear* lin = jb.lin;
+// One pass over dY: V, dB, dm and the bf16 copy of g (then V's partials
+// summed when the plan says so).
+void launch_bwd_k3(const BwdJob& jb, hipStream_t st) {
   const Layout& y = jb.y;
-  const int64_t T = jb.T, K = jb.K, N = jb.N, r = jb.r;
-  const bool bf = lin->w_dtype == LORA_BF16;
-  const int rp = jb.rp;
+  const int64_t T = jb.T, N = jb.N, r = jb.r;
   {
     prof::Scope ps("k3_v_db", T, N, r, jb.k3_flops, jb.k3_bytes);
     const dim3 grid((unsigned)y.strips, (unsigned)y.k3.n);
-    LORA_RP_DISPATCH(rp, launch(k3_kernel<RP>, grid, st, ps, jb.ka));
+    LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP>, grid, st, ps, jb.ka));
   }
   if (y.vreduce) {
     RedJob jv = {jb.o.Vpart, jb.o.V, nullptr, T * r, 1, (int)y.strips, 0, 1.0f};
     launch_reduce(&jv, 1, st);
   }
+}
+
+// dA = s V^T X~, then the fixed-order reductions of the token-range splits.
+void launch_bwd_k4(const BwdJob& jb, hipStream_t st) {
+  const Layout& y = jb.y;
+  {
+    prof::Scope ps("k4_da", jb.T, jb.r, jb.K, jb.k4_flops, jb.k4_bytes);
+    const dim3 grid((unsigned)cdiv(jb.K, SK_C), (unsigned)y.k4.n);
+    LORA_RP_DISPATCH(jb.rp, launch(k4_kernel<RP>, grid, st, ps, jb.k4a));
+  }
+  RedJob jobs[4];
+  int nj = 0;
+  for (int i = 0; i < jb.nj; ++i) jobs[nj++] = jb.jobs[i];
+  if (jb.has_ja) jobs[nj++] = jb.ja;
+  if (nj) launch_reduce(jobs, nj, st);
+}
+
+void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
+  const lora_linear* lin = jb.lin;
+  const Layout& y = jb.y;
+  const int64_t T = jb.T, K = jb.K, N = jb.N, r = jb.r;
+  const bool bf = lin->w_dtype == LORA_BF16;
+  launch_bwd_k3(jb, st);
   if (jb.dX) {
     if (bf) {
       GemmBf16Args a;
       memset(&a, 0, sizeof(a));
       a.A = jb.o.gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
-      a.M = T; a.Nc = K; a.Kc = N;
-      a.xa = jb.xv; a.XB = lin->A; a.r = r; a.xs = lin->scale; a.drop = jb.d;
-      a.C = jb.dX;
+      a.M = T; a.Nc = K; a.Kc = N; a.r = r;
+      a.nslot = 1;
+      a.sl[0] = bf16_dx_slot(jb);
       a.ksplit = y.gd.k.len; a.nsplit = y.gd.k.n;
       a.part = y.gd.k.n > 1 ? (float*)(jb.w + y.gdpart) : nullptr;
       launch_gemm_bf16(y.gd, false, a, st);
@@ -802,16 +885,7 @@ void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
       launch_gemm_f32(y.gd, false, a, st);
     }
   }
-  {
-    prof::Scope ps("k4_da", T, r, K, jb.k4_flops, jb.k4_bytes);
-    const dim3 grid((unsigned)cdiv(K, SK_C), (unsigned)y.k4.n);
-    LORA_RP_DISPATCH(rp, launch(k4_kernel<RP>, grid, st, ps, jb.k4a));
-  }
-  RedJob jobs[4];
-  int nj = 0;
-  for (int i = 0; i < jb.nj; ++i) jobs[nj++] = jb.jobs[i];
-  if (jb.has_ja) jobs[nj++] = jb.ja;
-  if (nj) launch_reduce(jobs, nj, st);
+  launch_bwd_k4(jb, st);
 }
 
 // Linears of a group read one X: equal token count, input width and dtype.
@@ -823,6 +897,39 @@ int check_group(int n, const lora_linear* lins) {
     if (lins[i].w_dtype != lins[0].w_dtype) return LORA_E_DTYPE;
   }
   return LORA_OK;
+}
+
+// Slots: adapters over one W with equal shapes (each has its own data,
+// factors, dropout keys and DoRA magnitude).
+int check_slots(int n, const lora_linear* lins) {
+  const lora_linear& a = lins[0];
+  for (int i = 0; i < n; ++i) {
+    const lora_linear& b = lins[i];
+    const int rc = check_linear(&b);
+    if (rc) return rc;
+    if (b.W != a.W || b.tokens != a.tokens || b.in_dim != a.in_dim || b.out_dim != a.out_dim ||
+        b.rank != a.rank)
+      return LORA_E_SHAPE;
+    if (b.w_dtype != a.w_dtype) return LORA_E_DTYPE;
+    if ((b.dora_mag == nullptr) != (a.dora_mag == nullptr)) return LORA_E_INVALID;
+  }
+  return LORA_OK;
+}
+
+// The slots' frozen products run as one product over their stacked rows when
+// W is bf16, there is more than one slot, every slot covers whole 256-row
+// tiles and the stacked operands stay within 32-bit offsets; otherwise the
+// slots run one after another.
+bool slots_stacked(int n, const lora_linear* lins) {
+  const lora_linear& a = lins[0];
+  if (n < 2 || a.w_dtype != LORA_BF16 || a.tokens % 256) return false;
+  const int64_t M = n * a.tokens;
+  return M * a.in_dim < (1ll << 30) && M * a.out_dim < (1ll << 30);
+}
+
+size_t slot_share_bytes(const lora_linear* L, int stack) {
+  const Layout y = make_layout(L, stack);
+  return rup((int64_t)std::max(y.fwd_bytes, y.bwd_bytes), 256);
 }
 
 }  // namespace
@@ -957,6 +1064,131 @@ int lora_backward_group(int n, const lora_linear* lins, const float* X, const fl
       else launch_bwd_plain(jobs[i], st);
     }
   }
+  return hip_status();
+}
+
+static_assert(LORA_MAX_SLOTS <= BF16_MAX_SLOTS, "slot operands of the bf16 products");
+
+size_t lora_slots_workspace_bytes(int n, const lora_linear* lins) {
+  if (n < 1 || n > LORA_MAX_SLOTS || !lins || check_slots(n, lins) != LORA_OK) return 0;
+  size_t total = 0;
+  if (!slots_stacked(n, lins)) {
+    for (int i = 0; i < n; ++i) total += rup((int64_t)lora_workspace_bytes(&lins[i]), 256);
+    return total;
+  }
+  for (int i = 0; i < n; ++i) total += slot_share_bytes(&lins[i], n);
+  const StackLayout z = make_stack_layout(&lins[0], n);
+  return total + std::max(z.fwd_bytes, z.bwd_bytes);
+}
+
+int lora_forward_slots(int n, const lora_linear* lins, const float* const* X, float* const* Y,
+                       float* const* U, float* const* Z, const lora_dropout* drops, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (n < 1 || n > LORA_MAX_SLOTS || !lins || !X || !Y || !U) return LORA_E_INVALID;
+  int rc = check_slots(n, lins);
+  if (rc) return rc;
+  const size_t need = lora_slots_workspace_bytes(n, lins);
+  if (need && (!ws || ws_bytes < need || !al16(ws))) return LORA_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  FwdJob jobs[LORA_MAX_SLOTS];
+  const bool stacked = slots_stacked(n, lins);
+  const int64_t T = lins[0].tokens, K = lins[0].in_dim, N = lins[0].out_dim;
+  size_t off = 0;
+  uint16_t* xbf = nullptr;
+  StackLayout z;
+  if (stacked) {
+    for (int i = 0; i < n; ++i) off += slot_share_bytes(&lins[i], n);
+    z = make_stack_layout(&lins[0], n);
+    xbf = (uint16_t*)((char*)ws + off + z.xbf);
+    off = 0;
+  }
+  for (int i = 0; i < n; ++i) {
+    const size_t wi = stacked ? slot_share_bytes(&lins[i], n)
+                              : (size_t)rup((int64_t)lora_workspace_bytes(&lins[i]), 256);
+    rc = prepare_fwd(&lins[i], X[i], Y[i], U[i], Z ? Z[i] : nullptr, drops ? &drops[i] : nullptr,
+                     (char*)ws + off, wi, jobs[i], stacked ? n : 1,
+                     stacked ? xbf + (int64_t)i * T * K : nullptr);
+    if (rc) return rc;
+    off += wi;
+  }
+  if (!stacked) {
+    for (int i = 0; i < n; ++i) {
+      if (jobs[i].split) launch_fwd_split<1>(&jobs[i], st);
+      else launch_fwd_plain(jobs[i], st);
+    }
+    return hip_status();
+  }
+  for (int i = 0; i < n; ++i) launch_fwd_down(jobs[i], st);
+  GemmBf16Args a;
+  memset(&a, 0, sizeof(a));
+  a.A = xbf; a.lda = K; a.B = (const uint16_t*)lins[0].W; a.ldb = K;
+  a.M = n * T; a.Nc = N; a.Kc = K; a.r = lins[0].rank;
+  a.nslot = n; a.slot_rows = T;
+  for (int i = 0; i < n; ++i) a.sl[i] = bf16_fwd_slot(jobs[i]);
+  a.ksplit = z.gf.k.len; a.nsplit = z.gf.k.n;
+  a.part = z.gf.k.n > 1 ? (float*)((char*)ws + off + z.gfpart) : nullptr;
+  launch_gemm_bf16(z.gf, true, a, st);
+  return hip_status();
+}
+
+int lora_backward_slots(int n, const lora_linear* lins, const float* const* X,
+                        const float* const* dY, const float* const* U, const float* const* Z,
+                        float* const* dX, float* const* dA, float* const* dB, float* const* dMag,
+                        int accumulate, const lora_dropout* drops, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (n < 1 || n > LORA_MAX_SLOTS || !lins || !X || !dY || !U || !dA || !dB)
+    return LORA_E_INVALID;
+  int rc = check_slots(n, lins);
+  if (rc) return rc;
+  if (dX)
+    for (int i = 0; i < n; ++i)
+      if ((dX[i] == nullptr) != (dX[0] == nullptr)) return LORA_E_INVALID;
+  const size_t need = lora_slots_workspace_bytes(n, lins);
+  if (need && (!ws || ws_bytes < need || !al16(ws))) return LORA_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  BwdJob jobs[LORA_MAX_SLOTS];
+  const bool stacked = slots_stacked(n, lins);
+  const int64_t T = lins[0].tokens, K = lins[0].in_dim, N = lins[0].out_dim;
+  const bool want_dx = dX && dX[0];
+  size_t off = 0;
+  uint16_t* gbf = nullptr;
+  StackLayout z;
+  if (stacked) {
+    for (int i = 0; i < n; ++i) off += slot_share_bytes(&lins[i], n);
+    z = make_stack_layout(&lins[0], n);
+    gbf = (uint16_t*)((char*)ws + off + z.gbf);
+    off = 0;
+  }
+  for (int i = 0; i < n; ++i) {
+    const size_t wi = stacked ? slot_share_bytes(&lins[i], n)
+                              : (size_t)rup((int64_t)lora_workspace_bytes(&lins[i]), 256);
+    rc = prepare_bwd(&lins[i], X[i], dY[i], U[i], Z ? Z[i] : nullptr, dX ? dX[i] : nullptr,
+                     dA[i], dB[i], dMag ? dMag[i] : nullptr, accumulate,
+                     drops ? &drops[i] : nullptr, (char*)ws + off, wi, jobs[i], stacked ? n : 1,
+                     stacked ? gbf + (int64_t)i * T * N : nullptr);
+    if (rc) return rc;
+    off += wi;
+  }
+  if (!stacked) {
+    for (int i = 0; i < n; ++i) {
+      if (jobs[i].split) launch_bwd_split<1>(&jobs[i], st);
+      else launch_bwd_plain(jobs[i], st);
+    }
+    return hip_status();
+  }
+  for (int i = 0; i < n; ++i) launch_bwd_k3(jobs[i], st);
+  if (want_dx) {
+    GemmBf16Args a;
+    memset(&a, 0, sizeof(a));
+    a.A = gbf; a.lda = N; a.B = (const uint16_t*)lins[0].W; a.ldb = K;
+    a.M = n * T; a.Nc = K; a.Kc = N; a.r = lins[0].rank;
+    a.nslot = n; a.slot_rows = T;
+    for (int i = 0; i < n; ++i) a.sl[i] = bf16_dx_slot(jobs[i]);
+    a.ksplit = z.gd.k.len; a.nsplit = z.gd.k.n;
+    a.part = z.gd.k.n > 1 ? (float*)((char*)ws + off + z.gdpart) : nullptr;
+    launch_gemm_bf16(z.gd, false, a, st);
+  }
+  for (int i = 0; i < n; ++i) launch_bwd_k4(jobs[i], st);
   return hip_status();
 }
 

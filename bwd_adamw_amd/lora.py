@@ -22,7 +22,8 @@ __all__ = [
     "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
     "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
-    "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group", "EXPORTS",
+    "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
+    "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
@@ -39,6 +40,7 @@ EXPORTS = (
     "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
+    "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
 )
 
 
@@ -107,6 +109,9 @@ def lib() -> C.CDLL:
             "lora_group_workspace_bytes": (SZ, [I32, P]),
             "lora_forward_group": (I32, [I32, P, P, P, P, P, P, P, SZ, P]),
             "lora_backward_group": (I32, [I32, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
+            "lora_slots_workspace_bytes": (SZ, [I32, P]),
+            "lora_forward_slots": (I32, [I32, P, P, P, P, P, P, P, SZ, P]),
+            "lora_backward_slots": (I32, [I32, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -129,6 +134,15 @@ def _ptr(t, name, dtype=torch.float32):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _sized(t, name, need, dtype=torch.float32):
+    """_ptr that also refuses a tensor with fewer than `need` elements: the
+    kernels address every buffer from the linear's sizes alone."""
+    p = _ptr(t, name, dtype)
+    if p is not None and t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call reads or writes {need}")
+    return p
 
 
 def _stream(stream):
@@ -155,6 +169,13 @@ def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None) -> LoraLi
         raise TypeError(f"W must be float32 or bfloat16, got {W.dtype}")
     N, K = W.shape
     r = A.shape[0] if A is not None else 0
+    if A is not None and tuple(A.shape) != (r, K):
+        raise ValueError(f"A must be [{r}, {K}], got {list(A.shape)}")
+    if B is not None and tuple(B.shape) != (N, r):
+        raise ValueError(f"B must be [{N}, {r}], got {list(B.shape)}")
+    for t, nm in ((dora_mag, "dora_mag"), (dora_norm, "dora_norm")):
+        if t is not None and t.numel() != N:
+            raise ValueError(f"{nm} must hold {N} elements, got {t.numel()}")
     return LoraLinear(int(tokens), int(K), int(N), int(r), wd, float(scale),
                       _ptr(W, "W", None), _ptr(A, "A"), _ptr(B, "B"),
                       _ptr(dora_mag, "dora_mag"), _ptr(dora_norm, "dora_norm"))
@@ -188,22 +209,27 @@ def lora_workspace_bytes(lin: LoraLinear) -> int:
 
 def lora_forward(lin, X, Y, U, Z=None, drop=None, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    rc = lib().lora_forward(C.byref(lin), _ptr(X, "X"), _ptr(Y, "Y"), _ptr(U, "U"), _ptr(Z, "Z"),
-                            _ref(drop), _ptr(ws, "ws", None), ws_bytes, _stream(stream))
+    T, K, N, r = lin.tokens, lin.in_dim, lin.out_dim, lin.rank
+    rc = lib().lora_forward(C.byref(lin), _sized(X, "X", T * K), _sized(Y, "Y", T * N),
+                            _sized(U, "U", T * r), _sized(Z, "Z", T * N), _ref(drop),
+                            _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_forward", rc)
 
 
 def lora_backward(lin, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=False, drop=None,
                   ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    rc = lib().lora_backward(C.byref(lin), _ptr(X, "X"), _ptr(dY, "dY"), _ptr(U, "U"),
-                             _ptr(Z, "Z"), _ptr(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
-                             _ptr(dMag, "dMag"), 1 if accumulate else 0, _ref(drop),
+    T, K, N, r = lin.tokens, lin.in_dim, lin.out_dim, lin.rank
+    rc = lib().lora_backward(C.byref(lin), _sized(X, "X", T * K), _sized(dY, "dY", T * N),
+                             _sized(U, "U", T * r), _sized(Z, "Z", T * N), _sized(dX, "dX", T * K),
+                             _sized(dA, "dA", r * K), _sized(dB, "dB", N * r),
+                             _sized(dMag, "dMag", N), 1 if accumulate else 0, _ref(drop),
                              _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_backward", rc)
 
 
 MAX_GROUP = 4
+MAX_SLOTS = 4
 
 
 def _linears(lins):
@@ -211,14 +237,28 @@ def _linears(lins):
     return arr
 
 
-def _ptrs(ts, name, optional=False):
-    """Array of device pointers, or None when every entry is None and the
+# Elements of each per-linear tensor argument, from a linear's sizes.
+_NEED = {
+    "X": lambda l: l.tokens * l.in_dim, "dX": lambda l: l.tokens * l.in_dim,
+    "Y": lambda l: l.tokens * l.out_dim, "Z": lambda l: l.tokens * l.out_dim,
+    "dY": lambda l: l.tokens * l.out_dim, "U": lambda l: l.tokens * l.rank,
+    "dA": lambda l: l.rank * l.in_dim, "dB": lambda l: l.out_dim * l.rank,
+    "dMag": lambda l: l.out_dim,
+}
+
+
+def _ptrs(ts, name, lins, optional=False):
+    """Array of device pointers, one per linear of `lins`, each checked
+    against that linear's sizes; None when every entry is None and the
     argument is optional."""
     if ts is None or (optional and all(t is None for t in ts)):
         if not optional:
             raise ValueError(f"{name} is required")
         return None
-    return (C.c_void_p * len(ts))(*[_ptr(t, f"{name}[{i}]") for i, t in enumerate(ts)])
+    if len(ts) != len(lins):
+        raise ValueError(f"{name} has {len(ts)} entries for {len(lins)} linears")
+    return (C.c_void_p * len(ts))(*[_sized(t, f"{name}[{i}]", _NEED[name](l))
+                                    for i, (t, l) in enumerate(zip(ts, lins))])
 
 
 def _drops(drops, n):
@@ -237,8 +277,9 @@ def lora_forward_group(lins, X, Y, U, Z=None, drops=None, ws=None, stream=None):
     with one tensor per linear."""
     n = len(lins)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    rc = lib().lora_forward_group(n, _linears(lins), _ptr(X, "X"), _ptrs(Y, "Y"), _ptrs(U, "U"),
-                                  _ptrs(Z, "Z", True), _drops(drops, n), _ptr(ws, "ws", None),
+    rc = lib().lora_forward_group(n, _linears(lins), _sized(X, "X", _NEED["X"](lins[0])),
+                                  _ptrs(Y, "Y", lins), _ptrs(U, "U", lins),
+                                  _ptrs(Z, "Z", lins, True), _drops(drops, n), _ptr(ws, "ws", None),
                                   ws_bytes, _stream(stream))
     _check("lora_forward_group", rc)
 
@@ -249,12 +290,45 @@ def lora_backward_group(lins, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=Fal
     argument is a list with one entry per linear."""
     n = len(lins)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    rc = lib().lora_backward_group(n, _linears(lins), _ptr(X, "X"), _ptrs(dY, "dY"),
-                                   _ptrs(U, "U"), _ptrs(Z, "Z", True), _ptrs(dX, "dX", True),
-                                   _ptrs(dA, "dA"), _ptrs(dB, "dB"), _ptrs(dMag, "dMag", True),
+    rc = lib().lora_backward_group(n, _linears(lins), _sized(X, "X", _NEED["X"](lins[0])),
+                                   _ptrs(dY, "dY", lins), _ptrs(U, "U", lins),
+                                   _ptrs(Z, "Z", lins, True), _ptrs(dX, "dX", lins, True),
+                                   _ptrs(dA, "dA", lins), _ptrs(dB, "dB", lins),
+                                   _ptrs(dMag, "dMag", lins, True),
                                    1 if accumulate else 0, _drops(drops, n), _ptr(ws, "ws", None),
                                    ws_bytes, _stream(stream))
     _check("lora_backward_group", rc)
+
+
+def lora_slots_workspace_bytes(lins) -> int:
+    return int(lib().lora_slots_workspace_bytes(len(lins), _linears(lins)))
+
+
+def lora_forward_slots(lins, X, Y, U, Z=None, drops=None, ws=None, stream=None):
+    """Forward of adapter slots over one W: every tensor argument is a list
+    with one entry per slot."""
+    n = len(lins)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_forward_slots(n, _linears(lins), _ptrs(X, "X", lins), _ptrs(Y, "Y", lins),
+                                  _ptrs(U, "U", lins), _ptrs(Z, "Z", lins, True),
+                                  _drops(drops, n), _ptr(ws, "ws", None),
+                                  ws_bytes, _stream(stream))
+    _check("lora_forward_slots", rc)
+
+
+def lora_backward_slots(lins, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=False, drops=None,
+                        ws=None, stream=None):
+    """Backward of adapter slots over one W: every tensor argument is a list
+    with one entry per slot."""
+    n = len(lins)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_backward_slots(n, _linears(lins), _ptrs(X, "X", lins), _ptrs(dY, "dY", lins),
+                                   _ptrs(U, "U", lins), _ptrs(Z, "Z", lins, True),
+                                   _ptrs(dX, "dX", lins, True), _ptrs(dA, "dA", lins),
+                                   _ptrs(dB, "dB", lins), _ptrs(dMag, "dMag", lins, True),
+                                   1 if accumulate else 0, _drops(drops, n), _ptr(ws, "ws", None),
+                                   ws_bytes, _stream(stream))
+    _check("lora_backward_slots", rc)
 
 
 def lora_grad_prepare_workspace_bytes(n: int) -> int:
@@ -279,15 +353,17 @@ def lora_grad_prepare(grads, n_pred_tokens, max_norm, d_scale, d_stats=None, syn
 
 def lora_adamw_step(params, grads, m, v, segments, hp: LoraAdamwHparams, d_scale, stream=None):
     segs = (LoraSegment * len(segments))(*[LoraSegment(int(o), int(c), int(k)) for o, c, k in segments])
-    rc = lib().lora_adamw_step(_ptr(params, "params"), _ptr(grads, "grads"), _ptr(m, "m"),
-                               _ptr(v, "v"), segs, len(segments), C.byref(hp),
-                               _ptr(d_scale, "d_scale"), _stream(stream))
+    end = max((int(o) + int(c) for o, c, _ in segments), default=0)
+    rc = lib().lora_adamw_step(_sized(params, "params", end), _sized(grads, "grads", end),
+                               _sized(m, "m", end), _sized(v, "v", end), segs, len(segments),
+                               C.byref(hp), _sized(d_scale, "d_scale", 1), _stream(stream))
     _check("lora_adamw_step", rc)
 
 
 def lora_dropout_mask(drop: LoraDropout, tokens, in_dim, mask, stream=None):
     rc = lib().lora_dropout_mask(C.byref(drop), int(tokens), int(in_dim),
-                                 _ptr(mask, "mask", torch.uint8), _stream(stream))
+                                 _sized(mask, "mask", int(tokens) * int(in_dim), torch.uint8),
+                                 _stream(stream))
     _check("lora_dropout_mask", rc)
 
 
@@ -304,7 +380,7 @@ def lora_dora_row_norms(lin: LoraLinear, out_norm, ws=None, stream=None, split=T
         if need:
             ws = torch.empty(need, device=out_norm.device, dtype=torch.uint8)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    rc = lib().lora_dora_row_norms(C.byref(lin), _ptr(out_norm, "out_norm"),
+    rc = lib().lora_dora_row_norms(C.byref(lin), _sized(out_norm, "out_norm", lin.out_dim),
                                    _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_dora_row_norms", rc)
 
@@ -327,8 +403,8 @@ def lora_merge(lin: LoraLinear, W_out, rmse=None, ws=None, stream=None):
         ws = torch.empty(max(8, lora_merge_workspace_bytes(lin)), device=W_out.device,
                          dtype=torch.uint8)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    rc = lib().lora_merge(C.byref(lin), _ptr(W_out, "W_out", None), od,
-                          _ptr(rmse, "rmse", torch.float64), _ptr(ws, "ws", None), ws_bytes,
+    rc = lib().lora_merge(C.byref(lin), _sized(W_out, "W_out", lin.out_dim * lin.in_dim, None), od,
+                          _sized(rmse, "rmse", 1, torch.float64), _ptr(ws, "ws", None), ws_bytes,
                           _stream(stream))
     _check("lora_merge", rc)
 

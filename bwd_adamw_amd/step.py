@@ -97,10 +97,14 @@ class StepStats:
 class Trainer:
     """Runs optimizer updates of slots over one frozen model on one stream."""
 
-    def __init__(self, cfg: LoraConfig, model: FrozenModel, tokens=None, device="cuda"):
+    def __init__(self, cfg: LoraConfig, model: FrozenModel, tokens=None, device="cuda", slots=1):
         self.cfg = cfg
         self.model = model
         self.T = cfg.tokens if tokens is None else int(tokens)
+        # Slots over one W run their frozen products stacked (one pass over W
+        # per product) when the library can: bf16 W and whole 256-row tiles.
+        self.nslots = int(slots)
+        self.stack_slots = (self.nslots > 1 and cfg.w_dtype == "bf16" and self.T % 256 == 0)
         self.scale = L.lora_scaling(cfg.alpha, cfg.rank, cfg.scaling == "rslora")
         self.device = device
         f32 = dict(device=device, dtype=torch.float32)
@@ -121,14 +125,23 @@ class Trainer:
         if cfg.dora:   # the row-norm refresh runs on the same stream between steps
             for k in model.keys:
                 ws = max(ws, L.lora_dora_row_norms_workspace_bytes(self._linear(k, None)))
-        self.U, self.Z, self.Y, self.dX = {}, {}, {}, {}
-        for key in model.keys:
-            K, N = model.shape[key]
-            self.U[key] = torch.empty(self.T, r, **f32)
-            self.Y[key] = torch.empty(self.T, N, **f32)
-            self.dX[key] = torch.empty(self.T, K, **f32)
-            if cfg.dora:
-                self.Z[key] = torch.empty(self.T, N, **f32)
+        if self.stack_slots:
+            for k in model.keys:
+                ws = max(ws, L.lora_slots_workspace_bytes(
+                    [self._linear(k, None, dora=cfg.dora)] * self.nslots))
+        # Activations per slot (slot 0's are also U, Z, Y, dX).
+        self.acts = []
+        for _ in range(self.nslots if self.stack_slots else 1):
+            a = {"U": {}, "Z": {}, "Y": {}, "dX": {}}
+            for key in model.keys:
+                K, N = model.shape[key]
+                a["U"][key] = torch.empty(self.T, r, **f32)
+                a["Y"][key] = torch.empty(self.T, N, **f32)
+                a["dX"][key] = torch.empty(self.T, K, **f32)
+                if cfg.dora:
+                    a["Z"][key] = torch.empty(self.T, N, **f32)
+            self.acts.append(a)
+        self.U, self.Z, self.Y, self.dX = (self.acts[0][n] for n in ("U", "Z", "Y", "dX"))
         self.ws = torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
         self.d_scale = torch.zeros(1, **f32)
         self.d_stats = torch.zeros(2, device=device, dtype=torch.float64)
@@ -194,13 +207,58 @@ class Trainer:
                                       [slot.gmag[k] for k in keys] if cfg.dora else None,
                                       accumulate=g > 0, drops=drops(keys), ws=self.ws)
 
-    def step(self, slot: Slot, chunks: list, sync: bool = True) -> StepStats:
+    def forward_backward_slots(self, slots: list, chunks_per_slot: list):
+        """forward_backward of several slots together: each linear's forward
+        and backward go through the slot calls, whose frozen products run
+        once over all slots' stacked rows."""
         cfg = self.cfg
+        p = float(cfg.dropout)
+        n = len(slots)
+        acts = self.acts[:n]
+        G = len(chunks_per_slot[0])
+        for g in range(G):
+            def drops(key):
+                if p <= 0:
+                    return None
+                return [L.make_dropout(sl.seed, sl.k, g, key[0], key[1], p) for sl in slots]
+            for key in self.model.keys:
+                lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
+                L.lora_forward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
+                                     [a["Y"][key] for a in acts], [a["U"][key] for a in acts],
+                                     [a["Z"][key] for a in acts] if cfg.dora else None,
+                                     drops(key), self.ws)
+            for key in reversed(self.model.keys):
+                lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
+                L.lora_backward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
+                                      [c[g][key][1] for c in chunks_per_slot],
+                                      [a["U"][key] for a in acts],
+                                      [a["Z"][key] for a in acts] if cfg.dora else None,
+                                      [a["dX"][key] for a in acts], [sl.gA[key] for sl in slots],
+                                      [sl.gB[key] for sl in slots],
+                                      [sl.gmag[key] for sl in slots] if cfg.dora else None,
+                                      accumulate=g > 0, drops=drops(key), ws=self.ws)
+
+    def step_slots(self, slots: list, chunks_per_slot: list, sync: bool = True) -> list:
+        """One update of every slot; with stacked slots their forward and
+        backward passes share each frozen product, then each slot takes its
+        own prepare, AdamW step and DoRA refresh."""
+        if not self.stack_slots or len(slots) < 2:
+            return [self.step(sl, ch, sync) for sl, ch in zip(slots, chunks_per_slot)]
+        if len(slots) > self.nslots:
+            raise ValueError(f"trainer holds activations for {self.nslots} slots")
+        self.forward_backward_slots(slots, chunks_per_slot)
+        return [self._update(sl, len(ch), sync) for sl, ch in zip(slots, chunks_per_slot)]
+
+    def step(self, slot: Slot, chunks: list, sync: bool = True) -> StepStats:
         self.forward_backward(slot, chunks)
+        return self._update(slot, len(chunks), sync)
+
+    def _update(self, slot: Slot, n_chunks: int, sync: bool) -> StepStats:
+        cfg = self.cfg
         if self.prep_ws is None or self.prep_ws.numel() < L.lora_grad_prepare_workspace_bytes(slot.n):
             self.prep_ws = torch.empty(L.lora_grad_prepare_workspace_bytes(slot.n),
                                        device=self.device, dtype=torch.uint8)
-        n_pred = self.T * len(chunks)
+        n_pred = self.T * n_chunks
         lr = L.lora_lr_at(slot.k, cfg.lr, 1 if cfg.schedule == "cosine" else 0, cfg.warmup,
                           cfg.total_updates, cfg.lr_min)
         try:

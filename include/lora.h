@@ -159,6 +159,7 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY,
  * workspace is the per-linear workspaces laid end to end (each rounded up to
  * 256 bytes).  Validation of every linear precedes any launch. */
 #define LORA_MAX_GROUP 4
+#define LORA_MAX_SLOTS 4
 size_t lora_group_workspace_bytes(int n, const lora_linear* lins);
 int lora_forward_group(int n, const lora_linear* lins, const float* X, float* const* Y,
                        float* const* U, float* const* Z, const lora_dropout* drops, void* ws,
@@ -167,6 +168,32 @@ int lora_backward_group(int n, const lora_linear* lins, const float* X, const fl
                         const float* const* U, const float* const* Z, float* const* dX,
                         float* const* dA, float* const* dB, float* const* dMag, int accumulate,
                         const lora_dropout* drops, void* ws, size_t ws_bytes, void* stream);
+
+/* Adapter slots over one frozen W ("Multi-LoRA Training Example
+ * (fully-async)", "Design (decoupled per-adapter optimizers)": adapters
+ * share the base model, each with its own data, factors and optimizer).
+ * The same work as n separate lora_forward / lora_backward calls, slot i
+ * with lins[i], X[i], Y[i] ... and drops[i] (drops may be NULL).  When W is
+ * bf16, n > 1, every slot's token count is a multiple of 256 and n*tokens
+ * times in_dim and out_dim stay below 2^30, each frozen product runs once
+ * over the slots' stacked rows (one pass over W for all slots); otherwise the
+ * slots run one after another.  Results equal the separate calls up to the
+ * summation order of the frozen products.  lins[i] must share W, tokens,
+ * in_dim, out_dim, rank and w_dtype, and all or none be DoRA (LORA_E_SHAPE /
+ * LORA_E_DTYPE / LORA_E_INVALID otherwise); 1 <= n <= LORA_MAX_SLOTS.
+ * dX is NULL, or an array whose entries are all NULL or all set.  The
+ * workspace (lora_slots_workspace_bytes) holds every slot's share and the
+ * stacked bf16 operands and partials; its contents between calls do not
+ * matter. */
+size_t lora_slots_workspace_bytes(int n, const lora_linear* lins);
+int lora_forward_slots(int n, const lora_linear* lins, const float* const* X, float* const* Y,
+                       float* const* U, float* const* Z, const lora_dropout* drops, void* ws,
+                       size_t ws_bytes, void* stream);
+int lora_backward_slots(int n, const lora_linear* lins, const float* const* X,
+                        const float* const* dY, const float* const* U, const float* const* Z,
+                        float* const* dX, float* const* dA, float* const* dB, float* const* dMag,
+                        int accumulate, const lora_dropout* drops, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Workspace bytes lora_grad_prepare needs for n gradient elements. */
 size_t lora_grad_prepare_workspace_bytes(int64_t n);

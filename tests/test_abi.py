@@ -109,3 +109,15 @@ def test_optimizer_entry_validation():
     assert lib.lora_grad_prepare(256, 10, 0, 1.0, 256, None, None, 256, 1 << 16, None) == -1
     assert lib.lora_grad_prepare(256, 10, 4, -1.0, 256, None, None, 256, 1 << 16, None) == -1
     assert lib.lora_grad_prepare(256, 10, 4, 1.0, 256, None, None, 256, 16, None) == -5
+
+
+def test_binding_checks_factor_shapes_against_w():
+    """make_linear refuses factors that disagree with W's shape, on the host:
+    the kernels size every access from the descriptor alone."""
+    W = torch.zeros(64, 32)
+    with pytest.raises(ValueError, match="B must be"):
+        L.make_linear(W, torch.zeros(4, 32), torch.zeros(16, 4), 1.0, 8)
+    with pytest.raises(ValueError, match="A must be"):
+        L.make_linear(W, torch.zeros(4, 16), torch.zeros(64, 4), 1.0, 8)
+    with pytest.raises(ValueError, match="dora_mag"):
+        L.make_linear(W, torch.zeros(4, 32), torch.zeros(64, 4), 1.0, 8, torch.zeros(63))

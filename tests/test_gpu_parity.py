@@ -350,9 +350,10 @@ def test_dora_row_norms_workspace_checked():
 
 
 # ------------------------------------------------------ end-to-end steps ---
-def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None):
+def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None, together=False):
     """Run `steps` updates on the GPU and in the oracle from equal inputs;
-    return both states and gradients."""
+    return both states and gradients.  together: all slots step through the
+    trainer's stacked slot path."""
     layers = cfg.layers if layers is None else layers
     T = cfg.tokens if tokens is None else tokens
     nslots = cfg.slots if slots is None else slots
@@ -364,8 +365,9 @@ def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None):
             W[(l, pj.ordinal)] = inp["W"]
             Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"])
     model = S.FrozenModel(cfg, {k: v.to(DEV) for k, v in Wq.items()})
-    trainer = S.Trainer(cfg, model, tokens=T)
+    trainer = S.Trainer(cfg, model, tokens=T, slots=nslots if together else 1)
     results = []
+    staged = []
     for si in range(nslots):
         A, B, chunks = {}, {}, [dict() for _ in range(cfg.chunks)]
         for l in range(layers):
@@ -386,21 +388,25 @@ def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None):
                 ost.norms[k] = O.dora_row_norms(np64(W[k]), ost.params[k]["A"], ost.params[k]["B"], s)
         gchunks = [{k: (x.to(DEV), d.to(DEV)) for k, (x, d) in ch.items()} for ch in chunks]
         ochunks = [{k: (np64(x), np64(d)) for k, (x, d) in ch.items()} for ch in chunks]
-        lin64 = {k: np64(v) for k, v in W.items()}
-        hist = []
-        for it in range(steps):
-            p_before = slot.params.clone()
-            o_before = {k: {n: a.copy() for n, a in v.items()} for k, v in ost.params.items()}
-            st = trainer.step(slot, gchunks)
+        staged.append((si, slot, ost, gchunks, ochunks, []))
+    lin64 = {k: np64(v) for k, v in W.items()}
+    for it in range(steps):
+        before = [(slot.params.clone(), {k: {n: a.copy() for n, a in v.items()}
+                                          for k, v in ost.params.items()})
+                  for _, slot, ost, _, _, _ in staged]
+        if together:
+            sts = trainer.step_slots([x[1] for x in staged], [x[3] for x in staged])
+        else:
+            sts = [trainer.step(slot, gch) for _, slot, _, gch, _, _ in staged]
+        for (si, slot, ost, gch, och, hist), (p_before, o_before), st in zip(staged, before, sts):
             hp = dict(s=s, p=cfg.dropout, seed=cfg.seeds[si], n_pred=T * cfg.chunks,
                       max_norm=cfg.max_norm,
                       lr=O.lr_at(ost.k, cfg.lr, cfg.schedule, cfg.warmup, cfg.total_updates, cfg.lr_min),
                       weight_decay=cfg.weight_decay, plus_ratio=cfg.plus_ratio, dora=cfg.dora)
-            res = O.train_step(ost, lin64, ochunks, hp)
+            res = O.train_step(ost, lin64, och, hp)
             hist.append((p_before, o_before, st, res, slot.grads.clone()))
-        results.append((slot, ost, hist))
     torch.cuda.synchronize()
-    return results
+    return [(slot, ost, hist) for _, slot, ost, _, _, hist in staged]
 
 
 def _flat(slot, per_key, order=("A", "B", "mag")):
@@ -414,16 +420,17 @@ def _flat(slot, per_key, order=("A", "B", "mag")):
 
 
 E2E = [
-    ("wl1", 1, None, None, 3),
-    ("wl2", 2, None, None, 1),
-    ("wl3", 3, None, None, 1),
-    ("wl4-1layer-T512", 4, 1, 512, 2),
-    ("wl5-1layer-T256", 5, 1, 256, 2),
+    ("wl1", 1, None, None, 3, False),
+    ("wl2", 2, None, None, 1, False),
+    ("wl3", 3, None, None, 1, False),
+    ("wl4-1layer-T512", 4, 1, 512, 2, False),
+    ("wl5-1layer-T256", 5, 1, 256, 2, False),
+    ("wl5-1layer-T256-stacked-slots", 5, 1, 256, 2, True),
 ]
 
 
-@pytest.mark.parametrize("name,wl,layers,tokens,steps", E2E, ids=[e[0] for e in E2E])
-def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
+@pytest.mark.parametrize("name,wl,layers,tokens,steps,together", E2E, ids=[e[0] for e in E2E])
+def test_end_to_end_step_parity(name, wl, layers, tokens, steps, together):
     """Whole updates against the oracle's train_step.
 
     Gradients: A and B are float32-exact on every path (rank-side products
@@ -438,7 +445,7 @@ def test_end_to_end_step_parity(name, wl, layers, tokens, steps):
     step), whose error is ~1e-3 of the largest."""
     cfg = WL.get_config(wl)
     _say("e2e", name)
-    for slot, ost, hist in _e2e(cfg, layers, tokens, steps):
+    for slot, ost, hist in _e2e(cfg, layers, tokens, steps, together=together):
         seg = {}
         for off, cnt, kind in slot.segments:
             seg[kind] = slice(off, off + cnt)
@@ -495,6 +502,27 @@ def test_invalid_arguments_raise_before_work():
     with pytest.raises(L.LoraError) as e:
         L.lora_forward(lin, c["X"], Y, U, None, bad, None)
     assert e.value.status == -1
+    assert torch.count_nonzero(Y).item() == 0 and torch.count_nonzero(U).item() == 0
+
+
+def test_undersized_buffers_are_refused_on_the_host():
+    """A tensor smaller than the descriptor says raises before any launch,
+    in the single, group and slot calls alike."""
+    T, K, N, r = 64, 136, 264, 8
+    c = _gpu(_linear_case(T, K, N, r, seed=5))
+    lin = L.make_linear(c["Wq"], c["A"], c["B"], 2.0, T)
+    Y = torch.zeros(T, N, device=DEV)
+    U = torch.zeros(T, r, device=DEV)
+    ws = torch.empty(max(256, L.lora_workspace_bytes(lin)), device=DEV, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="Y holds"):
+        L.lora_forward(lin, c["X"], Y[: T - 1], U, None, None, ws)
+    with pytest.raises(ValueError, match=r"dY\[1\] holds"):
+        L.lora_backward_group([lin, lin], c["X"], [c["dY"], c["dY"][:, :8].contiguous()], [U, U],
+                              None, None, [torch.zeros(r, K, device=DEV)] * 2,
+                              [torch.zeros(N, r, device=DEV)] * 2, ws=ws)
+    with pytest.raises(ValueError, match=r"X\[0\] holds"):
+        L.lora_forward_slots([lin, lin], [c["X"][:1], c["X"]], [Y, Y], [U, U], None, None, ws)
+    torch.cuda.synchronize()
     assert torch.count_nonzero(Y).item() == 0 and torch.count_nonzero(U).item() == 0
 
 
@@ -692,7 +720,8 @@ def test_merge_parity(wd_, N, K, r, dora):
 def test_merge_of_zero_adapter_is_exact():
     c = _linear_case(8, 2560, 1024, 32, "bf16", seed=14)
     g = _gpu(c)
-    lin = L.make_linear(g["Wq"], g["A"], torch.zeros_like(g["B"]), 2.0, 8)
+    B0 = torch.zeros_like(g["B"])   # held: the descriptor keeps only its address
+    lin = L.make_linear(g["Wq"], g["A"], B0, 2.0, 8)
     outb = torch.empty_like(g["Wq"])
     rm = torch.full((1,), float("nan"), device=DEV, dtype=torch.float64)
     L.lora_merge(lin, outb, rm)
@@ -708,3 +737,123 @@ def test_merge_checks_its_workspace():
     rm = torch.zeros(1, device=DEV, dtype=torch.float64)
     with pytest.raises(L.LoraError):
         L.lora_merge(lin, outb, rm, torch.empty(need - 8, device=DEV, dtype=torch.uint8))
+
+
+# ------------------------------------------------------------ slots ---------
+def _slot_cases(T, K, N, r, n, seed):
+    """n adapter slots over one bf16 W: own X, dY, A, B per slot."""
+    cs = [_linear_case(T, K, N, r, "bf16", seed=seed + i, b_std=0.05) for i in range(n)]
+    for c in cs[1:]:
+        c["Wq"], c["W"] = cs[0]["Wq"], cs[0]["W"]
+    return cs
+
+
+def _run_slots(cs, s, p, together, dora=False, steps=2):
+    """Forward + backward of every slot over `steps` chunks (accumulating),
+    through the slot calls or one slot at a time."""
+    gs = [_gpu(c) for c in cs]
+    for g in gs[1:]:                # the slots share one device copy of W
+        g["Wq"], g["W"] = gs[0]["Wq"], gs[0]["W"]
+    T, K = gs[0]["X"].shape
+    N, r = gs[0]["W"].shape[0], gs[0]["A"].shape[0]
+    mags, nrms = [None] * len(gs), [None] * len(gs)
+    if dora:
+        for i, g in enumerate(gs):
+            mags[i] = torch.rand(N, device=DEV) + 0.5
+            nrms[i] = torch.empty(N, device=DEV)
+            L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], s, T), nrms[i])
+    lins = [L.make_linear(g["Wq"], g["A"], g["B"], s, T, mags[i], nrms[i]) for i, g in enumerate(gs)]
+    nanf = float("nan")
+    names = ("Y", "U", "dX", "dA", "dB") + (("Z", "dm") if dora else ())
+    shapes = dict(Y=(T, N), U=(T, r), dX=(T, K), dA=(r, K), dB=(N, r), Z=(T, N), dm=(N,))
+    out = {n: [torch.full(shapes[n], nanf, device=DEV) for _ in gs] for n in names}
+    ws = torch.empty(max(L.lora_slots_workspace_bytes(lins),
+                         max(L.lora_workspace_bytes(l) for l in lins)), device=DEV, dtype=torch.uint8)
+    for step in range(steps):
+        drops = [L.make_dropout(1234 + i, 3, step, 5, 4, p) if p > 0 else None for i in range(len(gs))]
+        X = [g["X"] if step == 0 else g["X"] * 0.5 for g in gs]
+        dYs = [g["dY"] if step == 0 else g["dY"] * -1.5 for g in gs]
+        Z = out["Z"] if dora else None
+        dm = out["dm"] if dora else None
+        if together:
+            L.lora_forward_slots(lins, X, out["Y"], out["U"], Z, drops, ws)
+            L.lora_backward_slots(lins, X, dYs, out["U"], Z, out["dX"], out["dA"], out["dB"], dm,
+                                  accumulate=step > 0, drops=drops, ws=ws)
+        else:
+            for i, lin in enumerate(lins):
+                L.lora_forward(lin, X[i], out["Y"][i], out["U"][i], Z[i] if dora else None,
+                               drops[i], ws)
+                L.lora_backward(lin, X[i], dYs[i], out["U"][i], Z[i] if dora else None,
+                                out["dX"][i], out["dA"][i], out["dB"][i], dm[i] if dora else None,
+                                accumulate=step > 0, drop=drops[i], ws=ws)
+    torch.cuda.synchronize()
+    return out, mags, nrms
+
+
+SLOT_CASES = [
+    # name, T, K, N, r, slots, dropout, DoRA
+    ("pair-stacked", 256, 264, 520, 16, 2, 0.1, False),
+    ("pair-stacked-dora", 256, 520, 264, 32, 2, 0.1, True),
+    ("four-stacked", 256, 136, 272, 8, 4, 0.0, False),
+    ("qwen-wgate-pair", 512, 2560, 9728, 64, 2, 0.1, True),
+]
+
+
+@pytest.mark.parametrize("case", SLOT_CASES, ids=[c[0] for c in SLOT_CASES])
+def test_slots_match_oracle(case):
+    """Each slot of a stacked slot call against the oracle (two accumulated
+    chunks), at the bf16-W bar."""
+    name, T, K, N, r, n, p, dora = case
+    _say("slots", name)
+    cs = _slot_cases(T, K, N, r, n, seed=zlib.crc32(name.encode()) % 1000)
+    got, mags, nrms = _run_slots(cs, 1.5, p, together=True, dora=dora)
+    for i, c in enumerate(cs):
+        refs = []
+        for step in range(2):
+            ci = dict(c)
+            if step:
+                ci["X"], ci["dY"] = c["X"] * 0.5, c["dY"] * -1.5
+            m = np64(mags[i]) if dora else None
+            nr = np64(nrms[i]) if dora else None
+            refs.append(_oracle(ci, 1.5, p, (1234 + i, 3, step, 5, 4), m, nr))
+        last = refs[-1]
+        checks = dict(Y=last["Y"], U=last["U"], dX=last["dX"], dA=refs[0]["dA"] + last["dA"],
+                      dB=refs[0]["dB"] + last["dB"])
+        if dora:
+            checks["Z"] = last["Z"]
+            checks["dm"] = refs[0]["dmag"] + last["dmag"]
+        for nme, ref in checks.items():
+            e = rel_err(got[nme][i], ref)
+            _say(f"  slot {i} {nme}: rel err {e:.3e}")
+            assert e <= 2e-2 if nme in ("Y", "dX", "Z", "dm") else e <= 1e-4, (i, nme, e)
+
+
+@pytest.mark.parametrize("T", [256, 100])
+def test_slots_equal_separate_calls(T):
+    """Stacked (T a multiple of 256) slot calls agree with separate calls up
+    to the frozen products' summation order; unstacked ones (ragged T) are
+    the separate calls, bitwise."""
+    cs = _slot_cases(T, 264, 136, 8, 2, seed=61)
+    a, _, _ = _run_slots(cs, 2.0, 0.1, together=True)
+    b, _, _ = _run_slots(cs, 2.0, 0.1, together=False)
+    for nme in a:
+        for i in range(2):
+            assert torch.isfinite(a[nme][i]).all(), (nme, i)
+            if T % 256:
+                assert torch.equal(a[nme][i], b[nme][i]), (nme, i)
+            else:
+                assert rel_err(a[nme][i], b[nme][i]) <= 1e-5, (nme, i)
+
+
+def test_slots_reject_different_w():
+    cs = [_gpu(c) for c in _slot_cases(256, 136, 64, 4, 2, seed=71)]
+    other = (cs[1]["Wq"].float() * 2).to(torch.bfloat16)
+    lins = [L.make_linear(cs[0]["Wq"], cs[0]["A"], cs[0]["B"], 1.0, 256),
+            L.make_linear(other, cs[1]["A"], cs[1]["B"], 1.0, 256)]
+    Y = [torch.zeros(256, 64, device=DEV) for _ in cs]
+    U = [torch.zeros(256, 4, device=DEV) for _ in cs]
+    ws = torch.empty(1 << 22, device=DEV, dtype=torch.uint8)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_forward_slots(lins, [c["X"] for c in cs], Y, U, None, None, ws)
+    assert e.value.status == -2
+    assert all(torch.count_nonzero(y).item() == 0 for y in Y)
