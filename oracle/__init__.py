@@ -10,7 +10,8 @@ numpy (a matrix product is the only library primitive it leans on).  It shares
 no code, constants or helpers with the HIP path.
 
 Pinning status of each function (what fixes it other than itself) is listed in
-the docstring of ``oracle.lora``.
+the docstrings of ``oracle.lora`` and ``oracle.quant`` (block-quantized frozen
+weights).
 """
 
 from .lora import *  # noqa: F401,F403

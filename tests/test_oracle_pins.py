@@ -438,3 +438,130 @@ def test_merge_rmse_of_ties_closed_form():
     W = np.where(np.arange(6 * 8).reshape(6, 8) % 2 == 0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8)
     _, rmse = O.merge(W, np.zeros((1, 8)), np.zeros((6, 1)), 1.0, out="bf16")
     assert rmse == 2.0**-8
+
+
+# ------------------------------------------------ block-quantized frozen W --
+from oracle import quant as Q
+
+
+def _pack_nibbles(codes):
+    """Independent packer (pure Python): element 2j -> low nibble of byte j."""
+    rows = []
+    for row in codes:
+        rows.append([int(row[2 * j]) | (int(row[2 * j + 1]) << 4) for j in range(len(row) // 2)])
+    return np.array(rows, dtype=np.uint8)
+
+
+def _pack_crumbs(fields):
+    """Independent packer: element 4j+i -> bits 2i..2i+1 of byte j."""
+    rows = []
+    for row in fields:
+        rows.append([sum(int(row[4 * j + i]) << (2 * i) for i in range(4))
+                     for j in range(len(row) // 4)])
+    return np.array(rows, dtype=np.uint8)
+
+
+def test_q4_0_decodes_closed_form_codes_per_block_scale():
+    # code of element k is k mod 16; block b (32 elements) has d = 2^-(b+3)
+    N, K = 2, 96
+    codes = np.array([[(k + 5 * n) % 16 for k in range(K)] for n in range(N)])
+    d = np.array([[2.0 ** -(b + 3) * (n + 1) for b in range(K // 32)] for n in range(N)],
+                 dtype=np.float16)
+    W = Q.dequantize("q4_0", {"qs": _pack_nibbles(codes), "d": d})
+    for n in range(N):
+        for k in range(K):
+            assert W[n, k] == 2.0 ** -(k // 32 + 3) * (n + 1) * (((k + 5 * n) % 16) - 8)
+
+
+def test_q8_0_is_the_signed_code_times_its_block_scale():
+    N, K = 3, 64
+    codes = np.array([[((7 * k + 3 * n) % 255) - 127 for k in range(K)] for n in range(N)],
+                     dtype=np.int8)
+    d = np.array([[0.5, 0.25], [1.0, 2.0], [0.125, 4.0]], dtype=np.float16)
+    W = Q.dequantize("q8_0", {"qs": codes, "d": d})
+    for n in range(N):
+        for k in range(K):
+            assert W[n, k] == float(d[n, k // 32]) * (((7 * k + 3 * n) % 255) - 127)
+
+
+def test_q4_k_scale_and_min_reach_exactly_their_sub_block():
+    N, K = 1, 512
+    codes = np.array([[(3 * k) % 16 for k in range(K)]])
+    sm = np.zeros((N, K // 32, 2), dtype=np.uint8)
+    for b in range(K // 32):
+        sm[0, b] = (b + 1, 63 - 2 * b)
+    dm = np.array([[[0.5, 0.25], [0.125, 2.0]]], dtype=np.float16)
+    W = Q.dequantize("q4_k", {"qs": _pack_nibbles(codes), "sm": sm, "dm": dm})
+    for k in range(K):
+        d, dmin = (0.5, 0.25) if k < 256 else (0.125, 2.0)
+        b = k // 32
+        assert W[0, k] == d * (b + 1) * ((3 * k) % 16) - dmin * (63 - 2 * b)
+
+
+def test_q6_k_six_bit_codes_and_signed_sub_scales():
+    N, K = 2, 256
+    codes = np.array([[(k + 11 * n) % 64 for k in range(K)] for n in range(N)])
+    ql = _pack_nibbles(codes & 15)
+    qh = _pack_crumbs(codes >> 4)
+    sc = np.array([[(-1) ** b * (b + 1) + n for b in range(16)] for n in range(N)], dtype=np.int8)
+    d = np.array([[0.25], [0.5]], dtype=np.float16)
+    W = Q.dequantize("q6_k", {"ql": ql, "qh": qh, "sc": sc, "d": d})
+    for n in range(N):
+        for k in range(K):
+            b = k // 16
+            assert W[n, k] == float(d[n, 0]) * ((-1) ** b * (b + 1) + n) * (((k + 11 * n) % 64) - 32)
+
+
+@pytest.mark.parametrize("fmt", Q.FORMATS)
+def test_neutral_codes_give_an_exactly_zero_weight(fmt):
+    rng = np.random.default_rng(3)
+    N, K = 4, 256
+    shp = Q.plane_shapes(fmt, N, K)
+    planes = {}
+    for name, (dt, shape) in shp.items():
+        if dt == np.float16:
+            planes[name] = rng.uniform(0.01, 1.0, shape).astype(np.float16)
+        else:
+            planes[name] = rng.integers(1, 64, shape).astype(dt)
+    neutral = {"q8_0": ("qs", 0), "q4_0": ("qs", 0x88), "q6_k": ("ql", 0)}
+    if fmt == "q4_k":
+        planes["qs"][:] = 0
+        planes["sm"][..., 1] = 0
+    elif fmt == "q6_k":
+        planes["ql"][:] = 0
+        planes["qh"][:] = 0b10101010            # q = 32 everywhere
+    else:
+        name, v = neutral[fmt]
+        planes[name][:] = v
+    assert np.all(Q.dequantize(fmt, planes) == 0.0)
+
+
+def test_q4_0_equals_q4_k_with_unit_sub_scales():
+    rng = np.random.default_rng(5)
+    N, K = 3, 512
+    qs = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    e = rng.integers(-12, -2, (N, K // 32))
+    d0 = (2.0 ** e).astype(np.float16)                     # powers of two: 8*d exact in fp16
+    # q4_k carries one (d, dmin) per 256 elements: make the q4_0 scales equal
+    # within each super-block
+    d0 = np.repeat(d0[:, ::8], 8, axis=1)
+    sm = np.ones((N, K // 32, 2), dtype=np.uint8)
+    dm = np.stack([d0[:, ::8], (8 * d0[:, ::8].astype(np.float64)).astype(np.float16)], axis=2)
+    a = Q.dequantize("q4_0", {"qs": qs, "d": d0})
+    b = Q.dequantize("q4_k", {"qs": qs, "sm": sm, "dm": dm})
+    assert np.array_equal(a, b)
+
+
+def test_q6_k_equals_q8_0_with_shifted_codes():
+    rng = np.random.default_rng(6)
+    N, K = 2, 256
+    codes = rng.integers(0, 64, (N, K))
+    sc = rng.integers(-4, 5, (N, K // 16)).astype(np.int8)
+    d = (2.0 ** rng.integers(-10, -4, (N, 1))).astype(np.float16)
+    # q8_0 blocks are 32 wide: give both 16-element halves one scale first
+    sc2 = np.repeat(sc[:, ::2], 2, axis=1)
+    W6b = Q.dequantize("q6_k", {"ql": _pack_nibbles(codes & 15), "qh": _pack_crumbs(codes >> 4),
+                                "sc": sc2, "d": d})
+    d8 = (d.astype(np.float64) * sc2[:, ::2]).astype(np.float16)
+    W8 = Q.dequantize("q8_0", {"qs": (codes - 32).astype(np.int8), "d": d8})
+    assert np.array_equal(W6b, W8)
