@@ -19,6 +19,11 @@
 // past the end), out-of-range elements are zeroed when stored to LDS, so the
 // compiler waits for exactly the stage it stores.
 //
+// Block-quantized W (qweight.hpp) takes the same kernel with WQ set: W is
+// staged as runs of 8 elements of a W row, decoded to bf16 on the way into
+// LDS, so the LDS layout and the MFMA loop are unchanged.  For dX a thread's
+// item is QR contraction rows x 8 columns, transposed while packing.
+//
 // The grid is one-dimensional.  Workgroups are dealt to the 8 XCDs round
 // robin, so block b runs on XCD b % 8, and each XCD starts its blocks in
 // order.  Block b is mapped to a contiguous run of tile indices per XCD, and
@@ -30,6 +35,7 @@
 
 #include "common.hpp"
 #include "gemm_f32.hpp"   // LoraOperand
+#include "qweight.hpp"
 
 namespace lora {
 
@@ -54,6 +60,8 @@ struct GemmBf16Args {
   int64_t lda;
   const uint16_t* B;       // fwd: W [Nc, Kc];  dx: W [Kc, Nc]   (bf16)
   int64_t ldb;
+  QPlanes q;               // the same W block-quantized (kernels with WQ != WQ_BF16)
+  int wq;                  // lora_dtype of W (host dispatch)
   int64_t M, Nc, Kc;
   int64_t r;
   Bf16Slot sl[BF16_MAX_SLOTS];
@@ -81,11 +89,23 @@ LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
   return so;
 }
 
+// Tile configurations: index, BM, BN, threads, wave rows, K-step, stages in
+// flight, directions (1 forward, 2 dX), then the host planner's fitted cost
+// coefficients (forward a, b; dX a, b).
+#define LORA_BF16_CFGS(X)                                        \
+  X(0, 256, 256, 512, 2, 32, 3, 1, 0.409, 15.2, 0, 0)            \
+  X(1, 256, 256, 512, 2, 64, 1, 2, 0, 0, 0.479, 13.3)            \
+  X(2, 256, 128, 512, 2, 64, 2, 1, 0.482, 8.9, 0, 0)             \
+  X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.696, 7.3)             \
+  X(4, 128, 128, 512, 2, 64, 2, 3, 0.588, 5.1, 0.962, 4.6)
+
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
 // EXACT: M, Nc and Kc are multiples of BM, BN and BK: nothing is out of range.
-template <int BM, int BN, int NT, int WGM, int BK, int DEPTH, bool FWD, bool EXACT>
+// WQ: the lora_dtype of W (WQ_BF16, or a block-quantized format).
+template <int BM, int BN, int NT, int WGM, int BK, int DEPTH, bool FWD, bool EXACT,
+          int WQ = WQ_BF16>
 __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   constexpr int WGN = NT / 64 / WGM;
   constexpr int LDS_ROW = BK + 8;                   // bf16 elements per LDS row
@@ -103,6 +123,14 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole chunks per thread");
   static_assert((BM + BN) * LROW <= 2 * (BM + BN) * LDS_ROW, "LoRA staging fits the LDS");
   static_assert(DEPTH >= 1, "stages in flight");
+  constexpr bool QW = wq_quantized(WQ);
+  constexpr int QWD = QW ? wq_words(WQ) : 1;          // words per staged 8-element run
+  constexpr int QR0 = BK * BN / (8 * NT);
+  constexpr int QR = QR0 < 2 ? 2 : (QR0 > 8 ? 8 : QR0);  // dX: contraction rows per item
+  constexpr int QCQ = BN / 8;                         // dX: 8-column groups per tile row
+  constexpr int QITEMS = (BK / QR) * QCQ;
+  constexpr int QIT = (QITEMS + NT - 1) / NT;
+  static_assert(!QW || FWD || (BK % QR == 0 && QR % 2 == 0), "whole row pairs per item");
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDS_ROW];
   auto As = [&](int b) -> uint16_t* { return smem + b * (BM * LDS_ROW); };
@@ -138,8 +166,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 
   struct Stage {
     u32x4 a[ACH];
-    u32x4 bf[FWD ? BCH : 1];
-    u32x2 bt[FWD ? 1 : BIT][8];
+    u32x4 bf[(FWD && !QW) ? BCH : 1];
+    u32x2 bt[(FWD || QW) ? 1 : BIT][8];
+    uint32_t qf[(FWD && QW) ? BCH : 1][QWD];          // quantized fwd: one run per chunk
+    uint32_t qt[(!FWD && QW) ? QIT : 1][QR][QWD];     // quantized dX: QR runs per item
   };
 
   // Operand loads are raw buffer loads with a 32-bit byte offset (the
@@ -166,6 +196,13 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   static_assert(NT % CPR == 0 && (FWD || NT % CQN == 0), "uniform chunk rows");
   const uint32_t voffB = FWD ? (uint32_t)(((tid / CPR) * p.ldb + 8 * (tid % CPR)) * 2)
                              : (uint32_t)(((tid / CQN) * 8 * p.ldb + 4 * (tid % CQN)) * 2);
+  // Quantized W: W row length, and the planes' resources.
+  const uint32_t qK = (uint32_t)(FWD ? p.Kc : p.Nc);
+  const QRes<QW ? WQ : WQ_Q8_0> QRs(p.q);
+  auto qt_ok = [&](int q) -> bool {
+    const int f = tid + NT * q;
+    return (EXACT || n0 + 8 * (f % QCQ) < p.Nc) && f < QITEMS;
+  };
 
   auto a_ok = [&](int64_t k0) -> bool { return EXACT || k0 + 8 * (tid % CPR) < kend; };
   auto bt_ok = [&](int q) -> bool {
@@ -177,7 +214,22 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       S.a[q] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                      rA, voffA + (uint32_t)((q * RPQ * p.lda + k0) * 2), 0, 0));
-    if constexpr (FWD) {
+    if constexpr (QW && FWD) {
+#pragma unroll
+      for (int q = 0; q < BCH; ++q) {
+        const int f = tid + NT * q;
+        wq_load<WQ>(QRs, qK, (uint32_t)(n0 + f / CPR), (uint32_t)(k0 + 8 * (f % CPR)), S.qf[q]);
+      }
+    } else if constexpr (QW) {
+#pragma unroll
+      for (int q = 0; q < QIT; ++q) {
+        const int f = tid + NT * q;
+        const uint32_t col = (uint32_t)(n0 + 8 * (f % QCQ));
+        const uint32_t row = (uint32_t)(k0 + QR * (f / QCQ));
+#pragma unroll
+        for (int i = 0; i < QR; ++i) wq_load<WQ>(QRs, qK, row + i, col, S.qt[q][i]);
+      }
+    } else if constexpr (FWD) {
 #pragma unroll
       for (int q = 0; q < BCH; ++q)
         S.bf[q] = __builtin_bit_cast(
@@ -201,7 +253,42 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       const int f = tid + NT * q;
       *reinterpret_cast<u32x4*>(&As(buf)[(f / CPR) * LDS_ROW + 8 * (f % CPR)]) = aok ? S.a[q] : z4;
     }
-    if constexpr (FWD) {
+    if constexpr (QW && FWD) {
+#pragma unroll
+      for (int q = 0; q < BCH; ++q) {
+        const int f = tid + NT * q;
+        float v[8];
+        wq_decode<WQ>(S.qf[q], v);
+        const u32x4 o = {wq_pack(v[0], v[1]), wq_pack(v[2], v[3]), wq_pack(v[4], v[5]),
+                         wq_pack(v[6], v[7])};
+        *reinterpret_cast<u32x4*>(&Bs(buf)[(f / CPR) * LDS_ROW + 8 * (f % CPR)]) = aok ? o : z4;
+      }
+    } else if constexpr (QW) {
+#pragma unroll
+      for (int q = 0; q < QIT; ++q) {
+        const int f = tid + NT * q;
+        if (f >= QITEMS) continue;
+        const bool ok = qt_ok(q);
+        float v[QR][8];
+#pragma unroll
+        for (int i = 0; i < QR; ++i) wq_decode<WQ>(S.qt[q][i], v[i]);
+        // column e of the QR x 8 run block becomes QR contraction values
+        uint16_t* dst = &Bs(buf)[(8 * (f % QCQ)) * LDS_ROW + QR * (f / QCQ)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t o[QR / 2];
+#pragma unroll
+          for (int d = 0; d < QR / 2; ++d) o[d] = ok ? wq_pack(v[2 * d][e], v[2 * d + 1][e]) : 0u;
+          if constexpr (QR == 8) {
+            *reinterpret_cast<u32x4*>(dst + e * LDS_ROW) = u32x4{o[0], o[1], o[2], o[3]};
+          } else if constexpr (QR == 4) {
+            *reinterpret_cast<u32x2*>(dst + e * LDS_ROW) = u32x2{o[0], o[1]};
+          } else {
+            *reinterpret_cast<uint32_t*>(dst + e * LDS_ROW) = o[0];
+          }
+        }
+      }
+    } else if constexpr (FWD) {
 #pragma unroll
       for (int q = 0; q < BCH; ++q) {
         const int f = tid + NT * q;
@@ -389,7 +476,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 
 // Sum of the split partials in split order, then the unsplit kernel's
 // epilogue, row by row into the row's slot (Z = sum; Y = sum * cn/cd).
-__global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(GemmBf16Args p) {
+static __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(GemmBf16Args p) {
   const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int64_t total = p.M * p.Nc;
   if (i4 >= total) return;

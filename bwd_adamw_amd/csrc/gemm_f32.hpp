@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
 
 // Sum of the split partials in split order, then the epilogue of the unsplit
 // kernel (Z = sum; Y = sum * cn/cd per column).
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int nsplit,
+static __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int nsplit,
                                                             int64_t M, int64_t Nc, float* C,
                                                             float* C2, const float* cn,
                                                             const float* cd) {

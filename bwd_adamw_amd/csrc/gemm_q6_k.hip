@@ -1,0 +1,8 @@
+// bf16 GEMM instances for Q6_K frozen W (a translation unit of its own).
+#define LORA_WQ_INSTANCES
+#include "gemm_wq.hpp"
+
+namespace lora {
+template void launch_gemm_wq_tiles<WQ_Q6_K>(int, bool, bool, dim3, hipStream_t,
+                                            const prof::Scope&, const GemmBf16Args&);
+}  // namespace lora

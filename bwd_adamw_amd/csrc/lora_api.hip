@@ -15,6 +15,8 @@
 #include "fused.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
+#include "gemm_wq.hpp"
+#include "launch.hpp"
 #include "optim.hpp"
 #include "profile.hpp"
 #include "skinny.hpp"
@@ -28,6 +30,37 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 inline int64_t clampi(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// bf16 or block-quantized W: the frozen products run on bf16 MFMA.
+inline bool bf16_ops(int32_t w_dtype) { return w_dtype != LORA_F32; }
+
+// Planes of a block-quantized W [N, K] in one buffer: offset and size of
+// each (a missing plane sits at the end with size 0); returns the total, 0
+// for an invalid format or shape.
+size_t qweight_layout(int f, int64_t N, int64_t K, size_t off[4], size_t bytes[4]) {
+  if (!wq_quantized(f) || N <= 0 || K <= 0 || K % wq_super(f)) return 0;
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t rb = wq_plane_row_bytes(f, i, K);
+    off[i] = o;
+    bytes[i] = (size_t)(rb * N);
+    o = rup((int64_t)(o + bytes[i]), 256);
+  }
+  for (int i = 0; i < 4; ++i)
+    if (bytes[i] == 0) off[i] = o;
+  return o;
+}
+
+QPlanes qplanes(const lora_linear* L) {
+  QPlanes q;
+  size_t off[4], bytes[4];
+  qweight_layout(L->w_dtype, L->out_dim, L->in_dim, off, bytes);
+  for (int i = 0; i < 4; ++i) {
+    q.p[i] = (const uint8_t*)L->W + off[i];
+    q.bytes[i] = (uint32_t)bytes[i];
+  }
+  return q;
+}
 
 uint64_t host_mix(uint64_t z) {   // SplitMix64 output function (see common.hpp)
   z += 0x9E3779B97F4A7C15ull;
@@ -98,17 +131,12 @@ struct GemmPlan {
 // and split on the Qwen3-4B-shaped projections at 2048 and 4096 tokens with
 // operands read from HBM (mean error 4 %; the plan it picks is within 0.1 %
 // of the sweep's best in total).  dX's transposing loads take more registers
-// per stage, so its wide tiles keep one stage.
+// per stage, so its wide tiles keep one stage.  The rows are LORA_BF16_CFGS
+// (gemm_bf16.hpp).
 struct Bf16Cfg {
   int bm, bn, nt, wgm, bk, depth, dirs;
   double a_fwd, b_fwd, a_dx, b_dx;
 };
-#define LORA_BF16_CFGS(X)                                        \
-  X(0, 256, 256, 512, 2, 32, 3, 1, 0.409, 15.2, 0, 0)            \
-  X(1, 256, 256, 512, 2, 64, 1, 2, 0, 0, 0.479, 13.3)            \
-  X(2, 256, 128, 512, 2, 64, 2, 1, 0.482, 8.9, 0, 0)             \
-  X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.696, 7.3)             \
-  X(4, 128, 128, 512, 2, 64, 2, 3, 0.588, 5.1, 0.962, 4.6)
 constexpr Bf16Cfg kBf16Cfg[] = {
 #define LORA_CFG_ROW(i, bm, bn, nt, wgm, bk, d, dirs, af, bf, ad, bd) \
   {bm, bn, nt, wgm, bk, d, dirs, af, bf, ad, bd},
@@ -214,7 +242,7 @@ size_t carve(size_t& off, size_t bytes) {
 Layout make_layout(const lora_linear* L, int stack = 1) {
   Layout y;
   const int64_t T = L->tokens, K = L->in_dim, N = L->out_dim, r = L->rank;
-  const bool bf = L->w_dtype == LORA_BF16;
+  const bool bf = bf16_ops(L->w_dtype);
   const bool own = stack <= 1;
   y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, SK_C);
   y.strips = cdiv(N, SK_C);
@@ -275,13 +303,16 @@ int check_linear(const lora_linear* L) {
   if (!L) return LORA_E_INVALID;
   if (L->tokens <= 0 || L->in_dim <= 0 || L->out_dim <= 0 || L->rank <= 0) return LORA_E_SHAPE;
   if (L->rank > 128 || L->rank > L->in_dim || L->rank > L->out_dim) return LORA_E_SHAPE;
-  if (L->w_dtype != LORA_F32 && L->w_dtype != LORA_BF16) return LORA_E_DTYPE;
-  // bf16 operands are read with 32-bit byte offsets.
-  if (L->w_dtype == LORA_BF16 &&
+  const int32_t f = L->w_dtype;
+  if (f != LORA_F32 && f != LORA_BF16 && !wq_quantized(f)) return LORA_E_DTYPE;
+  // bf16 operands and W's planes are read with 32-bit byte offsets (for
+  // quantized W also from rows a tile past the end: in_dim <= 2^22).
+  if (bf16_ops(f) &&
       (L->in_dim * L->out_dim >= (1ll << 30) || L->tokens * L->in_dim >= (1ll << 30) ||
        L->tokens * L->out_dim >= (1ll << 30)))
     return LORA_E_SHAPE;
-  const int64_t q = L->w_dtype == LORA_BF16 ? 8 : 4;
+  if (wq_quantized(f) && (L->in_dim % wq_super(f) || L->in_dim > (1 << 22))) return LORA_E_SHAPE;
+  const int64_t q = bf16_ops(f) ? 8 : 4;
   if (L->in_dim % q || L->out_dim % q || L->rank % 4) return LORA_E_ALIGN;
   if (!L->W || !L->A || !L->B) return LORA_E_INVALID;
   if (!al16(L->W) || !al16(L->A) || !al16(L->B)) return LORA_E_ALIGN;
@@ -295,18 +326,6 @@ int check_linear(const lora_linear* L) {
 int hip_status() { return hipGetLastError() == hipSuccess ? LORA_OK : LORA_E_HIP; }
 
 // ----------------------------------------------------------- launchers ---
-// Every kernel goes through here: 256 threads per block, on the caller's
-// stream, with the profile's packet-timestamp events when one is open.
-template <typename F, typename... Args>
-void launch_n(F kern, dim3 grid, unsigned threads, hipStream_t st, const prof::Scope& ps,
-              Args... args) {
-  hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, st, ps.start(), ps.stop(), 0, args...);
-}
-template <typename F, typename... Args>
-void launch(F kern, dim3 grid, hipStream_t st, const prof::Scope& ps, Args... args) {
-  launch_n(kern, grid, 256u, st, ps, args...);
-}
-
 #define LORA_RP_DISPATCH_32(rp, call)                 \
   if (rp <= 16) {                                     \
     constexpr int RP = 16;                            \
@@ -376,6 +395,13 @@ void launch_gemm_f32(const GemmPlan& g, bool fwd, const GemmF32Args& a, hipStrea
 
 void launch_gemm_bf16_tiles(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st);
 
+// W operand of a bf16 product: the bf16 matrix, or a quantized W's planes.
+void set_w(GemmBf16Args& a, const lora_linear* L) {
+  a.wq = L->w_dtype;
+  if (wq_quantized(L->w_dtype)) a.q = qplanes(L);
+  else a.B = (const uint16_t*)L->W;
+}
+
 // The bf16 GEMM, then (split contraction) the fixed-order sum of its partials
 // with the unsplit kernel's epilogue.
 void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st) {
@@ -390,12 +416,22 @@ void launch_gemm_bf16(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStr
 
 void launch_gemm_bf16_tiles(const GemmPlan& g, bool fwd, const GemmBf16Args& a, hipStream_t st) {
   const dim3 grid((unsigned)(cdiv(a.Nc, g.bn) * cdiv(a.M, g.bm) * g.k.n));
-  prof::Scope ps(fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx", a.M, a.Nc, a.Kc,
-                 2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
-                 2.0 * (a.M * a.Kc + a.Nc * a.Kc) +
+  const bool quant = wq_quantized(a.wq);
+  double wbytes = 2.0 * a.Nc * a.Kc;
+  if (quant) wbytes = (double)a.q.bytes[0] + a.q.bytes[1] + a.q.bytes[2] + a.q.bytes[3];
+  prof::Scope ps(quant ? (fwd ? "gemm_wq_fwd" : "gemm_wq_dx") : (fwd ? "gemm_bf16_fwd" : "gemm_bf16_dx"),
+                 a.M, a.Nc, a.Kc, 2.0 * a.M * a.Nc * a.Kc + 2.0 * a.M * a.r * a.Nc,
+                 2.0 * a.M * a.Kc + wbytes +
                      4.0 * a.M * a.Nc * (g.k.n > 1 ? g.k.n : (a.sl[0].C2 ? 2 : 1)));
   const Bf16Cfg& c = kBf16Cfg[g.cfg];
   const bool exact = a.M % c.bm == 0 && a.Nc % c.bn == 0 && a.Kc % c.bk == 0;
+  switch (a.wq) {
+    case LORA_Q8_0: launch_gemm_wq_tiles<WQ_Q8_0>(g.cfg, fwd, exact, grid, st, ps, a); return;
+    case LORA_Q4_0: launch_gemm_wq_tiles<WQ_Q4_0>(g.cfg, fwd, exact, grid, st, ps, a); return;
+    case LORA_Q4_K: launch_gemm_wq_tiles<WQ_Q4_K>(g.cfg, fwd, exact, grid, st, ps, a); return;
+    case LORA_Q6_K: launch_gemm_wq_tiles<WQ_Q6_K>(g.cfg, fwd, exact, grid, st, ps, a); return;
+    default: break;
+  }
 #define LORA_BF16_TILE(i, BM_, BN_, NT_, WGM_, BK_, D_, DIRS_, AF_, BF_, AD_, BD_)            \
   if (g.cfg == i) {                                                                        \
     if (fwd) {                                                                             \
@@ -472,7 +508,7 @@ int prepare_fwd(const lora_linear* lin, const float* X, float* Y, float* U, floa
   const Layout y = make_layout(lin, stack);
   if (y.fwd_bytes && (!ws || ws_bytes < y.fwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
-  const bool bf = lin->w_dtype == LORA_BF16;
+  const bool bf = bf16_ops(lin->w_dtype);
   char* w = (char*)ws;
   float* Upart = y.down.n > 1 ? (float*)(w + y.upart) : nullptr;
   j.lin = lin;
@@ -570,10 +606,11 @@ void launch_fwd_plain(const FwdJob& j, hipStream_t st) {
   const int64_t T = j.T, K = j.K, N = j.N, r = j.r;
   launch_fwd_down(j, st);
   // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
-  if (lin->w_dtype == LORA_BF16) {
+  if (bf16_ops(lin->w_dtype)) {
     GemmBf16Args a;
     memset(&a, 0, sizeof(a));
-    a.A = j.Xbf; a.lda = K; a.B = (const uint16_t*)lin->W; a.ldb = K;
+    a.A = j.Xbf; a.lda = K; a.ldb = K;
+    set_w(a, lin);
     a.M = T; a.Nc = N; a.Kc = K; a.r = r;
     a.nslot = 1;
     a.sl[0] = bf16_fwd_slot(j);
@@ -651,7 +688,7 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   const Layout y = make_layout(lin, stack);
   if (y.bwd_bytes && (!ws || ws_bytes < y.bwd_bytes || !al16(ws))) return LORA_E_WORKSPACE;
   const int64_t T = lin->tokens, K = lin->in_dim, N = lin->out_dim, r = lin->rank;
-  const bool bf = lin->w_dtype == LORA_BF16;
+  const bool bf = bf16_ops(lin->w_dtype);
   char* w = (char*)ws;
   const int acc = accumulate ? 1 : 0;
   j.lin = lin;
@@ -859,13 +896,14 @@ void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
   const lora_linear* lin = jb.lin;
   const Layout& y = jb.y;
   const int64_t T = jb.T, K = jb.K, N = jb.N, r = jb.r;
-  const bool bf = lin->w_dtype == LORA_BF16;
+  const bool bf = bf16_ops(lin->w_dtype);
   launch_bwd_k3(jb, st);
   if (jb.dX) {
     if (bf) {
       GemmBf16Args a;
       memset(&a, 0, sizeof(a));
-      a.A = jb.o.gbf; a.lda = N; a.B = (const uint16_t*)lin->W; a.ldb = K;
+      a.A = jb.o.gbf; a.lda = N; a.ldb = K;
+      set_w(a, lin);
       a.M = T; a.Nc = K; a.Kc = N; a.r = r;
       a.nslot = 1;
       a.sl[0] = bf16_dx_slot(jb);
@@ -922,7 +960,7 @@ int check_slots(int n, const lora_linear* lins) {
 // slots run one after another.
 bool slots_stacked(int n, const lora_linear* lins) {
   const lora_linear& a = lins[0];
-  if (n < 2 || a.w_dtype != LORA_BF16 || a.tokens % 256) return false;
+  if (n < 2 || !bf16_ops(a.w_dtype) || a.tokens % 256) return false;
   const int64_t M = n * a.tokens;
   return M * a.in_dim < (1ll << 30) && M * a.out_dim < (1ll << 30);
 }
@@ -936,6 +974,14 @@ size_t slot_share_bytes(const lora_linear* L, int stack) {
 
 // =========================================================================
 extern "C" {
+
+size_t lora_qweight_layout(int32_t w_dtype, int64_t out_dim, int64_t in_dim, size_t* offsets) {
+  size_t off[4], bytes[4];
+  const size_t total = qweight_layout(w_dtype, out_dim, in_dim, off, bytes);
+  if (total && offsets)
+    for (int i = 0; i < 4; ++i) offsets[i] = off[i];
+  return total;
+}
 
 const char* lora_status_string(int s) {
   switch (s) {
@@ -1121,7 +1167,8 @@ int lora_forward_slots(int n, const lora_linear* lins, const float* const* X, fl
   for (int i = 0; i < n; ++i) launch_fwd_down(jobs[i], st);
   GemmBf16Args a;
   memset(&a, 0, sizeof(a));
-  a.A = xbf; a.lda = K; a.B = (const uint16_t*)lins[0].W; a.ldb = K;
+  a.A = xbf; a.lda = K; a.ldb = K;
+  set_w(a, &lins[0]);
   a.M = n * T; a.Nc = N; a.Kc = K; a.r = lins[0].rank;
   a.nslot = n; a.slot_rows = T;
   for (int i = 0; i < n; ++i) a.sl[i] = bf16_fwd_slot(jobs[i]);
@@ -1180,7 +1227,8 @@ int lora_backward_slots(int n, const lora_linear* lins, const float* const* X,
   if (want_dx) {
     GemmBf16Args a;
     memset(&a, 0, sizeof(a));
-    a.A = gbf; a.lda = N; a.B = (const uint16_t*)lins[0].W; a.ldb = K;
+    a.A = gbf; a.lda = N; a.ldb = K;
+    set_w(a, &lins[0]);
     a.M = n * T; a.Nc = K; a.Kc = N; a.r = lins[0].rank;
     a.nslot = n; a.slot_rows = T;
     for (int i = 0; i < n; ++i) a.sl[i] = bf16_dx_slot(jobs[i]);

@@ -23,12 +23,16 @@ __all__ = [
     "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
-    "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots", "EXPORTS",
+    "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
+    "lora_qweight_layout", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
 
 F32, BF16 = 0, 1
+# Block-quantized W formats (lora_dtype): code and plane names in layout order.
+Q_FORMATS = {"q8_0": (2, ("qs", "d")), "q4_0": (3, ("qs", "d")),
+             "q4_k": (4, ("qs", "sm", "dm")), "q6_k": (5, ("ql", "qh", "sc", "d"))}
 KIND_A, KIND_B, KIND_MAG = 0, 1, 2
 LORA_E_NONFINITE = -6
 
@@ -41,6 +45,7 @@ EXPORTS = (
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
+    "lora_qweight_layout",
 )
 
 
@@ -112,6 +117,7 @@ def lib() -> C.CDLL:
             "lora_slots_workspace_bytes": (SZ, [I32, P]),
             "lora_forward_slots": (I32, [I32, P, P, P, P, P, P, P, SZ, P]),
             "lora_backward_slots": (I32, [I32, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
+            "lora_qweight_layout": (SZ, [I32, I64, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -158,15 +164,59 @@ def _check(fn, rc):
         raise LoraError(fn, rc)
 
 
+def lora_qweight_layout(fmt: str, out_dim: int, in_dim: int):
+    """(total bytes, [offset of each plane]) of a block-quantized W."""
+    code, names = Q_FORMATS[fmt]
+    off = (C.c_size_t * 4)()
+    total = int(lib().lora_qweight_layout(code, int(out_dim), int(in_dim), off))
+    if total == 0:
+        raise ValueError(f"{fmt} cannot hold a [{out_dim}, {in_dim}] weight")
+    return total, [int(o) for o in off[: len(names)]]
+
+
+class QWeight:
+    """A block-quantized W [out_dim, in_dim] in the library's layout: one
+    uint8 device buffer holding the format's planes (include/lora.h)."""
+
+    def __init__(self, fmt: str, out_dim: int, in_dim: int, buf: torch.Tensor):
+        self.fmt, self.out_dim, self.in_dim, self.buf = fmt, int(out_dim), int(in_dim), buf
+        self.code = Q_FORMATS[fmt][0]
+
+    @property
+    def shape(self):
+        return (self.out_dim, self.in_dim)
+
+
+def _plane_row_bytes(fmt, K):
+    return {"q8_0": (K, K // 16), "q4_0": (K // 2, K // 16),
+            "q4_k": (K // 2, K // 16, K // 64),
+            "q6_k": (K // 2, K // 4, K // 16, K // 128)}[fmt]
+
+
+def qweight_pack(fmt: str, out_dim: int, in_dim: int, planes: dict, device="cuda") -> QWeight:
+    """Copy the planes (tensors of any dtype, by their bytes, row-major) into
+    one device buffer laid out by lora_qweight_layout."""
+    total, offs = lora_qweight_layout(fmt, out_dim, in_dim)
+    names = Q_FORMATS[fmt][1]
+    buf = torch.zeros(total, dtype=torch.uint8, device=device)
+    for name, off, rb in zip(names, offs, _plane_row_bytes(fmt, int(in_dim))):
+        raw = planes[name].contiguous().view(torch.uint8).reshape(-1)
+        if raw.numel() != rb * out_dim:
+            raise ValueError(f"{fmt} plane {name} holds {raw.numel()} bytes, the layout "
+                             f"needs {rb * out_dim}")
+        buf[off:off + raw.numel()].copy_(raw)
+    return QWeight(fmt, out_dim, in_dim, buf)
+
+
 def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None) -> LoraLinear:
-    """Descriptor of one adapted linear: W [N,K] (float32 or bfloat16),
-    A [r,K], B [N,r] float32, optional DoRA magnitude and norm [N]."""
-    if W.dtype == torch.float32:
-        wd = F32
-    elif W.dtype == torch.bfloat16:
-        wd = BF16
+    """Descriptor of one adapted linear: W [N,K] (float32 or bfloat16, or a
+    QWeight), A [r,K], B [N,r] float32, optional DoRA magnitude and norm [N]."""
+    if isinstance(W, QWeight):
+        wd = W.code
+    elif W.dtype in (torch.float32, torch.bfloat16):
+        wd = F32 if W.dtype == torch.float32 else BF16
     else:
-        raise TypeError(f"W must be float32 or bfloat16, got {W.dtype}")
+        raise TypeError(f"W must be float32, bfloat16 or a QWeight, got {W.dtype}")
     N, K = W.shape
     r = A.shape[0] if A is not None else 0
     if A is not None and tuple(A.shape) != (r, K):
@@ -176,9 +226,10 @@ def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None) -> LoraLi
     for t, nm in ((dora_mag, "dora_mag"), (dora_norm, "dora_norm")):
         if t is not None and t.numel() != N:
             raise ValueError(f"{nm} must hold {N} elements, got {t.numel()}")
-    return LoraLinear(int(tokens), int(K), int(N), int(r), wd, float(scale),
-                      _ptr(W, "W", None), _ptr(A, "A"), _ptr(B, "B"),
-                      _ptr(dora_mag, "dora_mag"), _ptr(dora_norm, "dora_norm"))
+    wptr = _ptr(W.buf, "W", torch.uint8) if isinstance(W, QWeight) else _ptr(W, "W", None)
+    return LoraLinear(int(tokens), int(K), int(N), int(r), wd, float(scale), wptr,
+                      _ptr(A, "A"), _ptr(B, "B"), _ptr(dora_mag, "dora_mag"),
+                      _ptr(dora_norm, "dora_norm"))
 
 
 def make_dropout(seed, step, ordinal, layer, proj, p) -> LoraDropout:

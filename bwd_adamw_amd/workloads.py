@@ -32,6 +32,7 @@ __all__ = [
     "tensor_seed",
     "draw",
     "linear_inputs",
+    "qweight_planes",
 ]
 
 
@@ -147,6 +148,52 @@ def draw(shape, key: tuple, dist: str, param: float, device="cpu") -> torch.Tens
         t = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
         return t.mul_(2.0 * param).sub_(param)
     raise ValueError(dist)
+
+
+def _gen(key: tuple, plane: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(tensor_seed(*key, 1 + plane, "W"))
+    return g
+
+
+def _ints(shape, lo, hi, dtype, key, plane, device):
+    """Seeded integers, uniform in [lo, hi)."""
+    t = torch.randint(lo, hi, shape, generator=_gen(key, plane, device), device=device,
+                      dtype=torch.int32)
+    return t.to(dtype)
+
+
+def _halves(shape, lo, hi, key, plane, device):
+    """Seeded float16 values, uniform in [lo, hi)."""
+    t = torch.rand(shape, generator=_gen(key, plane, device), device=device, dtype=torch.float32)
+    return t.mul_(hi - lo).add_(lo).to(torch.float16)
+
+
+def qweight_planes(fmt: str, N: int, K: int, key: tuple, device="cpu") -> dict:
+    """Seeded planes of a block-quantized W [N, K] (formats and plane layouts
+    as in include/lora.h), drawn directly: codes uniform over their range,
+    fp16 scales uniform in a band chosen so that the decoded weights spread
+    about as widely as W ~ N(0, 0.02).  key = (workload, slot, layer, proj);
+    field i is drawn from the "W" kind with chunk index 1 + i."""
+    if fmt == "q8_0":
+        return {"qs": _ints((N, K), -127, 128, torch.int8, key, 0, device),
+                "d": _halves((N, K // 32), 2.0e-4, 3.4e-4, key, 1, device)}
+    if fmt == "q4_0":
+        return {"qs": _ints((N, K // 2), 0, 256, torch.uint8, key, 0, device),
+                "d": _halves((N, K // 32), 3.2e-3, 5.4e-3, key, 1, device)}
+    if fmt == "q4_k":
+        sc = _ints((N, K // 32, 1), 32, 64, torch.uint8, key, 1, device)
+        mn = _ints((N, K // 32, 1), 0, 64, torch.uint8, key, 2, device)
+        d = _halves((N, K // 256, 1), 6.8e-5, 1.1e-4, key, 3, device)
+        dmin = _halves((N, K // 256, 1), 7.5e-4, 1.25e-3, key, 4, device)
+        return {"qs": _ints((N, K // 2), 0, 256, torch.uint8, key, 0, device),
+                "sm": torch.cat([sc, mn], dim=2), "dm": torch.cat([d, dmin], dim=2)}
+    if fmt == "q6_k":
+        return {"ql": _ints((N, K // 2), 0, 256, torch.uint8, key, 0, device),
+                "qh": _ints((N, K // 4), 0, 256, torch.uint8, key, 1, device),
+                "sc": _ints((N, K // 16), -32, 32, torch.int8, key, 2, device),
+                "d": _halves((N, K // 256), 2.0 ** -14, 2.0 ** -13, key, 3, device)}
+    raise ValueError(f"unknown format {fmt!r}")
 
 
 def linear_inputs(cfg: LoraConfig, layer: int, proj: Projection, slot: int = 0,

@@ -54,7 +54,30 @@ typedef enum lora_status {
   LORA_E_HIP = -7         /* a HIP runtime call failed                      */
 } lora_status;
 
-typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+/* Frozen-weight (and merge output) element types.  The block-quantized
+ * formats hold W for a quantized base model ("8. LoRA Fundamentals", opening
+ * paragraph and "Training decisions"; "Backward Bug Hunts and Vulkan Tiled
+ * GEMM", "The fix", for the pages' Q4_0, Q4_K and Q6_K frozen paths).  Their
+ * arithmetic is that of the GGUF block types of the same names; their
+ * storage is planar, one array per field, in one buffer (see
+ * lora_qweight_layout):
+ *   LORA_Q8_0  qs int8 [N,K]; d fp16 [N,K/32]                 w = d*q
+ *   LORA_Q4_0  qs u4 [N,K]; d fp16 [N,K/32]                   w = d*(q-8)
+ *   LORA_Q4_K  qs u4 [N,K]; sm u8 [N,K/32][2] = (sc, mn), each < 64;
+ *              dm fp16 [N,K/256][2] = (d, dmin)               w = d*sc*q - dmin*mn
+ *   LORA_Q6_K  ql u4 [N,K]; qh u2 [N,K]; sc int8 [N,K/16]; d fp16 [N,K/256]
+ *                                              w = d*sc*(q-32), q = ql | qh<<4
+ * u4 planes hold element 2j in the low nibble of byte j and element 2j+1 in
+ * the high nibble; the u2 plane holds element 4j+i in bits 2i..2i+1 of
+ * byte j.  K must be a multiple of 32 (Q8_0, Q4_0) or 256 (Q4_K, Q6_K). */
+typedef enum lora_dtype {
+  LORA_F32 = 0,
+  LORA_BF16 = 1,
+  LORA_Q8_0 = 2,
+  LORA_Q4_0 = 3,
+  LORA_Q4_K = 4,
+  LORA_Q6_K = 5
+} lora_dtype;
 
 /* Train-only inverted dropout on the LoRA-branch input ("4.3. Training
  * Guide", "Dropout"): a stateless hash of (seed, optimizer step,
@@ -80,21 +103,34 @@ typedef struct lora_dropout {
  * detached input (see lora_dora_row_norms).
  * Constraints: tokens, in_dim, out_dim > 0; in_dim and out_dim multiples of 4
  * (of 8 for bf16 W); rank a multiple of 4 with rank <= min(in_dim, out_dim,
- * 128).  W is float32 or bf16.  Any T is accepted (ragged tails are masked).
- * Every pointer, dora_mag and dora_norm included, is 16-byte aligned
- * (LORA_E_ALIGN otherwise).  bf16 W also needs in_dim*out_dim, tokens*in_dim
- * and tokens*out_dim below 2^30 (its operands are addressed with 32-bit byte
- * offsets; LORA_E_SHAPE otherwise). */
+ * 128).  W is float32, bf16 or block-quantized (lora_dtype; the quantized
+ * products run in bf16 on the decoded weights).  Any T is accepted (ragged
+ * tails are masked).  Every pointer, dora_mag and dora_norm included, is
+ * 16-byte aligned (LORA_E_ALIGN otherwise).  bf16 and quantized W also need
+ * in_dim*out_dim, tokens*in_dim and tokens*out_dim below 2^30 (their operands
+ * are addressed with 32-bit byte offsets; LORA_E_SHAPE otherwise), and
+ * quantized W an in_dim that is a whole number of its blocks (LORA_E_SHAPE).
+ * lora_dora_row_norms and lora_merge take float32 or bf16 W only. */
 typedef struct lora_linear {
   int64_t tokens, in_dim, out_dim, rank;
   int32_t w_dtype;          /* lora_dtype                                  */
   float scale;              /* alpha/rank or alpha/sqrt(rank)              */
-  const void* W;            /* [N,K] float32 or bf16                       */
+  const void* W;            /* [N,K] float32 or bf16, or the planes of a
+                               quantized W laid out by lora_qweight_layout */
   const float* A;           /* [r,K]                                       */
   const float* B;           /* [N,r]                                       */
   const float* dora_mag;    /* [N] or NULL                                 */
   const float* dora_norm;   /* [N] or NULL                                 */
 } lora_linear;
+
+/* Layout of a block-quantized W [out_dim, in_dim] in one buffer: the planes
+ * of the format (table at lora_dtype) in that order, each starting at a
+ * multiple of 256 bytes from the buffer's start.  Writes the byte offset of
+ * each plane to offsets[0..3] (formats with fewer planes get the total for
+ * the missing ones) and returns the total size in bytes; returns 0, writing
+ * nothing, for a format that is not block-quantized, non-positive sizes or
+ * an in_dim that is not a whole number of blocks.  offsets may be NULL. */
+size_t lora_qweight_layout(int32_t w_dtype, int64_t out_dim, int64_t in_dim, size_t* offsets);
 
 /* A run of parameters in the optimizer arena. kind 0 = LoRA A (decayed,
  * rate lr), 1 = LoRA B (never decayed, rate lr * plus_ratio), 2 = DoRA

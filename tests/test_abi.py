@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -68,6 +69,8 @@ def _lin(**kw):
     (dict(rank=32), -2), (dict(w_dtype=7), -3), (dict(in_dim=18), -4), (dict(rank=6), -4),
     (dict(W=None), -1), (dict(A=264), -4), (dict(dora_mag=256), -1),
     (dict(w_dtype=L.BF16, in_dim=20), -4),
+    (dict(w_dtype=2, in_dim=48), -2), (dict(w_dtype=4, in_dim=288), -2),
+    (dict(w_dtype=5, in_dim=1 << 23, out_dim=8), -2), (dict(w_dtype=6), -3),
 ])
 def test_invalid_descriptor_is_rejected_before_any_launch(kw, status):
     lin = _lin(**kw)
@@ -121,3 +124,31 @@ def test_binding_checks_factor_shapes_against_w():
         L.make_linear(W, torch.zeros(4, 16), torch.zeros(64, 4), 1.0, 8)
     with pytest.raises(ValueError, match="dora_mag"):
         L.make_linear(W, torch.zeros(4, 32), torch.zeros(64, 4), 1.0, 8, torch.zeros(63))
+
+
+@pytest.mark.parametrize("fmt", sorted(L.Q_FORMATS))
+@pytest.mark.parametrize("N,K", [(8, 256), (264, 512), (4096, 2560)])
+def test_qweight_layout_holds_the_documented_planes(fmt, N, K):
+    """Plane offsets are 256-byte aligned, in table order, each plane fits
+    before the next one, and the total covers the last."""
+    from oracle import quant as Q
+    if K % Q.SUPER[fmt]:
+        assert L.lib().lora_qweight_layout(L.Q_FORMATS[fmt][0], N, K, None) == 0
+        return
+    total, offs = L.lora_qweight_layout(fmt, N, K)
+    shapes = Q.plane_shapes(fmt, N, K)
+    names = L.Q_FORMATS[fmt][1]
+    assert list(names) == list(shapes)
+    ends = offs[1:] + [total]
+    for name, off, end in zip(names, offs, ends):
+        dt, shp = shapes[name]
+        nbytes = int(np.prod(shp)) * np.dtype(dt).itemsize
+        assert off % 256 == 0 and off + nbytes <= end and end - (off + nbytes) < 256
+    assert total % 256 == 0
+
+
+def test_qweight_layout_rejects_non_block_shapes():
+    code = L.Q_FORMATS["q6_k"][0]
+    assert L.lib().lora_qweight_layout(code, 16, 128, None) == 0
+    assert L.lib().lora_qweight_layout(code, 0, 256, None) == 0
+    assert L.lib().lora_qweight_layout(L.BF16, 16, 256, None) == 0

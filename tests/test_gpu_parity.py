@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle as O
+from oracle import quant as Q
 from bwd_adamw_amd import lora as L
 from bwd_adamw_amd import step as S
 from bwd_adamw_amd import workloads as WL
@@ -22,6 +23,7 @@ from tests.helpers import np64, rel_err
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL.update({f: TOL["bf16"] for f in Q.FORMATS})   # bf16 products on the decoded weights
 
 
 def _say(*a):
@@ -34,7 +36,11 @@ def _linear_case(T, K, N, r, w_dtype="f32", seed=0, x_std=1.0, dy_std=1.0, b_std
     key = lambda kind, c=0: (900 + seed, 0, 0, 0, c, kind)
     W = WL.draw((N, K), key("W"), "normal", 0.02, device)
     out = {}
-    if w_dtype == "bf16":
+    if w_dtype in Q.FORMATS:
+        planes = WL.qweight_planes(w_dtype, N, K, (900 + seed, 0, 0, 0))
+        out["Wq"] = ("qweight", w_dtype, N, K, planes)
+        W = torch.from_numpy(Q.dequantize(w_dtype, {k: v.numpy() for k, v in planes.items()}))
+    elif w_dtype == "bf16":
         out["Wq"] = W.to(torch.bfloat16)
         W = out["Wq"].float()
     else:
@@ -48,7 +54,15 @@ def _linear_case(T, K, N, r, w_dtype="f32", seed=0, x_std=1.0, dy_std=1.0, b_std
 
 
 def _gpu(d):
-    return {k: v.to(DEV) for k, v in d.items()}
+    """Device copies; a quantized W is packed into the library's layout."""
+    out = {}
+    for k, v in d.items():
+        if isinstance(v, tuple) and v[0] == "qweight":
+            _, fmt, N, K, planes = v
+            out[k] = L.qweight_pack(fmt, N, K, {n: t.to(DEV) for n, t in planes.items()})
+        else:
+            out[k] = v.to(DEV)
+    return out
 
 
 def _run_gpu(c, s, p=0.0, dkeys=(1234, 0, 0, 0, 0), dora=False, accumulate=False):
@@ -151,6 +165,77 @@ def test_linear_forward_backward_parity(case):
         _say(f"  {n}: rel err {e:.3e}")
         assert torch.isfinite(got[n]).all(), f"{n} has unwritten (NaN) elements"
         assert e <= tol, (n, e)
+
+
+QUANT_CASES = [
+    # name, format, T, K, N, r, scale, dropout p
+    ("q8_0-ragged", "q8_0", 100, 544, 264, 8, 2.0, 0.1),
+    ("q4_0-ragged", "q4_0", 300, 1056, 520, 16, 2.0, 0.1),
+    ("q4_k-tiles", "q4_k", 256, 512, 264, 32, math.sqrt(32), 0.0),
+    ("q6_k-ragged", "q6_k", 72, 768, 136, 8, 2.0, 0.1),
+    ("q4_k-qwen-wq-slice", "q4_k", 256, 2560, 4096, 32, math.sqrt(32), 0.0),
+    ("q6_k-qwen-wdown-slice", "q6_k", 256, 9728, 2560, 32, math.sqrt(32), 0.1),
+    ("q4_0-split-k", "q4_0", 64, 4096, 512, 16, 2.0, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_quantized_w_forward_backward_parity(case):
+    """Block-quantized frozen W against the oracle on the decoded weights,
+    at the bf16 bar (the products run in bf16 on the decoded W)."""
+    name, fmt, T, K, N, r, s, p = case
+    _say("quantized linear", name)
+    c = _linear_case(T, K, N, r, fmt, seed=zlib.crc32(name.encode()) % 1000, dy_std=1e-2)
+    dk = (1234, 2, 1, 3, 4)
+    got = _run_gpu(c, s, p, dk)
+    ref = _oracle(c, s, p, dk)
+    for n in ("Y", "U", "dX", "dA", "dB"):
+        e = rel_err(got[n], ref[n])
+        _say(f"  {n}: rel err {e:.3e}")
+        assert torch.isfinite(got[n]).all(), f"{n} has unwritten (NaN) elements"
+        assert e <= TOL[fmt], (n, e)
+
+
+def _exact_planes(fmt, planes, seed):
+    """Scales that make every decoded weight a bf16 value: powers of two and
+    small sub-scales (and Q4_K's dmin equal to d, with mins below 16)."""
+    g = torch.Generator().manual_seed(seed)
+    pl = dict(planes)
+    pow2 = lambda shape: (2.0 ** -torch.randint(6, 12, shape, generator=g)).to(torch.float16)
+    if fmt in ("q8_0", "q4_0"):
+        pl["d"] = pow2(planes["d"].shape)
+    elif fmt == "q4_k":
+        d = pow2(planes["dm"].shape[:2] + (1,))
+        pl["dm"] = torch.cat([d, d], dim=2)
+        sc = torch.randint(1, 8, planes["sm"].shape[:2] + (1,), generator=g).to(torch.uint8)
+        mn = torch.randint(0, 16, planes["sm"].shape[:2] + (1,), generator=g).to(torch.uint8)
+        pl["sm"] = torch.cat([sc, mn], dim=2)
+    else:
+        pl["d"] = pow2(planes["d"].shape)
+        pl["sc"] = torch.randint(-3, 4, planes["sc"].shape, generator=g).to(torch.int8)
+    return pl
+
+
+@pytest.mark.parametrize("fmt,T,K,N", [("q8_0", 100, 544, 264), ("q4_0", 130, 1024, 520),
+                                       ("q4_k", 256, 512, 264), ("q6_k", 72, 768, 136)])
+def test_quantized_w_equals_bf16_w_when_exact(fmt, T, K, N):
+    """When every decoded weight is a bf16 value, the quantized path stages
+    bitwise the tiles the bf16 path stages: all outputs are equal."""
+    r = 8
+    _say("quantized vs bf16", fmt, T, K, N)
+    c = _linear_case(T, K, N, r, fmt, seed=31)
+    _, _, _, _, planes = c["Wq"]
+    planes = _exact_planes(fmt, planes, 7)
+    c["Wq"] = ("qweight", fmt, N, K, planes)
+    W = Q.dequantize(fmt, {k: v.numpy() for k, v in planes.items()})
+    Wb = torch.from_numpy(W).to(torch.bfloat16)
+    assert np.array_equal(Wb.double().numpy(), W)
+    cb = dict(c)
+    cb["Wq"], cb["W"] = Wb, Wb.float()
+    a = _run_gpu(c, 2.0, 0.1)
+    b = _run_gpu(cb, 2.0, 0.1)
+    for n in ("Y", "U", "dX", "dA", "dB"):
+        assert torch.equal(a[n], b[n]), n
 
 
 @pytest.mark.parametrize("T,K,N,r", [(64, 128, 96, 8), (128, 1024, 512, 8)])
@@ -740,9 +825,9 @@ def test_merge_checks_its_workspace():
 
 
 # ------------------------------------------------------------ slots ---------
-def _slot_cases(T, K, N, r, n, seed):
-    """n adapter slots over one bf16 W: own X, dY, A, B per slot."""
-    cs = [_linear_case(T, K, N, r, "bf16", seed=seed + i, b_std=0.05) for i in range(n)]
+def _slot_cases(T, K, N, r, n, seed, w_dtype="bf16"):
+    """n adapter slots over one bf16 (or quantized) W: own X, dY, A, B per slot."""
+    cs = [_linear_case(T, K, N, r, w_dtype, seed=seed + i, b_std=0.05) for i in range(n)]
     for c in cs[1:]:
         c["Wq"], c["W"] = cs[0]["Wq"], cs[0]["W"]
     return cs
@@ -796,6 +881,7 @@ SLOT_CASES = [
     ("pair-stacked-dora", 256, 520, 264, 32, 2, 0.1, True),
     ("four-stacked", 256, 136, 272, 8, 4, 0.0, False),
     ("qwen-wgate-pair", 512, 2560, 9728, 64, 2, 0.1, True),
+    ("q4_k-pair-stacked", 256, 512, 264, 16, 2, 0.1, False, "q4_k"),
 ]
 
 
@@ -803,9 +889,10 @@ SLOT_CASES = [
 def test_slots_match_oracle(case):
     """Each slot of a stacked slot call against the oracle (two accumulated
     chunks), at the bf16-W bar."""
-    name, T, K, N, r, n, p, dora = case
+    name, T, K, N, r, n, p, dora = case[:8]
+    wd = case[8] if len(case) > 8 else "bf16"
     _say("slots", name)
-    cs = _slot_cases(T, K, N, r, n, seed=zlib.crc32(name.encode()) % 1000)
+    cs = _slot_cases(T, K, N, r, n, seed=zlib.crc32(name.encode()) % 1000, w_dtype=wd)
     got, mags, nrms = _run_slots(cs, 1.5, p, together=True, dora=dora)
     for i, c in enumerate(cs):
         refs = []
