@@ -33,9 +33,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Block-quantized frozen W for the bf16 workloads: one format for every
+# projection, or "q4_k_m", a mix in the manner of the pages' Q4_K_M base
+# (wv and wdown in Q6_K, the other projections in Q4_K).
+W_FORMATS = ("q8_0", "q4_0", "q4_k", "q6_k", "q4_k_m")
+
+
+def projection_format(w_format, proj):
+    if w_format == "q4_k_m":
+        return "q6_k" if proj.name in ("wv", "wdown") else "q4_k"
+    return w_format
+
+
 def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
-    """Frozen model, slots and per-slot chunk inputs, all seeded."""
+    """Frozen model, slots and per-slot chunk inputs, all seeded.  A
+    workload whose w_dtype names a block-quantized format gets W drawn as
+    that format's planes."""
     import torch
+    from bwd_adamw_amd import lora as L
     from bwd_adamw_amd import step as S
     from bwd_adamw_amd import workloads as WL
 
@@ -45,6 +60,12 @@ def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
     Wq = {}
     for l in range(layers):
         for pj in cfg.projections:
+            if cfg.w_dtype in W_FORMATS:
+                fmt = projection_format(cfg.w_dtype, pj)
+                planes = WL.qweight_planes(fmt, pj.out_dim, pj.in_dim,
+                                           (cfg.number, 0, l, pj.ordinal), device=device)
+                Wq[(l, pj.ordinal)] = L.qweight_pack(fmt, pj.out_dim, pj.in_dim, planes, device)
+                continue
             inp = WL.linear_inputs(cfg, l, pj, chunks=0, tokens=T, device=device)
             Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"])
     model = S.FrozenModel(cfg, Wq)
@@ -138,7 +159,7 @@ def roofline_of(entries, cfg):
     dom = max(entries, key=lambda e: e["total_ms"])
     sec = dom["avg_ms"] / 1e3
     if dom["kernel"].startswith("gemm"):
-        peak = PEAK["bf16" if "bf16" in dom["kernel"] else "f32"]
+        peak = PEAK["f32" if "f32" in dom["kernel"] else "bf16"]
         achieved = dom["flops"] / sec / 1e12
         rl = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
     else:
@@ -160,7 +181,7 @@ def kernel_table(entries, total_ms):
         row = {"kernel": e["kernel"], "shape": [e["M"], e["N"], e["K"]], "launches": e["launches"],
                "avg_us": round(e["avg_ms"] * 1e3, 3), "share": round(e["total_ms"] / total_ms, 4)}
         if e["kernel"].startswith("gemm"):
-            peak = PEAK["bf16" if "bf16" in e["kernel"] else "f32"]
+            peak = PEAK["f32" if "f32" in e["kernel"] else "bf16"]
             row["tflops"] = round(e["flops"] / sec / 1e12, 2)
             row["frac_mfma"] = round(e["flops"] / sec / 1e12 / peak, 4)
         else:
@@ -190,7 +211,13 @@ def cpu_baseline(cfg, budget_s):
         for pj in cfg.projections:
             inp = WL.linear_inputs(cfg, l, pj)
             key = (l, pj.ordinal)
-            lin[key] = f64(inp["W"])
+            if cfg.w_dtype in W_FORMATS:
+                from oracle import quant as Q
+                fmt = projection_format(cfg.w_dtype, pj)
+                planes = WL.qweight_planes(fmt, pj.out_dim, pj.in_dim, (cfg.number, 0, l, pj.ordinal))
+                lin[key] = Q.dequantize(fmt, {k: v.numpy() for k, v in planes.items()})
+            else:
+                lin[key] = f64(inp["W"])
             params[key] = {"A": f64(inp["A"]), "B": f64(inp["B"])}
             if cfg.dora:
                 params[key]["mag"] = O.dora_row_norms(lin[key])
@@ -243,6 +270,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2,
                     help="workload number (default: the TinyLlama-shaped wq+wv workload)")
+    ap.add_argument("--w-format", choices=W_FORMATS, default=None,
+                    help="block-quantized frozen W for a bf16 workload (default: its bf16 W)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -266,6 +295,13 @@ def main():
         return
     L.lib()
     cfg = WL.get_config(args.config)
+    if args.w_format:
+        if cfg.w_dtype != "bf16" or cfg.dora:
+            log("bench.py: --w-format applies to the bf16 workloads without DoRA")
+            sys.exit(2)
+        import dataclasses
+        cfg = dataclasses.replace(cfg, w_dtype=args.w_format,
+                                  name=cfg.name.replace("-bf16-", f"-{args.w_format}-"))
     dev = "cuda"
     t0 = time.perf_counter()
     model, trainer, slots, inputs = build_workload(cfg, dev)
@@ -306,7 +342,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.w_dtype == "bf16" else "f32",
+        "dtype": "f32" if cfg.w_dtype == "f32" else "bf16",
         "data": "synthetic (seeded; inputs resident in HBM)",
         "config": {
             "workload": cfg.name, "layers": cfg.layers,

@@ -926,13 +926,13 @@ void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
   launch_bwd_k4(jb, st);
 }
 
-// Linears of a group read one X: equal token count, input width and dtype.
+// Linears of a group read one X: equal token count and input width.  Each
+// is planned on its own, so their W types may differ.
 int check_group(int n, const lora_linear* lins) {
   for (int i = 0; i < n; ++i) {
     const int rc = check_linear(&lins[i]);
     if (rc) return rc;
     if (lins[i].tokens != lins[0].tokens || lins[i].in_dim != lins[0].in_dim) return LORA_E_SHAPE;
-    if (lins[i].w_dtype != lins[0].w_dtype) return LORA_E_DTYPE;
   }
   return LORA_OK;
 }

@@ -31,8 +31,17 @@ from .workloads import LoraConfig
 __all__ = ["FrozenModel", "Slot", "Trainer"]
 
 
+def _w_desc(W):
+    """lora_dtype code and device address of a frozen weight (a float32 or
+    bfloat16 tensor, or a QWeight)."""
+    if isinstance(W, L.QWeight):
+        return W.code, W.buf.data_ptr()
+    return (L.BF16 if W.dtype == torch.bfloat16 else L.F32), W.data_ptr()
+
+
 class FrozenModel:
-    """The frozen weights of every adapted linear, keyed (layer, proj ordinal)."""
+    """The frozen weights of every adapted linear, keyed (layer, proj ordinal):
+    float32 or bfloat16 tensors, or block-quantized QWeights."""
 
     def __init__(self, cfg: LoraConfig, weights: dict):
         self.cfg = cfg
@@ -102,9 +111,10 @@ class Trainer:
         self.model = model
         self.T = cfg.tokens if tokens is None else int(tokens)
         # Slots over one W run their frozen products stacked (one pass over W
-        # per product) when the library can: bf16 W and whole 256-row tiles.
+        # per product) when the library can: bf16 or quantized W and whole
+        # 256-row tiles.
         self.nslots = int(slots)
-        self.stack_slots = (self.nslots > 1 and cfg.w_dtype == "bf16" and self.T % 256 == 0)
+        self.stack_slots = (self.nslots > 1 and cfg.w_dtype != "f32" and self.T % 256 == 0)
         self.scale = L.lora_scaling(cfg.alpha, cfg.rank, cfg.scaling == "rslora")
         self.device = device
         f32 = dict(device=device, dtype=torch.float32)
@@ -154,8 +164,8 @@ class Trainer:
         r = self.cfg.rank
         if slot is None:   # shape-only descriptor for workspace sizing (never launched)
             aligned = 256
-            return L.LoraLinear(self.T, K, N, r, L.BF16 if W.dtype == torch.bfloat16 else L.F32,
-                                float(self.scale), W.data_ptr(), aligned, aligned,
+            wd, wp = _w_desc(W)
+            return L.LoraLinear(self.T, K, N, r, wd, float(self.scale), wp, aligned, aligned,
                                 aligned if dora else None, aligned if dora else None)
         mag = slot.mag.get(key) if dora else None
         nrm = slot.norm.get(key) if dora else None
@@ -166,9 +176,8 @@ class Trainer:
         for key in self.model.keys:
             W = self.model.W[key]
             K, N = self.model.shape[key]
-            wd = L.BF16 if W.dtype == torch.bfloat16 else L.F32
-            bare = L.LoraLinear(self.T, K, N, 0, wd, float(self.scale), W.data_ptr(),
-                                None, None, None, None)
+            wd, wp = _w_desc(W)
+            bare = L.LoraLinear(self.T, K, N, 0, wd, float(self.scale), wp, None, None, None, None)
             L.lora_dora_row_norms(bare, slot.mag[key], self.ws)
             slot.norm[key] = torch.empty(N, device=self.device, dtype=torch.float32)
         self.refresh_dora(slot)

@@ -58,7 +58,7 @@ class LoraConfig:
     rank: int = 8
     alpha: float = 16.0
     scaling: str = "standard"   # or "rslora"
-    w_dtype: str = "f32"        # or "bf16"
+    w_dtype: str = "f32"        # "bf16", or a block-quantized format (bench --w-format)
     w_std: float = 0.02
     x_std: float = 1.0
     dy_std: float = 1.0

@@ -188,8 +188,8 @@ int lora_backward(const lora_linear* lin, const float* X, const float* dY,
  * list) may run as a group: the same results, bitwise, as calling
  * lora_forward / lora_backward on each in turn, with the group's launches
  * shared where the kernels allow (short chunks with fp32 W).  All linears of
- * a group must have equal tokens, in_dim and w_dtype (else LORA_E_SHAPE /
- * LORA_E_DTYPE); 1 <= n <= LORA_MAX_GROUP.  Array arguments hold one entry
+ * a group must have equal tokens and in_dim (else LORA_E_SHAPE); their W
+ * types may differ (a quantized base mixes formats); 1 <= n <= LORA_MAX_GROUP.  Array arguments hold one entry
  * per linear, in the order of `lins`; Z, dX, dMag and drops may be NULL as a
  * whole (meaning NULL for every linear) or hold NULL entries.  The group
  * workspace is the per-linear workspaces laid end to end (each rounded up to

@@ -641,9 +641,12 @@ def test_workspace_contents_do_not_matter(T, K, N, r):
 
 
 # ------------------------------------------------------------- groups -------
-def _group_case(T, K, Ns, rs, seed):
-    """Linears that read one X: per-linear W, A, B, dY; one shared X."""
-    cs = [_linear_case(T, K, N, r, seed=seed + i) for i, (N, r) in enumerate(zip(Ns, rs))]
+def _group_case(T, K, Ns, rs, seed, fmts=None):
+    """Linears that read one X: per-linear W (float32, or the given formats),
+    A, B, dY; one shared X."""
+    fmts = fmts or ["f32"] * len(Ns)
+    cs = [_linear_case(T, K, N, r, f, seed=seed + i)
+          for i, (N, r, f) in enumerate(zip(Ns, rs, fmts))]
     for c in cs[1:]:
         c["X"] = cs[0]["X"]
     return cs
@@ -693,6 +696,7 @@ GROUP_CASES = [
     ("mixed-rank-pair", 128, 1024, [512, 768], [8, 40], 0.1),     # one linear off the split path
     ("triple", 72, 520, [264, 136, 520], [4, 8, 16], 0.1),          # more than two: one at a time
     ("bf16-pair", 64, 264, [136, 272], [8, 8], 0.1),
+    ("q4_k-q6_k-pair", 96, 512, [264, 136], [8, 16], 0.1),        # a quantized base mixes formats
 ]
 
 
@@ -702,7 +706,8 @@ def test_group_calls_equal_single_calls(case):
     (the same kernels and fixed-order sums, only sharing launches)."""
     name, T, K, Ns, rs, p = case
     _say("group", name)
-    cs = _group_case(T, K, Ns, rs, seed=zlib.crc32(name.encode()) % 1000)
+    fmts = ["q4_k", "q6_k"] if name.startswith("q4_k-q6_k") else None
+    cs = _group_case(T, K, Ns, rs, seed=zlib.crc32(name.encode()) % 1000, fmts=fmts)
     if name.startswith("bf16"):
         for c in cs:
             c["Wq"] = c["W"].to(torch.bfloat16)
