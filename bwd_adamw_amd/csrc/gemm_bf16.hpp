@@ -93,11 +93,11 @@ LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
 // flight, directions (1 forward, 2 dX), then the host planner's fitted cost
 // coefficients (forward a, b; dX a, b).
 #define LORA_BF16_CFGS(X)                                        \
-  X(0, 256, 256, 512, 2, 32, 3, 1, 0.409, 15.2, 0, 0)            \
-  X(1, 256, 256, 512, 2, 64, 1, 2, 0, 0, 0.479, 13.3)            \
-  X(2, 256, 128, 512, 2, 64, 2, 1, 0.482, 8.9, 0, 0)             \
-  X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.696, 7.3)             \
-  X(4, 128, 128, 512, 2, 64, 2, 3, 0.588, 5.1, 0.962, 4.6)
+  X(0, 256, 256, 512, 2, 32, 3, 1, 0.417, 16.4, 0, 0)            \
+  X(1, 256, 256, 512, 2, 64, 1, 3, 0.393, 14.7, 0.475, 14.1)     \
+  X(2, 256, 128, 512, 2, 64, 2, 1, 0.483, 9.5, 0, 0)             \
+  X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.705, 7.8)             \
+  X(4, 128, 128, 512, 2, 64, 2, 3, 0.581, 5.4, 0.967, 5.1)
 
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }

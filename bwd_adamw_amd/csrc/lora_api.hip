@@ -129,9 +129,10 @@ struct GemmPlan {
 // per direction: a microseconds per million (contraction length x tile area)
 // plus b microseconds.  a and b were fitted to a sweep of every configuration
 // and split on the Qwen3-4B-shaped projections at 2048 and 4096 tokens with
-// operands read from HBM (mean error 4 %; the plan it picks is within 0.1 %
-// of the sweep's best in total).  dX's transposing loads take more registers
-// per stage, so its wide tiles keep one stage.  The rows are LORA_BF16_CFGS
+// operands read from HBM (mean error 3.4 %; the plans it picks are within
+// 0.4 % of the sweep's best in total).  The wide tile runs its K-steps of 64
+// with one stage in flight in both directions: fewer barriers per MFMA beat
+// deeper staging.  The rows are LORA_BF16_CFGS
 // (gemm_bf16.hpp).
 struct Bf16Cfg {
   int bm, bn, nt, wgm, bk, depth, dirs;
@@ -147,7 +148,7 @@ constexpr int kBf16NCfg = sizeof(kBf16Cfg) / sizeof(kBf16Cfg[0]);
 constexpr int kBf16Slots = 256;  // resident tiles per round
 // Cost of a split's fp32 partials (written once, read once by the reduction
 // that also writes the result): microseconds per MB, from the same fit.
-constexpr double kSplitUsPerMB = 0.103;
+constexpr double kSplitUsPerMB = 0.102;
 
 // bf16: the configuration and contraction split (whole K-steps per split,
 // at least 8 of them) with the least estimated time.
