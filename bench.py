@@ -296,8 +296,8 @@ def main():
     L.lib()
     cfg = WL.get_config(args.config)
     if args.w_format:
-        if cfg.w_dtype != "bf16" or cfg.dora:
-            log("bench.py: --w-format applies to the bf16 workloads without DoRA")
+        if cfg.w_dtype != "bf16":
+            log("bench.py: --w-format applies to the bf16 workloads")
             sys.exit(2)
         import dataclasses
         cfg = dataclasses.replace(cfg, w_dtype=args.w_format,

@@ -1,9 +1,11 @@
-// Launch of the bf16 GEMM's block-quantized-W instances.  Each format's
-// instances live in a translation unit of their own (gemm_q*.hip), so that
-// the library's objects compile in parallel.
+// Launch of the block-quantized-W instances of the bf16 GEMM and of the row
+// pass (DoRA norms, merge).  Each format's instances live in a translation
+// unit of their own (gemm_q*.hip), so that the library's objects compile in
+// parallel.
 #pragma once
 #include "gemm_bf16.hpp"
 #include "launch.hpp"
+#include "rowpass.hpp"
 
 namespace lora {
 
@@ -13,7 +15,28 @@ template <int WQ>
 void launch_gemm_wq_tiles(int cfg, bool fwd, bool exact, dim3 grid, hipStream_t st,
                           const prof::Scope& ps, const GemmBf16Args& a);
 
+// The row pass over W in format WQ: mode 0 DoRA norms, 1 merge (bf16 or
+// float32 output); lora_on adds s B A at padded rank rp.
+template <int WQ>
+void launch_row_pass_wq(int mode, bool lora_on, int rp, bool out_bf16, dim3 grid, hipStream_t st,
+                        const prof::Scope& ps, const RowPassArgs& a);
+
 #ifdef LORA_WQ_INSTANCES
+template <int WQ>
+void launch_row_pass_wq(int mode, bool lora_on, int rp, bool out_bf16, dim3 grid, hipStream_t st,
+                        const prof::Scope& ps, const RowPassArgs& a) {
+#define LORA_WQ_ROWS(RP_, LORA_)                                                               \
+  if (mode == 0) launch(row_pass_kernel<uint8_t, RP_, LORA_, 0, float, WQ>, grid, st, ps, a);   \
+  else if (out_bf16) launch(row_pass_kernel<uint8_t, RP_, LORA_, 1, uint16_t, WQ>, grid, st, ps, a); \
+  else launch(row_pass_kernel<uint8_t, RP_, LORA_, 1, float, WQ>, grid, st, ps, a);
+  if (!lora_on) { LORA_WQ_ROWS(16, false) }
+  else if (rp <= 16) { LORA_WQ_ROWS(16, true) }
+  else if (rp <= 32) { LORA_WQ_ROWS(32, true) }
+  else if (rp <= 64) { LORA_WQ_ROWS(64, true) }
+  else { LORA_WQ_ROWS(128, true) }
+#undef LORA_WQ_ROWS
+}
+
 template <int WQ>
 void launch_gemm_wq_tiles(int cfg, bool fwd, bool exact, dim3 grid, hipStream_t st,
                           const prof::Scope& ps, const GemmBf16Args& a) {

@@ -1375,14 +1375,45 @@ DoraNormPlan dora_norm_plan(int64_t N, int64_t K, int rp, bool split, int mode =
 
 int check_row_norm_linear(const lora_linear* lin) {
   if (!lin) return LORA_E_INVALID;
-  // in_dim <= 2^22 keeps the kernel's buffer offsets within 32 bits.
+  // in_dim <= 2^22 keeps the kernel's buffer offsets within 32 bits (for
+  // quantized W also every plane: in_dim * out_dim < 2^30).
   if (lin->in_dim <= 0 || lin->out_dim <= 0 || lin->in_dim > (1 << 22)) return LORA_E_SHAPE;
-  if (lin->w_dtype != LORA_F32 && lin->w_dtype != LORA_BF16) return LORA_E_DTYPE;
+  const int32_t f = lin->w_dtype;
+  if (f != LORA_F32 && f != LORA_BF16 && !wq_quantized(f)) return LORA_E_DTYPE;
+  if (wq_quantized(f) &&
+      (lin->in_dim % wq_super(f) || lin->in_dim * lin->out_dim >= (1ll << 30)))
+    return LORA_E_SHAPE;
   if (!lin->W) return LORA_E_INVALID;
   if ((lin->A == nullptr) != (lin->B == nullptr)) return LORA_E_INVALID;
   if (lin->A && (lin->rank <= 0 || lin->rank > 128)) return LORA_E_SHAPE;
   if (!std::isfinite(lin->scale)) return LORA_E_INVALID;
   return LORA_OK;
+}
+
+// Bytes of W per element for the launch records, and whether W and A rows
+// allow the row pass's 16-byte loads (quantized W is read in runs).
+double row_pass_w_bytes(const lora_linear* lin) {
+  if (!wq_quantized(lin->w_dtype)) return lin->w_dtype == LORA_BF16 ? 2.0 : 4.0;
+  size_t off[4], bytes[4];
+  qweight_layout(lin->w_dtype, lin->out_dim, lin->in_dim, off, bytes);
+  return (double)(bytes[0] + bytes[1] + bytes[2] + bytes[3]) /
+         ((double)lin->out_dim * (double)lin->in_dim);
+}
+int row_pass_vec(const lora_linear* lin) {
+  const bool a_ok = !lin->A || (al16(lin->A) && lin->in_dim % 4 == 0);
+  if (wq_quantized(lin->w_dtype)) return a_ok;
+  const int64_t wsz = lin->w_dtype == LORA_BF16 ? 2 : 4;
+  return al16(lin->W) && (lin->in_dim * wsz) % 16 == 0 && a_ok;
+}
+void launch_row_pass_quant(const lora_linear* lin, int mode, bool lora_on, int rp, bool out_bf16,
+                           dim3 grid, hipStream_t st, const prof::Scope& ps, RowPassArgs& a) {
+  a.q = qplanes(lin);
+  switch (lin->w_dtype) {
+    case LORA_Q8_0: launch_row_pass_wq<WQ_Q8_0>(mode, lora_on, rp, out_bf16, grid, st, ps, a); break;
+    case LORA_Q4_0: launch_row_pass_wq<WQ_Q4_0>(mode, lora_on, rp, out_bf16, grid, st, ps, a); break;
+    case LORA_Q4_K: launch_row_pass_wq<WQ_Q4_K>(mode, lora_on, rp, out_bf16, grid, st, ps, a); break;
+    default: launch_row_pass_wq<WQ_Q6_K>(mode, lora_on, rp, out_bf16, grid, st, ps, a); break;
+  }
 }
 
 size_t lora_dora_row_norms_workspace_bytes(const lora_linear* lin) {
@@ -1402,7 +1433,7 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace
   const int rp = rank_pad(r);
   const DoraNormPlan q = dora_norm_plan(N, K, lora_on ? rp : 16, workspace != nullptr);
   if (q.nsplit > 1 && workspace_bytes < sizeof(double) * q.nsplit * N) return LORA_E_WORKSPACE;
-  const size_t wsz = lin->w_dtype == LORA_BF16 ? 2 : 4;
+  const double wsz = row_pass_w_bytes(lin);
   RowPassArgs a;
   memset(&a, 0, sizeof(a));
   a.W = lin->W;
@@ -1413,15 +1444,17 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace
   a.r = (int)r;
   a.s = lin->scale;
   a.cpw = (int)q.cpw;
-  a.vec = al16(lin->W) && (K * wsz) % 16 == 0 && (!lora_on || (al16(lin->A) && K % 4 == 0));
+  a.vec = row_pass_vec(lin);
   a.part = static_cast<double*>(workspace);
   a.out = out_norm;
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)q.nb, (unsigned)q.nsplit);
   {
     prof::Scope ps("dora_rownorm", N, K, r, 2.0 * N * K * r + 3.0 * N * K,
-                   (double)wsz * N * K + 4.0 * r * (N + K) + (q.nsplit > 1 ? 8.0 : 4.0) * N);
-    if (!lora_on) {
+                   wsz * N * K + 4.0 * r * (N + K) + (q.nsplit > 1 ? 8.0 : 4.0) * N);
+    if (wq_quantized(lin->w_dtype)) {
+      launch_row_pass_quant(lin, 0, lora_on, rp, false, grid, st, ps, a);
+    } else if (!lora_on) {
       if (lin->w_dtype == LORA_BF16) launch(row_pass_kernel<uint16_t, 16, false, 0, float>, grid, st, ps, a);
       else launch(row_pass_kernel<float, 16, false, 0, float>, grid, st, ps, a);
     } else if (lin->w_dtype == LORA_BF16) {
@@ -1463,7 +1496,8 @@ int lora_merge(const lora_linear* lin, void* W_out, int out_dtype, double* rmse,
   const bool want_err = rmse != nullptr && out_dtype == LORA_BF16;
   const size_t need = sizeof(double) * q.nb * q.nsplit * 4;
   if (want_err && (!workspace || workspace_bytes < need)) return LORA_E_WORKSPACE;
-  const size_t wsz = lin->w_dtype == LORA_BF16 ? 2 : 4, osz = out_dtype == LORA_BF16 ? 2 : 4;
+  const double wsz = row_pass_w_bytes(lin);
+  const size_t osz = out_dtype == LORA_BF16 ? 2 : 4;
   RowPassArgs a;
   memset(&a, 0, sizeof(a));
   a.W = lin->W;
@@ -1474,7 +1508,7 @@ int lora_merge(const lora_linear* lin, void* W_out, int out_dtype, double* rmse,
   a.r = (int)r;
   a.s = lin->scale;
   a.cpw = (int)q.cpw;
-  a.vec = al16(lin->W) && (K * wsz) % 16 == 0 && (!lora_on || (al16(lin->A) && K % 4 == 0));
+  a.vec = row_pass_vec(lin);
   a.wout = W_out;
   a.vec_out = al16(W_out) && (K * osz) % 16 == 0;
   a.mag = lin->dora_mag;
@@ -1484,11 +1518,13 @@ int lora_merge(const lora_linear* lin, void* W_out, int out_dtype, double* rmse,
   const dim3 grid((unsigned)q.nb, (unsigned)q.nsplit);
   {
     prof::Scope ps("merge", N, K, r, 2.0 * N * K * r + 3.0 * N * K,
-                   (double)(wsz + osz) * N * K + 4.0 * r * (N + K));
+                   (wsz + osz) * N * K + 4.0 * r * (N + K));
 #define LORA_MERGE_LAUNCH(WT_, OT_)                                                            \
   if (!lora_on) launch(row_pass_kernel<WT_, 16, false, 1, OT_>, grid, st, ps, a);             \
   else LORA_RP_DISPATCH(rp, launch(row_pass_kernel<WT_, RP, true, 1, OT_>, grid, st, ps, a));
-    if (lin->w_dtype == LORA_BF16) {
+    if (wq_quantized(lin->w_dtype)) {
+      launch_row_pass_quant(lin, 1, lora_on, rp, out_dtype == LORA_BF16, grid, st, ps, a);
+    } else if (lin->w_dtype == LORA_BF16) {
       if (out_dtype == LORA_BF16) { LORA_MERGE_LAUNCH(uint16_t, uint16_t) }
       else { LORA_MERGE_LAUNCH(uint16_t, float) }
     } else {

@@ -67,26 +67,29 @@ struct QRes {
 
 // Raw words of elements [col, col + 8) of W row `row` (col a multiple of 8,
 // K the row length).  Offsets are 32-bit: every plane is below 2^30 bytes.
+// ok = false reads from past every plane: the run decodes to zeros.
 template <int F>
-LORA_DEV void wq_load(const QRes<F>& R, uint32_t K, uint32_t row, uint32_t col, uint32_t* w) {
+LORA_DEV void wq_load(const QRes<F>& R, uint32_t K, uint32_t row, uint32_t col, uint32_t* w,
+                      bool ok = true) {
+  auto o = [&](uint32_t x) { return ok ? x : 0xfffffff0u; };
   if constexpr (F == WQ_Q8_0) {
     const u32x2 c = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(R.r[0], row * K + col, 0, 0));
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(R.r[0], o(row * K + col), 0, 0));
     w[0] = c.x;
     w[1] = c.y;
-    w[2] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], row * (K / 16) + (col / 32) * 2, 0, 0);
+    w[2] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], o(row * (K / 16) + (col / 32) * 2), 0, 0);
   } else if constexpr (F == WQ_Q4_0) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(R.r[0], row * (K / 2) + col / 2, 0, 0);
-    w[1] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], row * (K / 16) + (col / 32) * 2, 0, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(R.r[0], o(row * (K / 2) + col / 2), 0, 0);
+    w[1] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], o(row * (K / 16) + (col / 32) * 2), 0, 0);
   } else if constexpr (F == WQ_Q4_K) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(R.r[0], row * (K / 2) + col / 2, 0, 0);
-    w[1] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], row * (K / 16) + (col / 32) * 2, 0, 0);
-    w[2] = __builtin_amdgcn_raw_buffer_load_b32(R.r[2], row * (K / 64) + (col / 256) * 4, 0, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(R.r[0], o(row * (K / 2) + col / 2), 0, 0);
+    w[1] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], o(row * (K / 16) + (col / 32) * 2), 0, 0);
+    w[2] = __builtin_amdgcn_raw_buffer_load_b32(R.r[2], o(row * (K / 64) + (col / 256) * 4), 0, 0);
   } else {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(R.r[0], row * (K / 2) + col / 2, 0, 0);
-    w[1] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], row * (K / 4) + col / 4, 0, 0);
-    w[2] = __builtin_amdgcn_raw_buffer_load_b8(R.r[2], row * (K / 16) + col / 16, 0, 0);
-    w[3] = __builtin_amdgcn_raw_buffer_load_b16(R.r[3], row * (K / 128) + (col / 256) * 2, 0, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(R.r[0], o(row * (K / 2) + col / 2), 0, 0);
+    w[1] = __builtin_amdgcn_raw_buffer_load_b16(R.r[1], o(row * (K / 4) + col / 4), 0, 0);
+    w[2] = __builtin_amdgcn_raw_buffer_load_b8(R.r[2], o(row * (K / 16) + col / 16), 0, 0);
+    w[3] = __builtin_amdgcn_raw_buffer_load_b16(R.r[3], o(row * (K / 128) + (col / 256) * 2), 0, 0);
   }
 }
 

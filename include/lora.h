@@ -109,8 +109,7 @@ typedef struct lora_dropout {
  * 16-byte aligned (LORA_E_ALIGN otherwise).  bf16 and quantized W also need
  * in_dim*out_dim, tokens*in_dim and tokens*out_dim below 2^30 (their operands
  * are addressed with 32-bit byte offsets; LORA_E_SHAPE otherwise), and
- * quantized W an in_dim that is a whole number of its blocks (LORA_E_SHAPE).
- * lora_dora_row_norms and lora_merge take float32 or bf16 W only. */
+ * quantized W an in_dim that is a whole number of its blocks (LORA_E_SHAPE). */
 typedef struct lora_linear {
   int64_t tokens, in_dim, out_dim, rank;
   int32_t w_dtype;          /* lora_dtype                                  */
@@ -273,7 +272,9 @@ int lora_dropout_mask(const lora_dropout* drop, int64_t tokens, int64_t in_dim,
  * lin->A == lin->B == NULL it gives ||W_i|| (the magnitude initialisation).
  * lin->tokens and lin->dora_* are ignored; any out_dim > 0, 0 < in_dim <=
  * 2^22 and 0 < rank <= 128 are accepted (LORA_E_SHAPE otherwise; unaligned
- * rows take element loads).
+ * rows take element loads).  A block-quantized W (the DoRA of a quantized
+ * base) is decoded to float32 (exactly, but for one rounding of Q4_K's sum);
+ * it needs in_dim a whole number of its blocks and in_dim * out_dim < 2^30.
  * The contraction is split over column ranges whose double partials go to
  * `workspace` (device, lora_dora_row_norms_workspace_bytes(lin) bytes, 0 for
  * small K: then it may be NULL) and are summed per row in a fixed order by a

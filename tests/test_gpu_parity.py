@@ -168,7 +168,7 @@ def test_linear_forward_backward_parity(case):
 
 
 QUANT_CASES = [
-    # name, format, T, K, N, r, scale, dropout p
+    # name, format, T, K, N, r, scale, dropout p (, DoRA)
     ("q8_0-ragged", "q8_0", 100, 544, 264, 8, 2.0, 0.1),
     ("q4_0-ragged", "q4_0", 300, 1056, 520, 16, 2.0, 0.1),
     ("q4_k-tiles", "q4_k", 256, 512, 264, 32, math.sqrt(32), 0.0),
@@ -176,6 +176,8 @@ QUANT_CASES = [
     ("q4_k-qwen-wq-slice", "q4_k", 256, 2560, 4096, 32, math.sqrt(32), 0.0),
     ("q6_k-qwen-wdown-slice", "q6_k", 256, 9728, 2560, 32, math.sqrt(32), 0.1),
     ("q4_0-split-k", "q4_0", 64, 4096, 512, 16, 2.0, 0.05),
+    ("q4_k-dora", "q4_k", 129, 512, 264, 64, 1.0, 0.1, True),
+    ("q6_k-dora-wdown-slice", "q6_k", 256, 9728, 2560, 64, 1.0, 0.1, True),
 ]
 
 
@@ -183,13 +185,20 @@ QUANT_CASES = [
 def test_quantized_w_forward_backward_parity(case):
     """Block-quantized frozen W against the oracle on the decoded weights,
     at the bf16 bar (the products run in bf16 on the decoded W)."""
-    name, fmt, T, K, N, r, s, p = case
+    name, fmt, T, K, N, r, s, p = case[:8]
+    dora = len(case) > 8 and case[8]
     _say("quantized linear", name)
     c = _linear_case(T, K, N, r, fmt, seed=zlib.crc32(name.encode()) % 1000, dy_std=1e-2)
     dk = (1234, 2, 1, 3, 4)
-    got = _run_gpu(c, s, p, dk)
-    ref = _oracle(c, s, p, dk)
-    for n in ("Y", "U", "dX", "dA", "dB"):
+    got = _run_gpu(c, s, p, dk, dora)
+    mag = np64(got["mag"]) if dora else None
+    nrm = np64(got["norm"]) if dora else None
+    if dora:   # the magnitude initialisation and the refresh over the decoded base
+        W = np64(c["W"])
+        assert rel_err(got["mag"], O.dora_row_norms(W)) <= 1e-5
+        assert rel_err(got["norm"], O.dora_row_norms(W, np64(c["A"]), np64(c["B"]), s)) <= 1e-5
+    ref = _oracle(c, s, p, dk, mag, nrm)
+    for n in ("Y", "U", "dX", "dA", "dB") + (("Z", "dmag") if dora else ()):
         e = rel_err(got[n], ref[n])
         _say(f"  {n}: rel err {e:.3e}")
         assert torch.isfinite(got[n]).all(), f"{n} has unwritten (NaN) elements"
@@ -411,6 +420,11 @@ def test_adamw_parity_on_shared_inputs(t):
     ("bf16", 2560, 9728, 64),     # DoRA workload shapes (wdown, wup)
     ("bf16", 9728, 2560, 64),
     ("f32", 2048, 2048, 8),
+    ("q4_k", 264, 512, 32),       # quantized bases: decoded to float32 in the pass
+    ("q6_k", 136, 768, 64),
+    ("q4_0", 100, 1056, 8),       # ragged rows, a half last chunk
+    ("q8_0", 45, 544, 12),
+    ("q4_k", 2560, 9728, 64),
 ])
 def test_dora_row_norms_parity(wd_, N, K, r, split):
     c = _linear_case(8, K, N, r, wd_, seed=11, b_std=0.05)
@@ -767,6 +781,9 @@ MERGE_CASES = [
     ("f32", 33, 4097, 128, True),     # rank 128, odd K
     ("bf16", 2560, 9728, 64, True),   # DoRA workload shapes (wdown, wup)
     ("bf16", 9728, 2560, 32, False),
+    ("q4_k", 264, 512, 32, True),     # merge of an adapter into a quantized base
+    ("q6_k", 136, 768, 16, False),
+    ("q8_0", 45, 544, 8, True),
 ]
 
 
