@@ -117,6 +117,44 @@ Split plan_rows(int64_t T, int64_t strips) {
   return plan_split(T, strips, 512, SK_T, SK_T);
 }
 
+// k3's grid on the plain path: column strips grouped spb per block (the
+// block's V partial sums its strips in strip order) by token ranges (one dB
+// partial per range).  V partials and re-reads of U grow with the number of
+// block columns, dB partials and re-reads of B with the ranges; among the
+// groupings with about 512 blocks (or as many as the shape has) the plan
+// takes the one with the least of that traffic.  Each strip a block visits
+// costs a B-tile load and the dB stores, so strips are grouped only over
+// token ranges of at least four 64-row stages.
+struct K3Plan {
+  Split rows;
+  int64_t spb, nvp;
+};
+K3Plan plan_k3(int64_t T, int64_t N, int64_t r, int64_t strips) {
+  auto cost = [&](int64_t nvp, int64_t nts) {
+    return 4.0 * r * ((double)nvp * T * (nvp > 1 ? 3 : 2) + (double)nts * N * (nts > 1 ? 3 : 2));
+  };
+  // One strip per block, its rows split until about 512 blocks run.
+  K3Plan best = {plan_rows(T, strips), 1, strips};
+  double cbest = cost(strips, best.rows.n);
+  const int64_t maxr = cdiv(T, SK_T);
+  const int64_t want = std::min<int64_t>(512, strips * maxr);
+  int64_t prev = strips;
+  for (int64_t spb = 2; spb <= strips; ++spb) {
+    const int64_t nvp = cdiv(strips, spb);
+    if (nvp == prev) continue;   // the same partial count with fewer strips per block
+    prev = nvp;
+    const int64_t len = rup(cdiv(T, clampi(cdiv(want, nvp), 1, maxr)), SK_T);
+    const int64_t nts = cdiv(T, len);
+    if (nvp * nts * 8 < want * 7 || len < 4 * SK_T) continue;
+    const double c = cost(nvp, nts);
+    if (c < cbest) {
+      cbest = c;
+      best = {{len, (int)nts}, spb, nvp};
+    }
+  }
+  return best;
+}
+
 struct GemmPlan {
   int bm, bn;
   Split k;           // contraction split across blocks (fp32 only)
@@ -224,7 +262,8 @@ constexpr double kPartialRereadBytes = 64.0 * 1024 * 1024;
 struct Layout {
   Split down, k3, k4;
   GemmPlan gf, gd;
-  int64_t strips;      // 64-column strips of dY (k3 grid x): V partial count
+  int64_t strips;      // 64-column strips of dY
+  int64_t k3spb, k3nvp;   // k3 strips per block; V partials (= k3 grid x)
   bool vreduce;        // V partials summed by a separate launch
   size_t upart, xbf, gfpart;                          // forward
   size_t vpart, v, dbpart, dmpart, gbf, gdpart, dapart;   // backward
@@ -247,25 +286,36 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
   const bool own = stack <= 1;
   y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, SK_C);
   y.strips = cdiv(N, SK_C);
-  y.k3 = plan_rows(T, y.strips);
   y.k4 = plan_rows(T, cdiv(K, SK_C));
   y.gf = plan_gemm(stack * T, N, K, bf, false);
   y.gd = plan_gemm(stack * T, K, N, bf, true);
+  // k3 beside the split dX GEMM keeps its own grid (one strip per block
+  // there); the plain path groups strips.
+  if (use_split_path(y.gd, r, bf)) {
+    y.k3 = plan_rows(T, y.strips);
+    y.k3spb = 1;
+    y.k3nvp = y.strips;
+  } else {
+    const K3Plan kp = plan_k3(T, N, r, y.strips);
+    y.k3 = kp.rows;
+    y.k3spb = kp.spb;
+    y.k3nvp = kp.nvp;
+  }
   // Beside the split GEMM the down projection needs no parallelism of its
   // own: 256 columns per block keeps its partials few for the epilogue.
   if (use_split_path(y.gf, r, bf)) {
     const int64_t len = rup(cdiv(K, cdiv(K, 256)), SK_C);
     y.down = {len, (int)cdiv(K, len)};
   }
-  const double vbytes = 4.0 * y.strips * T * r;
-  y.vreduce = y.strips > 1 && vbytes * (cdiv(K, y.gd.bn) + cdiv(K, SK_C)) > kPartialRereadBytes;
+  const double vbytes = 4.0 * y.k3nvp * T * r;
+  y.vreduce = y.k3nvp > 1 && vbytes * (cdiv(K, y.gd.bn) + cdiv(K, SK_C)) > kPartialRereadBytes;
   size_t off = 0;
   y.upart = carve(off, y.down.n > 1 ? sizeof(float) * y.down.n * T * r : 0);
   y.xbf = carve(off, (bf && own) ? sizeof(uint16_t) * T * K : 0);
   y.gfpart = carve(off, (own && y.gf.k.n > 1) ? sizeof(float) * y.gf.k.n * T * N : 0);
   y.fwd_bytes = off;
   off = 0;
-  y.vpart = carve(off, y.strips > 1 ? sizeof(float) * y.strips * T * r : 0);
+  y.vpart = carve(off, y.k3nvp > 1 ? sizeof(float) * y.k3nvp * T * r : 0);
   y.v = carve(off, sizeof(float) * T * r);
   y.dbpart = carve(off, y.k3.n > 1 ? sizeof(float) * y.k3.n * N * r : 0);
   y.dmpart = carve(off, (L->dora_mag && y.k3.n > 1) ? sizeof(float) * y.k3.n * N : 0);
@@ -701,9 +751,10 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   j.d = make_drop(drop);
   j.rp = rank_pad(r);
 
-  // One pass over dY: V (as per-strip partials), dB, DoRA dm and bf16 g.
+  // One pass over dY: V (as partials per block column), dB, DoRA dm and
+  // bf16 g.
   K3Out& o = j.o;
-  o.Vpart = y.strips > 1 ? (float*)(w + y.vpart) : nullptr;
+  o.Vpart = y.k3nvp > 1 ? (float*)(w + y.vpart) : nullptr;
   o.V = (float*)(w + y.v);
   o.dBpart = y.k3.n > 1 ? (float*)(w + y.dbpart) : nullptr;
   o.dB = dB;
@@ -716,12 +767,12 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   K3Args& ka = j.ka;
   ka.dY = dY; ka.T = T; ka.N = N; ka.B = lin->B; ka.U = U; ka.r = r;
   ka.mag = lin->dora_mag; ka.nrm = lin->dora_norm; ka.Z = Zin;
-  ka.tsplit = y.k3.len; ka.nstrip = y.strips; ka.spb = 1; ka.nts = y.k3.n; ka.o = o;
+  ka.tsplit = y.k3.len; ka.nstrip = y.strips; ka.spb = y.k3spb; ka.nts = y.k3.n; ka.o = o;
   j.k3_flops = 4.0 * T * N * r;
   j.k3_bytes = 4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
                (o.gbf ? 2.0 * T * N : 0.0);
-  j.xv = (y.strips == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
-                                       : LoraOperand{o.Vpart, T * r, (int)y.strips, nullptr};
+  j.xv = (y.k3nvp == 1 || y.vreduce) ? LoraOperand{o.V, T * r, 1, nullptr}
+                                      : LoraOperand{o.Vpart, T * r, (int)y.k3nvp, nullptr};
   float* dApart = y.k4.n > 1 ? (float*)(w + y.dapart) : nullptr;
   K4Args& k4a = j.k4a;
   k4a.X = X; k4a.T = T; k4a.K = K; k4a.V = j.xv.p; k4a.vparts = j.xv.nparts; k4a.r = r;
@@ -869,11 +920,11 @@ void launch_bwd_k3(const BwdJob& jb, hipStream_t st) {
   const int64_t T = jb.T, N = jb.N, r = jb.r;
   {
     prof::Scope ps("k3_v_db", T, N, r, jb.k3_flops, jb.k3_bytes);
-    const dim3 grid((unsigned)y.strips, (unsigned)y.k3.n);
+    const dim3 grid((unsigned)y.k3nvp, (unsigned)y.k3.n);
     LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP>, grid, st, ps, jb.ka));
   }
   if (y.vreduce) {
-    RedJob jv = {jb.o.Vpart, jb.o.V, nullptr, T * r, 1, (int)y.strips, 0, 1.0f};
+    RedJob jv = {jb.o.Vpart, jb.o.V, nullptr, T * r, 1, (int)y.k3nvp, 0, 1.0f};
     launch_reduce(&jv, 1, st);
   }
 }
