@@ -347,6 +347,96 @@ def test_full_size_linear_sampled(wl, pi, rows):
         assert rel_err(got["dmag"], (dY * Zfull).sum(0) / nrm) <= 1e-4
 
 
+def _check_sampled(got, c, s, p, dk, idx, tol, mag=None, nrm=None):
+    """Y, dX (and Z) on the sampled rows; U, dA, dB (and dm) in full, against
+    the oracle's definitions on the same inputs."""
+    X, W, A, B, dY = (np64(c[k]) for k in ("X", "W", "A", "B", "dY"))
+    T, K = X.shape
+    keep, ks = (O.dropout_keep(*dk, T, K, p), O.dropout_scale(p)) if p > 0 else (None, 1.0)
+    Yr, Ur, Zr = O.forward(X[idx], W, A, B, s, None if keep is None else keep[idx], ks, mag, nrm)
+    assert rel_err(np64(got["Y"])[idx], Yr) <= tol
+    Xt = X if keep is None else np.where(keep, X * ks, 0.0)
+    U_full = Xt @ A.T
+    assert rel_err(got["U"], U_full) <= 1e-4
+    g = dY * (mag / nrm)[None, :] if mag is not None else dY
+    V = g @ B
+    assert rel_err(got["dB"], s * (g.T @ U_full)) <= 1e-4
+    assert rel_err(got["dA"], s * (V.T @ Xt)) <= 1e-4
+    lora_rows = s * (V[idx] @ A)
+    if keep is not None:
+        lora_rows = np.where(keep[idx], lora_rows * ks, 0.0)
+    assert rel_err(np64(got["dX"])[idx], g[idx] @ W + lora_rows) <= tol
+    if mag is not None:
+        Zfull = np64(got["Z"])
+        assert rel_err(Zfull[idx], Zr) <= tol
+        assert rel_err(got["dm"], (dY * Zfull).sum(0) / nrm) <= 1e-4
+
+
+@pytest.mark.parametrize("pi", [4, 6], ids=["wgate", "wdown"])
+def test_full_size_stacked_slots_sampled(pi):
+    """The DoRA workload's two slots at full size in the launch plan the
+    bench times (one product over both slots' 2 x 2048 stacked rows per
+    direction); each slot checked on sampled rows and its rank-side
+    gradients in full."""
+    cfg = WL.get_config(5)
+    proj = cfg.projections[pi]
+    _say("full-size stacked slots", cfg.name, proj.name)
+    s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
+    T, N = cfg.tokens, proj.out_dim
+    cs = []
+    for si in range(2):
+        inp = WL.linear_inputs(cfg, 0, proj, slot=si, device=DEV, chunks=1)
+        cs.append({"Wq": inp["W_bf16"], "W": inp["W"], "A": inp["A"], "B": inp["B"],
+                   "X": inp["X"][0], "dY": inp["dY"][0]})
+    cs[1]["Wq"], cs[1]["W"] = cs[0]["Wq"], cs[0]["W"]
+    mags = [torch.rand(N, device=DEV) + 0.5 for _ in cs]
+    nrms = [torch.empty(N, device=DEV) for _ in cs]
+    for c, n in zip(cs, nrms):
+        L.lora_dora_row_norms(L.make_linear(c["Wq"], c["A"], c["B"], s, T), n)
+    lins = [L.make_linear(c["Wq"], c["A"], c["B"], s, T, m, n) for c, m, n in zip(cs, mags, nrms)]
+    shapes = dict(Y=(T, N), U=(T, cfg.rank), dX=(T, proj.in_dim), dA=(cfg.rank, proj.in_dim),
+                  dB=(N, cfg.rank), Z=(T, N), dm=(N,))
+    out = {k: [torch.full(v, float("nan"), device=DEV) for _ in cs] for k, v in shapes.items()}
+    ws = torch.empty(L.lora_slots_workspace_bytes(lins), device=DEV, dtype=torch.uint8)
+    dks = [(cfg.seeds[i], 0, 0, 0, proj.ordinal) for i in range(2)]
+    drops = [L.make_dropout(*k, cfg.dropout) for k in dks]
+    L.lora_forward_slots(lins, [c["X"] for c in cs], out["Y"], out["U"], out["Z"], drops, ws)
+    L.lora_backward_slots(lins, [c["X"] for c in cs], [c["dY"] for c in cs], out["U"], out["Z"],
+                          out["dX"], out["dA"], out["dB"], out["dm"], drops=drops, ws=ws)
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(50 + pi).choice(T, 24, replace=False))
+    for i, c in enumerate(cs):
+        got = {k: v[i] for k, v in out.items()}
+        _check_sampled(got, c, s, cfg.dropout, dks[i], idx, TOL["bf16"], np64(mags[i]), np64(nrms[i]))
+
+
+@pytest.mark.parametrize("fmt,pi", [("q4_k", 4), ("q6_k", 6), ("q8_0", 0)],
+                         ids=["q4_k-wgate", "q6_k-wdown", "q8_0-wq"])
+def test_full_size_quantized_sampled(fmt, pi):
+    """Qwen3-4B-shaped projection at its full 4096 tokens over a quantized
+    base, in the launch plan the bench's --w-format runs use; sampled rows
+    against the oracle on the decoded weights."""
+    cfg = WL.get_config(4)
+    proj = cfg.projections[pi]
+    _say("full-size quantized", fmt, proj.name)
+    s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
+    N, K, T = proj.out_dim, proj.in_dim, cfg.tokens
+    inp = WL.linear_inputs(cfg, 0, proj, device=DEV, chunks=1)
+    planes = WL.qweight_planes(fmt, N, K, (cfg.number, 0, 0, proj.ordinal), device=DEV)
+    c = {"Wq": L.qweight_pack(fmt, N, K, planes),
+         "W": torch.from_numpy(Q.dequantize(fmt, {k: v.cpu().numpy() for k, v in planes.items()})),
+         "A": inp["A"], "B": inp["B"], "X": inp["X"][0], "dY": inp["dY"][0]}
+    lin = L.make_linear(c["Wq"], c["A"], c["B"], s, T)
+    got = {k: torch.full(v, float("nan"), device=DEV) for k, v in
+           dict(Y=(T, N), U=(T, cfg.rank), dX=(T, K), dA=(cfg.rank, K), dB=(N, cfg.rank)).items()}
+    ws = torch.empty(L.lora_workspace_bytes(lin), device=DEV, dtype=torch.uint8)
+    L.lora_forward(lin, c["X"], got["Y"], got["U"], None, None, ws)
+    L.lora_backward(lin, c["X"], c["dY"], got["U"], None, got["dX"], got["dA"], got["dB"], ws=ws)
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(70 + pi).choice(T, 24, replace=False))
+    _check_sampled(got, c, s, 0.0, None, idx, TOL[fmt])
+
+
 # --------------------------------------------------- prepare and AdamW -----
 @pytest.mark.parametrize("n,scale,max_norm,n_pred", [
     (1, 3.0, 1.0, 1), (1003, 10.0, 1.0, 4), (131072, 1e-3, 1.0, 1536), (1126400, 1.0, 0.0, 512),
