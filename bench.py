@@ -154,6 +154,26 @@ def copy_calibration(mib):
                                            "dispatches": 5}}), flush=True)
 
 
+def stream_copy_gbps(mib=1024, reps=5):
+    """Bytes moved (read + write) per second by a plain device copy of `mib`
+    MiB: the attainable HBM rate reported beside the published peak."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbps = 2.0 * 4 * n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return gbps
+
+
 def roofline_of(entries, cfg):
     """Dominant kernel (largest summed time) and its place on the roofline."""
     dom = max(entries, key=lambda e: e["total_ms"])
@@ -331,6 +351,7 @@ def main():
     log(f"profiled pass: {prof_ms:.3f} ms/step, kernel time {kernel_ms:.3f} ms/step")
 
     rl = roofline_of(entries, cfg)
+    rl["stream_copy_gbps"] = stream_copy_gbps()
     out = {
         "metric": METRIC,
         "value": value,
