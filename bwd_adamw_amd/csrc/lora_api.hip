@@ -921,7 +921,11 @@ void launch_bwd_k3(const BwdJob& jb, hipStream_t st) {
   {
     prof::Scope ps("k3_v_db", T, N, r, jb.k3_flops, jb.k3_bytes);
     const dim3 grid((unsigned)y.k3nvp, (unsigned)y.k3.n);
-    LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP>, grid, st, ps, jb.ka));
+    if (jb.ka.Z) {
+      LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP, true>, grid, st, ps, jb.ka));
+    } else {
+      LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP, false>, grid, st, ps, jb.ka));
+    }
   }
   if (y.vreduce) {
     RedJob jv = {jb.o.Vpart, jb.o.V, nullptr, T * r, 1, (int)y.k3nvp, 0, 1.0f};

@@ -230,8 +230,9 @@ constexpr int k3_lds_floats() { return SK_T * SK_LD + RP * SK_LD + SK_T * (RP + 
 
 // Strips [bx*spb, bx*spb + spb) of row range by, in LDS `smem`
 // (k3_lds_floats<RP>() floats).  The block's V partial (index bx) sums its
-// strips in strip order.
-template <int RP>
+// strips in strip order.  ZT: the tiles carry Z (DoRA's dm); without it a
+// tile holds only g and U, which leaves room for a third wave per SIMD.
+template <int RP, bool ZT = true>
 LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
   const float* __restrict__ dY = p.dY;
   const float* __restrict__ B = p.B;
@@ -263,7 +264,7 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
   const int64_t nst = (te - tb + SK_T - 1) / SK_T;
   const int64_t ntot = (sx1 - sx0) * nst;
   struct Tile {
-    f32x4 g[4], z[4], u[RP / 16];
+    f32x4 g[4], z[ZT ? 4 : 1], u[RP / 16];
   };
   auto g_ok = [&](int q, int64_t idx, int64_t& t, int64_t& ncol) -> bool {
     const int64_t sx = sx0 + idx / nst, t0 = tb + (idx % nst) * SK_T;
@@ -286,7 +287,9 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
       int64_t t, ncol;
       const bool ok = g_ok(q, idx, t, ncol);
       S.g[q] = *reinterpret_cast<const f32x4*>(ok ? dY + t * N + ncol : dY);
-      if (Z) S.z[q] = *reinterpret_cast<const f32x4*>(ok ? Z + t * N + ncol : Z);
+      if constexpr (ZT) {
+        if (Z) S.z[q] = *reinterpret_cast<const f32x4*>(ok ? Z + t * N + ncol : Z);
+      }
     }
 #pragma unroll
     for (int q = 0; q < RP / 16; ++q) {
@@ -308,9 +311,11 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
       const bool ok = g_ok(q, idx, t, ncol);
       f32x4 v = ok ? S.g[q] : f32x4{0.f, 0.f, 0.f, 0.f};
       if (ok) {
-        if (Z) {
+        if constexpr (ZT) {
+          if (Z) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dm[e] += v[e] * S.z[q][e];
+            for (int e = 0; e < 4; ++e) dm[e] += v[e] * S.z[q][e];
+          }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] *= cmul[e];
@@ -444,10 +449,15 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
   if (idx < ntot) step(idx, R[0], R[1]);
 }
 
-template <int RP>
-__global__ __launch_bounds__(256) void k3_kernel(K3Args p) {
+// Waves per SIMD k3 is built for: without Z, ranks up to 32 fit three.
+LORA_HD constexpr int k3_waves_per_simd(int rp, bool zt) { return (!zt && rp <= 32) ? 3 : 2; }
+
+// ZT must be true whenever p.Z is set.
+template <int RP, bool ZT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(k3_waves_per_simd(RP, ZT))))
+void k3_kernel(K3Args p) {
   __shared__ __attribute__((aligned(16))) float smem[k3_lds_floats<RP>()];
-  k3_block<RP>(p, smem, blockIdx.x, blockIdx.y);
+  k3_block<RP, ZT>(p, smem, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
