@@ -45,7 +45,7 @@ def projection_format(w_format, proj):
     return w_format
 
 
-def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
+def build_workload(cfg, device, layers=None, tokens=None, chunks=None, streams=4):
     """Frozen model, slots and per-slot chunk inputs, all seeded.  A
     workload whose w_dtype names a block-quantized format gets W drawn as
     that format's planes."""
@@ -69,7 +69,7 @@ def build_workload(cfg, device, layers=None, tokens=None, chunks=None):
             inp = WL.linear_inputs(cfg, l, pj, chunks=0, tokens=T, device=device)
             Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"])
     model = S.FrozenModel(cfg, Wq)
-    trainer = S.Trainer(cfg, model, tokens=T, device=device, slots=cfg.slots)
+    trainer = S.Trainer(cfg, model, tokens=T, device=device, slots=cfg.slots, streams=streams)
     slots, inputs = [], []
     for si in range(cfg.slots):
         A, B = {}, {}
@@ -294,6 +294,9 @@ def main():
                     help="block-quantized frozen W for a bf16 workload (default: its bf16 W)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--streams", type=int, default=4,
+                    help="HIP streams the layers' calls are spread over (default 4; at most "
+                         "one per layer group)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -324,7 +327,7 @@ def main():
                                   name=cfg.name.replace("-bf16-", f"-{args.w_format}-"))
     dev = "cuda"
     t0 = time.perf_counter()
-    model, trainer, slots, inputs = build_workload(cfg, dev)
+    model, trainer, slots, inputs = build_workload(cfg, dev, streams=args.streams)
     torch.cuda.synchronize()
     log(f"setup {cfg.name}: {time.perf_counter() - t0:.1f} s")
 
@@ -371,6 +374,7 @@ def main():
             "tokens_per_chunk": cfg.tokens, "chunks": cfg.chunks, "slots": cfg.slots,
             "tokens_per_step": cfg.tokens_per_step, "rank": cfg.rank, "w_dtype": cfg.w_dtype,
             "dropout": cfg.dropout, "dora": cfg.dora, "parallelism": "single GPU",
+            "streams": 1 + len(trainer.side),
         },
         "roofline": rl,
         "kernels": {"sum_kernel_ms_per_step": kernel_ms, "table": kernel_table(entries, kernel_ms * args.steps)},

@@ -24,7 +24,7 @@ __all__ = [
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
-    "lora_qweight_layout", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS",
+    "lora_qweight_layout", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS", "GroupCall",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
@@ -349,6 +349,67 @@ def lora_backward_group(lins, X, dY, U, Z, dX, dA, dB, dMag=None, accumulate=Fal
                                    1 if accumulate else 0, _drops(drops, n), _ptr(ws, "ws", None),
                                    ws_bytes, _stream(stream))
     _check("lora_backward_group", rc)
+
+
+class GroupCall:
+    """Marshalled arguments of lora_forward_group / lora_backward_group for
+    one group of linears whose descriptors and trainer-owned buffers stay
+    put across calls (Y, U, Z, dX, the gradients, the workspace, the
+    stream): they are checked and marshalled once, here.  Each call checks
+    and marshals only its own inputs (X, dY, dropout keys); an X or dY list
+    whose tensors are the ones of the previous call reuses their pointers."""
+
+    def __init__(self, lins, Y, U, Z=None, dX=None, dA=None, dB=None, dMag=None, ws=None,
+                 stream=None):
+        self.n = len(lins)
+        self.lins = list(lins)
+        self.arr = _linears(self.lins)
+        self.Y, self.U = _ptrs(Y, "Y", lins), _ptrs(U, "U", lins)
+        self.Z = _ptrs(Z, "Z", lins, True)
+        self.dX = _ptrs(dX, "dX", lins, True)
+        self.dA = None if dA is None else _ptrs(dA, "dA", lins)
+        self.dB = None if dB is None else _ptrs(dB, "dB", lins)
+        self.dMag = _ptrs(dMag, "dMag", lins, True)
+        self.ws = _ptr(ws, "ws", None)
+        self.ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+        self.stream = _stream(stream)
+        self._held = (Y, U, Z, dX, dA, dB, dMag, ws, stream)   # the marshalled buffers stay alive
+        self._x = self._xp = None
+        self._dy = self._dyp = None
+
+    def _x_ptr(self, X):
+        if X is not self._x:
+            self._xp = _sized(X, "X", _NEED["X"](self.lins[0]))
+            self._x = X
+        return self._xp
+
+    def _dy_ptrs(self, dY):
+        if self._dy is None or len(dY) != len(self._dy) or any(a is not b for a, b in zip(dY, self._dy)):
+            self._dyp = _ptrs(dY, "dY", self.lins)
+            self._dy = list(dY)
+        return self._dyp
+
+    def dropouts(self, drops):
+        """The marshalled dropout keys (one LoraDropout or None per linear),
+        to pass to forward and backward of the same chunk."""
+        return _drops(drops, self.n)
+
+    def _d(self, drops):
+        return drops if drops is None or isinstance(drops, C.Array) else _drops(drops, self.n)
+
+    def forward(self, X, drops=None):
+        rc = lib().lora_forward_group(self.n, self.arr, self._x_ptr(X), self.Y, self.U, self.Z,
+                                      self._d(drops), self.ws, self.ws_bytes, self.stream)
+        _check("lora_forward_group", rc)
+
+    def backward(self, X, dY, accumulate=False, drops=None):
+        if self.dA is None or self.dB is None:
+            raise ValueError("this GroupCall was prepared without gradients")
+        rc = lib().lora_backward_group(self.n, self.arr, self._x_ptr(X), self._dy_ptrs(dY),
+                                       self.U, self.Z, self.dX, self.dA, self.dB, self.dMag,
+                                       1 if accumulate else 0, self._d(drops), self.ws,
+                                       self.ws_bytes, self.stream)
+        _check("lora_backward_group", rc)
 
 
 def lora_slots_workspace_bytes(lins) -> int:

@@ -104,9 +104,21 @@ class StepStats:
 
 
 class Trainer:
-    """Runs optimizer updates of slots over one frozen model on one stream."""
+    """Runs optimizer updates of slots over one frozen model.
 
-    def __init__(self, cfg: LoraConfig, model: FrozenModel, tokens=None, device="cuda", slots=1):
+    The layers' linears are independent within a step (each has its own
+    activations and gradients; only a layer's own chunks accumulate into the
+    same gradients), so their calls can be spread over `streams` HIP streams:
+    layer groups are dealt round robin, each stream with its own workspace,
+    and every group keeps its chunk order on its stream.  The results are
+    bitwise those of one stream.  The optimizer update runs on the current
+    stream after all of them.  Short chunks leave most of the chip idle
+    between a layer's dependent launches, and other layers' launches fill it.
+    The default, four, is the number of hardware queues HIP gives a process
+    by default; more streams share them."""
+
+    def __init__(self, cfg: LoraConfig, model: FrozenModel, tokens=None, device="cuda", slots=1,
+                 streams=4):
         self.cfg = cfg
         self.model = model
         self.T = cfg.tokens if tokens is None else int(tokens)
@@ -153,6 +165,15 @@ class Trainer:
             self.acts.append(a)
         self.U, self.Z, self.Y, self.dX = (self.acts[0][n] for n in ("U", "Z", "Y", "dX"))
         self.ws = torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
+        # Streams beyond the current one (default priority), each with a
+        # workspace; no more streams than units to spread (layer groups; layers
+        # on the stacked-slot path).
+        units = len({k[0] for k in model.keys}) if self.stack_slots else len(self.groups)
+        nstreams = max(1, min(int(streams), units))
+        self.side = [torch.cuda.Stream(device=device) for _ in range(nstreams - 1)]
+        self.side_ws = [torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
+                        for _ in self.side]
+        self._calls = {}   # (id(slot), group index) -> (slot, stream handle, GroupCall)
         self.d_scale = torch.zeros(1, **f32)
         self.d_stats = torch.zeros(2, device=device, dtype=torch.float64)
         self.prep_ws = None
@@ -189,32 +210,64 @@ class Trainer:
             L.lora_dora_row_norms(lin, slot.norm[key], self.ws)
 
     # ------------------------------------------------------------------
+    def _fork(self):
+        """Streams and workspaces for the calls; the extra streams first wait
+        for the work already on the current stream."""
+        main = torch.cuda.current_stream()
+        if self.side:
+            ev = torch.cuda.Event()
+            ev.record(main)
+            for s in self.side:
+                s.wait_event(ev)
+        return [main] + self.side, [self.ws] + self.side_ws
+
+    def _join(self):
+        main = torch.cuda.current_stream()
+        for s in self.side:
+            ev = torch.cuda.Event()
+            ev.record(s)
+            main.wait_event(ev)
+
+    def _group_call(self, slot: Slot, gi: int, stream, ws) -> L.GroupCall:
+        """The marshalled call of group gi for this slot on this stream
+        (built on first use: descriptors, outputs and gradients stay put)."""
+        handle = stream.cuda_stream
+        ent = self._calls.get((id(slot), gi))
+        if ent is None or ent[0] is not slot or ent[1] != handle:
+            cfg = self.cfg
+            keys = self.groups[gi]
+            call = L.GroupCall([self._linear(k, slot, dora=cfg.dora) for k in keys],
+                               [self.Y[k] for k in keys], [self.U[k] for k in keys],
+                               [self.Z[k] for k in keys] if cfg.dora else None,
+                               [self.dX[k] for k in keys], [slot.gA[k] for k in keys],
+                               [slot.gB[k] for k in keys],
+                               [slot.gmag[k] for k in keys] if cfg.dora else None, ws, stream)
+            ent = (slot, handle, call)
+            self._calls[(id(slot), gi)] = ent
+        return ent[2]
+
     def forward_backward(self, slot: Slot, chunks: list):
         """Every chunk: forward over the layers 0..L-1, then backward L-1..0;
         the projections of a layer that share X go through the group calls."""
         cfg = self.cfg
         p = float(cfg.dropout)
+        streams, wss = self._fork()
+        ng = len(self.groups)
+        calls = [self._group_call(slot, gi, streams[gi % len(streams)], wss[gi % len(streams)])
+                 for gi in range(ng)]
         for g, chunk in enumerate(chunks):
-            def drops(keys):
-                if p <= 0:
-                    return None
-                return [L.make_dropout(slot.seed, slot.k, g, k[0], k[1], p) for k in keys]
-            lins = {k: self._linear(k, slot, dora=cfg.dora) for k in self.model.keys}
-            for keys in self.groups:
-                X = chunk[keys[0]][0]
-                L.lora_forward_group([lins[k] for k in keys], X, [self.Y[k] for k in keys],
-                                     [self.U[k] for k in keys],
-                                     [self.Z[k] for k in keys] if cfg.dora else None,
-                                     drops(keys), self.ws)
-            for keys in reversed(self.groups):
-                X = chunk[keys[0]][0]
-                L.lora_backward_group([lins[k] for k in keys], X, [chunk[k][1] for k in keys],
-                                      [self.U[k] for k in keys],
-                                      [self.Z[k] for k in keys] if cfg.dora else None,
-                                      [self.dX[k] for k in keys], [slot.gA[k] for k in keys],
-                                      [slot.gB[k] for k in keys],
-                                      [slot.gmag[k] for k in keys] if cfg.dora else None,
-                                      accumulate=g > 0, drops=drops(keys), ws=self.ws)
+            dr = [None] * ng
+            if p > 0:
+                dr = [calls[gi].dropouts([L.make_dropout(slot.seed, slot.k, g, k[0], k[1], p)
+                                          for k in keys])
+                      for gi, keys in enumerate(self.groups)]
+            for gi, keys in enumerate(self.groups):
+                calls[gi].forward(chunk[keys[0]][0], dr[gi])
+            for gi in reversed(range(ng)):
+                keys = self.groups[gi]
+                calls[gi].backward(chunk[keys[0]][0], [chunk[k][1] for k in keys],
+                                   accumulate=g > 0, drops=dr[gi])
+        self._join()
 
     def forward_backward_slots(self, slots: list, chunks_per_slot: list):
         """forward_backward of several slots together: each linear's forward
@@ -225,6 +278,9 @@ class Trainer:
         n = len(slots)
         acts = self.acts[:n]
         G = len(chunks_per_slot[0])
+        streams, wss = self._fork()
+        layers = sorted({k[0] for k in self.model.keys})
+        on = {k: layers.index(k[0]) % len(streams) for k in self.model.keys}
         for g in range(G):
             def drops(key):
                 if p <= 0:
@@ -235,7 +291,7 @@ class Trainer:
                 L.lora_forward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
                                      [a["Y"][key] for a in acts], [a["U"][key] for a in acts],
                                      [a["Z"][key] for a in acts] if cfg.dora else None,
-                                     drops(key), self.ws)
+                                     drops(key), wss[on[key]], streams[on[key]])
             for key in reversed(self.model.keys):
                 lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
                 L.lora_backward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
@@ -245,7 +301,9 @@ class Trainer:
                                       [a["dX"][key] for a in acts], [sl.gA[key] for sl in slots],
                                       [sl.gB[key] for sl in slots],
                                       [sl.gmag[key] for sl in slots] if cfg.dora else None,
-                                      accumulate=g > 0, drops=drops(key), ws=self.ws)
+                                      accumulate=g > 0, drops=drops(key), ws=wss[on[key]],
+                                      stream=streams[on[key]])
+        self._join()
 
     def step_slots(self, slots: list, chunks_per_slot: list, sync: bool = True) -> list:
         """One update of every slot; with stacked slots their forward and

@@ -677,6 +677,81 @@ def test_seeded_runs_give_identical_adapters():
     assert digests[0] == digests[1]
 
 
+def _stream_inputs(cfg, layers, tokens):
+    """Frozen W, and per slot A, B and chunks, on the GPU (seeded)."""
+    Wq, per_slot = {}, []
+    for l in range(layers):
+        for pj in cfg.projections:
+            inp = WL.linear_inputs(cfg, l, pj, chunks=0, tokens=tokens)
+            Wq[(l, pj.ordinal)] = inp.get("W_bf16", inp["W"]).to(DEV)
+    for si in range(cfg.slots):
+        a, b, ch = {}, {}, [dict() for _ in range(cfg.chunks)]
+        for l in range(layers):
+            for pj in cfg.projections:
+                inp = WL.linear_inputs(cfg, l, pj, slot=si, tokens=tokens)
+                key = (l, pj.ordinal)
+                a[key], b[key] = inp["A"].to(DEV), inp["B"].to(DEV)
+                for g in range(cfg.chunks):
+                    ch[g][key] = (inp["X"][g].to(DEV), inp["dY"][g].to(DEV))
+        per_slot.append((a, b, ch))
+    return Wq, per_slot
+
+
+def _trained(cfg, inputs, tokens, steps, streams, together):
+    """Adapters and gradients after `steps` updates of every slot through a
+    trainer that spreads its calls over `streams` streams."""
+    Wq, per_slot = inputs
+    model = S.FrozenModel(cfg, Wq)
+    trainer = S.Trainer(cfg, model, tokens=tokens, slots=cfg.slots if together else 1,
+                        streams=streams)
+    slots = []
+    for si, (a, b, _) in enumerate(per_slot):
+        slot = S.Slot(cfg, model, a, b, cfg.seeds[si])
+        if cfg.dora:
+            trainer.init_dora(slot)
+        slots.append(slot)
+    chunks = [ch for _, _, ch in per_slot]
+    for _ in range(steps):
+        if together:
+            trainer.step_slots(slots, chunks)
+        else:
+            for slot, ch in zip(slots, chunks):
+                trainer.step(slot, ch)
+    torch.cuda.synchronize()
+    return 1 + len(trainer.side), [(sl.params.clone(), sl.grads.clone()) for sl in slots]
+
+
+STREAM_CASES = [
+    ("wl2-4layers-f32-dropout", 2, 4, 128, False),
+    ("wl4-1layer-T256-bf16-groups", 4, 1, 256, False),
+    ("wl5-3layers-T256-dora-stacked-slots", 5, 3, 256, True),
+]
+
+
+@pytest.mark.parametrize("name,wl,layers,tokens,together", STREAM_CASES,
+                         ids=[c[0] for c in STREAM_CASES])
+def test_streams_give_bitwise_the_one_stream_results(name, wl, layers, tokens, together):
+    """Layer groups spread over three streams, each with its own workspace,
+    keep every linear's call order, so two updates give bitwise the adapters
+    and gradients of the one-stream schedule."""
+    cfg = WL.get_config(wl)
+    _say("streams", name)
+    inputs = _stream_inputs(cfg, layers, tokens)
+    n1, one = _trained(cfg, inputs, tokens, 2, 1, together)
+    n3, three = _trained(cfg, inputs, tokens, 2, 3, together)
+    assert n1 == 1 and n3 == 3
+    for (p1, g1), (p3, g3) in zip(one, three):
+        assert torch.equal(p1, p3)
+        assert torch.equal(g1, g3)
+
+
+def test_streams_capped_by_layer_groups():
+    cfg = WL.get_config(1)
+    W = WL.linear_inputs(cfg, 0, cfg.projections[0], chunks=0)["W"].to(DEV)
+    trainer = S.Trainer(cfg, S.FrozenModel(cfg, {(0, cfg.projections[0].ordinal): W}), streams=4)
+    assert trainer.side == []
+
+
 def test_invalid_arguments_raise_before_work():
     T, K, N, r = 128, 2048, 2048, 8          # a shape that needs split partials
     c = _gpu(_linear_case(T, K, N, r))
