@@ -129,7 +129,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdMain<NG> p) {
     for (int i = 0; i < NG; ++i)
       if (b < p.sstart[i + 1]) {
         const int64_t sb = b - p.sstart[i];
-        k3_block<RP>(p.k[i], smem, sb % p.f[i].side_x, (int)(sb / p.f[i].side_x));
+        // Z reaches k3 only with a DoRA gradient, which also sets the dX
+        // operand's column scale (SCALEA); without it the tile needs no Z slot.
+        k3_block<RP, SCALEA>(p.k[i], smem, sb % p.f[i].side_x, (int)(sb / p.f[i].side_x));
         return;
       }
   }

@@ -359,10 +359,12 @@ LORA_DEV void gemm_f32_block(const GemmF32Args& p, float* smem, int64_t tn, int6
     }
 }
 
-// K-steps of loads in flight per tile size (register budget of a stage).
+// K-steps of loads in flight: two for every tile.  The 64x64 split tiles
+// measured 2-3 % slower per step at four (and slower still at six and
+// eight); their loads are not what bounds a K-step.
 template <int BM, int BN>
 constexpr int gemm_f32_depth() {
-  return BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 64 ? 3 : 2;
+  return 2;
 }
 
 // Grid (Nc/BN, M/BM, nsplit).
