@@ -173,7 +173,7 @@ class Trainer:
         self.side = [torch.cuda.Stream(device=device) for _ in range(nstreams - 1)]
         self.side_ws = [torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
                         for _ in self.side]
-        self._calls = {}   # (id(slot), group index) -> (slot, stream handle, GroupCall)
+        self._calls = {}   # (id(slot), group index) -> (slot, stream handle, norms, GroupCall)
         self.d_scale = torch.zeros(1, **f32)
         self.d_stats = torch.zeros(2, device=device, dtype=torch.float64)
         self.prep_ws = None
@@ -232,19 +232,23 @@ class Trainer:
         """The marshalled call of group gi for this slot on this stream
         (built on first use: descriptors, outputs and gradients stay put)."""
         handle = stream.cuda_stream
+        keys = self.groups[gi]
+        # DoRA descriptors point at the slot's norm vectors, which init_dora
+        # creates; the entry holds them, so they are compared by identity.
+        norms = tuple(slot.norm.get(k) for k in keys) if self.cfg.dora else ()
         ent = self._calls.get((id(slot), gi))
-        if ent is None or ent[0] is not slot or ent[1] != handle:
+        if (ent is None or ent[0] is not slot or ent[1] != handle or len(ent[2]) != len(norms)
+                or any(a is not b for a, b in zip(ent[2], norms))):
             cfg = self.cfg
-            keys = self.groups[gi]
             call = L.GroupCall([self._linear(k, slot, dora=cfg.dora) for k in keys],
                                [self.Y[k] for k in keys], [self.U[k] for k in keys],
                                [self.Z[k] for k in keys] if cfg.dora else None,
                                [self.dX[k] for k in keys], [slot.gA[k] for k in keys],
                                [slot.gB[k] for k in keys],
                                [slot.gmag[k] for k in keys] if cfg.dora else None, ws, stream)
-            ent = (slot, handle, call)
+            ent = (slot, handle, norms, call)
             self._calls[(id(slot), gi)] = ent
-        return ent[2]
+        return ent[3]
 
     def forward_backward(self, slot: Slot, chunks: list):
         """Every chunk: forward over the layers 0..L-1, then backward L-1..0;
