@@ -752,6 +752,52 @@ def test_streams_capped_by_layer_groups():
     assert trainer.side == []
 
 
+def test_group_call_matches_the_group_entry_points():
+    """GroupCall marshals the fixed arguments once and reuses X and dY
+    pointers while the tensors stay the same; over calls that switch X and
+    dY (and use dropout) it gives bitwise the results of lora_forward_group
+    and lora_backward_group."""
+    T, K, r, Ns = 128, 256, 8, (256, 64)
+    cases = [_gpu(_linear_case(T, K, N, r, seed=30 + i)) for i, N in enumerate(Ns)]
+    Xs = [WL.draw((T, K), (931, i, 0, 0, 0, "X"), "normal", 1.0, DEV) for i in range(2)]
+    dYs = [[WL.draw((T, N), (932, i, j, 0, 0, "dY"), "normal", 1.0, DEV) for j, N in enumerate(Ns)]
+           for i in range(2)]
+    lins = [L.make_linear(c["Wq"], c["A"], c["B"], 2.0, T) for c in cases]
+    order = [0, 1, 1, 0]
+
+    def outputs():
+        return dict(Y=[torch.empty(T, N, device=DEV) for N in Ns],
+                    U=[torch.empty(T, r, device=DEV) for _ in Ns],
+                    dX=[torch.empty(T, K, device=DEV) for _ in Ns],
+                    dA=[torch.empty(r, K, device=DEV) for _ in Ns],
+                    dB=[torch.empty(N, r, device=DEV) for N in Ns])
+
+    def drops(step):
+        return [L.make_dropout(5, step, 0, 0, j, 0.1) for j in range(len(Ns))]
+
+    ws = torch.empty(L.lora_group_workspace_bytes(lins), dtype=torch.uint8, device=DEV)
+    a, b = outputs(), outputs()
+    ra, rb = [], []
+    call = L.GroupCall(lins, b["Y"], b["U"], None, b["dX"], b["dA"], b["dB"], None, ws)
+    for step, i in enumerate(order):
+        L.lora_forward_group(lins, Xs[i], a["Y"], a["U"], None, drops(step), ws)
+        L.lora_backward_group(lins, Xs[i], dYs[i], a["U"], None, a["dX"], a["dA"], a["dB"],
+                              accumulate=step > 0, drops=drops(step), ws=ws)
+        ra.append([t.clone() for n in ("Y", "U", "dX") for t in a[n]])
+        d = call.dropouts(drops(step))
+        call.forward(Xs[i], d)
+        call.backward(Xs[i], dYs[i], accumulate=step > 0, drops=d)
+        rb.append([t.clone() for n in ("Y", "U", "dX") for t in b[n]])
+    torch.cuda.synchronize()
+    for x, y in zip(ra, rb):
+        for u, v in zip(x, y):
+            assert torch.equal(u, v)
+    for n in ("dA", "dB"):
+        for u, v in zip(a[n], b[n]):
+            assert torch.equal(u, v)
+    assert not torch.equal(ra[0][0], ra[1][0])   # the switched inputs did change Y
+
+
 def test_invalid_arguments_raise_before_work():
     T, K, N, r = 128, 2048, 2048, 8          # a shape that needs split partials
     c = _gpu(_linear_case(T, K, N, r))
