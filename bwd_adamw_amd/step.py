@@ -144,7 +144,7 @@ class Trainer:
         for g in self.groups:
             ws = max(ws, L.lora_group_workspace_bytes([self._linear(k, None, dora=cfg.dora)
                                                        for k in g]))
-        if cfg.dora:   # the row-norm refresh runs on the same stream between steps
+        if cfg.dora:   # the row-norm refresh shares the workspaces between steps
             for k in model.keys:
                 ws = max(ws, L.lora_dora_row_norms_workspace_bytes(self._linear(k, None)))
         if self.stack_slots:
@@ -204,10 +204,16 @@ class Trainer:
         self.refresh_dora(slot)
 
     def refresh_dora(self, slot: Slot):
+        """Row norms of W + s B A for every linear; each linear writes only
+        its own norm vector, so the layers are spread over the streams."""
+        streams, wss = self._fork()
+        layers = sorted({k[0] for k in self.model.keys})
         for key in self.model.keys:
+            q = layers.index(key[0]) % len(streams)
             W = self.model.W[key]
             lin = L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T)
-            L.lora_dora_row_norms(lin, slot.norm[key], self.ws)
+            L.lora_dora_row_norms(lin, slot.norm[key], wss[q], stream=streams[q])
+        self._join()
 
     # ------------------------------------------------------------------
     def _fork(self):
