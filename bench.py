@@ -3,8 +3,8 @@
 
 One step = one optimizer update of every adapter slot: for each of the G
 accumulation chunks, forward and backward of every adapted linear (all
-layers, all projections), then gradient preparation, AdamW and (DoRA) the
-row-norm refresh.  Inputs are seeded synthetic tensors already resident in
+layers, all projections; the layers' calls spread over `--streams` HIP
+streams), then gradient preparation, AdamW and (DoRA) the row-norm refresh.  Inputs are seeded synthetic tensors already resident in
 HBM; the timed region contains exactly `--steps` updates.
 
 Prints one JSON line: tokens/s for the whole job, the roofline position of
