@@ -185,8 +185,12 @@ constexpr Bf16Cfg kBf16Cfg[] = {
 constexpr int kBf16NCfg = sizeof(kBf16Cfg) / sizeof(kBf16Cfg[0]);
 constexpr int kBf16Slots = 256;  // resident tiles per round
 // Cost of a split's fp32 partials (written once, read once by the reduction
-// that also writes the result): microseconds per MB, from the same fit.
-constexpr double kSplitUsPerMB = 0.102;
+// that also writes the result): microseconds per MB.  The single-launch fit
+// gave 0.102; launches of other layers running beside the product compete
+// for the same bandwidth, and 4x that measured best with four streams
+// (DoRA two-slot Qwen3-4B step 279 -> 264 ms; on one stream 0.7-2.5 %
+// slower).
+constexpr double kSplitUsPerMB = 0.408;
 
 // bf16: the configuration and contraction split (whole K-steps per split,
 // at least 8 of them) with the least estimated time.
