@@ -315,22 +315,27 @@ class Trainer:
                                       stream=streams[on[key]])
         self._join()
 
-    def step_slots(self, slots: list, chunks_per_slot: list, sync: bool = True) -> list:
+    def step_slots(self, slots: list, chunks_per_slot: list) -> list:
         """One update of every slot; with stacked slots their forward and
         backward passes share each frozen product, then each slot takes its
         own prepare, AdamW step and DoRA refresh."""
         if not self.stack_slots or len(slots) < 2:
-            return [self.step(sl, ch, sync) for sl, ch in zip(slots, chunks_per_slot)]
+            return [self.step(sl, ch) for sl, ch in zip(slots, chunks_per_slot)]
         if len(slots) > self.nslots:
             raise ValueError(f"trainer holds activations for {self.nslots} slots")
         self.forward_backward_slots(slots, chunks_per_slot)
-        return [self._update(sl, len(ch), sync) for sl, ch in zip(slots, chunks_per_slot)]
+        return [self._update(sl, len(ch)) for sl, ch in zip(slots, chunks_per_slot)]
 
-    def step(self, slot: Slot, chunks: list, sync: bool = True) -> StepStats:
+    def step(self, slot: Slot, chunks: list) -> StepStats:
         self.forward_backward(slot, chunks)
-        return self._update(slot, len(chunks), sync)
+        return self._update(slot, len(chunks))
 
-    def _update(self, slot: Slot, n_chunks: int, sync: bool) -> StepStats:
+    def _update(self, slot: Slot, n_chunks: int) -> StepStats:
+        """Prepare, AdamW and DoRA refresh of one slot.  The prepare waits
+        for its veto flag on the host (one synchronisation per update): the
+        slot's update count t (bias corrections) and update index k (schedule
+        and dropout step key) live on the host and must not advance on a
+        vetoed update ("4.3. Training Guide", "Gradient clipping")."""
         cfg = self.cfg
         if self.prep_ws is None or self.prep_ws.numel() < L.lora_grad_prepare_workspace_bytes(slot.n):
             self.prep_ws = torch.empty(L.lora_grad_prepare_workspace_bytes(slot.n),
@@ -340,7 +345,7 @@ class Trainer:
                           cfg.total_updates, cfg.lr_min)
         try:
             norm = L.lora_grad_prepare(slot.grads, n_pred, cfg.max_norm, self.d_scale,
-                                       self.d_stats, sync=sync, ws=self.prep_ws)
+                                       self.d_stats, sync=True, ws=self.prep_ws)
         except L.LoraError as e:
             if e.status == L.LORA_E_NONFINITE:
                 return StepStats(float("nan"), True, lr)
@@ -352,4 +357,4 @@ class Trainer:
             self.refresh_dora(slot)
         slot.t += 1
         slot.k += 1
-        return StepStats(norm if norm is not None else float("nan"), False, lr)
+        return StepStats(norm, False, lr)

@@ -26,9 +26,12 @@
  *     lora_grad_prepare when `h_norm` is not NULL.
  *   - Every argument is validated before anything is enqueued.  On a negative
  *     status no buffer has been touched.  HIP launch failures return
- *     LORA_E_HIP.  No exceptions cross the ABI; there is no global mutable
- *     state, so calls on different streams may run concurrently as long as
- *     their buffers do not overlap.
+ *     LORA_E_HIP.  No exceptions cross the ABI.  The compute entry points
+ *     keep no mutable state between calls, so calls on different streams may
+ *     run concurrently as long as their buffers do not overlap.  The launch
+ *     profiler is the exception: lora_profile_begin / lora_profile_end keep
+ *     one process-wide profile that every launch of the library records
+ *     into while it is open (not thread-safe; meant for benchmarks).
  *   - Results are deterministic: every reduction runs in a fixed order (no
  *     floating-point atomics), so equal inputs give bitwise equal outputs.
  */

@@ -72,3 +72,34 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_trace_summary_groups_dispatches_by_kernel_and_grid(tmp_path):
+    hdr = ("Kind,Kernel_Name,Workgroup_Size_X,Workgroup_Size_Y,Workgroup_Size_Z,"
+           "Grid_Size_X,Grid_Size_Y,Grid_Size_Z,Start_Timestamp,End_Timestamp\n")
+    rows = ["KERNEL_DISPATCH,k_a,256,1,1,2560,1,1,1000,4000\n",
+            "KERNEL_DISPATCH,k_a,256,1,1,2560,1,1,5000,6000\n",
+            "KERNEL_DISPATCH,k_a,256,1,1,5120,1,1,7000,7500\n",
+            "KERNEL_DISPATCH,k_b,64,1,1,64,2,1,0,500\n"]
+    (tmp_path / "x_kernel_trace.csv").write_text(hdr + "".join(rows))
+    table = bench.summarize_trace(str(tmp_path)).splitlines()
+    assert table[2].startswith("| `k_a` | 10x1x1 | 256 | 2 | 0.004 | 2.00 | 1.00 | 3.00 |")
+    assert any(l.startswith("| `k_a` | 20x1x1 | 256 | 1 |") for l in table)
+    assert any(l.startswith("| `k_b` | 1x2x1 | 64 | 1 | 0.001 | 0.50 |") for l in table)
+
+
+def test_pmc_summary_averages_each_counter_per_dispatch(tmp_path):
+    hdr = "Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+    rows = ["1,k,512,FETCH_SIZE,10\n", "1,k,512,FETCH_SIZE,6\n", "2,k,512,FETCH_SIZE,20\n",
+            "3,k,1024,FETCH_SIZE,1\n"]
+    (tmp_path / "f_counter_collection.csv").write_text(hdr + "".join(rows))
+    table = bench.summarize_pmc(str(tmp_path)).splitlines()
+    assert table[0] == "| kernel | grid threads | dispatches | FETCH_SIZE |"
+    assert table[2] == "| `k` | 512 | 2 | 18.0 |"
+    assert table[3] == "| `k` | 1024 | 1 | 1.0 |"
+
+
+def test_frozen_flops_of_the_dora_two_slot_step():
+    from bwd_adamw_amd import workloads as WL
+    # 4 T N K per linear (forward and dX), 36 layers, 2 slots x 2 chunks x 2048 tokens
+    assert bench.frozen_flops_per_step(WL.get_config(5)) == 4 * 8192 * 36 * 100925440

@@ -106,6 +106,30 @@ def _oracle(c, s, p=0.0, dkeys=(1234, 0, 0, 0, 0), mag=None, nrm=None):
     return dict(Y=Y, U=U, Z=Z, **gr)
 
 
+def _dora_vectors(got, c, s):
+    """The oracle's DoRA magnitude (||W_i||) and detached norm (||W_i + s B_i A||)
+    for case c; the GPU's own vectors (lora_dora_row_norms) must agree with
+    them to 1e-5 before the oracle runs on its own."""
+    W, A, B = np64(c["W"]), np64(c["A"]), np64(c["B"])
+    mag, nrm = O.dora_row_norms(W), O.dora_row_norms(W, A, B, s)
+    assert rel_err(got["mag"], mag) <= 1e-5
+    assert rel_err(got["norm"], nrm) <= 1e-5
+    return mag, nrm
+
+
+def _check_full(got, ref, tol, dora, names=("Y", "U", "dX", "dA", "dB")):
+    """Every output against the oracle, element by element over the whole
+    tensor.  Y, dX (and Z) meet the path's bar; U, dA and dB are float32-exact
+    on every path (rank-side products in float32); the DoRA magnitude gradient
+    reads Z and so meets the path's bar."""
+    for n in tuple(names) + (("Z", "dmag") if dora else ()):
+        e = rel_err(got[n], ref[n])
+        bar = 1e-4 if n in ("U", "dA", "dB") else tol
+        _say(f"  {n}: rel err {e:.3e} (bar {bar:g})")
+        assert torch.isfinite(got[n]).all(), f"{n} has unwritten (NaN) elements"
+        assert e <= bar, (n, e)
+
+
 # ------------------------------------------------------------- dropout -----
 @pytest.mark.parametrize("T,K,p,keys", [
     (33, 72, 0.05, (1234, 0, 0, 0, 0)),
@@ -155,8 +179,7 @@ def test_linear_forward_backward_parity(case):
     c = _linear_case(T, K, N, r, wd, seed=zlib.crc32(name.encode()) % 1000, x_std=xs, dy_std=dys)
     dk = (1234, 2, 1, 3, 4)
     got = _run_gpu(c, s, p, dk, dora)
-    mag = np64(got["mag"]) if dora else None
-    nrm = np64(got["norm"]) if dora else None
+    mag, nrm = _dora_vectors(got, c, s) if dora else (None, None)
     ref = _oracle(c, s, p, dk, mag, nrm)
     tol = TOL[wd]
     names = ["Y", "U", "dX", "dA", "dB"] + (["Z", "dmag"] if dora else [])
@@ -191,12 +214,8 @@ def test_quantized_w_forward_backward_parity(case):
     c = _linear_case(T, K, N, r, fmt, seed=zlib.crc32(name.encode()) % 1000, dy_std=1e-2)
     dk = (1234, 2, 1, 3, 4)
     got = _run_gpu(c, s, p, dk, dora)
-    mag = np64(got["mag"]) if dora else None
-    nrm = np64(got["norm"]) if dora else None
-    if dora:   # the magnitude initialisation and the refresh over the decoded base
-        W = np64(c["W"])
-        assert rel_err(got["mag"], O.dora_row_norms(W)) <= 1e-5
-        assert rel_err(got["norm"], O.dora_row_norms(W, np64(c["A"]), np64(c["B"]), s)) <= 1e-5
+    # the magnitude initialisation and the refresh over the decoded base
+    mag, nrm = _dora_vectors(got, c, s) if dora else (None, None)
     ref = _oracle(c, s, p, dk, mag, nrm)
     for n in ("Y", "U", "dX", "dA", "dB") + (("Z", "dmag") if dora else ()):
         e = rel_err(got[n], ref[n])
@@ -297,18 +316,20 @@ def test_linear_outputs_are_deterministic():
         assert torch.equal(a[n], b[n]), n
 
 
-# --------------------------------------------- full-size, sampled outputs --
+# ------------------------------------------------ full-size, every output --
 FULL_CASES = [
-    # workload, projection index, rows sampled (the launch plans include
-    # split-contraction bf16 products in both directions)
-    (4, 0, 48), (4, 6, 48), (5, 0, 32), (5, 4, 32), (5, 6, 32),
+    # workload, projection index: the launch plans the bench times, including
+    # split-contraction bf16 products in both directions.  Every projection
+    # shape of the Qwen3-4B-shaped layers at 4096 tokens, and the DoRA
+    # workload's shapes at 2048 tokens.
+    (4, 0), (4, 1), (4, 3), (4, 4), (4, 6), (5, 0), (5, 2), (5, 3), (5, 4), (5, 6),
 ]
 
 
-@pytest.mark.parametrize("wl,pi,rows", FULL_CASES, ids=[f"wl{a}-p{b}" for a, b, _ in FULL_CASES])
-def test_full_size_linear_sampled(wl, pi, rows):
-    """Full workload shape in the launch plan the bench uses; Y and dX are
-    checked on sampled rows, U, dA, dB (and dm) in full."""
+@pytest.mark.parametrize("wl,pi", FULL_CASES, ids=[f"wl{a}-p{b}" for a, b in FULL_CASES])
+def test_full_size_linear(wl, pi):
+    """Full workload shape in the launch plan the bench uses; every output
+    against the oracle's forward and backward on the same full inputs."""
     cfg = WL.get_config(wl)
     proj = cfg.projections[pi]
     _say("full-size", cfg.name, proj.name)
@@ -319,65 +340,16 @@ def test_full_size_linear_sampled(wl, pi, rows):
     p = cfg.dropout
     dk = (cfg.seeds[0], 0, 0, 0, proj.ordinal)
     got = _run_gpu(c, s, p, dk, cfg.dora)
-    T = cfg.tokens
-    idx = np.sort(np.random.default_rng(wl * 10 + pi).choice(T, rows, replace=False))
-    X, W, A, B, dY = (np64(c[k]) for k in ("X", "W", "A", "B", "dY"))
-    keep, ks = (O.dropout_keep(*dk, T, proj.in_dim, p), O.dropout_scale(p)) if p > 0 else (None, 1.0)
-    mag = np64(got["mag"]) if cfg.dora else None
-    nrm = np64(got["norm"]) if cfg.dora else None
-    Yr, Ur, Zr = O.forward(X[idx], W, A, B, s, None if keep is None else keep[idx], ks, mag, nrm)
-    tol = TOL[cfg.w_dtype]
-    assert rel_err(np64(got["Y"])[idx], Yr) <= tol
-    # U in full (cheap), then the rank-side gradients in full
-    Xt = X if keep is None else np.where(keep, X * ks, 0.0)
-    U_full = Xt @ A.T
-    assert rel_err(got["U"], U_full) <= 1e-4
-    g = dY * (mag / nrm)[None, :] if cfg.dora else dY
-    V = g @ B
-    assert rel_err(got["dB"], s * (g.T @ U_full)) <= 1e-4
-    assert rel_err(got["dA"], s * (V.T @ Xt)) <= 1e-4
-    lora_rows = s * (V[idx] @ A)
-    if keep is not None:
-        lora_rows = np.where(keep[idx], lora_rows * ks, 0.0)
-    dXr = g[idx] @ W + lora_rows
-    assert rel_err(np64(got["dX"])[idx], dXr) <= tol
-    if cfg.dora:
-        Zfull = np64(got["Z"])
-        assert rel_err(Zfull[idx], Zr) <= tol
-        assert rel_err(got["dmag"], (dY * Zfull).sum(0) / nrm) <= 1e-4
-
-
-def _check_sampled(got, c, s, p, dk, idx, tol, mag=None, nrm=None):
-    """Y, dX (and Z) on the sampled rows; U, dA, dB (and dm) in full, against
-    the oracle's definitions on the same inputs."""
-    X, W, A, B, dY = (np64(c[k]) for k in ("X", "W", "A", "B", "dY"))
-    T, K = X.shape
-    keep, ks = (O.dropout_keep(*dk, T, K, p), O.dropout_scale(p)) if p > 0 else (None, 1.0)
-    Yr, Ur, Zr = O.forward(X[idx], W, A, B, s, None if keep is None else keep[idx], ks, mag, nrm)
-    assert rel_err(np64(got["Y"])[idx], Yr) <= tol
-    Xt = X if keep is None else np.where(keep, X * ks, 0.0)
-    U_full = Xt @ A.T
-    assert rel_err(got["U"], U_full) <= 1e-4
-    g = dY * (mag / nrm)[None, :] if mag is not None else dY
-    V = g @ B
-    assert rel_err(got["dB"], s * (g.T @ U_full)) <= 1e-4
-    assert rel_err(got["dA"], s * (V.T @ Xt)) <= 1e-4
-    lora_rows = s * (V[idx] @ A)
-    if keep is not None:
-        lora_rows = np.where(keep[idx], lora_rows * ks, 0.0)
-    assert rel_err(np64(got["dX"])[idx], g[idx] @ W + lora_rows) <= tol
-    if mag is not None:
-        Zfull = np64(got["Z"])
-        assert rel_err(Zfull[idx], Zr) <= tol
-        assert rel_err(got["dm"], (dY * Zfull).sum(0) / nrm) <= 1e-4
+    mag, nrm = _dora_vectors(got, c, s) if cfg.dora else (None, None)
+    ref = _oracle(c, s, p, dk, mag, nrm)
+    _check_full(got, ref, TOL[cfg.w_dtype], cfg.dora)
 
 
 @pytest.mark.parametrize("pi", [4, 6], ids=["wgate", "wdown"])
-def test_full_size_stacked_slots_sampled(pi):
+def test_full_size_stacked_slots(pi):
     """The DoRA workload's two slots at full size in the launch plan the
     bench times (one product over both slots' 2 x 2048 stacked rows per
-    direction); each slot checked on sampled rows and its rank-side
-    gradients in full."""
+    direction); each slot against the oracle over every output."""
     cfg = WL.get_config(5)
     proj = cfg.projections[pi]
     _say("full-size stacked slots", cfg.name, proj.name)
@@ -389,32 +361,36 @@ def test_full_size_stacked_slots_sampled(pi):
         cs.append({"Wq": inp["W_bf16"], "W": inp["W"], "A": inp["A"], "B": inp["B"],
                    "X": inp["X"][0], "dY": inp["dY"][0]})
     cs[1]["Wq"], cs[1]["W"] = cs[0]["Wq"], cs[0]["W"]
-    mags = [torch.rand(N, device=DEV) + 0.5 for _ in cs]
+    # seeded magnitudes away from ||W|| (an input, like A and B)
+    mags = [WL.draw((N,), (5, i, 0, proj.ordinal, 0, "B"), "uniform", 0.5, DEV) + 1.0
+            for i in range(2)]
     nrms = [torch.empty(N, device=DEV) for _ in cs]
     for c, n in zip(cs, nrms):
         L.lora_dora_row_norms(L.make_linear(c["Wq"], c["A"], c["B"], s, T), n)
     lins = [L.make_linear(c["Wq"], c["A"], c["B"], s, T, m, n) for c, m, n in zip(cs, mags, nrms)]
     shapes = dict(Y=(T, N), U=(T, cfg.rank), dX=(T, proj.in_dim), dA=(cfg.rank, proj.in_dim),
-                  dB=(N, cfg.rank), Z=(T, N), dm=(N,))
+                  dB=(N, cfg.rank), Z=(T, N), dmag=(N,))
     out = {k: [torch.full(v, float("nan"), device=DEV) for _ in cs] for k, v in shapes.items()}
     ws = torch.empty(L.lora_slots_workspace_bytes(lins), device=DEV, dtype=torch.uint8)
     dks = [(cfg.seeds[i], 0, 0, 0, proj.ordinal) for i in range(2)]
     drops = [L.make_dropout(*k, cfg.dropout) for k in dks]
     L.lora_forward_slots(lins, [c["X"] for c in cs], out["Y"], out["U"], out["Z"], drops, ws)
     L.lora_backward_slots(lins, [c["X"] for c in cs], [c["dY"] for c in cs], out["U"], out["Z"],
-                          out["dX"], out["dA"], out["dB"], out["dm"], drops=drops, ws=ws)
+                          out["dX"], out["dA"], out["dB"], out["dmag"], drops=drops, ws=ws)
     torch.cuda.synchronize()
-    idx = np.sort(np.random.default_rng(50 + pi).choice(T, 24, replace=False))
     for i, c in enumerate(cs):
         got = {k: v[i] for k, v in out.items()}
-        _check_sampled(got, c, s, cfg.dropout, dks[i], idx, TOL["bf16"], np64(mags[i]), np64(nrms[i]))
+        nrm = O.dora_row_norms(np64(c["W"]), np64(c["A"]), np64(c["B"]), s)
+        assert rel_err(nrms[i], nrm) <= 1e-5
+        ref = _oracle(c, s, cfg.dropout, dks[i], np64(mags[i]), nrm)
+        _check_full(got, ref, TOL["bf16"], True)
 
 
 @pytest.mark.parametrize("fmt,pi", [("q4_k", 4), ("q6_k", 6), ("q8_0", 0)],
                          ids=["q4_k-wgate", "q6_k-wdown", "q8_0-wq"])
-def test_full_size_quantized_sampled(fmt, pi):
+def test_full_size_quantized(fmt, pi):
     """Qwen3-4B-shaped projection at its full 4096 tokens over a quantized
-    base, in the launch plan the bench's --w-format runs use; sampled rows
+    base, in the launch plan the bench's --w-format runs use; every output
     against the oracle on the decoded weights."""
     cfg = WL.get_config(4)
     proj = cfg.projections[pi]
@@ -433,8 +409,7 @@ def test_full_size_quantized_sampled(fmt, pi):
     L.lora_forward(lin, c["X"], got["Y"], got["U"], None, None, ws)
     L.lora_backward(lin, c["X"], c["dY"], got["U"], None, got["dX"], got["dA"], got["dB"], ws=ws)
     torch.cuda.synchronize()
-    idx = np.sort(np.random.default_rng(70 + pi).choice(T, 24, replace=False))
-    _check_sampled(got, c, s, 0.0, None, idx, TOL[fmt])
+    _check_full(got, _oracle(c, s), TOL[fmt], False)
 
 
 # --------------------------------------------------- prepare and AdamW -----
@@ -499,6 +474,62 @@ def test_adamw_parity_on_shared_inputs(t):
         assert rel_err(np64(P[sl]) - np64(p0[sl]), pr - np64(p0[sl])) <= 1e-4
         assert rel_err(M[sl], mr) <= 1e-5
         assert rel_err(V[sl], vr) <= 1e-5
+
+
+def _arena_segments(cfg):
+    """Sizes of a slot's arena segments [all A | all B | all DoRA magnitudes]
+    over every layer and projection of a workload."""
+    na = cfg.layers * sum(cfg.rank * p.in_dim for p in cfg.projections)
+    nb = cfg.layers * sum(p.out_dim * cfg.rank for p in cfg.projections)
+    nm = cfg.layers * sum(p.out_dim for p in cfg.projections) if cfg.dora else 0
+    segs = [(0, na, L.KIND_A), (na, nb, L.KIND_B)] + ([(na + nb, nm, L.KIND_MAG)] if nm else [])
+    return na + nb + nm, segs
+
+
+@pytest.mark.parametrize("wl,n_expect", [(4, 66_060_288), (5, 133_226_496)])
+def test_prepare_and_adamw_on_the_full_arena(wl, n_expect):
+    """Gradient preparation and AdamW over a whole slot's arena at the
+    workload's size (all 36 layers x 7 projections: the clip norm is global
+    over it), against the oracle's grad_prepare and adamw_update on the same
+    values.  Third update of the slot (nonzero moments), the workload's
+    hyper-parameters; the arena's gradient is scaled so that the clip acts."""
+    cfg = WL.get_config(wl)
+    n, segs = _arena_segments(cfg)
+    assert n == n_expect
+    _say("full arena", cfg.name, n)
+    key = lambda kind: (600 + wl, 0, 0, 0, 3, kind)
+    g = WL.draw((n,), key("dY"), "normal", 2.0, DEV)   # norm/Npred about 3: the clip acts
+    p0 = WL.draw((n,), key("A"), "normal", 0.02, DEV)
+    m0 = WL.draw((n,), key("X"), "normal", 1e-4, DEV)
+    v0 = WL.draw((n,), key("B"), "uniform", 1e-8, DEV).abs_()
+    P, M, V = p0.clone(), m0.clone(), v0.clone()
+    n_pred = cfg.tokens * cfg.chunks
+    d_scale = torch.zeros(1, device=DEV)
+    stats = torch.zeros(2, device=DEV, dtype=torch.float64)
+    ws = torch.empty(L.lora_grad_prepare_workspace_bytes(n), device=DEV, dtype=torch.uint8)
+    norm = L.lora_grad_prepare(g, n_pred, cfg.max_norm, d_scale, stats, True, ws)
+    t, lr = 3, O.lr_at(2, cfg.lr, cfg.schedule, cfg.warmup, cfg.total_updates, cfg.lr_min)
+    L.lora_adamw_step(P, g, M, V, segs,
+                      L.LoraAdamwHparams(lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay,
+                                         cfg.plus_ratio, t), d_scale)
+    torch.cuda.synchronize()
+    gh = np64(g)
+    ref = O.grad_prepare([gh], n_pred, cfg.max_norm)
+    assert ref["clip"] < 1.0   # the clip acts at this scale
+    assert norm == pytest.approx(ref["norm"], rel=1e-12)
+    assert stats[1].item() == pytest.approx(ref["clip"], rel=1e-12)
+    assert d_scale.item() == pytest.approx(ref["scale"], rel=1e-6)
+    kinds = {L.KIND_A: "A", L.KIND_B: "B", L.KIND_MAG: "mag"}
+    Ph, Mh, Vh, p0h, m0h, v0h = (np64(x) for x in (P, M, V, p0, m0, v0))
+    for off, cnt, kind in segs:
+        for c0 in range(off, off + cnt, 1 << 24):   # bounded host memory
+            sl = slice(c0, min(off + cnt, c0 + (1 << 24)))
+            pr, mr, vr = O.adamw_update(p0h[sl], gh[sl], m0h[sl], v0h[sl], kinds[kind], lr, t,
+                                        ref["scale"], cfg.beta1, cfg.beta2, cfg.eps,
+                                        cfg.weight_decay, cfg.plus_ratio)
+            assert rel_err(Ph[sl] - p0h[sl], pr - p0h[sl]) <= 1e-4, (kind, c0)
+            assert rel_err(Mh[sl], mr) <= 1e-5, (kind, c0)
+            assert rel_err(Vh[sl], vr) <= 1e-5, (kind, c0)
 
 
 @pytest.mark.parametrize("split", [True, False], ids=["split", "whole-rows"])
@@ -573,8 +604,11 @@ def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None, together=False):
         ost = O.SlotState(params={k: {"A": np64(A[k]), "B": np64(B[k])} for k in A})
         if cfg.dora:
             for k in A:
-                ost.params[k]["mag"] = np64(slot.mag[k])   # ||W_i|| from the shared bf16/f32 W
+                # the oracle's own ||W_i||; the GPU's initialisation must agree
+                ost.params[k]["mag"] = O.dora_row_norms(np64(W[k]))
+                assert rel_err(slot.mag[k], ost.params[k]["mag"]) <= 1e-5
                 ost.norms[k] = O.dora_row_norms(np64(W[k]), ost.params[k]["A"], ost.params[k]["B"], s)
+                assert rel_err(slot.norm[k], ost.norms[k]) <= 1e-5
         gchunks = [{k: (x.to(DEV), d.to(DEV)) for k, (x, d) in ch.items()} for ch in chunks]
         ochunks = [{k: (np64(x), np64(d)) for k, (x, d) in ch.items()} for ch in chunks]
         staged.append((si, slot, ost, gchunks, ochunks, []))
@@ -615,7 +649,25 @@ E2E = [
     ("wl4-1layer-T512", 4, 1, 512, 2, False),
     ("wl5-1layer-T256", 5, 1, 256, 2, False),
     ("wl5-1layer-T256-stacked-slots", 5, 1, 256, 2, True),
+    # real shapes: one full layer (all 7 projections) at the workloads' own
+    # token counts, in the launch plans the bench times
+    ("wl4-1layer-T4096", 4, 1, None, 2, False),
+    ("wl5-1layer-2slots-2x2048-stacked", 5, 1, None, 2, True),
 ]
+
+
+def _update_floor(e_grad, bar):
+    """Smallest |g_ref| / max|g_ref| at which an element's update is compared.
+
+    Adam divides each moment by its own root mean square, so an element's
+    update moves with its gradient's error relative to that element, not to
+    the segment's largest gradient; at t = 1 it is about -lr*sign(g).  An
+    element whose reference gradient is at least e_grad/bar of the segment's
+    largest has a relative gradient error of at most `bar` (e_grad being the
+    measured max|g_gpu - g_ref| / max|g_ref| of the segment over all steps),
+    so its update must meet `bar`.  Never below 1e-3 of the largest gradient
+    (the exclusion the comparison reading starts from)."""
+    return max(1e-3, e_grad / bar)
 
 
 @pytest.mark.parametrize("name,wl,layers,tokens,steps,together", E2E, ids=[e[0] for e in E2E])
@@ -624,36 +676,34 @@ def test_end_to_end_step_parity(name, wl, layers, tokens, steps, together):
 
     Gradients: A and B are float32-exact on every path (rank-side products
     run in float32), so they meet 1e-4; the DoRA magnitude gradient reads Z,
-    which a bf16-W frozen product rounds, so it meets the bf16 bar.
-    Updates: Adam normalises each element by its own gradient history, so an
-    element whose gradient is within the path's error of zero may move by up
-    to 2 lr either way.  Elements are compared where every step's reference
-    gradient exceeds `floor` times the segment's largest, with floor = 1e-3
-    for float32-exact gradients and 0.1 for bf16-affected ones (the DoRA
-    magnitude gradient, and on bf16 DoRA slots every segment after the first
-    step), whose error is ~1e-3 of the largest."""
+    which a bf16-W frozen product rounds, so it meets the bf16 bar, and after
+    a DoRA update the magnitude (trained on that gradient) scales every later
+    gradient, so from the second step on a bf16 DoRA slot meets the bf16 bar
+    throughout.  Updates meet the bar of their segment's gradients (1e-4 for
+    float32-exact ones, 2e-2 for bf16-affected ones), compared where every
+    step's reference gradient exceeds _update_floor of the segment's largest."""
     cfg = WL.get_config(wl)
     _say("e2e", name)
     for slot, ost, hist in _e2e(cfg, layers, tokens, steps, together=together):
         seg = {}
         for off, cnt, kind in slot.segments:
             seg[kind] = slice(off, off + cnt)
-        ok = np.ones(slot.n, dtype=bool)
+        e_grad = {kind: 0.0 for kind in seg}
+        bf_seg = {kind: False for kind in seg}
+        g_refs = []
         for it, (p_before, o_before, st, res, grads) in enumerate(hist):
             assert not st.vetoed and not res["vetoed"]
             assert st.norm == pytest.approx(res["prep"]["norm"], rel=1e-4)
             g_ref = _flat(slot, res["grads"])
+            g_refs.append(g_ref)
             g_gpu = np64(grads)
             for kind, sl in seg.items():
                 e = rel_err(g_gpu[sl], g_ref[sl])
-                # After a DoRA update the magnitude (trained on the bf16-rounded
-                # gradient) scales every later gradient, so from the second step
-                # on a bf16 DoRA slot meets the bf16 bar throughout.
                 bf_dora = cfg.dora and cfg.w_dtype == "bf16"
                 bf_hit = (kind == L.KIND_MAG and cfg.w_dtype == "bf16") or (bf_dora and it > 0)
-                bar = TOL[cfg.w_dtype] if (kind == L.KIND_MAG or bf_hit) else 1e-4
-                floor = 0.1 if bf_hit else 1e-3
-                ok[sl] &= np.abs(g_ref[sl]) >= floor * np.abs(g_ref[sl]).max()
+                bar = TOL[cfg.w_dtype] if bf_hit else 1e-4
+                bf_seg[kind] |= bf_hit
+                e_grad[kind] = max(e_grad[kind], e)
                 _say(f"  step {it} seg {kind}: grad rel err {e:.3e} (bar {bar:g})")
                 assert e <= bar, (it, kind, e)
         p_before, o_before, st, res, grads = hist[-1]
@@ -661,10 +711,15 @@ def test_end_to_end_step_parity(name, wl, layers, tokens, steps, together):
                              for k in ost.params})
         d_gpu = np64(slot.params) - np64(p_before)
         for kind, sl in seg.items():
-            m = ok[sl]
+            bar = 2e-2 if bf_seg[kind] else 1e-4
+            floor = _update_floor(e_grad[kind], bar)
+            m = np.ones(sl.stop - sl.start, dtype=bool)
+            for g_ref in g_refs:
+                m &= np.abs(g_ref[sl]) >= floor * np.abs(g_ref[sl]).max()
             e = rel_err(d_gpu[sl][m], d_ref[sl][m])
-            bar = 2e-2 if (cfg.w_dtype == "bf16" and (kind == L.KIND_MAG or cfg.dora)) else 1e-3
-            _say(f"  update seg {kind}: rel err {e:.3e} over {m.sum()} of {m.size}")
+            _say(f"  update seg {kind}: rel err {e:.3e} (bar {bar:g}) over {m.sum()} of {m.size}"
+                 f" (floor {floor:.2e})")
+            assert m.sum() >= 0.25 * m.size, (kind, "too few elements compared")
             assert e <= bar, (kind, e)
 
 
@@ -743,6 +798,70 @@ def test_streams_give_bitwise_the_one_stream_results(name, wl, layers, tokens, t
     for (p1, g1), (p3, g3) in zip(one, three):
         assert torch.equal(p1, p3)
         assert torch.equal(g1, g3)
+
+
+def _fresh(cfg, inputs, tokens, together):
+    """A new trainer and freshly initialised slots over the seeded inputs."""
+    Wq, per_slot = inputs
+    model = S.FrozenModel(cfg, Wq)
+    trainer = S.Trainer(cfg, model, tokens=tokens, slots=cfg.slots if together else 1)
+    slots = []
+    for si, (a, b, _) in enumerate(per_slot):
+        slot = S.Slot(cfg, model, a, b, cfg.seeds[si])
+        if cfg.dora:
+            trainer.init_dora(slot)
+        slots.append(slot)
+    return trainer, slots, [ch for _, _, ch in per_slot]
+
+
+def _advance(trainer, slots, chunks, steps, together):
+    for _ in range(steps):
+        sts = (trainer.step_slots(slots, chunks) if together else
+               [trainer.step(sl, ch) for sl, ch in zip(slots, chunks)])
+        assert not any(st.vetoed for st in sts)
+
+
+RESUME_CASES = [
+    ("wl2-2layers-f32-dropout", 2, 2, 128, False),
+    ("wl4-1layer-T256-cosine", 4, 1, 256, False),
+    ("wl5-1layer-T256-dora-stacked-slots", 5, 1, 256, True),
+]
+
+
+@pytest.mark.parametrize("name,wl,layers,tokens,together", RESUME_CASES,
+                         ids=[c[0] for c in RESUME_CASES])
+def test_resume_from_copied_state_is_bitwise(name, wl, layers, tokens, together):
+    """A slot's whole state is its caller-owned buffers (A, B and DoRA
+    magnitude in the params arena, Adam m and v) plus its counters t and k
+    and its seed; the DoRA norms are derived from A and B.  k + j updates in
+    one run equal k updates, a copy of that state to the host and into a
+    fresh trainer and slots, then j updates: bitwise."""
+    cfg = WL.get_config(wl)
+    _say("resume", name)
+    inputs = _stream_inputs(cfg, layers, tokens)
+    k, j = 2, 2
+    tr, slots, chunks = _fresh(cfg, inputs, tokens, together)
+    _advance(tr, slots, chunks, k + j, together)
+    straight = [(sl.params.clone(), sl.m.clone(), sl.v.clone(), sl.t, sl.k) for sl in slots]
+    tr, slots, chunks = _fresh(cfg, inputs, tokens, together)
+    _advance(tr, slots, chunks, k, together)
+    saved = [(sl.params.cpu(), sl.m.cpu(), sl.v.cpu(), sl.t, sl.k) for sl in slots]
+    del tr, slots
+    tr, slots, chunks = _fresh(cfg, inputs, tokens, together)
+    for sl, (p, m, v, t, kk) in zip(slots, saved):
+        sl.params.copy_(p)
+        sl.m.copy_(m)
+        sl.v.copy_(v)
+        sl.t, sl.k = t, kk
+        if cfg.dora:
+            tr.refresh_dora(sl)
+    _advance(tr, slots, chunks, j, together)
+    torch.cuda.synchronize()
+    for sl, (p, m, v, t, kk) in zip(slots, straight):
+        assert (sl.t, sl.k) == (t, kk) == (k + j, k + j)
+        assert torch.equal(sl.params, p)
+        assert torch.equal(sl.m, m)
+        assert torch.equal(sl.v, v)
 
 
 def test_streams_capped_by_layer_groups():
@@ -1012,7 +1131,9 @@ def test_merge_parity(wd_, N, K, r, dora):
     lin = L.make_linear(g["Wq"], g["A"], g["B"], s, 8, mag, nrm)
     W, A, B = np64(c["W"]), np64(c["A"]), np64(c["B"])
     m64 = np64(mag) if dora else None
-    n64 = np64(nrm) if dora else None
+    n64 = O.dora_row_norms(W, A, B, s) if dora else None
+    if dora:
+        assert rel_err(nrm, n64) <= 1e-5
     # float32 output
     out = torch.full((N, K), float("nan"), device=DEV)
     rm = torch.full((1,), float("nan"), device=DEV, dtype=torch.float64)
@@ -1134,7 +1255,9 @@ def test_slots_match_oracle(case):
             if step:
                 ci["X"], ci["dY"] = c["X"] * 0.5, c["dY"] * -1.5
             m = np64(mags[i]) if dora else None
-            nr = np64(nrms[i]) if dora else None
+            nr = O.dora_row_norms(np64(c["W"]), np64(c["A"]), np64(c["B"]), 1.5) if dora else None
+            if dora:
+                assert rel_err(nrms[i], nr) <= 1e-5
             refs.append(_oracle(ci, 1.5, p, (1234 + i, 3, step, 5, 4), m, nr))
         last = refs[-1]
         checks = dict(Y=last["Y"], U=last["U"], dX=last["dX"], dA=refs[0]["dA"] + last["dA"],
