@@ -211,19 +211,47 @@ def kernel_table(entries, total_ms):
     return rows
 
 
-def cpu_baseline(cfg, budget_s):
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, budget_s, threads=None):
     """The oracle's whole step on a bounded sample: the full per-layer step
     (all projections, all G chunks, one slot) layer after layer, wrapping
     round to layer 0 again, until about `budget_s` of work; the per-layer
-    time is scaled to the whole workload."""
+    time is scaled to the whole workload (extrapolated when the sample is
+    not the whole step).  threads: BLAS thread limit (None = all)."""
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=int(threads)):
+            return cpu_baseline(cfg, budget_s)
     import numpy as np
     import oracle as O
     from bwd_adamw_amd import workloads as WL
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
     f64 = lambda t: t.double().numpy()
     def layer_inputs(l):
@@ -275,12 +303,105 @@ def cpu_baseline(cfg, budget_s):
     # whole-step time of the full workload, scaled from the sampled layers
     step_s = elapsed_total / layers_done * cfg.layers * cfg.slots
     value = cfg.tokens_per_step / step_s
+    whole = layers_done >= cfg.layers and cfg.slots == 1
     sample = (f"oracle train_step, one layer at a time (all projections, {cfg.chunks} chunk(s) of "
               f"{cfg.tokens} tokens, slot 0): {layers_done} layer-steps over the {cfg.layers} "
               f"layers in {elapsed_total:.1f} s, scaled to the full {cfg.layers}-layer x "
               f"{cfg.slots}-slot step")
     return {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample}
+            "sample": sample, "extrapolated": not whole, "cpu_model": cpu_model(),
+            "workload": cfg.name}
+
+
+# ---------------------------------------------------------------------------
+# Summaries of rocprofv3 CSV output (no GPU needed): the tables committed
+# under profiles/ are printed by these, from the directory a run wrote.
+def _rocprof_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _field(row, name):
+    if name in row:
+        return row[name]
+    for k, v in row.items():
+        if k.lower() == name.lower():
+            return v
+    raise KeyError(name)
+
+
+def _short(name, width=110):
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def summarize_trace(directory, top=30):
+    """Kernel-trace table: dispatches grouped by kernel, grid (workgroups)
+    and workgroup size, with durations from the trace's timestamps (ns)."""
+    groups = {}
+    for r in _rocprof_rows(directory, "kernel_trace.csv"):
+        wgs = [int(_field(r, f"Workgroup_Size_{a}")) for a in "XYZ"]
+        grid = [int(_field(r, f"Grid_Size_{a}")) for a in "XYZ"]
+        blocks = "x".join(str(g // max(w, 1)) for g, w in zip(grid, wgs))
+        key = (_field(r, "Kernel_Name"), blocks, wgs[0] * wgs[1] * wgs[2])
+        dur = (int(_field(r, "End_Timestamp")) - int(_field(r, "Start_Timestamp"))) / 1e3
+        groups.setdefault(key, []).append(dur)
+    total = sum(sum(v) for v in groups.values()) or 1.0
+    out = ["| kernel | grid | threads | calls | total ms | avg us | min us | max us | % |",
+           "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (name, blocks, nt), d in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        out.append(f"| `{_short(name)}` | {blocks} | {nt} | {len(d)} | {sum(d) / 1e3:.3f} | "
+                   f"{sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
+                   f"{100.0 * sum(d) / total:.2f} |")
+    return "\n".join(out)
+
+
+def summarize_pmc(directory, top=30):
+    """Counter table: per (kernel, grid threads), each counter's value per
+    dispatch (summed over a dispatch's rows, averaged over dispatches)."""
+    per_dispatch = {}
+    for r in _rocprof_rows(directory, "counter_collection.csv"):
+        key = (_field(r, "Kernel_Name"), int(_field(r, "Grid_Size")))
+        d = per_dispatch.setdefault(key, {}).setdefault(_field(r, "Dispatch_Id"), {})
+        c = _field(r, "Counter_Name")
+        d[c] = d.get(c, 0.0) + float(_field(r, "Counter_Value"))
+    counters = sorted({c for disp in per_dispatch.values() for d in disp.values() for c in d})
+    out = ["| kernel | grid threads | dispatches | " + " | ".join(counters) + " |",
+           "|---|---:|---:|" + "---:|" * len(counters)]
+    rank = sorted(per_dispatch.items(),
+                  key=lambda kv: -sum(sum(d.values()) for d in kv[1].values()))
+    for (name, grid), disp in rank[:top]:
+        means = [sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in counters]
+        out.append(f"| `{_short(name)}` | {grid} | {len(disp)} | " +
+                   " | ".join(f"{m:.1f}" for m in means) + " |")
+    return "\n".join(out)
+
+
+def frozen_flops_per_step(cfg):
+    """Algorithmic flops of the frozen products in one step: forward and dX,
+    2*T*N*K each, for every linear, chunk and slot."""
+    per_token = sum(2 * 2 * p.in_dim * p.out_dim for p in cfg.projections) * cfg.layers
+    return per_token * cfg.tokens_per_step
+
+
+def one_stream(trainer):
+    """Context: the trainer's calls all on the current stream (its side
+    streams and their workspaces set aside), for the instrumented pass."""
+    import contextlib
+
+    @contextlib.contextmanager
+    def ctx():
+        side, side_ws = trainer.side, trainer.side_ws
+        trainer.side, trainer.side_ws = [], []
+        try:
+            yield
+        finally:
+            trainer.side, trainer.side_ws = side, side_ws
+    return ctx()
 
 
 def main():
@@ -288,18 +409,34 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload number (default: the TinyLlama-shaped wq+wv workload)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload number (default 5: DoRA on the Qwen3-4B-shaped all-linear "
+                         "layers, two slots, the largest single-GPU workload)")
     ap.add_argument("--w-format", choices=W_FORMATS, default=None,
                     help="block-quantized frozen W for a bf16 workload (default: its bf16 W)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-others", type=float, default=3.0,
+                    help="seconds of oracle work per extra CPU figure (the small float32 "
+                         "workloads at all threads and at one thread; 0 = skip)")
     ap.add_argument("--streams", type=int, default=4,
-                    help="HIP streams the layers' calls are spread over (default 4; at most "
-                         "one per layer group)")
+                    help="HIP streams the layers' calls are spread over in the timed pass "
+                         "(default 4; at most one per layer group)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="only print the kernel-trace table of a rocprofv3 --kernel-trace "
+                         "CSV run under DIR (no GPU)")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="only print the counter table of a rocprofv3 --pmc CSV run under DIR "
+                         "(no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_pmc:
+        if args.summarize_trace:
+            print(summarize_trace(args.summarize_trace))
+        if args.summarize_pmc:
+            print(summarize_pmc(args.summarize_pmc))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -342,19 +479,31 @@ def main():
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
     value = cfg.tokens_per_step * args.steps / elapsed
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value:.1f} tokens/s")
+    log(f"timed {args.steps} steps on {1 + len(trainer.side)} stream(s): {ms:.3f} ms/step, "
+        f"{value:.1f} tokens/s")
 
-    # instrumented pass over the same number of steps: per-kernel HIP events
-    L.lora_profile_begin(200000)
-    t1 = time.perf_counter()
-    run_steps(trainer, slots, inputs, args.steps)
-    entries = L.lora_profile_end()
-    prof_ms = (time.perf_counter() - t1) / args.steps * 1e3
+    # Instrumented pass over the same number of steps, every call on one
+    # stream so that a launch's duration is its own and not shared with
+    # other layers' launches: per-kernel HIP events on the launch stream.
+    with one_stream(trainer):
+        run_steps(trainer, slots, inputs, 1)
+        torch.cuda.synchronize()
+        L.lora_profile_begin(200000)
+        t1 = time.perf_counter()
+        run_steps(trainer, slots, inputs, args.steps)
+        entries = L.lora_profile_end()
+        prof_ms = (time.perf_counter() - t1) / args.steps * 1e3
     kernel_ms = sum(e["total_ms"] for e in entries) / args.steps
-    log(f"profiled pass: {prof_ms:.3f} ms/step, kernel time {kernel_ms:.3f} ms/step")
+    log(f"profiled pass (one stream): {prof_ms:.3f} ms/step, kernel time {kernel_ms:.3f} ms/step")
 
     rl = roofline_of(entries, cfg)
+    rl["streams"] = 1
     rl["stream_copy_gbps"] = stream_copy_gbps()
+    # chip level: the frozen products' flops of a step over the timed step
+    peak = PEAK["f32" if cfg.w_dtype == "f32" else "bf16"]
+    fl = frozen_flops_per_step(cfg)
+    rl["step"] = {"frozen_flops": fl, "achieved": fl / (ms * 1e-3) / 1e12, "peak": peak,
+                  "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / 1e12 / peak}
     out = {
         "metric": METRIC,
         "value": value,
@@ -377,11 +526,23 @@ def main():
             "streams": 1 + len(trainer.side),
         },
         "roofline": rl,
-        "kernels": {"sum_kernel_ms_per_step": kernel_ms, "table": kernel_table(entries, kernel_ms * args.steps)},
+        "kernels": {"streams": 1, "ms_per_step": prof_ms, "sum_kernel_ms_per_step": kernel_ms,
+                    "table": kernel_table(entries, kernel_ms * args.steps)},
     }
+    del model, trainer, slots, inputs
+    torch.cuda.empty_cache()
     if args.cpu_budget > 0:
         t2 = time.perf_counter()
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        cb = cpu_baseline(cfg, args.cpu_budget)
+        if args.cpu_others > 0:
+            # the small float32 workloads, at all threads and at one
+            cb["others"] = []
+            for n in (1, 2, 3):
+                for th in (None, 1):
+                    o = cpu_baseline(WL.get_config(n), args.cpu_others, threads=th)
+                    cb["others"].append({k: o[k] for k in ("workload", "value", "unit", "cores",
+                                                           "extrapolated")})
+        out["cpu_baseline"] = cb
         log(f"cpu baseline: {time.perf_counter() - t2:.1f} s")
     else:
         out["cpu_baseline"] = None
