@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/lora.h"
 #include "common.hpp"
@@ -1305,13 +1306,22 @@ size_t lora_grad_prepare_workspace_bytes(int64_t n) {
   return 4096 + 1024 * (sizeof(double) + sizeof(int)) + 256;
 }
 
-int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, float max_norm,
-                      float* d_scale, double* d_stats, double* h_norm, void* ws,
-                      size_t ws_bytes, void* stream) {
-  if (!grads || !d_scale || n <= 0 || n_pred_tokens <= 0) return LORA_E_INVALID;
-  if (!(max_norm >= 0.0f) || !std::isfinite(max_norm)) return LORA_E_INVALID;
-  if (!al16(grads)) return LORA_E_ALIGN;
-  if (!ws || !al16(ws) || ws_bytes < lora_grad_prepare_workspace_bytes(n)) return LORA_E_WORKSPACE;
+}  // extern "C"
+
+// Scratch of lora_grad_prepare_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel or a copy (on the host the name is only a stand-in for
+// the symbol); it takes the device address from hipGetSymbolAddress, once
+// per device with that device current, and keeps it per device.
+constexpr size_t kNoallocScratchBytes = 16640;   // lora_grad_prepare's workspace, any n
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+// The two gradient-norm passes over `ws` (per-block partials, flags and the
+// {norm, clip} pair; every word read is written earlier in the same call).
+int grad_prepare_on(const float* grads, int64_t n, int64_t n_pred_tokens, float max_norm,
+                    float* d_scale, double* d_stats, double* h_norm, void* ws, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int64_t nb0 = clampi(cdiv(n, 8192), 1, 1024);
   const int64_t per = rup(cdiv(n, nb0), 1024);
@@ -1339,6 +1349,54 @@ int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, floa
     if (std::isnan(host[0])) return LORA_E_NONFINITE;
   }
   return LORA_OK;
+}
+
+int check_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, float max_norm,
+                       const float* d_scale) {
+  if (!grads || !d_scale || n <= 0 || n_pred_tokens <= 0) return LORA_E_INVALID;
+  if (!(max_norm >= 0.0f) || !std::isfinite(max_norm)) return LORA_E_INVALID;
+  if (!al16(grads)) return LORA_E_ALIGN;
+  return LORA_OK;
+}
+
+constexpr int kNoallocMaxDevices = 64;
+std::once_flag scratch_once[kNoallocMaxDevices];
+void* scratch_ptr[kNoallocMaxDevices];
+hipError_t scratch_err[kNoallocMaxDevices];
+
+// Device address of this device's scratch, or NULL when the device index or
+// the symbol lookup fails.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices) return nullptr;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens, float max_norm,
+                      float* d_scale, double* d_stats, double* h_norm, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (int e = check_grad_prepare(grads, n, n_pred_tokens, max_norm, d_scale)) return e;
+  if (!ws || !al16(ws) || ws_bytes < lora_grad_prepare_workspace_bytes(n)) return LORA_E_WORKSPACE;
+  return grad_prepare_on(grads, n, n_pred_tokens, max_norm, d_scale, d_stats, h_norm, ws, stream);
+}
+
+int lora_grad_prepare_noalloc(const float* grads, int64_t n, int64_t n_pred_tokens,
+                              float max_norm, float* d_scale, double* d_stats, double* h_norm,
+                              void* stream) {
+  if (int e = check_grad_prepare(grads, n, n_pred_tokens, max_norm, d_scale)) return e;
+  if (lora_grad_prepare_workspace_bytes(n) > kNoallocScratchBytes) return LORA_E_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return LORA_E_HIP;
+  return grad_prepare_on(grads, n, n_pred_tokens, max_norm, d_scale, d_stats, h_norm, ws, stream);
 }
 
 int lora_adamw_step(float* params, const float* grads, float* m, float* v,

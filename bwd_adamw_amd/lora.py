@@ -24,7 +24,7 @@ __all__ = [
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
-    "lora_qweight_layout", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS", "GroupCall",
+    "lora_qweight_layout", "lora_grad_prepare_noalloc", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS", "GroupCall",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
@@ -45,7 +45,7 @@ EXPORTS = (
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
-    "lora_qweight_layout",
+    "lora_qweight_layout", "lora_grad_prepare_noalloc",
 )
 
 
@@ -100,6 +100,7 @@ def lib() -> C.CDLL:
             "lora_backward": (I32, [P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
             "lora_grad_prepare_workspace_bytes": (SZ, [I64]),
             "lora_grad_prepare": (I32, [P, I64, I64, F, P, P, P, P, SZ, P]),
+            "lora_grad_prepare_noalloc": (I32, [P, I64, I64, F, P, P, P, P]),
             "lora_adamw_step": (I32, [P, P, P, P, P, I32, P, P, P]),
             "lora_dropout_mask": (I32, [P, I64, I64, P, P]),
             "lora_dora_row_norms_workspace_bytes": (SZ, [P]),
@@ -460,6 +461,19 @@ def lora_grad_prepare(grads, n_pred_tokens, max_norm, d_scale, d_stats=None, syn
                                  C.byref(h) if sync else None, _ptr(ws, "ws", None), ws_bytes,
                                  _stream(stream))
     _check("lora_grad_prepare", rc)
+    return h.value if sync else None
+
+
+def lora_grad_prepare_noalloc(grads, n_pred_tokens, max_norm, d_scale, d_stats=None, sync=True,
+                              stream=None):
+    """lora_grad_prepare with the library's static device scratch in place of
+    a workspace (nothing is allocated); same returns and errors."""
+    h = C.c_double(0.0)
+    rc = lib().lora_grad_prepare_noalloc(_ptr(grads, "grads"), grads.numel(), int(n_pred_tokens),
+                                         float(max_norm), _ptr(d_scale, "d_scale"),
+                                         _ptr(d_stats, "d_stats", torch.float64),
+                                         C.byref(h) if sync else None, _stream(stream))
+    _check("lora_grad_prepare_noalloc", rc)
     return h.value if sync else None
 
 

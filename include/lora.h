@@ -251,6 +251,25 @@ int lora_grad_prepare(const float* grads, int64_t n, int64_t n_pred_tokens,
                       float max_norm, float* d_scale, double* d_stats,
                       double* h_norm, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free lora_grad_prepare, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The same two passes and
+ * results as lora_grad_prepare (bitwise: the same kernels over the same
+ * partition), with its partials, flags and {norm, clip} pair in a static
+ * device scratch array of 16,640 bytes per GPU (held until the process
+ * ends; its device address is looked up once per device, on the first call
+ * on that device).  That size holds the passes' scratch for any n; a size
+ * it could not hold would be refused with LORA_E_WORKSPACE.  Allocates
+ * nothing and calls no allocating routine.  Every call on one GPU uses that
+ * GPU's one array, which keeps the last call's contents (each call writes
+ * every word it reads before reading it): calls that overlap on one GPU
+ * (concurrent streams or host threads) race and must be serialised by the
+ * caller.  h_norm != NULL synchronises the stream, as in lora_grad_prepare.
+ * Returns LORA_E_HIP if the scratch's address cannot be obtained. */
+int lora_grad_prepare_noalloc(const float* grads, int64_t n, int64_t n_pred_tokens,
+                              float max_norm, float* d_scale, double* d_stats, double* h_norm,
+                              void* stream);
+
 /* Decoupled AdamW over the arena segments ("4.3. Training Guide",
  * "Optimizer"; "8. LoRA Fundamentals", "The training loop"):
  *   g' = grads * (*d_scale)
