@@ -424,6 +424,9 @@ def main():
                          "(default 4; at most one per layer group)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--no-profile-pass", action="store_true",
+                    help="skip the instrumented pass (per-launch HIP events); the line then "
+                         "has no roofline or kernel table (for counter-collection runs)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="only print the kernel-trace table of a rocprofv3 --kernel-trace "
                          "CSV run under DIR (no GPU)")
@@ -482,6 +485,12 @@ def main():
     log(f"timed {args.steps} steps on {1 + len(trainer.side)} stream(s): {ms:.3f} ms/step, "
         f"{value:.1f} tokens/s")
 
+    if args.no_profile_pass:
+        print(json.dumps({"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                          "higher_is_better": True, "config": {"workload": cfg.name,
+                          "streams": 1 + len(trainer.side)}, "roofline": None}), flush=True)
+        return
     # Instrumented pass over the same number of steps, every call on one
     # stream so that a launch's duration is its own and not shared with
     # other layers' launches: per-kernel HIP events on the launch stream.

@@ -113,8 +113,16 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
   constexpr int ACH = BM * CPR / NT;                // 16-byte A chunks per thread
   constexpr int BCH = BN * CPR / NT;                // 16-byte B chunks per thread (fwd)
-  constexpr int BITEMS = CPR * (BN / 4);            // transposed 8x4 blocks (dx)
-  constexpr int BIT = (BITEMS + NT - 1) / NT;
+  // dX with bf16 W: the W tile is stored as loaded, [BK][BN] with its rows'
+  // 32-byte segments XOR-swizzled by row, and the MFMA operand is read with
+  // LDS transpose reads (TRB).  Quantized W decodes and transposes while
+  // staging instead.
+  constexpr bool TRB = !FWD && !wq_quantized(WQ);
+  constexpr int BDC = BK * BN / 8;                  // TRB: 16-byte chunks of the W tile
+  constexpr int BDCH = (BDC + NT - 1) / NT;
+  constexpr int RPQB = NT / (BN / 8);               // TRB: W rows per thread pass
+  static_assert(!TRB || (BDC % NT == 0 && NT % (BN / 8) == 0), "whole W chunks per thread");
+  static_assert(!TRB || BK * BN <= BN * LDS_ROW, "TRB tile fits the B buffer");
   constexpr int KS = BK / 16;                       // MFMAs per K-step per output tile
   constexpr int LBK = 64;                           // K-step of the LoRA contraction
   constexpr int LROW = LBK + 8;
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   struct Stage {
     u32x4 a[ACH];
     u32x4 bf[(FWD && !QW) ? BCH : 1];
-    u32x2 bt[(FWD || QW) ? 1 : BIT][8];
+    u32x4 bd[TRB ? BDCH : 1];
     uint32_t qf[(FWD && QW) ? BCH : 1][QWD];          // quantized fwd: one run per chunk
     uint32_t qt[(!FWD && QW) ? QIT : 1][QR][QWD];     // quantized dX: QR runs per item
   };
@@ -191,11 +199,9 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
           : __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(p.B + n0), (short)0,
                 (int)(uint32_t)min<int64_t>(0xffffffffll, (p.Kc * p.ldb - n0) * 2), 0x00020000);
-  constexpr int CQN = BN / 4;                       // dX: 4-column quads per row
-  constexpr int KGQ = NT / CQN;                     // dX: 8-row groups per thread pass
-  static_assert(NT % CPR == 0 && (FWD || NT % CQN == 0), "uniform chunk rows");
+  static_assert(NT % CPR == 0, "uniform chunk rows");
   const uint32_t voffB = FWD ? (uint32_t)(((tid / CPR) * p.ldb + 8 * (tid % CPR)) * 2)
-                             : (uint32_t)(((tid / CQN) * 8 * p.ldb + 4 * (tid % CQN)) * 2);
+                             : (uint32_t)(((tid / (BN / 8)) * p.ldb + 8 * (tid % (BN / 8))) * 2);
   // Quantized W: W row length, and the planes' resources.
   const uint32_t qK = (uint32_t)(FWD ? p.Kc : p.Nc);
   const QRes<QW ? WQ : WQ_Q8_0> QRs(p.q);
@@ -205,8 +211,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   };
 
   auto a_ok = [&](int64_t k0) -> bool { return EXACT || k0 + 8 * (tid % CPR) < kend; };
-  auto bt_ok = [&](int q) -> bool {
-    return (EXACT || n0 + 4 * (tid % CQN) < p.Nc) && tid + NT * q < BITEMS;
+  auto bd_ok = [&]() -> bool { return EXACT || n0 + 8 * (tid % (BN / 8)) < p.Nc; };
+  // TRB: byte offset of 16-byte chunk c of W-tile row kk in the B buffer.
+  auto bd_off = [&](int kk, int c) -> int {
+    return kk * (BN * 2) + (((c >> 1) ^ (2 * (kk & 3))) << 5) + ((c & 1) << 4);
   };
   auto load = [&](Stage& S, int64_t k0) {
 #pragma unroll
@@ -237,12 +245,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
                        rB, voffB + (uint32_t)((q * RPQ * p.ldb + k0) * 2), 0, 0));
     } else {
 #pragma unroll
-      for (int q = 0; q < BIT; ++q)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          S.bt[q][i] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                         rB, voffB + (uint32_t)(((int64_t)q * KGQ * 8 + i + k0) * p.ldb * 2), 0, 0));
+      for (int q = 0; q < BDCH; ++q)
+        S.bd[q] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rB, voffB + (uint32_t)(((int64_t)q * RPQB + k0) * p.ldb * 2), 0, 0));
     }
   };
   auto store = [&](const Stage& S, int64_t k0, int buf) {
@@ -295,33 +301,37 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
         *reinterpret_cast<u32x4*>(&Bs(buf)[(f / CPR) * LDS_ROW + 8 * (f % CPR)]) = aok ? S.bf[q] : z4;
       }
     } else {
+      const bool ok = bd_ok();
+      char* bb = reinterpret_cast<char*>(Bs(buf));
 #pragma unroll
-      for (int q = 0; q < BIT; ++q) {
+      for (int q = 0; q < BDCH; ++q) {
         const int f = tid + NT * q;
-        if (f >= BITEMS) continue;
-        const int cq = f % CQN, kg = f / CQN;
-        const bool ok = bt_ok(q);
-        u32x2 w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = ok ? S.bt[q][i] : u32x2{0u, 0u};
-        // column e of the 8x4 block becomes 8 contraction values
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u32x4 o;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const uint32_t x0 = (e < 2) ? w[2 * d].x : w[2 * d].y;
-            const uint32_t x1 = (e < 2) ? w[2 * d + 1].x : w[2 * d + 1].y;
-            o[d] = (e & 1) ? (hi16(x0) | (hi16(x1) << 16)) : (lo16(x0) | (lo16(x1) << 16));
-          }
-          *reinterpret_cast<u32x4*>(&Bs(buf)[(4 * cq + e) * LDS_ROW + 8 * kg]) = o;
-        }
+        *reinterpret_cast<u32x4*>(bb + bd_off(f / (BN / 8), f % (BN / 8))) = ok ? S.bd[q] : z4;
       }
     }
   };
   // MFMA over one staged K-step: STEPS MFMAs of 16 contraction indices per
   // output tile, lane half hl holding indices hl*HALF .. of each LD-wide row.
-  auto compute = [&](const uint16_t* Ab, const uint16_t* Bb, auto LD, auto HALF, auto STEPS) {
+  // TRB: lane l = 16 g + i reads W-tile rows kb + i/4 and kb + 4 + i/4 at
+  // columns nb + 4 (i%4) .. +3, kb = 32 (g/2) + 8 s, nb = the n-tile's
+  // 16 (g%2); the transpose read hands lane l column nb + i with 4 rows each,
+  // so the pair is the 8 contraction values 32 (l/32) + 8 s .. +7 of column
+  // l%32, the order the A operand uses.
+  const int trg = lane >> 4, tri = lane & 15;
+  auto tr_frag = [&](const uint16_t* Bb, int n, int s) -> u32x4 {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int kk = 32 * (trg >> 1) + 8 * s + (tri >> 2);
+    const int col = n + 16 * (trg & 1) + 4 * (tri & 3);
+    const int off = kk * (BN * 2) + (((col >> 4) ^ (2 * (kk & 3))) << 5) + ((col & 15) << 1);
+    auto* b = (__attribute__((address_space(3))) char*)(Bb);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(b + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(b + off + 4 * (BN * 2)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  auto compute = [&](const uint16_t* Ab, const uint16_t* Bb, auto LD, auto HALF, auto STEPS,
+                     auto TR) {
     constexpr int ld = decltype(LD)::value, half = decltype(HALF)::value;
 #pragma unroll
     for (int s = 0; s < decltype(STEPS)::value; ++s) {
@@ -330,8 +340,12 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       for (int i = 0; i < MI; ++i)
         av[i] = *reinterpret_cast<const u32x4*>(&Ab[(wm0 + i * 32 + l32) * ld + half * hl + 8 * s]);
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
-        bv[j] = *reinterpret_cast<const u32x4*>(&Bb[(wn0 + j * 32 + l32) * ld + half * hl + 8 * s]);
+      for (int j = 0; j < NI; ++j) {
+        if constexpr (decltype(TR)::value)
+          bv[j] = tr_frag(Bb, wn0 + j * 32, s);
+        else
+          bv[j] = *reinterpret_cast<const u32x4*>(&Bb[(wn0 + j * 32 + l32) * ld + half * hl + 8 * s]);
+      }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -341,6 +355,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   using MainLd = std::integral_constant<int, LDS_ROW>;
   using MainHalf = std::integral_constant<int, BK / 2>;
   using MainSteps = std::integral_constant<int, KS>;
+  using MainTr = std::integral_constant<bool, TRB>;
   // LoRA contraction over the rank: float32 operands rounded to bf16 in LDS,
   // in 64-wide K-steps over the same LDS.
   auto lora_contraction = [&]() {
@@ -386,7 +401,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       }
       __syncthreads();
       compute(La, Lb, std::integral_constant<int, LROW>{}, std::integral_constant<int, LBK / 2>{},
-              std::integral_constant<int, LBK / 16>{});
+              std::integral_constant<int, LBK / 16>{}, std::false_type{});
     }
     __syncthreads();
   };
@@ -431,7 +446,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
         // lifetimes, which exposes their whole latency.
         __builtin_amdgcn_sched_barrier(0);
         const int buf = (int)(kk & 1);
-        compute(As(buf), Bs(buf), MainLd{}, MainHalf{}, MainSteps{});
+        compute(As(buf), Bs(buf), MainLd{}, MainHalf{}, MainSteps{}, MainTr{});
         store(R[(u + 1) % DEPTH], kstep(kk + 1), buf ^ 1);
         __syncthreads();
       }
@@ -442,7 +457,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       const int64_t kk = k + u;
       if (kk < nk) {
         const int buf = (int)(kk & 1);
-        compute(As(buf), Bs(buf), MainLd{}, MainHalf{}, MainSteps{});
+        compute(As(buf), Bs(buf), MainLd{}, MainHalf{}, MainSteps{}, MainTr{});
         if (kk + 1 < nk) store(R[(u + 1) % DEPTH], kstep(kk + 1), buf ^ 1);
         __syncthreads();
       }

@@ -110,12 +110,45 @@ Split plan_split(int64_t L, int64_t other, int64_t want, int64_t q, int64_t min_
   return {len, (int)cdiv(L, len)};
 }
 
+// Blocks of 256 threads of `kern` resident per CU, from the runtime (what
+// its registers and LDS allow); 2 where the runtime cannot say (no GPU).
+template <typename F>
+int64_t resident_per_cu(F kern) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 2;
+  }
+  return n;
+}
+constexpr int64_t kCUs = 256;
+
+// Resident blocks of k4 on the whole chip, per padded rank; looked up once
+// per instance.  (k3 keeps its target of 512 blocks: measured on the
+// 9728-wide products, shorter blocks beyond one round of them beat one round
+// of longer blocks.)
+int64_t k4_slots(int rp) {
+  static const int64_t s[4] = {kCUs * resident_per_cu(k4_kernel<16>), kCUs * resident_per_cu(k4_kernel<32>),
+                               kCUs * resident_per_cu(k4_kernel<64>), kCUs * resident_per_cu(k4_kernel<128>)};
+  return s[rp <= 16 ? 0 : rp <= 32 ? 1 : rp <= 64 ? 2 : 3];
+}
+
 // Row range of the rank-side backward kernels: whole T (results written
 // directly, no reduction launch) when T is short or the column strips alone
-// fill the chip; otherwise split to about 512 blocks.
-Split plan_rows(int64_t T, int64_t strips) {
+// fill the chip; otherwise split into as many ranges as keep the grid within
+// the `slots` blocks the chip holds at once (rounded down: a grid just past
+// it would run a second, nearly empty round).
+// k3's rows: the same, but rounded up to about `slots` blocks (k3 gains
+// more from shorter blocks than it loses to a partly filled second round).
+Split plan_rows_k3(int64_t T, int64_t strips, int64_t slots) {
   if (T <= 256 || strips >= 256) return {rup(T, SK_T), 1};
-  return plan_split(T, strips, 512, SK_T, SK_T);
+  return plan_split(T, strips, slots, SK_T, SK_T);
+}
+Split plan_rows(int64_t T, int64_t strips, int64_t slots = 512) {
+  if (T <= 256 || strips >= 256) return {rup(T, SK_T), 1};
+  const int64_t n = clampi(slots / strips, 1, cdiv(T, SK_T));
+  const int64_t len = rup(cdiv(T, n), SK_T);
+  return {len, (int)cdiv(T, len)};
 }
 
 // k3's grid on the plain path: column strips grouped spb per block (the
@@ -130,15 +163,15 @@ struct K3Plan {
   Split rows;
   int64_t spb, nvp;
 };
-K3Plan plan_k3(int64_t T, int64_t N, int64_t r, int64_t strips) {
+K3Plan plan_k3(int64_t T, int64_t N, int64_t r, int64_t strips, int64_t slots) {
   auto cost = [&](int64_t nvp, int64_t nts) {
     return 4.0 * r * ((double)nvp * T * (nvp > 1 ? 3 : 2) + (double)nts * N * (nts > 1 ? 3 : 2));
   };
-  // One strip per block, its rows split until about 512 blocks run.
-  K3Plan best = {plan_rows(T, strips), 1, strips};
+  // One strip per block, its rows split until about `slots` blocks run.
+  K3Plan best = {plan_rows_k3(T, strips, slots), 1, strips};
   double cbest = cost(strips, best.rows.n);
   const int64_t maxr = cdiv(T, SK_T);
-  const int64_t want = std::min<int64_t>(512, strips * maxr);
+  const int64_t want = std::min<int64_t>(slots, strips * maxr);
   int64_t prev = strips;
   for (int64_t spb = 2; spb <= strips; ++spb) {
     const int64_t nvp = cdiv(strips, spb);
@@ -291,17 +324,18 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
   const bool own = stack <= 1;
   y.down = plan_split(K, cdiv(T, SK_T), 512, SK_C, SK_C);
   y.strips = cdiv(N, SK_C);
-  y.k4 = plan_rows(T, cdiv(K, SK_C));
+  const int rpad = rank_pad(r);
+  y.k4 = plan_rows(T, cdiv(K, SK_C), k4_slots(rpad));
   y.gf = plan_gemm(stack * T, N, K, bf, false);
   y.gd = plan_gemm(stack * T, K, N, bf, true);
   // k3 beside the split dX GEMM keeps its own grid (one strip per block
   // there); the plain path groups strips.
   if (use_split_path(y.gd, r, bf)) {
-    y.k3 = plan_rows(T, y.strips);
+    y.k3 = plan_rows_k3(T, y.strips, 512);
     y.k3spb = 1;
     y.k3nvp = y.strips;
   } else {
-    const K3Plan kp = plan_k3(T, N, r, y.strips);
+    const K3Plan kp = plan_k3(T, N, r, y.strips, 512);
     y.k3 = kp.rows;
     y.k3spb = kp.spb;
     y.k3nvp = kp.nvp;
