@@ -349,7 +349,12 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32x32x16_bf16(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < NI; ++j) {
+          // dX computes its tile transposed (epilogue below); the forward
+          // keeps rows across lanes so that its stores are whole lines.
+          if constexpr (FWD) acc[i][j] = mfma32x32x16_bf16(av[i], bv[j], acc[i][j]);
+          else acc[i][j] = mfma32x32x16_bf16(bv[j], av[i], acc[i][j]);
+        }
     }
   };
   using MainLd = std::integral_constant<int, LDS_ROW>;
@@ -411,17 +416,17 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     const Bf16Slot so = bf16_slot(p, slot);
     if (so.drop.on) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i) {
+        const int64_t gm = m0 + wm0 + i * 32 + l32;
+        const uint64_t rk = drop_row(so.drop, gm - moff);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
-          const uint64_t rk = drop_row(so.drop, gm - moff);
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            const int64_t gn = n0 + wn0 + j * 32 + l32;
+          for (int v = 0; v < 16; ++v) {
+            const int64_t gn = n0 + wn0 + j * 32 + row32(v, lane);
             acc[i][j][v] *= drop_mul(so.drop, rk, gn);
           }
-        }
+      }
     }
   }
 
@@ -467,26 +472,62 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   if (FWD && lora) lora_contraction();
 
   const Bf16Slot so = bf16_slot(p, slot);
+  if constexpr (FWD) {
+    // Lane l holds column n = .. + l%32 of 16 rows: each store instruction
+    // writes whole 128-byte rows of the tile.
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t gn = n0 + wn0 + j * 32 + l32;
-      if (gn >= p.Nc) continue;
-      const float c = (p.nsplit == 1 && so.cn) ? so.cn[gn] / so.cd[gn] : 1.0f;
+      for (int j = 0; j < NI; ++j) {
+        const int64_t gn = n0 + wn0 + j * 32 + l32;
+        if (gn >= p.Nc) continue;
+        const float c = (p.nsplit == 1 && so.cn) ? so.cn[gn] / so.cd[gn] : 1.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
-        if (gm >= p.M) continue;
-        const float x = acc[i][j][v];
-        if (p.nsplit == 1) {
-          so.C[(gm - moff) * p.Nc + gn] = x * c;
-          if (so.C2) so.C2[(gm - moff) * p.Nc + gn] = x;
-        } else {
-          p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
+          if (gm >= p.M) continue;
+          const float x = acc[i][j][v];
+          if (p.nsplit == 1) {
+            so.C[(gm - moff) * p.Nc + gn] = x * c;
+            if (so.C2) so.C2[(gm - moff) * p.Nc + gn] = x;
+          } else {
+            p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
+          }
         }
       }
-    }
+    return;
+  }
+  // dX: the MFMA computes the tile transposed (W-side operand first), so lane
+  // l holds output row m = .. + l%32 and, per group of four accumulators,
+  // four consecutive columns: every store is a 16-byte vector, and the
+  // dropout mask above needed one row key per row.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int64_t gm = m0 + wm0 + i * 32 + l32;
+    if (gm >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int64_t gn = n0 + wn0 + j * 32 + row32(4 * v4, lane);   // Nc is a multiple of 8
+        if (gn >= p.Nc) continue;
+        f32x4 x = {acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                   acc[i][j][4 * v4 + 3]};
+        if (p.nsplit == 1) {
+          const int64_t o = (gm - moff) * p.Nc + gn;
+          if (so.C2) *reinterpret_cast<f32x4*>(so.C2 + o) = x;
+          if (so.cn) {
+            const f32x4 cn = *reinterpret_cast<const f32x4*>(so.cn + gn);
+            const f32x4 cd = *reinterpret_cast<const f32x4*>(so.cd + gn);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= cn[e] / cd[e];
+          }
+          *reinterpret_cast<f32x4*>(so.C + o) = x;
+        } else {
+          *reinterpret_cast<f32x4*>(p.part + ((int64_t)split * p.M + gm) * p.Nc + gn) = x;
+        }
+      }
+  }
 }
 
 // Sum of the split partials in split order, then the unsplit kernel's
