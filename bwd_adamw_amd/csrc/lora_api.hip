@@ -960,7 +960,18 @@ void launch_bwd_k3(const BwdJob& jb, hipStream_t st) {
   {
     prof::Scope ps("k3_v_db", T, N, r, jb.k3_flops, jb.k3_bytes);
     const dim3 grid((unsigned)y.k3nvp, (unsigned)y.k3.n);
-    if (jb.ka.Z) {
+    // Whole 64 x 64 tiles at rank 32 or 64 with at most two strips per
+    // block: the row-major variant (same outputs, V partials written once).
+    const bool whole = (jb.rp == 32 || jb.rp == 64) && T % SK_T == 0 && N % SK_C == 0 &&
+                       y.k3.len % SK_T == 0 && y.k3spb <= 2;
+    const bool z = jb.ka.Z != nullptr;
+    if (whole) {
+#define LORA_K3R(RP_, ZT_, SPB_) \
+  if (jb.rp == RP_ && z == ZT_ && y.k3spb == SPB_) launch(k3r_kernel<RP_, ZT_, SPB_>, grid, st, ps, jb.ka);
+      LORA_K3R(32, false, 1) LORA_K3R(32, false, 2) LORA_K3R(32, true, 1) LORA_K3R(32, true, 2)
+      LORA_K3R(64, false, 1) LORA_K3R(64, false, 2) LORA_K3R(64, true, 1) LORA_K3R(64, true, 2)
+#undef LORA_K3R
+    } else if (z) {
       LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP, true>, grid, st, ps, jb.ka));
     } else {
       LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP, false>, grid, st, ps, jb.ka));

@@ -461,6 +461,252 @@ void k3_kernel(K3Args p) {
 }
 
 // ---------------------------------------------------------------------------
+// k3r: the same pass as k3 for whole tiles (T and N multiples of 64, tsplit
+// a multiple of 64, rank padded to RP = 32 or 64, at most SPB = 2 strips per
+// block), in row-major tile order: for each 64-row stage the block visits
+// its strips one after another, so the stage's V rows are summed over the
+// block's strips in registers and written once (no read-modify-write of the
+// V partial), while each strip keeps its dB tile and dm in registers over
+// all stages.  Both contractions run on v_mfma_f32_32x32x2f32:
+//   V  [t][j] (+)= sum_n g[t][n] B[n][j]: MFMA e of group c takes n = 8c + 4h + e
+//                  (h = lane / 32), so a lane reads four of its n as one
+//                  128-bit LDS read from g and from the strip's B^T;
+//   dB [n][j] (+)= sum_t g[t][n] U[t][j]: MFMA e of group c takes
+//                  t = 16c + 8h + e, the lane halves' rows eight apart, which
+//                  puts their 32-bit reads on different LDS banks.
+// RP = 64: every wave owns one 32 x 32 tile of V and one of each strip's dB;
+// RP = 32: waves 0-1 own V's tiles, waves 2-3 dB's.
+// ---------------------------------------------------------------------------
+constexpr int K3R_LD = 68;   // row stride (floats) of the g and B^T tiles
+
+template <int RP, int SPB>
+constexpr int k3r_lds_floats() { return 64 * K3R_LD + 64 * (RP + 4) + SPB * RP * K3R_LD; }
+
+template <int RP, bool ZT, int SPB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k3r_kernel(K3Args p) {
+  static_assert(RP == 32 || RP == 64, "rank 32 or 64");
+  static_assert(SPB == 1 || SPB == 2, "one or two strips per block");
+  constexpr int LDU = RP + 4;
+  constexpr bool BOTH = RP == 64;
+  __shared__ __attribute__((aligned(16))) float smem[k3r_lds_floats<RP, SPB>()];
+  float* Gs = smem;                      // g tile [t][n]
+  float* Us = Gs + 64 * K3R_LD;          // U tile [t][j]
+  float* Bt = Us + 64 * LDU;             // strip q's B^T at Bt + q * RP * K3R_LD, [j][n]
+  const float* __restrict__ dY = p.dY;
+  const float* __restrict__ Z = p.Z;
+  const float* __restrict__ U = p.U;
+  const int64_t T = p.T, N = p.N, r = p.r;
+  const K3Out& o = p.o;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int tr = tid >> 4, tc = tid & 15;          // VALU: rows 4tr..4tr+3, columns 4tc..4tc+3
+  const int64_t bx = blockIdx.x;
+  const int by = blockIdx.y;
+  const int64_t tb = (int64_t)by * p.tsplit, te = min(T, tb + p.tsplit);
+  const int64_t sx0 = bx * p.spb;
+  const int ns = (int)min<int64_t>(p.spb, p.nstrip - sx0);
+  const int nvp = (int)((p.nstrip + p.spb - 1) / p.spb), nts = p.nts;
+  const bool want_v = o.V != nullptr || o.Vpart != nullptr;
+  float* vdst = !want_v ? nullptr : nvp == 1 ? o.V : o.Vpart + bx * T * r;
+  const int nst = (int)((te - tb) / 64);
+  const int ntot = nst * ns;
+  const bool do_v = BOTH || wave < 2, do_b = BOTH || wave >= 2;
+  const int tv = BOTH ? (wave & 1) : wave, jv = BOTH ? (wave >> 1) : 0;
+  const int tn = BOTH ? (wave & 1) : wave - 2, jb = BOTH ? (wave >> 1) : 0;
+
+  // Per strip: the column scale of this thread's four columns and B^T.
+  float cmul[SPB][4];
+#pragma unroll
+  for (int q = 0; q < SPB; ++q) {
+    const int64_t n0 = (sx0 + (q < ns ? q : 0)) * 64;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      cmul[q][e] = p.mag ? p.mag[n0 + 4 * tc + e] / p.nrm[n0 + 4 * tc + e] : 1.f;
+    if (want_v && q < ns) {
+      float* bt = Bt + q * RP * K3R_LD;
+      for (int i = tid; i < 64 * (RP / 4); i += 256) {
+        const int n = i / (RP / 4), jq = i % (RP / 4);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (4 * jq < r) v = *reinterpret_cast<const f32x4*>(p.B + (n0 + n) * r + 4 * jq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bt[(4 * jq + e) * K3R_LD + n] = v[e];
+      }
+    }
+  }
+  f32x16 vacc, dbacc[SPB];
+  float dm[SPB][4];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) vacc[v] = 0.f;
+#pragma unroll
+  for (int q = 0; q < SPB; ++q) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dbacc[q][v] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dm[q][e] = 0.f;
+  }
+
+  // Tile idx: row stage idx / ns, strip idx % ns.  The next tile's loads go
+  // out before this tile is scaled, stored and contracted; the U rows of a
+  // stage (one register set) are loaded one tile before the stage opens.
+  constexpr int UQ = RP / 16;   // U float4s per thread (stage rows x RP / 256)
+  struct Tile {
+    f32x4 g[4], z[ZT ? 4 : 1];
+  };
+  auto load = [&](Tile& S, int idx) {
+    idx = idx < ntot ? idx : ntot - 1;
+    const int64_t t0 = tb + (int64_t)(idx / ns) * 64, n0 = (sx0 + idx % ns) * 64;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int64_t off = (t0 + 4 * tr + qq) * N + n0 + 4 * tc;
+      S.g[qq] = *reinterpret_cast<const f32x4*>(dY + off);
+      if constexpr (ZT) S.z[qq] = *reinterpret_cast<const f32x4*>(Z + off);
+    }
+  };
+  f32x4 un[UQ];
+  auto load_u = [&](int stage) {
+    stage = stage < nst ? stage : nst - 1;
+    const int64_t t0 = tb + (int64_t)stage * 64;
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      const int i = tid + 256 * u, row = i / (RP / 4), jq = i % (RP / 4);
+      un[u] = 4 * jq < r ? *reinterpret_cast<const f32x4*>(U + (t0 + row) * r + 4 * jq)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  Tile R[2];
+  if (ntot > 0) {
+    load(R[0], 0);
+    load_u(0);
+  }
+  // Q: the tile's strip, a compile-time index (the loop below visits strips
+  // in order, so that each strip's accumulators stay in fixed registers);
+  // LAST: the tile closes its row stage.
+  auto step = [&](auto QC, auto LASTC, int idx, const Tile& S, Tile& nxt) {
+    constexpr int Q = decltype(QC)::value;
+    constexpr bool LAST = decltype(LASTC)::value;
+    const int64_t t0 = tb + (int64_t)(idx / ns) * 64, n0 = (sx0 + Q) * 64;
+    if constexpr (Q == 0) {   // the stage's U rows, loaded one tile ago
+#pragma unroll
+      for (int u = 0; u < UQ; ++u) {
+        const int i = tid + 256 * u, row = i / (RP / 4), jq = i % (RP / 4);
+        *reinterpret_cast<f32x4*>(&Us[row * LDU + 4 * jq]) = un[u];
+      }
+    }
+    load(nxt, idx + 1);
+    if constexpr (LAST) load_u(idx / ns + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      f32x4 g = S.g[qq];
+      if constexpr (ZT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dm[Q][e] += g[e] * S.z[qq][e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[e] *= cmul[Q][e];
+      if (o.gbf) {
+        const u32x2 b = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+        *reinterpret_cast<u32x2*>(o.gbf + (t0 + 4 * tr + qq) * N + n0 + 4 * tc) = b;
+      }
+      *reinterpret_cast<f32x4*>(&Gs[(4 * tr + qq) * K3R_LD + 4 * tc]) = g;
+    }
+    __syncthreads();
+    if (want_v && do_v) {
+      const float* bt = Bt + Q * RP * K3R_LD;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&Gs[(32 * tv + l32) * K3R_LD + 8 * c + 4 * h]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&bt[(32 * jv + l32) * K3R_LD + 8 * c + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vacc = mfma32x32x2(a[e], b[e], vacc);
+      }
+    }
+    if (do_b) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float av[8], bv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = 16 * c + 8 * h + e;
+          av[e] = Gs[t * K3R_LD + 32 * tn + l32];
+          bv[e] = Us[t * LDU + 32 * jb + l32];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dbacc[Q] = mfma32x32x2(av[e], bv[e], dbacc[Q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    if constexpr (LAST) {   // the stage's V rows, summed over the block's strips
+      if (want_v && do_v) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t t = t0 + 32 * tv + row32(v, lane);
+          const int64_t j = 32 * jv + l32;
+          if (j < r) vdst[t * r + j] = vacc[v];
+          vacc[v] = 0.f;
+        }
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (SPB == 2 && ns == 2) {
+    for (int idx = 0; idx < ntot; idx += 2) {
+      step(I0{}, std::false_type{}, idx, R[0], R[1]);
+      step(std::integral_constant<int, SPB - 1>{}, std::true_type{}, idx + 1, R[1], R[0]);
+    }
+  } else {   // one strip: every tile closes its stage
+    for (int idx = 0; idx < ntot; idx += 2) {
+      step(I0{}, std::true_type{}, idx, R[0], R[1]);
+      if (idx + 1 < ntot) step(I0{}, std::true_type{}, idx + 1, R[1], R[0]);
+    }
+  }
+
+  // dB and dm of each strip: direct when there is one row range.
+  const bool bdirect = nts == 1;
+  float(*red)[64] = reinterpret_cast<float(*)[64]>(Gs);   // [16][64], g tile no longer read
+#pragma unroll
+  for (int q = 0; q < SPB; ++q) {
+    if (q >= ns) break;
+    const int64_t n0 = (sx0 + q) * 64;
+    if (do_b) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t n = n0 + 32 * tn + row32(v, lane);
+        const int64_t j = 32 * jb + l32;
+        if (j < r) {
+          if (bdirect) {
+            const float x = dbacc[q][v] * o.scale;
+            o.dB[n * r + j] = o.accumulate ? o.dB[n * r + j] + x : x;
+          } else {
+            o.dBpart[((int64_t)by * N + n) * r + j] = dbacc[q][v];
+          }
+        }
+      }
+    }
+    if (o.dm) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[tr][4 * tc + e] = dm[q][e];
+      __syncthreads();
+      if (tid < 64) {
+        float sum = 0.f;
+        for (int g = 0; g < 16; ++g) sum += red[g][tid];
+        if (bdirect) {
+          sum /= p.nrm[n0 + tid];
+          o.dm[n0 + tid] = o.accumulate ? o.dm[n0 + tid] + sum : sum;
+        } else {
+          o.dmpart[(int64_t)by * N + n0 + tid] = sum;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k4: dApart[y][j][k] = sum_{t in range y} V[t,j] X~[t,k], V given as vparts
 // partials [vparts][T][r] summed in order while staging.
 // Grid: (ceil(K/64), nts).  Wave w owns columns 16w..16w+15 of the strip.
