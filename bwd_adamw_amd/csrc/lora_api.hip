@@ -18,6 +18,7 @@
 #include "gemm_f32.hpp"
 #include "gemm_wq.hpp"
 #include "launch.hpp"
+#include "normbatch.hpp"
 #include "optim.hpp"
 #include "profile.hpp"
 #include "skinny.hpp"
@@ -1631,6 +1632,210 @@ int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace
     launch(dora_norm_finish_kernel, dim3((unsigned)cdiv(N, 256)), st, ps, a.part,
            (int)q.nsplit, N, out_norm);
   }
+  return hip_status();
+}
+
+namespace {
+
+// Batched DoRA norms: bf16-W linears with LoRA factors (rank <= 64) go
+// through the expansion kernels (normbatch.hpp), adjacent linears over one W
+// stacked as slots of one job; the rest take lora_dora_row_norms one by one.
+struct NbJob {
+  int first, S;             // lins[first .. first + S - 1]
+  int64_t N, K, Kp, klen;
+  int nsplit, RP, C, r;
+  size_t parts, P, G, wsq;  // workspace offsets within the job's chunk
+};
+
+bool nb_eligible(const lora_linear* l) {
+  return l->w_dtype == LORA_BF16 && l->A != nullptr && l->rank <= NB_MAX_RP &&
+         l->in_dim % 8 == 0 && al16(l->W);
+}
+bool nb_same_w(const lora_linear* a, const lora_linear* b) {
+  return a->W == b->W && a->out_dim == b->out_dim && a->in_dim == b->in_dim &&
+         a->rank == b->rank;
+}
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Contraction splits: about 3072 per tile, whole steps of 32, none empty.
+constexpr int64_t kNbSplitLen = 3072;
+
+// Jobs of the eligible linears in order, with their workspace offsets
+// inside their chunk of NB_MAX_JOBS jobs; returns the largest chunk's bytes.
+size_t nb_plan(int n, const lora_linear* lins, std::vector<NbJob>& jobs) {
+  jobs.clear();
+  for (int i = 0; i < n;) {
+    if (!nb_eligible(&lins[i])) {
+      ++i;
+      continue;
+    }
+    NbJob j;
+    memset(&j, 0, sizeof(j));
+    j.first = i;
+    j.S = 1;
+    while (j.S < NB_MAX_SLOTS && i + j.S < n && nb_eligible(&lins[i + j.S]) &&
+           nb_same_w(&lins[i], &lins[i + j.S]))
+      ++j.S;
+    const lora_linear* l = &lins[i];
+    j.N = l->out_dim;
+    j.K = l->in_dim;
+    j.r = (int)l->rank;
+    j.RP = (int)rup(l->rank, 32);
+    j.C = j.S * j.RP;
+    j.Kp = rup(j.K, NB_KS);
+    const int64_t ns = cdiv(j.Kp, kNbSplitLen);
+    j.klen = rup(cdiv(j.Kp, ns), NB_KS);
+    j.nsplit = (int)cdiv(j.Kp, j.klen);
+    jobs.push_back(j);
+    i += j.S;
+  }
+  size_t best = 0, cur = 0;
+  for (size_t k = 0; k < jobs.size(); ++k) {
+    if (k % NB_MAX_JOBS == 0) cur = 0;
+    NbJob& j = jobs[k];
+    j.parts = cur;
+    cur += a256((size_t)j.S * 3 * j.RP * j.Kp * 2);
+    j.P = cur;
+    cur += a256((size_t)j.nsplit * j.N * j.C * 4);
+    j.G = cur;
+    cur += a256((size_t)j.nsplit * 3 * j.S * j.RP * j.C * 4);
+    j.wsq = cur;
+    cur += a256((size_t)j.nsplit * j.N * 8);
+    best = std::max(best, cur);
+  }
+  return best;
+}
+
+// Split, products and combine of jobs[c0, c1) on one stream.
+void nb_launch(const lora_linear* lins, float* const* out, const std::vector<NbJob>& jobs,
+               size_t c0, size_t c1, char* w, hipStream_t st) {
+  {
+    NbSplitArgs a;
+    memset(&a, 0, sizeof(a));
+    int64_t g = 0;
+    double by = 0.0;
+    for (size_t k = c0; k < c1; ++k) {
+      const NbJob& j = jobs[k];
+      NbSplitJob& s = a.job[k - c0];
+      for (int q = 0; q < j.S; ++q) s.A[q] = lins[j.first + q].A;
+      s.parts = reinterpret_cast<uint16_t*>(w + j.parts);
+      s.K = j.K;
+      s.Kp = j.Kp;
+      s.r = j.r;
+      s.RP = j.RP;
+      s.S = j.S;
+      s.g0 = g;
+      g += (int64_t)j.S * j.RP * j.Kp / 8;
+      by += 4.0 * j.S * j.r * j.K + 6.0 * j.S * j.RP * j.Kp;
+    }
+    a.njobs = (int)(c1 - c0);
+    a.ngroups = g;
+    prof::Scope ps("dora_norm_split", g, a.njobs, 0, 0.0, by);
+    launch(nb_split_kernel, dim3((unsigned)cdiv(g, 256)), st, ps, a);
+  }
+  {
+    NbProdArgs a;
+    memset(&a, 0, sizeof(a));
+    int64_t tiles = 0, nsum = 0;
+    double fl = 0.0, by = 0.0;
+    int ni = 0;
+    for (int pass = 0; pass < 2; ++pass)   // every job's P tiles, then the G tiles
+      for (size_t k = c0; k < c1; ++k) {
+        const NbJob& j = jobs[k];
+        NbItem& it = a.it[ni++];
+        const bool P = pass == 0;
+        it.M = P ? static_cast<const uint16_t*>(lins[j.first].W)
+                 : reinterpret_cast<const uint16_t*>(w + j.parts);
+        it.parts = reinterpret_cast<const uint16_t*>(w + j.parts);
+        it.out = reinterpret_cast<float*>(w + (P ? j.P : j.G));
+        it.wsq = P ? reinterpret_cast<double*>(w + j.wsq) : nullptr;
+        it.rows = P ? j.N : 3ll * j.S * j.RP;
+        it.ldm = P ? j.K : j.Kp;
+        it.K = j.K;
+        it.Kp = j.Kp;
+        it.klen = j.klen;
+        it.C = j.C;
+        it.RP = j.RP;
+        it.nsplit = j.nsplit;
+        it.ncolt = (int)cdiv(j.C, NB_TN);
+        it.tile0 = tiles;
+        tiles += cdiv(it.rows, NB_TM) * it.nsplit * it.ncolt;
+        fl += 6.0 * it.rows * j.C * j.K;
+        by += (P ? 2.0 * j.N * j.K + 8.0 * j.nsplit * j.N : 0.0) + 6.0 * j.C * j.Kp +
+              4.0 * j.nsplit * it.rows * j.C;
+        if (P) nsum += j.N;
+      }
+    a.nitems = ni;
+    prof::Scope ps("dora_norm_prod", nsum, jobs[c0].C, jobs[c0].K, fl, by);
+    launch(nb_prod_kernel, dim3((unsigned)tiles), st, ps, a);
+  }
+  {
+    NbFinArgs a;
+    memset(&a, 0, sizeof(a));
+    int64_t blocks = 0;
+    double by = 0.0;
+    for (size_t k = c0; k < c1; ++k) {
+      const NbJob& j = jobs[k];
+      NbFinJob& f = a.job[k - c0];
+      f.P = reinterpret_cast<const float*>(w + j.P);
+      f.wsq = reinterpret_cast<const double*>(w + j.wsq);
+      f.G = reinterpret_cast<const float*>(w + j.G);
+      for (int q = 0; q < j.S; ++q) {
+        f.B[q] = lins[j.first + q].B;
+        f.out[q] = out[j.first + q];
+        f.s[q] = lins[j.first + q].scale;
+      }
+      f.N = j.N;
+      f.C = j.C;
+      f.RP = j.RP;
+      f.S = j.S;
+      f.r = j.r;
+      f.nsplit = j.nsplit;
+      f.blk0 = blocks;
+      blocks += j.S * cdiv(j.N, 256);
+      by += (double)j.S * j.N * (4.0 * j.nsplit * j.RP + 8.0 * j.nsplit + 4.0 * j.r + 4.0);
+    }
+    a.njobs = (int)(c1 - c0);
+    prof::Scope ps("dora_norm_combine", blocks, a.njobs, 0, 0.0, by);
+    launch(nb_finish_kernel, dim3((unsigned)blocks), st, ps, a);
+  }
+}
+
+}  // namespace
+
+size_t lora_dora_row_norms_batch_workspace_bytes(int n, const lora_linear* lins) {
+  if (n < 1 || !lins) return 0;
+  for (int i = 0; i < n; ++i)
+    if (check_row_norm_linear(&lins[i]) != LORA_OK) return 0;
+  std::vector<NbJob> jobs;
+  size_t need = nb_plan(n, lins, jobs);
+  for (int i = 0; i < n; ++i)
+    if (!nb_eligible(&lins[i])) need = std::max(need, lora_dora_row_norms_workspace_bytes(&lins[i]));
+  return need;
+}
+
+int lora_dora_row_norms_batch(int n, const lora_linear* lins, float* const* out_norms,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 1 || !lins || !out_norms) return LORA_E_INVALID;
+  for (int i = 0; i < n; ++i) {
+    const int rc = check_row_norm_linear(&lins[i]);
+    if (rc != LORA_OK) return rc;
+    if (!out_norms[i]) return LORA_E_INVALID;
+  }
+  const size_t need = lora_dora_row_norms_batch_workspace_bytes(n, lins);
+  if (need && (!workspace || workspace_bytes < need)) return LORA_E_WORKSPACE;
+  if (need && !al16(workspace)) return LORA_E_ALIGN;
+  std::vector<NbJob> jobs;
+  nb_plan(n, lins, jobs);
+  hipStream_t st = (hipStream_t)stream;
+  for (size_t c0 = 0; c0 < jobs.size(); c0 += NB_MAX_JOBS)
+    nb_launch(lins, out_norms, jobs, c0, std::min(jobs.size(), c0 + NB_MAX_JOBS),
+              static_cast<char*>(workspace), st);
+  for (int i = 0; i < n; ++i)
+    if (!nb_eligible(&lins[i])) {
+      const int rc = lora_dora_row_norms(&lins[i], out_norms[i], workspace, workspace_bytes, stream);
+      if (rc != LORA_OK) return rc;
+    }
   return hip_status();
 }
 

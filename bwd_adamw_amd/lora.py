@@ -24,7 +24,8 @@ __all__ = [
     "lora_status_string", "lora_profile_begin", "lora_profile_end",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
-    "lora_qweight_layout", "lora_grad_prepare_noalloc", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS", "GroupCall",
+    "lora_qweight_layout", "lora_grad_prepare_noalloc",
+    "lora_dora_row_norms_batch_workspace_bytes", "lora_dora_row_norms_batch", "QWeight", "qweight_pack", "Q_FORMATS", "EXPORTS", "GroupCall",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora.so")
@@ -46,6 +47,7 @@ EXPORTS = (
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
     "lora_qweight_layout", "lora_grad_prepare_noalloc",
+    "lora_dora_row_norms_batch_workspace_bytes", "lora_dora_row_norms_batch",
 )
 
 
@@ -119,6 +121,8 @@ def lib() -> C.CDLL:
             "lora_forward_slots": (I32, [I32, P, P, P, P, P, P, P, SZ, P]),
             "lora_backward_slots": (I32, [I32, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
             "lora_qweight_layout": (SZ, [I32, I64, I64, P]),
+            "lora_dora_row_norms_batch_workspace_bytes": (SZ, [I32, P]),
+            "lora_dora_row_norms_batch": (I32, [I32, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -295,7 +299,7 @@ _NEED = {
     "Y": lambda l: l.tokens * l.out_dim, "Z": lambda l: l.tokens * l.out_dim,
     "dY": lambda l: l.tokens * l.out_dim, "U": lambda l: l.tokens * l.rank,
     "dA": lambda l: l.rank * l.in_dim, "dB": lambda l: l.out_dim * l.rank,
-    "dMag": lambda l: l.out_dim,
+    "dMag": lambda l: l.out_dim, "out_norm": lambda l: l.out_dim,
 }
 
 
@@ -509,6 +513,27 @@ def lora_dora_row_norms(lin: LoraLinear, out_norm, ws=None, stream=None, split=T
     rc = lib().lora_dora_row_norms(C.byref(lin), _sized(out_norm, "out_norm", lin.out_dim),
                                    _ptr(ws, "ws", None), ws_bytes, _stream(stream))
     _check("lora_dora_row_norms", rc)
+
+
+def lora_dora_row_norms_batch_workspace_bytes(lins) -> int:
+    return int(lib().lora_dora_row_norms_batch_workspace_bytes(len(lins), _linears(lins)))
+
+
+def lora_dora_row_norms_batch(lins, out_norms, ws=None, stream=None):
+    """Row norms of W + s B A for every linear of `lins` into the matching
+    entry of `out_norms`; `ws` as lora_dora_row_norms_batch_workspace_bytes
+    asks (taken from torch's allocator when None)."""
+    if len(lins) == 0:
+        return
+    if ws is None:
+        need = lora_dora_row_norms_batch_workspace_bytes(lins)
+        if need:
+            ws = torch.empty(need, device=out_norms[0].device, dtype=torch.uint8)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().lora_dora_row_norms_batch(len(lins), _linears(lins),
+                                         _ptrs(out_norms, "out_norm", lins), _ptr(ws, "ws", None),
+                                         ws_bytes, _stream(stream))
+    _check("lora_dora_row_norms_batch", rc)
 
 
 def lora_merge_workspace_bytes(lin: LoraLinear) -> int:

@@ -147,6 +147,9 @@ class Trainer:
         if cfg.dora:   # the row-norm refresh shares the workspaces between steps
             for k in model.keys:
                 ws = max(ws, L.lora_dora_row_norms_workspace_bytes(self._linear(k, None)))
+            nref = self.nslots if self.stack_slots else 1
+            ws = max(ws, L.lora_dora_row_norms_batch_workspace_bytes(
+                [self._linear(k, None) for k in model.keys for _ in range(nref)]))
         if self.stack_slots:
             for k in model.keys:
                 ws = max(ws, L.lora_slots_workspace_bytes(
@@ -174,6 +177,7 @@ class Trainer:
         self.side_ws = [torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
                         for _ in self.side]
         self._calls = {}   # (id(slot), group index) -> (slot, stream handle, norms, GroupCall)
+        self._refresh = {}  # (streams, slot ids) -> (slots, [(stream, linears, norms)])
         self.d_scale = torch.zeros(1, **f32)
         self.d_stats = torch.zeros(2, device=device, dtype=torch.float64)
         self.prep_ws = None
@@ -201,18 +205,38 @@ class Trainer:
             bare = L.LoraLinear(self.T, K, N, 0, wd, float(self.scale), wp, None, None, None, None)
             L.lora_dora_row_norms(bare, slot.mag[key], self.ws)
             slot.norm[key] = torch.empty(N, device=self.device, dtype=torch.float32)
-        self.refresh_dora(slot)
+        self.refresh_dora([slot])
 
-    def refresh_dora(self, slot: Slot):
-        """Row norms of W + s B A for every linear; each linear writes only
-        its own norm vector, so the layers are spread over the streams."""
+    def refresh_dora(self, slots: list):
+        """Row norms of W + s B A for every linear of `slots`, as batched
+        calls: the layers are dealt to the streams in contiguous runs, one
+        call per stream, and within a call the slots of each W are adjacent,
+        so that one pass over W serves all of them.  Each linear writes only
+        its own norm vector; the descriptors are built once per slot set
+        (the tensors are updated in place)."""
+        nst = 1 + len(self.side)
+        key_ = (nst,) + tuple(id(sl) for sl in slots)
+        hit = self._refresh.get(key_)
+        if hit is None or any(a is not b for a, b in zip(hit[0], slots)):
+            layers = sorted({k[0] for k in self.model.keys})
+            per = -(-len(layers) // nst)
+            calls = []
+            for q in range(nst):
+                run = set(layers[q * per:(q + 1) * per])
+                lins, outs = [], []
+                for key in self.model.keys:
+                    if key[0] in run:
+                        for sl in slots:
+                            lins.append(L.make_linear(self.model.W[key], sl.A[key], sl.B[key],
+                                                      self.scale, self.T))
+                            outs.append(sl.norm[key])
+                if lins:
+                    calls.append((q, lins, outs))
+            hit = (list(slots), calls)
+            self._refresh[key_] = hit
         streams, wss = self._fork()
-        layers = sorted({k[0] for k in self.model.keys})
-        for key in self.model.keys:
-            q = layers.index(key[0]) % len(streams)
-            W = self.model.W[key]
-            lin = L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T)
-            L.lora_dora_row_norms(lin, slot.norm[key], wss[q], stream=streams[q])
+        for q, lins, outs in hit[1]:
+            L.lora_dora_row_norms_batch(lins, outs, wss[q], stream=streams[q])
         self._join()
 
     # ------------------------------------------------------------------
@@ -324,14 +348,17 @@ class Trainer:
         if len(slots) > self.nslots:
             raise ValueError(f"trainer holds activations for {self.nslots} slots")
         self.forward_backward_slots(slots, chunks_per_slot)
-        return [self._update(sl, len(ch)) for sl, ch in zip(slots, chunks_per_slot)]
+        stats = [self._update(sl, len(ch), refresh=False) for sl, ch in zip(slots, chunks_per_slot)]
+        if self.cfg.dora:   # one refresh for all slots (a vetoed slot's norms stay the same)
+            self.refresh_dora(slots)
+        return stats
 
     def step(self, slot: Slot, chunks: list) -> StepStats:
         self.forward_backward(slot, chunks)
         return self._update(slot, len(chunks))
 
-    def _update(self, slot: Slot, n_chunks: int) -> StepStats:
-        """Prepare, AdamW and DoRA refresh of one slot.  The prepare waits
+    def _update(self, slot: Slot, n_chunks: int, refresh: bool = True) -> StepStats:
+        """Prepare, AdamW and (unless `refresh` is False) DoRA refresh of one slot.  The prepare waits
         for its veto flag on the host (one synchronisation per update): the
         slot's update count t (bias corrections) and update index k (schedule
         and dropout step key) live on the host and must not advance on a
@@ -353,8 +380,8 @@ class Trainer:
         hp = L.LoraAdamwHparams(lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay,
                                 cfg.plus_ratio, slot.t + 1)
         L.lora_adamw_step(slot.params, slot.grads, slot.m, slot.v, slot.segments, hp, self.d_scale)
-        if cfg.dora:
-            self.refresh_dora(slot)
+        if cfg.dora and refresh:
+            self.refresh_dora([slot])
         slot.t += 1
         slot.k += 1
         return StepStats(norm, False, lr)

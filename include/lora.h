@@ -308,6 +308,30 @@ size_t lora_dora_row_norms_workspace_bytes(const lora_linear* lin);
 int lora_dora_row_norms(const lora_linear* lin, float* out_norm, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* The DoRA row norms of n linears (the refresh after an update; "8. LoRA
+ * Fundamentals", "How it works"), out_norms[i] for lins[i], each accepted as
+ * by lora_dora_row_norms (the first invalid one's status is returned before
+ * any launch).  Linears with bf16 W whose rows are 16-byte aligned (in_dim a
+ * multiple of 8), LoRA factors and rank <= 64 expand the square:
+ *   n_i^2 = ||W_i||^2 + 2 scale sum_j B_ij (W A^T)_ij
+ *           + scale^2 sum_jl B_ij (A A^T)_jl B_il,
+ * with A split exactly into three bf16 parts so that the products over the
+ * inputs are exact bf16 products summed in float32, and the three terms
+ * combined in double; adjacent such linears with the same W, out_dim, in_dim
+ * and rank (adapter slots over one base, up to 4) share one pass over W.
+ * The expansion matches the direct form to float32 rounding relative to
+ * ||W_i||^2 + |2 scale <W_i,(B A)_i>| + scale^2 ||(B A)_i||^2, so rows whose
+ * adapted norm is far below ||W_i|| lose relative accuracy; use
+ * lora_dora_row_norms for such rows.  The other linears run as
+ * lora_dora_row_norms, one after another.  workspace: device,
+ * lora_dora_row_norms_batch_workspace_bytes(n, lins) bytes (0 only when no
+ * linear needs any), 16-byte aligned (LORA_E_WORKSPACE / LORA_E_ALIGN
+ * otherwise); its contents between calls do not matter.  The results equal
+ * lora_dora_row_norms up to rounding. */
+size_t lora_dora_row_norms_batch_workspace_bytes(int n, const lora_linear* lins);
+int lora_dora_row_norms_batch(int n, const lora_linear* lins, float* const* out_norms,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Merge for export ("8. LoRA Fundamentals": "How it works" for the
  * effective weight W + scale*B*A merged in F32 and DoRA's row rescale;
  * "Profiling with --jfr" for the RMSE a merge reports):

@@ -114,6 +114,53 @@ def test_optimizer_entry_validation():
     assert lib.lora_grad_prepare(256, 10, 4, 1.0, 256, None, None, 256, 16, None) == -5
 
 
+def _nb_need(W, N, K, r, S):
+    """Workspace of one expansion job as the library lays it out: the split
+    parts, the P partials, the G partials and the row sums of squares, each
+    rounded up to 256 bytes."""
+    a = lambda x: (x + 255) // 256 * 256
+    RP = -(-r // 32) * 32
+    Kp = -(-K // 32) * 32
+    ns = -(-Kp // 3072)
+    klen = -(-(-(-Kp // ns)) // 32) * 32
+    ns = -(-Kp // klen)
+    C_ = S * RP
+    return (a(S * 3 * RP * Kp * 2) + a(ns * N * C_ * 4) + a(ns * 3 * S * RP * C_ * 4) +
+            a(ns * N * 8))
+
+
+@no_device
+def test_dora_norm_batch_workspace_and_validation():
+    lib = L.lib()
+    bf = lambda W, **kw: _lin(w_dtype=L.BF16, W=W, **kw)
+    # Two slots over one W share a job; a third linear over another W is its own.
+    lins = [bf(256, in_dim=2048, out_dim=300, rank=16), bf(256, in_dim=2048, out_dim=300, rank=16),
+            bf(512, in_dim=2048, out_dim=300, rank=16)]
+    arr = (L.LoraLinear * 3)(*lins)
+    assert lib.lora_dora_row_norms_batch_workspace_bytes(3, arr) == \
+        _nb_need(256, 300, 2048, 16, 2) + _nb_need(512, 300, 2048, 16, 1)
+    # Nine W matrices: two launches that reuse the workspace; the largest counts.
+    many = (L.LoraLinear * 9)(*[bf(256 * (i + 1), in_dim=512, out_dim=64 + i, rank=8)
+                                for i in range(9)])
+    chunk1 = sum(_nb_need(0, 64 + i, 512, 8, 1) for i in range(8))
+    assert lib.lora_dora_row_norms_batch_workspace_bytes(9, many) == chunk1
+    # Linears the expansion does not take need only what lora_dora_row_norms needs.
+    f32 = (L.LoraLinear * 1)(_lin(in_dim=9728, out_dim=64, rank=16))
+    assert lib.lora_dora_row_norms_batch_workspace_bytes(1, f32) == \
+        lib.lora_dora_row_norms_workspace_bytes(C.byref(f32[0]))
+    assert lib.lora_dora_row_norms_batch_workspace_bytes(0, arr) == 0
+    outs = (C.c_void_p * 3)(256, 256, 256)
+    need = lib.lora_dora_row_norms_batch_workspace_bytes(3, arr)
+    assert lib.lora_dora_row_norms_batch(0, arr, outs, 256, need, None) == -1
+    assert lib.lora_dora_row_norms_batch(3, arr, outs, 256, need - 1, None) == -5
+    assert lib.lora_dora_row_norms_batch(3, arr, outs, None, need, None) == -5
+    assert lib.lora_dora_row_norms_batch(3, arr, outs, 264, need, None) == -4
+    bad = (L.LoraLinear * 3)(lins[0], lins[1], bf(512, in_dim=2048, out_dim=300, rank=200))
+    assert lib.lora_dora_row_norms_batch(3, bad, outs, 256, need, None) == -2
+    assert lib.lora_dora_row_norms_batch(3, arr, (C.c_void_p * 3)(256, None, 256), 256, need,
+                                         None) == -1
+
+
 def test_binding_checks_factor_shapes_against_w():
     """make_linear refuses factors that disagree with W's shape, on the host:
     the kernels size every access from the descriptor alone."""

@@ -569,6 +569,101 @@ def test_dora_row_norms_workspace_checked():
         L.lora_dora_row_norms(lin, out, torch.empty(need - 8, device=DEV, dtype=torch.uint8))
 
 
+def _slot_factors(K, N, r, slots, seed, b_std):
+    """Per-slot A and B over one W (the adapters of one base)."""
+    out = []
+    for q in range(slots):
+        key = lambda kind: (950 + seed, q, 0, 0, 0, kind)
+        out.append((WL.draw((r, K), key("A"), "uniform", 1 / math.sqrt(K)),
+                    WL.draw((N, r), key("B"), "normal", b_std)))
+    return out
+
+
+# (N, K, r, slots, b_std): ragged rows and K (K % 32 != 0), ranks padded to
+# 32 or 64, four slots (two column tiles), long K (contraction splits), a
+# LoRA term as large as W (b_std 1.0), the DoRA workload's shapes.
+BATCH_CASES = [
+    (100, 136, 8, 1, 0.05),
+    (37, 1000, 40, 2, 1.0),
+    (264, 520, 64, 4, 0.5),
+    (300, 7000, 16, 3, 1.0),
+    (129, 2048, 64, 2, 0.05),
+    (9728, 2560, 64, 2, 0.05),
+    (2560, 9728, 64, 2, 0.05),
+]
+
+
+@pytest.mark.parametrize("N,K,r,slots,b_std", BATCH_CASES,
+                         ids=[f"{c[0]}x{c[1]}-r{c[2]}-s{c[3]}" for c in BATCH_CASES])
+def test_dora_row_norms_batch_parity(N, K, r, slots, b_std):
+    """The expansion over bf16 W (slots stacked over one pass of W) against
+    the oracle's norms of the formed rows."""
+    W = WL.draw((N, K), (960, 0, 0, 0, 0, "W"), "normal", 0.02).to(torch.bfloat16)
+    fac = _slot_factors(K, N, r, slots, 1, b_std)
+    Wd = W.to(DEV)
+    dev = [(A.to(DEV), B.to(DEV)) for A, B in fac]
+    scales = [1.7 + 0.3 * q for q in range(slots)]
+    lins = [L.make_linear(Wd, A, B, s, 8) for (A, B), s in zip(dev, scales)]
+    outs = [torch.full((N,), float("nan"), device=DEV) for _ in range(slots)]
+    L.lora_dora_row_norms_batch(lins, outs)
+    Wh = np64(W.float())
+    for q, ((A, B), s) in enumerate(zip(fac, scales)):
+        assert rel_err(outs[q], O.dora_row_norms(Wh, np64(A), np64(B), s)) <= 1e-5, q
+
+
+def test_dora_row_norms_batch_mixed_list():
+    """Linears the expansion does not take (float32 or quantized W, rank
+    above 64, no factors) run as lora_dora_row_norms, bitwise, in a list that
+    also holds more W matrices than one launch takes (chunked launches)."""
+    lins, outs, refs, direct = [], [], [], []
+    keep = []
+    for i in range(11):
+        wd = ["bf16", "f32", "q4_k", "bf16"][i % 4] if i < 8 else "bf16"
+        N, K = 64 + 40 * i, 512 if wd == "q4_k" else 256 + 72 * (i % 3)
+        r = 128 if i == 3 else 8 + 8 * (i % 4)
+        c = _linear_case(8, K, N, r, wd, seed=40 + i, b_std=0.3)
+        g = _gpu(c)
+        keep.append(g)
+        bare = i == 7
+        lin = L.make_linear(g["Wq"], None if bare else g["A"], None if bare else g["B"],
+                            1.3, 8)
+        lins.append(lin)
+        outs.append(torch.full((N,), float("nan"), device=DEV))
+        refs.append(O.dora_row_norms(np64(c["W"])) if bare else
+                    O.dora_row_norms(np64(c["W"]), np64(c["A"]), np64(c["B"]), 1.3))
+        direct.append(wd != "bf16" or r > 64 or bare)
+    L.lora_dora_row_norms_batch(lins, outs)
+    for i, (lin, out, ref) in enumerate(zip(lins, outs, refs)):
+        assert rel_err(out, ref) <= 1e-5, i
+        if direct[i]:
+            one = torch.empty_like(out)
+            L.lora_dora_row_norms(lin, one)
+            assert torch.equal(out, one), i
+
+
+def test_dora_row_norms_batch_checks():
+    c = _linear_case(8, 512, 300, 16, "bf16", seed=5)
+    g = _gpu(c)
+    lins = [L.make_linear(g["Wq"], g["A"], g["B"], 1.0, 8)] * 2
+    outs = [torch.empty(300, device=DEV) for _ in range(2)]
+    need = L.lora_dora_row_norms_batch_workspace_bytes(lins)
+    assert need > 0
+    with pytest.raises(L.LoraError):
+        L.lora_dora_row_norms_batch(lins, outs, torch.empty(need - 256, device=DEV,
+                                                            dtype=torch.uint8))
+    bad = L.make_linear(g["Wq"], g["A"], g["B"], 1.0, 8)
+    bad.rank = 200
+    with pytest.raises(L.LoraError):
+        L.lora_dora_row_norms_batch([lins[0], bad], outs)
+    # Repeated calls give the same bits (fixed-order sums, no atomics).
+    ws = torch.empty(need, device=DEV, dtype=torch.uint8)
+    L.lora_dora_row_norms_batch(lins, outs, ws)
+    first = [o.clone() for o in outs]
+    ws.fill_(7)
+    L.lora_dora_row_norms_batch(lins, outs, ws)
+    assert all(torch.equal(a, b) for a, b in zip(first, outs))
+
+
 # ------------------------------------------------------ end-to-end steps ---
 def _e2e(cfg, layers=None, tokens=None, steps=1, slots=None, together=False):
     """Run `steps` updates on the GPU and in the oracle from equal inputs;
@@ -853,8 +948,8 @@ def test_resume_from_copied_state_is_bitwise(name, wl, layers, tokens, together)
         sl.m.copy_(m)
         sl.v.copy_(v)
         sl.t, sl.k = t, kk
-        if cfg.dora:
-            tr.refresh_dora(sl)
+    if cfg.dora:   # the norms are derived from the restored A and B
+        tr.refresh_dora(slots)
     _advance(tr, slots, chunks, j, together)
     torch.cuda.synchronize()
     for sl, (p, m, v, t, kk) in zip(slots, straight):
@@ -862,6 +957,32 @@ def test_resume_from_copied_state_is_bitwise(name, wl, layers, tokens, together)
         assert torch.equal(sl.params, p)
         assert torch.equal(sl.m, m)
         assert torch.equal(sl.v, v)
+
+
+def test_refresh_on_one_stream_equals_spread_refresh():
+    """The refresh's per-stream calls are rebuilt when the trainer's side
+    streams are set aside (the bench's one-stream pass); the norms are the
+    same bits either way, and both slots' norms match the oracle."""
+    cfg = WL.get_config(5)
+    inputs = _stream_inputs(cfg, 2, 256)
+    tr, slots, _ = _fresh(cfg, inputs, 256, True)
+    assert tr.side, "the DoRA workload spreads two layers over two streams"
+    tr.refresh_dora(slots)
+    spread = [{k: v.clone() for k, v in sl.norm.items()} for sl in slots]
+    side, side_ws = tr.side, tr.side_ws
+    tr.side, tr.side_ws = [], []
+    for sl in slots:
+        for v in sl.norm.values():
+            v.fill_(float("nan"))
+    tr.refresh_dora(slots)
+    tr.side, tr.side_ws = side, side_ws
+    s = O.scaling(cfg.alpha, cfg.rank, cfg.scaling)
+    for sl, ref in zip(slots, spread):
+        for key, v in sl.norm.items():
+            assert torch.equal(v, ref[key]), key
+            W = np64(tr.model.W[key].float())
+            want = O.dora_row_norms(W, np64(sl.A[key]), np64(sl.B[key]), s)
+            assert rel_err(v, want) <= 1e-5, key
 
 
 def test_streams_capped_by_layer_groups():
