@@ -211,6 +211,15 @@ def kernel_table(entries, total_ms):
     return rows
 
 
+def per_label_ms(entries, steps):
+    """Kernel time per step of each launch label (all shapes together),
+    largest first."""
+    tot = {}
+    for e in entries:
+        tot[e["kernel"]] = tot.get(e["kernel"], 0.0) + e["total_ms"] / steps
+    return {k: round(v, 3) for k, v in sorted(tot.items(), key=lambda kv: -kv[1])}
+
+
 def cpu_model():
     """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
     import subprocess
@@ -536,7 +545,8 @@ def main():
         },
         "roofline": rl,
         "kernels": {"streams": 1, "ms_per_step": prof_ms, "sum_kernel_ms_per_step": kernel_ms,
-                    "table": kernel_table(entries, kernel_ms * args.steps)},
+                    "table": kernel_table(entries, kernel_ms * args.steps),
+                    "per_label_ms": per_label_ms(entries, args.steps)},
     }
     del model, trainer, slots, inputs
     torch.cuda.empty_cache()

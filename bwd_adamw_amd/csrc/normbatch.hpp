@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void nb_split_kernel(NbSplitArgs p) {
 // rows (four 32 x 32 accumulators).  The row tile of a step (128 x 32 bf16)
 // is staged through LDS, double-buffered, one barrier per step, stored so
 // that every MFMA operand read is one conflict-free 16-byte read per lane;
-// each wave loads its own columns' parts straight into registers one step
-// ahead.  Rows past `rows` read as zero (buffer bounds) and elements at k >=
+// each wave loads its own columns' parts straight into registers.  Loads run
+// two steps ahead (a ring of three register stages).  Rows past `rows` read as zero (buffer bounds) and elements at k >=
 // K are masked per 8-element group (K is a multiple of 8).
 // ---------------------------------------------------------------------------
 struct NbItem {
@@ -118,7 +118,10 @@ void nb_prod_kernel(NbProdArgs p) {
   __shared__ __attribute__((aligned(16))) u32x4 Ms[2][NB_TM * NB_KS / 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t b = blockIdx.x;
+  // Tiles are numbered item by item (a job's P tiles, then its G tiles);
+  // each XCD takes a contiguous run of them, so that the parts a job's
+  // tiles share stay in one XCD's L2 instead of every L2 holding all jobs'.
+  const int64_t b = xcd_tile(blockIdx.x, gridDim.x);
   int i = 0;
   while (i + 1 < p.nitems && b >= p.it[i + 1].tile0) ++i;
   const NbItem& I = p.it[i];
@@ -163,32 +166,29 @@ void nb_prod_kernel(NbProdArgs p) {
       S.m[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                              rm, in ? (uint32_t)((sbase + k + 8 * h) * 2) : OUT, 0, 0));
     }
-    if (has_cols) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
-          S.c[kk][q] = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         rc, coff + q * pstride + (uint32_t)(2 * (k + 16 * kk)), 0, 0));
-    }
+      for (int q = 0; q < 3; ++q)
+        S.c[kk][q] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rc, coff + q * pstride + (uint32_t)(2 * (k + 16 * kk)), 0, 0));
   };
   double dsq = 0.0;
-  auto put = [&](const Stage& S, int buf) {
+  // `count`: the stage is a real step (not a repeat past the last one).
+  auto put = [&](const Stage& S, int buf, bool count) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) Ms[buf][sdst + 32 * h] = S.m[h];
-    if (want_sq) {
-      float sq = 0.f;
+    float sq = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = bf16_bits_to_f32(S.m[h][e] & 0xffffu);
-          const float hi = bf16_bits_to_f32(S.m[h][e] >> 16);
-          sq += lo * lo + hi * hi;
-        }
-      dsq += (double)sq;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_bits_to_f32(S.m[h][e] & 0xffffu);
+        const float hi = bf16_bits_to_f32(S.m[h][e] >> 16);
+        sq += lo * lo + hi * hi;
+      }
+    dsq += (count && want_sq) ? (double)sq : 0.0;
   };
   f32x16 acc[4];
 #pragma unroll
@@ -207,25 +207,32 @@ void nb_prod_kernel(NbProdArgs p) {
         for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32x32x16_bf16(a[rt], S.c[kk][q], acc[rt]);
     }
   };
-  // Step s: the next step's loads go out, this step's MFMAs run, the next
-  // row tile is stored to the other buffer, one barrier.
-  auto step = [&](int s, const Stage& cur, Stage& nxt) {
-    load(nxt, s + 1);
+  // Step s: the loads of step s + 2 go out (a ring of three register
+  // stages), this step's MFMAs run, step s + 1's row tile is stored to the
+  // other buffer, one barrier.  The body is straight-line: past the last
+  // step the loads repeat its addresses and the stores go to a buffer no
+  // step reads (a branch there made the compiler wait for every load in
+  // flight at the loop head); a wave without columns multiplies zeros.
+  auto step = [&](int s, const Stage& cur, const Stage& nxt, Stage& nxt2) {
+    load(nxt2, s + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (has_cols) compute(cur, s & 1);
-    if (s + 1 < nsteps) put(nxt, (s + 1) & 1);
+    compute(cur, s & 1);
+    put(nxt, (s + 1) & 1, s + 1 < nsteps);
     __syncthreads();
   };
-  Stage R[2];
-  if (nsteps > 0) {
-    load(R[0], 0);
-    put(R[0], 0);
-  }
+  Stage R[3];
+  load(R[0], 0);
+  load(R[1], 1);
+  put(R[0], 0, true);
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, R[0], R[1]);
-    if (s + 1 < nsteps) step(s + 1, R[1], R[0]);
+  int s = 0;
+  for (; s + 3 <= nsteps; s += 3) {
+    step(s, R[0], R[1], R[2]);
+    step(s + 1, R[1], R[2], R[0]);
+    step(s + 2, R[2], R[0], R[1]);
   }
+  if (s < nsteps) step(s, R[0], R[1], R[2]);
+  if (s + 1 < nsteps) step(s + 1, R[1], R[2], R[0]);
 
   if (has_cols) {
     float* out = I.out + (int64_t)sp * I.rows * I.C;
@@ -245,11 +252,19 @@ void nb_prod_kernel(NbProdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine, one thread per row i of one slot q of a job:
-//   n_i^2 = sum_splits wsq + 2 s sum_j B_ij P_ij + s^2 sum_j B_ij (G B_i^T)_j,
-// G of the slot summed over splits and parts in a fixed order (double) and
-// held in LDS with a row stride of NB_MAX_RP (zero past RP).
+// Combine, four threads per row i of one slot q of a job:
+//   n_i^2 = sum_splits wsq + 2 s sum_j B_ij P_ij + s^2 sum_j B_ij (G B_i^T)_j.
+// G of the slot is summed over splits and parts in a fixed order (double)
+// and held in LDS (zero past RP) with a row stride of 68 floats.  Every
+// thread of a row holds the row of B in registers (16-byte loads when B's
+// rows are 16-byte aligned); thread part c takes rank rows j = 4k + c of G
+// and the P columns 16c..16c+15, so that a wave's G reads are four 16-byte
+// pieces on distinct banks, each a broadcast.  The four partial sums meet by
+// lane shuffles (double), in a fixed order.
 // ---------------------------------------------------------------------------
+constexpr int NB_FIN_ROWS = 64;    // one block: 64 rows of one slot, 4 threads each
+constexpr int NB_GLD = 68;         // LDS row stride of G (floats)
+
 struct NbFinJob {
   const float* P;      // [nsplit][N][C]
   const double* wsq;   // [nsplit][N]
@@ -259,7 +274,7 @@ struct NbFinJob {
   float s[NB_MAX_SLOTS];
   int64_t N;
   int C, RP, S, r, nsplit;
-  int64_t blk0;        // first block; S * ceil(N / 256) blocks
+  int64_t blk0;        // first block; S * ceil(N / NB_FIN_ROWS) blocks
 };
 struct NbFinArgs {
   NbFinJob job[NB_MAX_JOBS];
@@ -268,64 +283,128 @@ struct NbFinArgs {
 
 __global__ __launch_bounds__(256) void nb_finish_kernel(NbFinArgs p) {
   constexpr int R = NB_MAX_RP;
-  __shared__ __attribute__((aligned(16))) float Gs[R * R];
+  __shared__ __attribute__((aligned(16))) float Gs[R * NB_GLD];
+  __shared__ __attribute__((aligned(16))) float Ys[NB_FIN_ROWS * NB_GLD];   // B rows
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
   int j = 0;
   while (j + 1 < p.njobs && b >= p.job[j + 1].blk0) ++j;
   const NbFinJob& J = p.job[j];
-  const int64_t nch = (J.N + 255) / 256, l = b - J.blk0;
+  const int64_t nch = (J.N + NB_FIN_ROWS - 1) / NB_FIN_ROWS, l = b - J.blk0;
   const int q = (int)(l / nch);
-  const int64_t i = (l % nch) * 256 + tid;
+  const int c = tid & 3;
+  const int64_t i = (l % nch) * NB_FIN_ROWS + (tid >> 2);
   const int64_t grows = 3ll * J.S * J.RP;
-  for (int e = tid; e < R * R; e += 256) {
-    const int jj = e / R, ll = e % R;
-    double g = 0.0;
-    if (jj < J.RP && ll < J.RP)
-      for (int s = 0; s < J.nsplit; ++s)
-        for (int pp = 0; pp < 3; ++pp)
-          g += J.G[((int64_t)s * grows + (int64_t)(q * 3 + pp) * J.RP + jj) * J.C + q * J.RP + ll];
-    Gs[e] = (float)g;
+  {
+    // Element e = tid + 256 u of the slot's G: every partial's loads of all
+    // sixteen elements go out together (fixed order of the sums).
+    constexpr int U = R * R / 256;
+    double g[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) g[u] = 0.0;
+    for (int s = 0; s < J.nsplit; ++s) {
+      float v[3][U];
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) {
+        const float* Gp = J.G + ((int64_t)s * grows + (int64_t)(q * 3 + pp) * J.RP) * J.C + q * J.RP;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = tid + 256 * u, jj = e / R, ll = e % R;
+          v[pp][u] = Gp[(int64_t)min(jj, J.RP - 1) * J.C + min(ll, J.RP - 1)];
+        }
+      }
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = tid + 256 * u, jj = e / R, ll = e % R;
+          g[u] += (jj < J.RP && ll < J.RP) ? (double)v[pp][u] : 0.0;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = tid + 256 * u;
+      Gs[(e / R) * NB_GLD + e % R] = (float)g[u];
+    }
   }
   __syncthreads();
-  if (i >= J.N) return;
+  if (i >= J.N) return;   // the four threads of a row leave together
   const float* Bq = J.B[q];
+  const int r = J.r;
+  // Every load below is unconditional (clamped address, value selected):
+  // guarded loads became branches, and the compiler then waited for each
+  // load before the next.
   float y[R];
+  if ((r & 3) == 0 && ((uintptr_t)Bq & 15) == 0) {
 #pragma unroll
-  for (int jj = 0; jj < R; ++jj) y[jj] = jj < J.r ? Bq[i * J.r + jj] : 0.f;
-  double cross = 0.0;
+    for (int j4 = 0; j4 < R / 4; ++j4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(Bq + i * r + min(4 * j4, r - 4));
 #pragma unroll
-  for (int j4 = 0; j4 < R / 4; ++j4) {
-    if (4 * j4 < J.RP) {
-      f32x4 pv = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < J.nsplit; ++s)
-        pv += *reinterpret_cast<const f32x4*>(J.P + ((int64_t)s * J.N + i) * J.C + q * J.RP + 4 * j4);
+      for (int e = 0; e < 4; ++e) y[4 * j4 + e] = 4 * j4 < r ? v[e] : 0.f;
+    }
+  } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cross += (double)y[4 * j4 + e] * (double)pv[e];
+    for (int jj = 0; jj < R; ++jj) {
+      const float v = Bq[i * r + min(jj, r - 1)];
+      y[jj] = jj < r ? v : 0.f;
     }
   }
-  // z = G^T y over the slot's rank rows (y_j re-read from B, an L1 hit, so
-  // that y and z are indexed by constants only), then y . z.
-  float z[R];
+  // Cross term over P columns 16c .. 16c + 15.
+  double cross = 0.0;
+  f32x4 pv[4];
 #pragma unroll
-  for (int l = 0; l < R; ++l) z[l] = 0.f;
-  for (int jj = 0; jj < J.r; ++jj) {
-    const float yj = Bq[i * J.r + jj];
+  for (int u = 0; u < 4; ++u) pv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < J.nsplit; ++s) {
+    const float* Pr = J.P + ((int64_t)s * J.N + i) * J.C + q * J.RP;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)   // columns past RP: the slot's last four, not used
+      pv[u] += *reinterpret_cast<const f32x4*>(Pr + min(4 * (4 * c + u), J.RP - 4));
+  }
+  // The thread's own sixteen B values (columns 16c ..), read from the row's
+  // copy in LDS below: selecting them from y by c would index registers by a
+  // lane-dependent value.
+  float* Yrow = Ys + (tid >> 2) * NB_GLD;
+  if (c == 0) {
+#pragma unroll
+    for (int j4 = 0; j4 < R / 4; ++j4)
+      *reinterpret_cast<f32x4*>(&Yrow[4 * j4]) =
+          f32x4{y[4 * j4], y[4 * j4 + 1], y[4 * j4 + 2], y[4 * j4 + 3]};
+  }
+  __builtin_amdgcn_wave_barrier();   // the row's four threads are in one wave
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const bool in = 4 * (4 * c + u) < J.RP;
+    const f32x4 yc = *reinterpret_cast<const f32x4*>(&Yrow[16 * c + 4 * u]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cross += in ? (double)yc[e] * (double)pv[u][e] : 0.0;
+  }
+  // Quadratic term over rank rows jj = 4k + c (zero rows past RP): a loop
+  // kept rolled (unrolled, the compiler hoisted every G read of the 16 rows
+  // and spilled), with B_i,jj read back from the row's copy in LDS.
+  double quad = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < R / 4; ++k) {
+    const int jj = 4 * k + c;
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int l4 = 0; l4 < R / 4; ++l4) {
-      const f32x4 g = *reinterpret_cast<const f32x4*>(&Gs[jj * R + 4 * l4]);
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&Gs[jj * NB_GLD + 4 * l4]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[4 * l4 + e] += g[e] * yj;
+      for (int e = 0; e < 4; ++e) d[e] += g[e] * y[4 * l4 + e];
     }
+    quad += (double)Yrow[jj] * (double)((d[0] + d[1]) + (d[2] + d[3]));
   }
-  double quad = 0.0;
-#pragma unroll
-  for (int l = 0; l < R; ++l) quad += (double)y[l] * (double)z[l];
-  double w2 = 0.0;
-  for (int s = 0; s < J.nsplit; ++s) w2 += J.wsq[(int64_t)s * J.N + i];
-  const double sc = J.s[q];
-  const double n2 = w2 + 2.0 * sc * cross + sc * sc * quad;
-  J.out[q][i] = (float)sqrt(n2 > 0.0 ? n2 : 0.0);
+  cross += __shfl_xor(cross, 1, 64);
+  cross += __shfl_xor(cross, 2, 64);
+  quad += __shfl_xor(quad, 1, 64);
+  quad += __shfl_xor(quad, 2, 64);
+  if (c == 0) {
+    double w2 = 0.0;
+    for (int s = 0; s < J.nsplit; ++s) w2 += J.wsq[(int64_t)s * J.N + i];
+    const double sc = J.s[q];
+    const double n2 = w2 + 2.0 * sc * cross + sc * sc * quad;
+    J.out[q][i] = (float)sqrt(n2 > 0.0 ? n2 : 0.0);
+  }
 }
 
 }  // namespace lora

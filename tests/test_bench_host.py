@@ -52,6 +52,15 @@ def test_kernel_table_shares_sum_over_the_listed_kernels():
     assert "frac_mfma" in rows[0] and "frac_hbm" in rows[1]
 
 
+def test_per_label_time_sums_shapes_per_step():
+    entries = [_entry("gemm_bf16_fwd", 30.0, 30, 4096, 9728, 2560, 1.0, 0.0),
+               _entry("reduce", 5.0, 50, 64, 1, 4, 0.0, 1.0),
+               _entry("gemm_bf16_fwd", 10.0, 10, 4096, 2560, 9728, 1.0, 0.0)]
+    got = bench.per_label_ms(entries, 10)
+    assert list(got) == ["gemm_bf16_fwd", "reduce"]
+    assert got["gemm_bf16_fwd"] == pytest.approx(4.0) and got["reduce"] == pytest.approx(0.5)
+
+
 def test_stored_traffic_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
     rec = {"source_sha256": bench.kernel_source_digest(), "copy_factor_fetch": 2.0,
            "copy_factor_write": 1.0,
