@@ -114,17 +114,22 @@ LORA_DEV void sum_partials(const float* part, int64_t stride, int nparts, int64_
 
 // Fixed-order sum of nparts float4 partials at part[q*stride + i]: loads are
 // issued sixteen at a time so their latencies overlap (one round trip for up
-// to 17 partials); the additions still run in index order.
+// to 17 partials); the additions still run in index order.  Every load is
+// unconditional (past the last partial it repeats the last one's address and
+// its value is not added): a guarded load becomes a branch, at whose join the
+// compiler waits for every load in flight.
 LORA_DEV f32x4 sum_parts4(const float* part, int64_t stride, int nparts, int64_t i) {
   f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
   for (int q = 1; q < nparts; q += 16) {
     f32x4 v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      if (q + u < nparts) v[u] = *reinterpret_cast<const f32x4*>(part + (int64_t)(q + u) * stride + i);
+      v[u] = *reinterpret_cast<const f32x4*>(part + (int64_t)min(q + u, nparts - 1) * stride + i);
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (q + u < nparts) s += v[u];
+    for (int u = 0; u < 16; ++u) {
+      const f32x4 t = s + v[u];
+      s = q + u < nparts ? t : s;
+    }
   }
   return s;
 }
@@ -136,11 +141,9 @@ LORA_DEV T sum_parts1(const T* part, int64_t stride, int nparts, int64_t i) {
   for (int q = 1; q < nparts; q += 16) {
     T v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (q + u < nparts) v[u] = part[(int64_t)(q + u) * stride + i];
+    for (int u = 0; u < 16; ++u) v[u] = part[(int64_t)min(q + u, nparts - 1) * stride + i];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (q + u < nparts) s += v[u];
+    for (int u = 0; u < 16; ++u) s = q + u < nparts ? s + v[u] : s;
   }
   return s;
 }

@@ -441,8 +441,9 @@ void launch_reduce(const RedJob* jobs, int n, hipStream_t st) {
   double bytes = 0.0;
   for (int i = 0; i < n; ++i) {
     J.job[i] = jobs[i];
+    J.job[i].vec = red_vec(jobs[i]);
     J.blk[i] = blocks;
-    blocks += cdiv(jobs[i].n, 256);
+    blocks += red_blocks(J.job[i]);
     bytes += 4.0 * (double)jobs[i].n * (jobs[i].nparts + 1 + jobs[i].accumulate);
   }
   J.blk[n] = blocks;
@@ -862,8 +863,9 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   int64_t rblocks = 0;
   for (int i = 0; i < j.nj; ++i) {
     j.J.job[i] = j.jobs[i];
+    j.J.job[i].vec = red_vec(j.jobs[i]);
     j.J.blk[i] = rblocks;
-    rblocks += cdiv(j.jobs[i].n, 256);
+    rblocks += red_blocks(j.J.job[i]);
   }
   j.J.blk[j.nj] = rblocks;
   j.J.njobs = j.nj;

@@ -959,7 +959,16 @@ struct RedJob {
   int nparts;
   int accumulate;
   float alpha;
+  int vec;   // 4: four elements per thread as 16-byte vectors (set by red_vec)
 };
+
+// Whether a job can take 16-byte vectors: n a multiple of four, partials and
+// output 16-byte aligned.
+LORA_HD inline int red_vec(const RedJob& j) {
+  return (j.n % 4 == 0 && ((uintptr_t)j.part & 15) == 0 && ((uintptr_t)j.out & 15) == 0) ? 4 : 1;
+}
+// Blocks of 256 threads a job takes.
+LORA_HD inline int64_t red_blocks(const RedJob& j) { return (j.n + 256 * j.vec - 1) / (256 * j.vec); }
 struct RedJobs {
   RedJob job[4];
   int64_t blk[5];   // prefix of block counts
@@ -970,6 +979,19 @@ LORA_DEV void reduce_block(const RedJobs& jobs, int64_t b) {
   int j = 0;
   while (j + 1 < jobs.njobs && b >= jobs.blk[j + 1]) ++j;
   const RedJob& J = jobs.job[j];
+  if (J.vec == 4) {   // the same sums in the same order, sixteen loads in flight
+    const int64_t i = ((b - jobs.blk[j]) * 256 + threadIdx.x) * 4;
+    if (i >= J.n) return;
+    f32x4 s = sum_parts4(J.part, J.n, J.nparts, i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[e] *= J.alpha;
+      if (J.div) s[e] /= J.div[(i + e) % J.divn];
+    }
+    f32x4* o = reinterpret_cast<f32x4*>(J.out + i);
+    *o = J.accumulate ? *o + s : s;
+    return;
+  }
   const int64_t i = (b - jobs.blk[j]) * 256 + threadIdx.x;
   if (i >= J.n) return;
   sum_partials(J.part, J.n, J.nparts, i, J.alpha, J.div, J.div ? i % J.divn : 0, J.out,
