@@ -50,11 +50,12 @@ LORA_DEV float drop_mul(const DropParams& d, uint64_t row, int64_t k) {
 // ---------------------------------------------------------------------------
 // bf16 <-> f32 (round to nearest even; NaN stays NaN)
 // ---------------------------------------------------------------------------
+// Written as a select: an early return for NaN became a divergent branch
+// around every conversion.
 LORA_DEV uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rn = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : rn;
 }
 LORA_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);

@@ -516,22 +516,40 @@ void k3r_kernel(K3Args p) {
   const int tv = BOTH ? (wave & 1) : wave, jv = BOTH ? (wave >> 1) : 0;
   const int tn = BOTH ? (wave & 1) : wave - 2, jb = BOTH ? (wave >> 1) : 0;
 
-  // Per strip: the column scale of this thread's four columns and B^T.
+  // Per strip: the column scale of this thread's four columns and B^T.  All
+  // of these loads go out before any is used (unconditional, clamped
+  // addresses; a strip past the block's last repeats its first), so the
+  // prologue costs one round trip instead of one per load.
+  constexpr int BQ = RP / 16;   // B float4s per thread and strip
   float cmul[SPB][4];
+  {
+    const bool hasmag = p.mag != nullptr;
+    const float* mg = hasmag ? p.mag : p.B;   // any valid address when there is no scale
+    const float* nr = hasmag ? p.nrm : p.B;
+    f32x4 mv[SPB], nv[SPB], bv[SPB][BQ];
 #pragma unroll
-  for (int q = 0; q < SPB; ++q) {
-    const int64_t n0 = (sx0 + (q < ns ? q : 0)) * 64;
+    for (int q = 0; q < SPB; ++q) {
+      const int64_t n0 = (sx0 + (q < ns ? q : 0)) * 64;
+      mv[q] = *reinterpret_cast<const f32x4*>(mg + (hasmag ? n0 + 4 * tc : 0));
+      nv[q] = *reinterpret_cast<const f32x4*>(nr + (hasmag ? n0 + 4 * tc : 0));
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      cmul[q][e] = p.mag ? p.mag[n0 + 4 * tc + e] / p.nrm[n0 + 4 * tc + e] : 1.f;
-    if (want_v && q < ns) {
-      float* bt = Bt + q * RP * K3R_LD;
-      for (int i = tid; i < 64 * (RP / 4); i += 256) {
-        const int n = i / (RP / 4), jq = i % (RP / 4);
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (4 * jq < r) v = *reinterpret_cast<const f32x4*>(p.B + (n0 + n) * r + 4 * jq);
+      for (int u = 0; u < BQ; ++u) {
+        const int i = tid + 256 * u, n = i / (RP / 4), jq = i % (RP / 4);
+        bv[q][u] = *reinterpret_cast<const f32x4*>(p.B + (n0 + n) * r + min(4 * jq, (int)r - 4));
+      }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bt[(4 * jq + e) * K3R_LD + n] = v[e];
+    for (int q = 0; q < SPB; ++q) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cmul[q][e] = hasmag ? mv[q][e] / nv[q][e] : 1.f;
+      if (want_v && q < ns) {
+        float* bt = Bt + q * RP * K3R_LD;
+#pragma unroll
+        for (int u = 0; u < BQ; ++u) {
+          const int i = tid + 256 * u, n = i / (RP / 4), jq = i % (RP / 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bt[(4 * jq + e) * K3R_LD + n] = 4 * jq < r ? bv[q][u][e] : 0.f;
+        }
       }
     }
   }
@@ -569,10 +587,10 @@ void k3r_kernel(K3Args p) {
     stage = stage < nst ? stage : nst - 1;
     const int64_t t0 = tb + (int64_t)stage * 64;
 #pragma unroll
-    for (int u = 0; u < UQ; ++u) {
+    for (int u = 0; u < UQ; ++u) {   // unconditional load (clamped), value selected
       const int i = tid + 256 * u, row = i / (RP / 4), jq = i % (RP / 4);
-      un[u] = 4 * jq < r ? *reinterpret_cast<const f32x4*>(U + (t0 + row) * r + 4 * jq)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 v = *reinterpret_cast<const f32x4*>(U + (t0 + row) * r + min(4 * jq, (int)r - 4));
+      un[u] = 4 * jq < r ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   Tile R[2];
