@@ -85,6 +85,18 @@ LORA_DEV f32x16 mfma32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 LORA_DEV int row32(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// Fragment-tiled bf16 operand (the A operand of the direct-operand bf16
+// products, gemm_bf16.hpp): element offset of (row t, contraction index k)
+// for a contraction of nkq * 64.  Each 1 KB is one MFMA operand in lane
+// order: 32 rows x 16 indices of K-step k / 64, sub-step s = (k % 32) / 8,
+// lane t % 32 + 32 ((k % 64) / 32) holding the 8 indices k - k % 8 .. +7.
+// Rows stay contiguous in groups of 32, so stacked row ranges that start at
+// multiples of 32 start at multiples of 32 * nkq * 64 elements.
+LORA_HD inline int64_t atile_off(int64_t t, int64_t k, int64_t nkq) {
+  return ((((t >> 5) * nkq + (k >> 6)) * 4 + ((k >> 3) & 3)) * 64 + (t & 31) + 32 * ((k >> 5) & 1)) * 8 +
+         (k & 7);
+}
 LORA_DEV int row16(int v, int lane) { return 4 * (lane >> 4) + v; }
 
 // Wave-wide sum of a double (butterfly over 64 lanes; every lane gets it).

@@ -19,6 +19,20 @@
 // past the end), out-of-range elements are zeroed when stored to LDS, so the
 // compiler waits for exactly the stage it stores.
 //
+// DEPTH 0 selects the direct-operand loop (bf16 W only, 256 x 256 tiles of
+// four waves, K-step 64): LDS is the limit of the loop above (a K-step moves
+// 192 KB of fragment reads and 64 KB of staging writes through it, and
+// interleaved reads and writes share about 110 bytes per clock per CU).
+// Here the activation operand bypasses LDS: it is stored in fragment tiles
+// (atile_off: each 1 KB is one MFMA operand of 32 rows x 16 contraction
+// indices in lane order, written so by down and k3), and each wave loads its
+// own fragments into registers one K-step ahead.  Only W goes through LDS,
+// by direct-to-LDS loads two K-steps ahead into a ring of three stages, read
+// back as in the loop above (forward: rows of 128 bytes with their 16-byte
+// chunks XOR-swizzled by row; dX: the transposed tile).  A K-step is four
+// phases of sixteen MFMAs, each overlapping the next phase's W fragment
+// reads and a quarter of the loads, with one barrier per K-step.
+//
 // Block-quantized W (qweight.hpp) takes the same kernel with WQ set: W is
 // staged as runs of 8 elements of a W row, decoded to bf16 on the way into
 // LDS, so the LDS layout and the MFMA loop are unchanged.  For dX a thread's
@@ -32,6 +46,7 @@
 // whose A and B K-slices are shared in that XCD's L2.
 #pragma once
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "gemm_f32.hpp"   // LoraOperand
@@ -90,17 +105,33 @@ LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
 }
 
 // Tile configurations: index, BM, BN, threads, wave rows, K-step, stages in
-// flight, directions (1 forward, 2 dX), then the host planner's fitted cost
+// flight (0: the direct-operand loop, whose A operand is fragment-tiled),
+// directions (1 forward, 2 dX), then the host planner's fitted cost
 // coefficients (forward a, b; dX a, b).
 #define LORA_BF16_CFGS(X)                                        \
   X(0, 256, 256, 512, 2, 32, 3, 1, 0.417, 16.4, 0, 0)            \
   X(1, 256, 256, 512, 2, 64, 1, 3, 0.393, 14.7, 0.475, 14.1)     \
   X(2, 256, 128, 512, 2, 64, 2, 1, 0.483, 9.5, 0, 0)             \
   X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.705, 7.8)             \
-  X(4, 128, 128, 512, 2, 64, 2, 3, 0.581, 5.4, 0.967, 5.1)
+  X(4, 128, 128, 512, 2, 64, 2, 3, 0.581, 5.4, 0.967, 5.1)      \
+  X(5, 256, 256, 256, 2, 64, 0, 1, 0.326, 12.2, 0, 0)
 
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
+
+// Instruction order of one phase of the direct-operand loop: MFMA i is
+// followed by the phase's i-th LDS read (NRD of them) and, from the fifth
+// MFMA on, by one of its NV global loads.
+template <int NRD, int NV, int I>
+LORA_DEV void phase_slot() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (I < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  if constexpr (I >= 4 && I < 4 + NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+}
+template <int NRD, int NV, int... I>
+LORA_DEV void phase_order(std::integer_sequence<int, I...>) {
+  (phase_slot<NRD, NV, I>(), ...);
+}
 
 // EXACT: M, Nc and Kc are multiples of BM, BN and BK: nothing is out of range.
 // WQ: the lora_dtype of W (WQ_BF16, or a block-quantized format).
@@ -130,8 +161,12 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   static_assert(ACH >= 1 && BCH >= 1 && MI >= 1 && NI >= 1, "tile too small");
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole chunks per thread");
   static_assert((BM + BN) * LROW <= 2 * (BM + BN) * LDS_ROW, "LoRA staging fits the LDS");
-  static_assert(DEPTH >= 1, "stages in flight");
+  static_assert(DEPTH >= 0, "stages in flight");
   constexpr bool QW = wq_quantized(WQ);
+  constexpr bool AD = DEPTH == 0;                     // direct-operand loop
+  static_assert(!AD || (BM == 256 && BN == 256 && NT == 256 && WGM == 2 && BK == 64 && !QW),
+                "direct-operand loop shape");
+  constexpr int AD_NB = 3;                            // W stages in LDS (direct-operand loop)
   constexpr int QWD = QW ? wq_words(WQ) : 1;          // words per staged 8-element run
   constexpr int QR0 = BK * BN / (8 * NT);
   constexpr int QR = QR0 < 2 ? 2 : (QR0 > 8 ? 8 : QR0);  // dX: contraction rows per item
@@ -140,7 +175,9 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   constexpr int QIT = (QITEMS + NT - 1) / NT;
   static_assert(!QW || FWD || (BK % QR == 0 && QR % 2 == 0), "whole row pairs per item");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDS_ROW];
+  constexpr int SMEM = AD ? (AD_NB * BN * BK > (BM + BN) * LROW ? AD_NB * BN * BK : (BM + BN) * LROW)
+                          : 2 * (BM + BN) * LDS_ROW;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
   auto As = [&](int b) -> uint16_t* { return smem + b * (BM * LDS_ROW); };
   auto Bs = [&](int b) -> uint16_t* { return smem + 2 * BM * LDS_ROW + b * (BN * LDS_ROW); };
 
@@ -370,6 +407,95 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     uint16_t* Lb = smem + BM * LROW;
     for (int64_t k0 = 0; k0 < p.r; k0 += LBK) {
       __syncthreads();
+      if constexpr (AD) {
+      // The direct-operand kernel (accumulators apart from its vector
+      // registers) issues all its staging loads before any is used (clamped
+      // addresses, values selected): one round trip rather than one per item.
+      // A side: XA [M, r] rows m, scaled by s; as split partials, summed in
+      // split order (and stored once, by the first column of tiles).
+      // Forward B side: B_lora [Nc, r], rows n, rank contiguous.  dX B side:
+      // A_lora [r, Nc], rows the contraction index, transposed on store.
+      constexpr int AIT = BM * (LBK / 4) / NT;        // A items (four floats) per thread
+      constexpr int BIT = FWD ? BN * (LBK / 4) / NT : 0;   // forward B items
+      constexpr int NIT = AIT > BIT ? AIT : BIT;
+      constexpr int DIT = BN * LBK / NT;              // dX B items (floats)
+      constexpr int SB = NIT, SD = DIT;
+      static_assert(NIT % SB == 0 && DIT % SD == 0 && BM * (LBK / 4) % NT == 0 &&
+                        BN * (LBK / 4) % NT == 0 && BN * LBK % NT == 0, "whole staging batches");
+      auto item = [&](int it, int64_t o0, int64_t lim, int& row, int& c4, bool& ok) -> int64_t {
+        const int f = tid + NT * it;
+        row = f / (LBK / 4);
+        c4 = f % (LBK / 4);
+        const int64_t g = o0 + row, gk = k0 + 4 * c4;
+        ok = g < lim && gk < p.r;
+        return ok ? g * p.r + gk : 0;
+      };
+      auto put = [&](uint16_t* dst, int row, int c4, bool ok, f32x4 v) {
+        v = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(&dst[row * LROW + 4 * c4]) = w;
+      };
+#pragma unroll
+      for (int b0 = 0; b0 < NIT; b0 += SB) {
+        f32x4 va[SB], vb[SB];
+        if (so.xa.nparts == 1) {
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            if (b0 + u >= AIT) continue;
+            int row, c4;
+            bool ok;
+            va[u] = *reinterpret_cast<const f32x4*>(so.xa.p + item(b0 + u, m0 - moff, p.M - moff, row, c4, ok));
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            if (b0 + u >= AIT) continue;
+            int row, c4;
+            bool ok;
+            const int64_t i = item(b0 + u, m0 - moff, p.M - moff, row, c4, ok);
+            va[u] = sum_parts4(so.xa.p, so.xa.stride, so.xa.nparts, i);
+            if (store_xa && ok) *reinterpret_cast<f32x4*>(so.xa.out + i) = va[u];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          if (b0 + u >= BIT) continue;
+          int row, c4;
+          bool ok;
+          vb[u] = *reinterpret_cast<const f32x4*>(so.XB + item(b0 + u, n0, p.Nc, row, c4, ok));
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          int row, c4;
+          bool ok;
+          if (b0 + u < AIT) {
+            item(b0 + u, m0 - moff, p.M - moff, row, c4, ok);
+            put(La, row, c4, ok, va[u] * so.xs);
+          }
+          if (b0 + u < BIT) {
+            item(b0 + u, n0, p.Nc, row, c4, ok);
+            put(Lb, row, c4, ok, vb[u]);
+          }
+        }
+      }
+      if constexpr (!FWD) {
+        for (int b0 = 0; b0 < DIT; b0 += SD) {
+          float vd[SD];
+#pragma unroll
+          for (int u = 0; u < SD; ++u) {
+            const int f = tid + NT * (b0 + u), n = f % BN, kk = f / BN;
+            const int64_t gn = n0 + n, gk = k0 + kk;
+            vd[u] = so.XB[(gn < p.Nc && gk < p.r) ? gk * p.Nc + gn : 0];
+          }
+#pragma unroll
+          for (int u = 0; u < SD; ++u) {
+            const int f = tid + NT * (b0 + u), n = f % BN, kk = f / BN;
+            const bool ok = n0 + n < p.Nc && k0 + kk < p.r;
+            Lb[n * LROW + kk] = (uint16_t)f32_to_bf16_bits(ok ? vd[u] : 0.f);
+          }
+        }
+      }
+      } else {
       // A side: XA [M, r] rows m (split partials summed), scaled by s.
       for (int f = tid; f < BM * (LBK / 4); f += NT) {
         const int row = f / (LBK / 4), c4 = f % (LBK / 4);
@@ -404,6 +530,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
           Lb[n * LROW + kk] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
+      }
       __syncthreads();
       compute(La, Lb, std::integral_constant<int, LROW>{}, std::integral_constant<int, LBK / 2>{},
               std::integral_constant<int, LBK / 16>{}, std::false_type{});
@@ -433,7 +560,148 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // Main contraction over [kbeg, kend); every split but the last is a whole
   // number of K-steps, so a K-step never reaches into the next split.
   const int64_t nk = (kend - kbeg + BK - 1) / BK;
-  {
+  if constexpr (AD) {
+    constexpr int STG = BN * BK;                      // bf16 elements per W stage
+    const int64_t nkq = p.Kc / BK;                    // K-steps of the tiled operand's rows
+    // The wave index as a scalar: resources and LDS destinations built from
+    // it stay in scalar registers.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // This wave's four 32-row fragment rows of the tiled operand, from its
+    // first; the resource ends at the operand's end (rows past M read zero).
+    const int64_t rb0 = (m0 + (wv / WGN) * WM) / 32, rbn = (p.M + 31) / 32;
+    // (integer selects: a max() here resolves to a floating-point overload,
+    // which would put the resource in vector registers)
+    const int64_t abytes = (rbn > rb0 ? rbn - rb0 : 0) * nkq * 4096;
+    const __amdgpu_buffer_rsrc_t rAt = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.A + rb0 * nkq * 2048), (short)0, (int)(abytes > 0xffffffffll ? 0xffffffffu : (uint32_t)abytes),
+        0x00020000);
+    auto kq = [&](int64_t k) { return kbeg / BK + min(k, nk - 1); };
+    // Fragment (row block i, K-step q, sub-step s) is at byte
+    // ((i * nkq + q) * 4 + s) * 1024 + 16 lane: the lane and row-block part
+    // is a per-lane constant, the step part a scalar offset.
+    uint32_t voffA[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) voffA[i] = (uint32_t)(lane * 16 + (int64_t)i * nkq * 4096);
+    auto lda_sub = [&](u32x4 (&R)[MI][KS], int s, int64_t k) {
+      const int so = (int)(kq(k) * 4096 + s * 1024);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        R[i][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rAt, voffA[i], so, 0));
+    };
+    // W: each wave's eight direct-to-LDS loads per stage write 1 KB each.
+    // Forward: load q covers W rows 8 (8 wave + q) .. +7, lane l the row's
+    // 16-byte slot l%8, which holds chunk (l%8) ^ swz(row).  dX: load q
+    // covers contraction rows 2 (8 wave + q) and the next, lane l the row's
+    // slot l%32 of the transposed layout (bd_off).
+    auto swz = [](int row) { return (row ^ (row >> 3)) & 7; };
+    uint32_t voffW[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if constexpr (FWD) {
+        const int row = 8 * (8 * wave + q) + (lane >> 3);
+        voffW[q] = (uint32_t)(((int64_t)row * p.ldb + 8 * ((lane & 7) ^ swz(row))) * 2);
+      } else {
+        const int kk = 2 * (8 * wave + q) + (lane >> 5), sl = lane & 31;
+        const int c = ((((sl >> 1) ^ (2 * (kk & 3)))) << 1) | (sl & 1);
+        voffW[q] = (uint32_t)(((int64_t)kk * p.ldb + 8 * c) * 2);
+      }
+    }
+    auto dma = [&](int q, int64_t k, int buf) {
+      const int64_t k0 = kbeg + min(k, nk - 1) * BK;
+      uint16_t* dst = smem + buf * STG + (FWD ? 8 * (8 * wv + q) * BK : 2 * (8 * wv + q) * BN);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)dst, 16, voffW[q],
+                                               (int)(uint32_t)(FWD ? k0 * 2 : k0 * p.ldb * 2), 0, 0);
+    };
+    // W fragment of column block j, sub-step s: forward, row n = wn0 + 32 j
+    // + l%32 at chunk (4 (l/32) + s) ^ swz(n), i.e. byte wb[j] + 16 (s ^
+    // wm[j]); dX, the transposed read at byte wb[j] + 4096 s (its swizzle
+    // depends on the row only modulo 4, which s does not change).
+    uint32_t wb[NI], wm[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      if constexpr (FWD) {
+        const int row = wn0 + j * 32 + l32, sw = swz(row);
+        wb[j] = (uint32_t)(row * BK * 2 + 64 * (hl ^ (sw >> 2)));
+        wm[j] = (uint32_t)(sw & 3);
+      } else {
+        const int kk = 32 * (trg >> 1) + (tri >> 2);
+        const int col = wn0 + j * 32 + 16 * (trg & 1) + 4 * (tri & 3);
+        wb[j] = (uint32_t)(kk * (BN * 2) + (((col >> 4) ^ (2 * (kk & 3))) << 5) + ((col & 15) << 1));
+        wm[j] = 0;
+      }
+    }
+    u32x4 Bf[2][NI];
+    auto rdb = [&](u32x4 (&F)[NI], int buf, int s) {
+      const char* Bb = reinterpret_cast<const char*>(smem + buf * STG);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        if constexpr (FWD) {
+          F[j] = *reinterpret_cast<const u32x4*>(Bb + wb[j] + 16 * (s ^ wm[j]));
+        } else {
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          auto* b = (__attribute__((address_space(3))) const char*)(Bb + wb[j] + 4096 * s);
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)b);
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(b + 4 * (BN * 2)));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          F[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+      }
+    };
+    auto mma = [&](const u32x4 (&R)[MI][KS], int s, const u32x4 (&F)[NI]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          if constexpr (FWD) acc[i][j] = mfma32x32x16_bf16(R[i][s], F[j], acc[i][j]);
+          else acc[i][j] = mfma32x32x16_bf16(F[j], R[i][s], acc[i][j]);
+        }
+    };
+    // Phase s of K-step k: W fragments of sub-step s + 1 (the last phase:
+    // sub-step 0 of the next stage, after the barrier), the tiled operand's
+    // sub-step s of step k + 1 (used a whole K-step later), W loads 2s and
+    // 2s + 1 for step k + 2, and the sixteen MFMAs of sub-step s.  The
+    // barrier waits for this wave's loads of stage k + 1: at most 18 loads
+    // (three phases of four fragment and two W loads) were issued after them.
+    using Seq = std::make_integer_sequence<int, MI * NI>;
+    u32x4 Ar[2][MI][KS];
+    auto step = [&](int64_t k, u32x4 (&Rc)[MI][KS], u32x4 (&Rn)[MI][KS]) {
+      const int cur = (int)(k % AD_NB), nx1 = (int)((k + 1) % AD_NB), nx2 = (int)((k + 2) % AD_NB);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s == KS - 1) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        rdb(Bf[(s + 1) & 1], s == KS - 1 ? nx1 : cur, (s + 1) % KS);
+        lda_sub(Rn, s, k + 1);
+        dma(2 * s, k + 2, nx2);
+        dma(2 * s + 1, k + 2, nx2);
+        mma(Rc, s, Bf[s & 1]);
+        phase_order<FWD ? NI : 2 * NI, MI + 2>(Seq{});
+      }
+    };
+    // Issue order (fixed by the scheduling barriers): W stage 0, W stage 1,
+    // the operand's step 0; stage 0 is in once 24 later loads may remain.
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma(q, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma(q, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ss = 0; ss < KS; ++ss) lda_sub(Ar[0], ss, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    rdb(Bf[0], 0, 0);
+    int64_t k = 0;
+    for (; k + 2 <= nk; k += 2) {
+      step(k, Ar[0], Ar[1]);
+      step(k + 1, Ar[1], Ar[0]);
+    }
+    if (k < nk) step(k, Ar[0], Ar[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // No W load may still be writing LDS when it is reused or released.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
     Stage R[DEPTH];
     auto kstep = [&](int64_t k) { return kbeg + min(k, nk - 1) * BK; };
 #pragma unroll

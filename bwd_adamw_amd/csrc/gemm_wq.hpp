@@ -42,7 +42,9 @@ void launch_gemm_wq_tiles(int cfg, bool fwd, bool exact, dim3 grid, hipStream_t 
                           const prof::Scope& ps, const GemmBf16Args& a) {
 #define LORA_WQ_TILE(i, BM_, BN_, NT_, WGM_, BK_, D_, DIRS_, AF_, BF_, AD_, BD_)                \
   if (cfg == i) {                                                                             \
-    if (fwd) {                                                                                \
+    if constexpr (D_ == 0) {                                                                  \
+      /* the direct-operand loop takes bf16 W only; the planner never picks it here */       \
+    } else if (fwd) {                                                                         \
       if constexpr ((DIRS_)&1) {                                                              \
         if (exact)                                                                            \
           launch_n(gemm_bf16_kernel<BM_, BN_, NT_, WGM_, BK_, D_, true, true, WQ>, grid,       \

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -228,13 +229,20 @@ constexpr int kBf16Slots = 256;  // resident tiles per round
 constexpr double kSplitUsPerMB = 0.408;
 
 // bf16: the configuration and contraction split (whole K-steps per split,
-// at least 8 of them) with the least estimated time.
-GemmPlan plan_gemm_bf16(int64_t M, int64_t Nc, int64_t Kc, bool dx) {
+// at least 8 of them) with the least estimated time.  The direct-operand
+// configuration (stages 0) is a candidate only where `tiled` says its A
+// operand can be written in fragment tiles.
+std::atomic<int> g_bf16_cfg{-1};   // lora_set_bf16_config
+
+GemmPlan plan_gemm_bf16(int64_t M, int64_t Nc, int64_t Kc, bool dx, bool tiled) {
   GemmPlan best = {0, 0, {Kc, 1}, -1};
   double tbest = 1e30;
+  auto runs = [&](const Bf16Cfg& c) { return (c.dirs & (dx ? 2 : 1)) && (c.depth != 0 || tiled); };
+  const int forced = g_bf16_cfg.load(std::memory_order_relaxed);
+  const bool force = forced >= 0 && runs(kBf16Cfg[forced]);
   for (int i = 0; i < kBf16NCfg; ++i) {
     const Bf16Cfg& c = kBf16Cfg[i];
-    if (!(c.dirs & (dx ? 2 : 1))) continue;
+    if (!runs(c) || (force && i != forced)) continue;
     const double a = dx ? c.a_dx : c.a_fwd, b = dx ? c.b_dx : c.b_fwd;
     const int64_t tiles = cdiv(M, c.bm) * cdiv(Nc, c.bn);
     for (int s = 1; s <= 8; ++s) {
@@ -256,11 +264,22 @@ GemmPlan plan_gemm_bf16(int64_t M, int64_t Nc, int64_t Kc, bool dx) {
 
 // fp32: 128x128 when that fills the chip, else the split tile with the
 // contraction split across blocks until about 256 blocks run.
-GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx) {
-  if (bf16) return plan_gemm_bf16(M, Nc, Kc, dx);
+GemmPlan plan_gemm(int64_t M, int64_t Nc, int64_t Kc, bool bf16, bool dx, bool tiled = false) {
+  if (bf16) return plan_gemm_bf16(M, Nc, Kc, dx, tiled);
   if (cdiv(M, 128) * cdiv(Nc, 128) >= 256) return {128, 128, {rup(Kc, 32), 1}, 0};
   const int64_t tiles = cdiv(M, SPLIT_BM) * cdiv(Nc, SPLIT_BN);
   return {SPLIT_BM, SPLIT_BN, plan_split(Kc, tiles, 256, 32, 128), 0};
+}
+
+// The bf16 product of plan g reads its A operand in fragment tiles.
+bool plan_tiled(const GemmPlan& g) { return g.cfg >= 0 && kBf16Cfg[g.cfg].depth == 0; }
+
+// Products over T-row chunks of a linear whose A operand (bf16 X or g, a
+// contraction of Kc) may be fragment-tiled: plain bf16 W (the quantized
+// loop decodes W while staging it), whole 32-row fragment rows per chunk,
+// whole 64-wide K-steps.
+bool tiled_ok(const lora_linear* L, int64_t Kc) {
+  return L->w_dtype == LORA_BF16 && L->tokens % 32 == 0 && Kc % 64 == 0;
 }
 
 // Short chunks: the contraction is split across blocks, and each linear runs
@@ -327,8 +346,8 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
   y.strips = cdiv(N, SK_C);
   const int rpad = rank_pad(r);
   y.k4 = plan_rows(T, cdiv(K, SK_C), k4_slots(rpad));
-  y.gf = plan_gemm(stack * T, N, K, bf, false);
-  y.gd = plan_gemm(stack * T, K, N, bf, true);
+  y.gf = plan_gemm(stack * T, N, K, bf, false, tiled_ok(L, K));
+  y.gd = plan_gemm(stack * T, K, N, bf, true, tiled_ok(L, N));
   // k3 beside the split dX GEMM keeps its own grid (one strip per block
   // there); the plain path groups strips.
   if (use_split_path(y.gd, r, bf)) {
@@ -377,8 +396,8 @@ struct StackLayout {
 StackLayout make_stack_layout(const lora_linear* L, int n) {
   StackLayout z;
   const int64_t M = n * L->tokens, K = L->in_dim, N = L->out_dim;
-  z.gf = plan_gemm(M, N, K, true, false);
-  z.gd = plan_gemm(M, K, N, true, true);
+  z.gf = plan_gemm(M, N, K, true, false, tiled_ok(L, K));
+  z.gd = plan_gemm(M, K, N, true, true, tiled_ok(L, N));
   size_t off = 0;
   z.xbf = carve(off, sizeof(uint16_t) * M * K);
   z.gfpart = carve(off, z.gf.k.n > 1 ? sizeof(float) * z.gf.k.n * M * N : 0);
@@ -571,6 +590,8 @@ struct FwdJob {
   uint16_t* Xbf;
   const float* X;
   float *Y, *Z, *gfpart;
+  RedJob ured;      // U's split partials summed once before the product, if has_ured
+  bool has_ured;
 };
 
 // One linear's operands of the bf16 forward product.
@@ -612,10 +633,19 @@ int prepare_fwd(const lora_linear* lin, const float* X, float* Y, float* U, floa
   DownArgs& da = j.da;
   da.X = X; da.T = T; da.K = K; da.A = lin->A; da.r = r; da.drop = make_drop(drop);
   da.ksplit = y.down.len; da.nsplit = y.down.n; da.Upart = Upart; da.U = U; da.Xbf = j.Xbf;
+  da.xbf_nkq = (j.Xbf && plan_tiled(y.gf)) ? K / 64 : 0;
   j.down_flops = 2.0 * T * K * r;
   j.down_bytes = 4.0 * (T * K + r * K + T * r) + (j.Xbf ? 2.0 * T * K : 0.0);
   j.xa = y.down.n > 1 ? LoraOperand{Upart, T * r, y.down.n, U} : LoraOperand{U, T * r, 1, nullptr};
   j.split = use_split_path(y.gf, r, bf);
+  // The direct-operand product stages U once per column of tiles: it reads
+  // U summed by one reduction launch rather than summing the partials in
+  // every tile.
+  j.has_ured = bf && !j.split && y.down.n > 1 && plan_tiled(y.gf);
+  if (j.has_ured) {
+    j.ured = RedJob{Upart, U, nullptr, T * r, 1, (int)y.down.n, 0, 1.0f, 1};
+    j.xa = LoraOperand{U, T * r, 1, nullptr};
+  }
   if (j.split) {
     GemmF32Args& a = j.g;
     memset(&a, 0, sizeof(a));
@@ -697,6 +727,7 @@ void launch_fwd_plain(const FwdJob& j, hipStream_t st) {
   const lora_linear* lin = j.lin;
   const int64_t T = j.T, K = j.K, N = j.N, r = j.r;
   launch_fwd_down(j, st);
+  if (j.has_ured) launch_reduce(&j.ured, 1, st);
   // Z = X W^T + s U B^T; Y = Z or (mag/norm) * Z.
   if (bf16_ops(lin->w_dtype)) {
     GemmBf16Args a;
@@ -802,6 +833,7 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   o.dmpart = (dMag && y.k3.n > 1) ? (float*)(w + y.dmpart) : nullptr;
   o.dm = dMag;
   o.gbf = (bf && dX) ? (stack > 1 ? bf_rows : (uint16_t*)(w + y.gbf)) : nullptr;
+  o.gbf_nkq = (o.gbf && plan_tiled(y.gd)) ? N / 64 : 0;
   o.scale = lin->scale;
   o.accumulate = acc;
   const float* Zin = dMag ? Z : nullptr;
@@ -1092,6 +1124,12 @@ size_t lora_qweight_layout(int32_t w_dtype, int64_t out_dim, int64_t in_dim, siz
   return total;
 }
 
+int lora_set_bf16_config(int cfg) {
+  if (cfg < -1 || cfg >= kBf16NCfg) return LORA_E_INVALID;
+  g_bf16_cfg.store(cfg, std::memory_order_relaxed);
+  return LORA_OK;
+}
+
 const char* lora_status_string(int s) {
   switch (s) {
     case LORA_OK: return "ok";
@@ -1274,6 +1312,13 @@ int lora_forward_slots(int n, const lora_linear* lins, const float* const* X, fl
     return hip_status();
   }
   for (int i = 0; i < n; ++i) launch_fwd_down(jobs[i], st);
+  {
+    RedJob red[LORA_MAX_SLOTS];
+    int nr = 0;
+    for (int i = 0; i < n; ++i)
+      if (jobs[i].has_ured) red[nr++] = jobs[i].ured;
+    if (nr) launch_reduce(red, nr, st);
+  }
   GemmBf16Args a;
   memset(&a, 0, sizeof(a));
   a.A = xbf; a.lda = K; a.ldb = K;

@@ -30,7 +30,8 @@ constexpr int SK_LD = SK_C + 4;
 
 // ---------------------------------------------------------------------------
 // down: Upart[split][t][j] = sum_{k in split} X~[t,k] A[j,k]; also writes the
-// unmasked bf16 copy of X (used by the bf16 frozen GEMM) when Xbf != NULL.
+// unmasked bf16 copy of X (used by the bf16 frozen GEMM) when Xbf != NULL,
+// row-major or, when xbf_nkq > 0, in fragment tiles (atile_off).
 // Grid: (ceil(T/64), nsplit).  RP = rank padded to a multiple of 16.
 // With one split the block writes U itself.
 // ---------------------------------------------------------------------------
@@ -45,6 +46,7 @@ struct DownArgs {
   float* Upart;
   float* U;
   uint16_t* Xbf;
+  int64_t xbf_nkq;   // > 0: Xbf in fragment tiles of a contraction of xbf_nkq * 64
 };
 
 template <int RP>
@@ -115,7 +117,7 @@ LORA_DEV void down_block(const DownArgs& p, float* smem, int64_t bx, int split) 
       if (ok) {
         if (Xbf) {
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(Xbf + t * K + k) = b;
+          *reinterpret_cast<u32x2*>(Xbf + (p.xbf_nkq ? atile_off(t, k, p.xbf_nkq) : t * K + k)) = b;
         }
         if (drop.on) {
           const uint64_t rk = drop_row(drop, t);
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
 //   Vpart[x][t][j]   = sum_{n in strip} g[t,n] B[n,j]
 //   dBpart[y][n][j]  = sum_{t in range} g[t,n] U[t,j]
 //   dmpart[y][n]     = sum_{t in range} dY[t,n] Z[t,n]          (DoRA)
-//   gbf[t][n]        = bf16(g)                                   (optional)
+//   gbf[t][n]        = bf16(g)            (optional; tiled when gbf_nkq > 0)
 // With one strip V is written directly; with one row range dB (and dm) are
 // scaled and written (or added) directly.
 // ---------------------------------------------------------------------------
@@ -205,6 +207,7 @@ struct K3Out {
   float* dmpart;
   float* dm;
   uint16_t* gbf;
+  int64_t gbf_nkq;   // > 0: gbf in fragment tiles (atile_off) of a contraction of gbf_nkq * 64
   float scale;
   int accumulate;
 };
@@ -321,7 +324,7 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
         for (int e = 0; e < 4; ++e) v[e] *= cmul[e];
         if (o.gbf) {
           u32x2 b = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(o.gbf + t * N + ncol) = b;
+          *reinterpret_cast<u32x2*>(o.gbf + (o.gbf_nkq ? atile_off(t, ncol, o.gbf_nkq) : t * N + ncol)) = b;
         }
       }
       *reinterpret_cast<f32x4*>(&Gs[((tid >> 4) + 16 * q) * SK_LD + 4 * c4]) = v;
@@ -626,7 +629,8 @@ void k3r_kernel(K3Args p) {
       for (int e = 0; e < 4; ++e) g[e] *= cmul[Q][e];
       if (o.gbf) {
         const u32x2 b = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-        *reinterpret_cast<u32x2*>(o.gbf + (t0 + 4 * tr + qq) * N + n0 + 4 * tc) = b;
+        const int64_t t = t0 + 4 * tr + qq, n = n0 + 4 * tc;
+        *reinterpret_cast<u32x2*>(o.gbf + (o.gbf_nkq ? atile_off(t, n, o.gbf_nkq) : t * N + n)) = b;
       }
       *reinterpret_cast<f32x4*>(&Gs[(4 * tr + qq) * K3R_LD + 4 * tc]) = g;
     }

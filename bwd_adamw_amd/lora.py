@@ -21,7 +21,7 @@ __all__ = [
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
     "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
-    "lora_status_string", "lora_profile_begin", "lora_profile_end",
+    "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_set_bf16_config",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
     "lora_qweight_layout", "lora_grad_prepare_noalloc",
@@ -43,7 +43,7 @@ EXPORTS = (
     "lora_grad_prepare_workspace_bytes", "lora_grad_prepare", "lora_adamw_step",
     "lora_dropout_mask", "lora_dora_row_norms_workspace_bytes", "lora_dora_row_norms",
     "lora_merge_workspace_bytes", "lora_merge", "lora_scaling", "lora_lr_at",
-    "lora_status_string", "lora_profile_begin", "lora_profile_end",
+    "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_set_bf16_config",
     "lora_group_workspace_bytes", "lora_forward_group", "lora_backward_group",
     "lora_slots_workspace_bytes", "lora_forward_slots", "lora_backward_slots",
     "lora_qweight_layout", "lora_grad_prepare_noalloc",
@@ -114,6 +114,7 @@ def lib() -> C.CDLL:
             "lora_status_string": (C.c_char_p, [I32]),
             "lora_profile_begin": (I32, [I32]),
             "lora_profile_end": (I32, [P, I32]),
+            "lora_set_bf16_config": (I32, [I32]),
             "lora_group_workspace_bytes": (SZ, [I32, P]),
             "lora_forward_group": (I32, [I32, P, P, P, P, P, P, P, SZ, P]),
             "lora_backward_group": (I32, [I32, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
@@ -558,6 +559,12 @@ def lora_merge(lin: LoraLinear, W_out, rmse=None, ws=None, stream=None):
                           _sized(rmse, "rmse", 1, torch.float64), _ptr(ws, "ws", None), ws_bytes,
                           _stream(stream))
     _check("lora_merge", rc)
+
+
+def lora_set_bf16_config(cfg: int):
+    """Pin the tile configuration of the bf16-W products (-1: the planner
+    chooses per product).  Process-wide; size workspaces after setting it."""
+    _check("lora_set_bf16_config", lib().lora_set_bf16_config(int(cfg)))
 
 
 def lora_profile_begin(max_launches: int = 100000):

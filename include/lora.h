@@ -368,6 +368,18 @@ typedef struct lora_profile_entry {
 int lora_profile_begin(int max_launches);
 int lora_profile_end(lora_profile_entry* out, int max_entries);
 
+/* Tile configuration of the bf16-W frozen products (a tuning and testing
+ * control; "8. LoRA Fundamentals", "How it works", is the product itself).
+ * cfg -1 (the default) lets the planner choose per product; cfg 0-5 makes
+ * every bf16 product the configuration can run use it (with the planner's
+ * contraction split), others keep the planner's choice.  Configuration 5
+ * loads the activation operand straight into registers from a fragment-tiled
+ * copy and needs plain bf16 W, tokens a multiple of 32 and a contraction a
+ * multiple of 64.  Process-wide; workspace sizes follow the setting, so set
+ * it before sizing workspaces and while no call is being planned.  Returns
+ * LORA_OK, or LORA_E_INVALID for cfg outside -1..5. */
+int lora_set_bf16_config(int cfg);
+
 /* Host helpers. */
 /* alpha/rank, or alpha/sqrt(rank) when rslora != 0 ("How it works"). */
 double lora_scaling(double alpha, int64_t rank, int rslora);

@@ -199,3 +199,10 @@ def test_qweight_layout_rejects_non_block_shapes():
     assert L.lib().lora_qweight_layout(code, 16, 128, None) == 0
     assert L.lib().lora_qweight_layout(code, 0, 256, None) == 0
     assert L.lib().lora_qweight_layout(L.BF16, 16, 256, None) == 0
+
+
+def test_bf16_config_control_rejects_unknown_configurations():
+    lib = L.lib()
+    assert lib.lora_set_bf16_config(6) == -1
+    assert lib.lora_set_bf16_config(-2) == -1
+    assert lib.lora_set_bf16_config(-1) == 0

@@ -190,6 +190,44 @@ def test_linear_forward_backward_parity(case):
         assert e <= tol, (n, e)
 
 
+# The direct-operand bf16 loop (tile configuration 5: the activation operand
+# in fragment tiles, loaded straight into registers; W through LDS).  Pinned
+# so that small shapes take it; each product uses it where its contraction
+# is a multiple of 64 (the forward's in_dim, the dX product's out_dim).
+DIRECT_CASES = [
+    # name, T, K, N, r, scale, dropout p, DoRA
+    ("direct-fwd-ragged-tiles", 288, 640, 1000, 32, math.sqrt(32), 0.1, True),
+    ("direct-dx-ragged-cols", 96, 600, 1088, 16, 2.0, 0.1, False),
+    ("direct-split-contraction", 256, 2560, 512, 64, 1.0, 0.1, True),
+    ("direct-whole-tiles", 512, 1024, 768, 64, 1.0, 0.0, False),
+]
+
+
+@pytest.fixture
+def bf16_config_5():
+    L.lora_set_bf16_config(5)
+    try:
+        yield
+    finally:
+        L.lora_set_bf16_config(-1)
+
+
+@pytest.mark.parametrize("case", DIRECT_CASES, ids=[c[0] for c in DIRECT_CASES])
+def test_direct_operand_products_match_oracle(case, bf16_config_5):
+    name, T, K, N, r, s, p, dora = case
+    _say("direct", name)
+    c = _linear_case(T, K, N, r, "bf16", seed=zlib.crc32(name.encode()) % 1000, dy_std=1e-2)
+    dk = (1234, 2, 1, 3, 4)
+    got = _run_gpu(c, s, p, dk, dora)
+    mag, nrm = _dora_vectors(got, c, s) if dora else (None, None)
+    ref = _oracle(c, s, p, dk, mag, nrm)
+    for n in ["Y", "U", "dX", "dA", "dB"] + (["Z", "dmag"] if dora else []):
+        e = rel_err(got[n], ref[n])
+        _say(f"  {n}: rel err {e:.3e}")
+        assert torch.isfinite(got[n]).all(), f"{n} has unwritten (NaN) elements"
+        assert e <= TOL["bf16"], (n, e)
+
+
 QUANT_CASES = [
     # name, format, T, K, N, r, scale, dropout p (, DoRA)
     ("q8_0-ragged", "q8_0", 100, 544, 264, 8, 2.0, 0.1),
@@ -1390,6 +1428,13 @@ def test_slots_match_oracle(case):
             e = rel_err(got[nme][i], ref)
             _say(f"  slot {i} {nme}: rel err {e:.3e}")
             assert e <= 2e-2 if nme in ("Y", "dX", "Z", "dm") else e <= 1e-4, (i, nme, e)
+
+
+def test_direct_operand_stacked_slots_match_oracle(bf16_config_5):
+    """Two stacked slots on the direct-operand loop: the slots' bf16 copies
+    of X and g are fragment-tiled one above another (forward 1024 whole
+    columns; dX 640 columns, the last tile ragged)."""
+    test_slots_match_oracle(("direct-pair-stacked-dora", 256, 640, 1024, 32, 2, 0.1, True))
 
 
 @pytest.mark.parametrize("T", [256, 100])
