@@ -27,9 +27,9 @@
 // (atile_off: each 1 KB is one MFMA operand of 32 rows x 16 contraction
 // indices in lane order, written so by down and k3), and each wave loads its
 // own fragments into registers one K-step ahead.  Only W goes through LDS,
-// by direct-to-LDS loads two K-steps ahead into a ring of three stages, read
-// back as in the loop above (forward: rows of 128 bytes with their 16-byte
-// chunks XOR-swizzled by row; dX: the transposed tile).  A K-step is four
+// by direct-to-LDS loads three K-steps ahead into a ring of four stages, read
+// back as in the loop above (rows of 128 bytes with their 16-byte chunks
+// XOR-swizzled by row).  A K-step is four
 // phases of sixteen MFMAs, each overlapping the next phase's W fragment
 // reads and a quarter of the loads, with one barrier per K-step.
 //
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   constexpr bool AD = DEPTH == 0;                     // direct-operand loop
   static_assert(!AD || (BM == 256 && BN == 256 && NT == 256 && WGM == 2 && BK == 64 && !QW),
                 "direct-operand loop shape");
-  constexpr int AD_NB = 3;                            // W stages in LDS (direct-operand loop)
+  constexpr int AD_NB = 4;                            // W stages in LDS (direct-operand loop)
   constexpr int QWD = QW ? wq_words(WQ) : 1;          // words per staged 8-element run
   constexpr int QR0 = BK * BN / (8 * NT);
   constexpr int QR = QR0 < 2 ? 2 : (QR0 > 8 ? 8 : QR0);  // dX: contraction rows per item
@@ -660,27 +660,28 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     // Phase s of K-step k: W fragments of sub-step s + 1 (the last phase:
     // sub-step 0 of the next stage, after the barrier), the tiled operand's
     // sub-step s of step k + 1 (used a whole K-step later), W loads 2s and
-    // 2s + 1 for step k + 2, and the sixteen MFMAs of sub-step s.  The
-    // barrier waits for this wave's loads of stage k + 1: at most 18 loads
-    // (three phases of four fragment and two W loads) were issued after them.
+    // 2s + 1 for step k + 3, and the sixteen MFMAs of sub-step s.  The
+    // barrier waits for this wave's loads of stage k + 1 (issued in step
+    // k - 2): at most 42 loads were issued after them (step k - 1's 24, six
+    // per phase, and step k's first three phases' 18).
     using Seq = std::make_integer_sequence<int, MI * NI>;
     u32x4 Ar[2][MI][KS];
     auto step = [&](int64_t k, u32x4 (&Rc)[MI][KS], u32x4 (&Rn)[MI][KS]) {
-      const int cur = (int)(k % AD_NB), nx1 = (int)((k + 1) % AD_NB), nx2 = (int)((k + 2) % AD_NB);
+      const int cur = (int)(k % AD_NB), nx1 = (int)((k + 1) % AD_NB), nx3 = (int)((k + 3) % AD_NB);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         __builtin_amdgcn_sched_barrier(0);
-        if (s == KS - 1) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s == KS - 1) asm volatile("s_waitcnt vmcnt(42) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         rdb(Bf[(s + 1) & 1], s == KS - 1 ? nx1 : cur, (s + 1) % KS);
         lda_sub(Rn, s, k + 1);
-        dma(2 * s, k + 2, nx2);
-        dma(2 * s + 1, k + 2, nx2);
+        dma(2 * s, k + 3, nx3);
+        dma(2 * s + 1, k + 3, nx3);
         mma(Rc, s, Bf[s & 1]);
         phase_order<FWD ? NI : 2 * NI, MI + 2>(Seq{});
       }
     };
-    // Issue order (fixed by the scheduling barriers): W stage 0, W stage 1,
-    // the operand's step 0; stage 0 is in once 24 later loads may remain.
+    // Issue order (fixed by the scheduling barriers): W stages 0, 1 and 2,
+    // the operand's step 0; stage 0 is in once 32 later loads may remain.
 #pragma unroll
     for (int q = 0; q < 8; ++q) dma(q, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -688,9 +689,12 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     for (int q = 0; q < 8; ++q) dma(q, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
+    for (int q = 0; q < 8; ++q) dma(q, 2, 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
     for (int ss = 0; ss < KS; ++ss) lda_sub(Ar[0], ss, 0);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
     rdb(Bf[0], 0, 0);
     int64_t k = 0;
     for (; k + 2 <= nk; k += 2) {

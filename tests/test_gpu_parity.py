@@ -262,6 +262,21 @@ def test_quantized_w_forward_backward_parity(case):
         assert e <= TOL[fmt], (n, e)
 
 
+@pytest.mark.parametrize("wd_,T,K,N", [("f32", 64, 256, 320), ("q4_k", 96, 512, 264), ("bf16", 96, 600, 1000)])
+def test_pinned_direct_configuration_leaves_ineligible_products_alone(wd_, T, K, N, bf16_config_5):
+    """With configuration 5 pinned, products it cannot run (float32 W, a
+    quantized base, bf16 contractions that are not whole 64-wide K-steps:
+    here both the forward's 600 and the dX product's 1000) keep the
+    planner's choice and their results."""
+    c = _linear_case(T, K, N, 16, wd_, seed=T + K, dy_std=1e-2)
+    dk = (1234, 2, 1, 3, 4)
+    got = _run_gpu(c, 2.0, 0.1, dk, False)
+    ref = _oracle(c, 2.0, 0.1, dk, None, None)
+    for n in ("Y", "U", "dX", "dA", "dB"):
+        assert torch.isfinite(got[n]).all(), n
+        assert rel_err(got[n], ref[n]) <= TOL[wd_], n
+
+
 def _exact_planes(fmt, planes, seed):
     """Scales that make every decoded weight a bf16 value: powers of two and
     small sub-scales (and Q4_K's dmin equal to d, with mins below 16)."""
