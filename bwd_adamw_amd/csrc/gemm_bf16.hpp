@@ -10,8 +10,9 @@
 // 16-byte pad, so every MFMA operand is one 128-bit LDS read: lane half h
 // takes contraction indices h*BK/2 .. (h+1)*BK/2 - 1 of the K-step.  For dX
 // the W tile arrives with the contraction index as its row (W's native [N,K]
-// layout); each thread loads an 8-row x 4-column block and transposes it in
-// registers before the LDS write.
+// layout); it goes to LDS as loaded (16-byte pieces of W rows, XOR-swizzled)
+// and each lane reads its operand with the LDS transpose load
+// (ds_read_b64_tr_b16).
 //
 // The main loop keeps DEPTH K-steps of global loads in flight in registers
 // (the load for step k + DEPTH is issued while step k is computed; DEPTH 1
@@ -28,10 +29,11 @@
 // indices in lane order, written so by down and k3), and each wave loads its
 // own fragments into registers one K-step ahead.  Only W goes through LDS,
 // by direct-to-LDS loads three K-steps ahead into a ring of four stages, read
-// back as in the loop above (rows of 128 bytes with their 16-byte chunks
-// XOR-swizzled by row).  A K-step is four
-// phases of sixteen MFMAs, each overlapping the next phase's W fragment
-// reads and a quarter of the loads, with one barrier per K-step.
+// back as in the loop above (forward: rows of 128 bytes with their 16-byte
+// chunks XOR-swizzled by row; dX: the tile as loaded, transpose reads).  A
+// K-step is four phases of sixteen MFMAs, each overlapping the next phase's
+// W fragment reads and a quarter of the loads, with one barrier per K-step.
+// dX's LoRA term, which carries the dropout mask, is added after the loop.
 //
 // Block-quantized W (qweight.hpp) takes the same kernel with WQ set: W is
 // staged as runs of 8 elements of a W row, decoded to bf16 on the way into
@@ -68,6 +70,8 @@ struct Bf16Slot {
   float* C2;               // fwd DoRA: Z, or NULL
   const float* cn;         // fwd DoRA column scale cn/cd, or NULL
   const float* cd;
+  const uint32_t* keep;    // dx: the mask's keep bits [slot rows, kw] (k4 writes
+  int64_t kw;              // them), or NULL: the mask is hashed here
 };
 
 struct GemmBf16Args {
@@ -99,7 +103,7 @@ LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
   LORA_SEL(xa.p) LORA_SEL(xa.stride) LORA_SEL(xa.nparts) LORA_SEL(xa.out)
   LORA_SEL(XB) LORA_SEL(xs)
   LORA_SEL(drop.base) LORA_SEL(drop.thr) LORA_SEL(drop.keep) LORA_SEL(drop.on)
-  LORA_SEL(C) LORA_SEL(C2) LORA_SEL(cn) LORA_SEL(cd)
+  LORA_SEL(C) LORA_SEL(C2) LORA_SEL(cn) LORA_SEL(cd) LORA_SEL(keep) LORA_SEL(kw)
 #undef LORA_SEL
   return so;
 }
@@ -114,7 +118,7 @@ LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
   X(2, 256, 128, 512, 2, 64, 2, 1, 0.483, 9.5, 0, 0)             \
   X(3, 256, 128, 512, 2, 64, 1, 2, 0, 0, 0.705, 7.8)             \
   X(4, 128, 128, 512, 2, 64, 2, 3, 0.581, 5.4, 0.967, 5.1)      \
-  X(5, 256, 256, 256, 2, 64, 0, 1, 0.326, 12.2, 0, 0)
+  X(5, 256, 256, 256, 2, 64, 0, 3, 0.326, 12.2, 0.300, 20.0)
 
 LORA_DEV uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 LORA_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
@@ -131,6 +135,25 @@ LORA_DEV void phase_slot() {
 template <int NRD, int NV, int... I>
 LORA_DEV void phase_order(std::integer_sequence<int, I...>) {
   (phase_slot<NRD, NV, I>(), ...);
+}
+
+// Two floats to bf16 (round to nearest even, NaN stays NaN) in one
+// v_cvt_pk_bf16_f32; a first in the low half.
+LORA_DEV uint32_t cvt_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// Two LDS transpose reads APART bytes apart, as one MFMA operand.  The
+// restrict-qualified LDS pointer tells the compiler that these reads do not
+// alias the direct-to-LDS loads in flight, which it would otherwise wait for.
+LORA_DEV u32x4 tr_pair(const __attribute__((address_space(3))) char* __restrict__ b, int apart) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)b);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(b + apart));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
 // EXACT: M, Nc and Kc are multiples of BM, BN and BK: nothing is out of range.
@@ -188,9 +211,17 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // neighbouring tiles of one split, which share that split's K-slices.
   const int64_t tiles = ntm * ntn;
   const int64_t ts = xcd_tile(blockIdx.x, tiles * p.nsplit);
-  const int split = (int)(ts / tiles);
+  int split = (int)(ts / tiles);
   int64_t tm, tn;
   grouped_tile(ts % tiles, ntm, ntn, tm, tn);
+  if constexpr (AD) {
+    // Scalar tile coordinates: W's direct-to-LDS loads take their resource
+    // and offsets from them, and where the compiler cannot prove those
+    // uniform it wraps every such load in a readfirstlane loop.
+    split = __builtin_amdgcn_readfirstlane(split);
+    tm = __builtin_amdgcn_readfirstlane((int)tm);
+    tn = __builtin_amdgcn_readfirstlane((int)tn);
+  }
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t kbeg = (int64_t)split * p.ksplit;
   const int64_t kend = min(p.Kc, kbeg + p.ksplit);
@@ -398,9 +429,99 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   using MainHalf = std::integral_constant<int, BK / 2>;
   using MainSteps = std::integral_constant<int, KS>;
   using MainTr = std::integral_constant<bool, TRB>;
+  // dX's LoRA term on the direct-operand loop, added after the main loop (the
+  // dropout mask applies to this term only).  Per 32 x 32 fragment: the term
+  // t into a 16-register temporary, d = mask * t, then d into the
+  // accumulators by MFMA, never by vector ALU work on them (which makes the
+  // compiler move all 256 accumulators out of the AGPRs and spill).  The
+  // injection uses that lane (m, h) holds d at n = 16u + 8(e/4) + 4h + e%4
+  // for its element v = 8u + e: read as contraction slot 8h + e of MFMA u,
+  // its own eight values are the m-side operand, and the W-side operand is
+  // the constant 0/1 matrix P_u that maps slot 8h + e to that n.  d goes in
+  // as bf16 hi and lo parts (hi + lo equals d to about 2^-18 relative).
+  auto compute_masked = [&](const uint16_t* Ab, const uint16_t* Bb, DropParams dp, const uint32_t* keep,
+                            int64_t kw) {
+    constexpr int half = LBK / 2, NS = LBK / 16;
+    // Opaque per call: the multipliers and the lane's indices do not depend
+    // on the rank chunk, and hoisted out of the chunk loop (or above the main
+    // loop) they would hold registers across it.
+    int ln = lane;
+    asm volatile("" : "+s"(dp.base), "+s"(dp.thr), "+v"(ln));
+    const int h = ln >> 5, r32 = ln & 31;
+    u32x4 P[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int n_lo = 16 * u + 8 * (e >> 2) + 4 * h + (e & 3);
+        P[u][e / 2] = (r32 == n_lo ? 0x3f80u : 0u) | (r32 == n_lo + 1 ? 0x3f800000u : 0u);
+      }
+    // Stored keep bits: row m's words for the wave's 128 columns (j = 0..3),
+    // one 16-byte load per row block, all issued first.  A wave whose columns
+    // start past Nc (ragged last tile) reads none; its results are not stored.
+    u32x4 kwd[MI];
+    if (dp.on && keep != nullptr) {
+      const bool cok = n0 + wn0 < p.Nc;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int64_t m = m0 + wm0 + i * 32 + r32;
+        const bool ok = cok && m < p.M;
+        kwd[i] = *reinterpret_cast<const u32x4*>(keep + (ok ? (m - moff) * kw + ((n0 + wn0) >> 5) : 0));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      u32x4 av[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        av[s] = *reinterpret_cast<const u32x4*>(&Ab[(wm0 + i * 32 + r32) * LROW + half * h + 8 * s]);
+      const uint64_t rk = keep != nullptr ? 0 : drop_row(dp, m0 + wm0 + i * 32 + r32 - moff);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        f32x16 t;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) t[v] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          t = mfma32x32x16_bf16(
+              *reinterpret_cast<const u32x4*>(&Bb[(wn0 + j * 32 + r32) * LROW + half * h + 8 * s]), av[s], t);
+        // the fragment's keep bits first, one word (short hash lifetimes)
+        uint32_t kb = 0xffffu;
+        if (dp.on && keep != nullptr) {
+          // bit v: column 8 (v/4) + 4h + v%4 of the fragment's 32
+          const uint32_t w = kwd[i][j] >> (4 * h);
+          kb = (w & 0xfu) | (w >> 4 & 0xf0u) | (w >> 8 & 0xf00u) | (w >> 12 & 0xf000u);
+        } else if (dp.on) {
+          kb = 0;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) kb |= (uint32_t)drop_keep(dp, rk, n0 + wn0 + j * 32 + row32(v, ln)) << v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t hi[8], lo[8];   // packed pairs (v, v + 1)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float m0_ = (kb >> v & 1u) ? (dp.on ? dp.keep : 1.0f) : 0.0f;
+          const float m1_ = (kb >> (v + 1) & 1u) ? (dp.on ? dp.keep : 1.0f) : 0.0f;
+          const float d0 = m0_ * t[v], d1 = m1_ * t[v + 1];
+          hi[v / 2] = cvt_bf16x2(d0, d1);
+          const float r0 = d0 - __uint_as_float(hi[v / 2] << 16);
+          const float r1 = d1 - __uint_as_float(hi[v / 2] & 0xffff0000u);
+          lo[v / 2] = cvt_bf16x2(r0 == r0 ? r0 : 0.0f, r1 == r1 ? r1 : 0.0f);   // d infinite: hi alone
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 h = {hi[4 * u], hi[4 * u + 1], hi[4 * u + 2], hi[4 * u + 3]};
+          const u32x4 l = {lo[4 * u], lo[4 * u + 1], lo[4 * u + 2], lo[4 * u + 3]};
+          acc[i][j] = mfma32x32x16_bf16(P[u], h, acc[i][j]);
+          acc[i][j] = mfma32x32x16_bf16(P[u], l, acc[i][j]);
+        }
+      }
+    }
+  };
   // LoRA contraction over the rank: float32 operands rounded to bf16 in LDS,
-  // in 64-wide K-steps over the same LDS.
-  auto lora_contraction = [&]() {
+  // in 64-wide K-steps over the same LDS (MASKED: dX after the direct-operand
+  // loop, through compute_masked).
+  auto lora_contraction = [&](auto MASKED) {
     const Bf16Slot so = bf16_slot(p, slot);
     const bool store_xa = so.xa.out != nullptr && n0 == 0 && split == 0;
     uint16_t* La = smem;
@@ -414,14 +535,16 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       // A side: XA [M, r] rows m, scaled by s; as split partials, summed in
       // split order (and stored once, by the first column of tiles).
       // Forward B side: B_lora [Nc, r], rows n, rank contiguous.  dX B side:
-      // A_lora [r, Nc], rows the contraction index, transposed on store.
+      // A_lora [r, Nc]: a thread reads four columns of sixteen consecutive
+      // rows as 16-byte pieces (each load a contiguous 1 KB per wave) and
+      // stores each column's sixteen values transposed, as two 16-byte writes.
       constexpr int AIT = BM * (LBK / 4) / NT;        // A items (four floats) per thread
       constexpr int BIT = FWD ? BN * (LBK / 4) / NT : 0;   // forward B items
       constexpr int NIT = AIT > BIT ? AIT : BIT;
-      constexpr int DIT = BN * LBK / NT;              // dX B items (floats)
-      constexpr int SB = NIT, SD = DIT;
-      static_assert(NIT % SB == 0 && DIT % SD == 0 && BM * (LBK / 4) % NT == 0 &&
-                        BN * (LBK / 4) % NT == 0 && BN * LBK % NT == 0, "whole staging batches");
+      constexpr int QD = LBK / (NT / 64);             // dX: A_lora rows per thread
+      constexpr int SB = NIT;
+      static_assert(BM * (LBK / 4) % NT == 0 && BN * (LBK / 4) % NT == 0, "whole staging batches");
+      static_assert(FWD || (BN == 4 * 64 && QD == 16), "dX: four columns per lane, 16 rows per wave");
       auto item = [&](int it, int64_t o0, int64_t lim, int& row, int& c4, bool& ok) -> int64_t {
         const int f = tid + NT * it;
         row = f / (LBK / 4);
@@ -464,6 +587,16 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
           bool ok;
           vb[u] = *reinterpret_cast<const f32x4*>(so.XB + item(b0 + u, n0, p.Nc, row, c4, ok));
         }
+        f32x4 vd[FWD ? 1 : QD];
+        const int dc = 4 * (tid & 63), dr = QD * (tid >> 6);   // dX: first column, first row
+        if constexpr (!FWD) {
+          const bool cok = n0 + dc < p.Nc;                     // Nc is a multiple of 8
+#pragma unroll
+          for (int q = 0; q < QD; ++q) {
+            const int64_t gk = k0 + dr + q;
+            vd[q] = *reinterpret_cast<const f32x4*>(so.XB + ((cok && gk < p.r) ? gk * p.Nc + n0 + dc : 0));
+          }
+        }
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
           int row, c4;
@@ -477,22 +610,19 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
             put(Lb, row, c4, ok, vb[u]);
           }
         }
-      }
-      if constexpr (!FWD) {
-        for (int b0 = 0; b0 < DIT; b0 += SD) {
-          float vd[SD];
+        if constexpr (!FWD) {
+          const bool cok = n0 + dc < p.Nc;
 #pragma unroll
-          for (int u = 0; u < SD; ++u) {
-            const int f = tid + NT * (b0 + u), n = f % BN, kk = f / BN;
-            const int64_t gn = n0 + n, gk = k0 + kk;
-            vd[u] = so.XB[(gn < p.Nc && gk < p.r) ? gk * p.Nc + gn : 0];
-          }
+          for (int q = 0; q < QD; ++q)
+            if (!(cok && k0 + dr + q < p.r)) vd[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int u = 0; u < SD; ++u) {
-            const int f = tid + NT * (b0 + u), n = f % BN, kk = f / BN;
-            const bool ok = n0 + n < p.Nc && k0 + kk < p.r;
-            Lb[n * LROW + kk] = (uint16_t)f32_to_bf16_bits(ok ? vd[u] : 0.f);
-          }
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int h8 = 0; h8 < QD; h8 += 8) {
+              const u32x4 w = {pack_bf16x2(vd[h8][e], vd[h8 + 1][e]), pack_bf16x2(vd[h8 + 2][e], vd[h8 + 3][e]),
+                               pack_bf16x2(vd[h8 + 4][e], vd[h8 + 5][e]), pack_bf16x2(vd[h8 + 6][e], vd[h8 + 7][e])};
+              *reinterpret_cast<u32x4*>(&Lb[(dc + e) * LROW + dr + h8]) = w;
+            }
         }
       }
       } else {
@@ -532,14 +662,17 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       }
       }
       __syncthreads();
-      compute(La, Lb, std::integral_constant<int, LROW>{}, std::integral_constant<int, LBK / 2>{},
-              std::integral_constant<int, LBK / 16>{}, std::false_type{});
+      if constexpr (decltype(MASKED)::value)
+        compute_masked(La, Lb, so.drop, so.keep, so.kw);
+      else
+        compute(La, Lb, std::integral_constant<int, LROW>{}, std::integral_constant<int, LBK / 2>{},
+                std::integral_constant<int, LBK / 16>{}, std::false_type{});
     }
     __syncthreads();
   };
 
-  if (!FWD && lora) {
-    lora_contraction();
+  if (!FWD && !AD && lora) {
+    lora_contraction(std::false_type{});
     const Bf16Slot so = bf16_slot(p, slot);
     if (so.drop.on) {
 #pragma unroll
@@ -638,13 +771,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
         if constexpr (FWD) {
           F[j] = *reinterpret_cast<const u32x4*>(Bb + wb[j] + 16 * (s ^ wm[j]));
         } else {
-          typedef short v4i16 __attribute__((ext_vector_type(4)));
-          auto* b = (__attribute__((address_space(3))) const char*)(Bb + wb[j] + 4096 * s);
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)b);
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)(b + 4 * (BN * 2)));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          F[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+          F[j] = tr_pair((__attribute__((address_space(3))) const char*)(Bb + wb[j] + 4096 * s), 4 * (BN * 2));
         }
       }
     };
@@ -741,7 +868,8 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     }
   }
 
-  if (FWD && lora) lora_contraction();
+  if (FWD && lora) lora_contraction(std::false_type{});
+  if (!FWD && AD && lora) lora_contraction(std::true_type{});
 
   const Bf16Slot so = bf16_slot(p, slot);
   if constexpr (FWD) {
@@ -772,7 +900,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // dX: the MFMA computes the tile transposed (W-side operand first), so lane
   // l holds output row m = .. + l%32 and, per group of four accumulators,
   // four consecutive columns: every store is a 16-byte vector, and the
-  // dropout mask above needed one row key per row.
+  // dropout mask of the LoRA term needs one row key per row.
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int64_t gm = m0 + wm0 + i * 32 + l32;

@@ -325,6 +325,8 @@ struct Layout {
   bool vreduce;        // V partials summed by a separate launch
   size_t upart, xbf, gfpart;                          // forward
   size_t vpart, v, dbpart, dmpart, gbf, gdpart, dapart;   // backward
+  size_t keep;         // the dropout mask's keep bits, [T, kw] words (k4 -> dX)
+  int64_t kw;
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -381,6 +383,10 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
   y.gbf = carve(off, (bf && own) ? sizeof(uint16_t) * T * N : 0);
   y.gdpart = carve(off, (own && y.gd.k.n > 1) ? sizeof(float) * y.gd.k.n * T * K : 0);
   y.dapart = carve(off, y.k4.n > 1 ? sizeof(float) * y.k4.n * r * K : 0);
+  // dX on the direct-operand loop takes the LoRA term's mask as bits that
+  // k4 (which hashes every element of X anyway) leaves behind.
+  y.kw = rup(cdiv(K, 32), 4);
+  y.keep = carve(off, (bf && plan_tiled(y.gd)) ? sizeof(uint32_t) * T * y.kw : 0);
   y.bwd_bytes = off;
   return y;
 }
@@ -791,6 +797,8 @@ Bf16Slot bf16_dx_slot(const BwdJob& j) {
   so.xs = j.lin->scale;
   so.drop = j.d;
   so.C = j.dX;
+  so.keep = j.k4a.keep;
+  so.kw = j.k4a.kw;
   return so;
 }
 
@@ -851,6 +859,8 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   k4a.X = X; k4a.T = T; k4a.K = K; k4a.V = j.xv.p; k4a.vparts = j.xv.nparts; k4a.r = r;
   k4a.drop = j.d; k4a.tsplit = y.k4.len; k4a.nts = y.k4.n; k4a.dApart = dApart; k4a.dA = dA;
   k4a.scale = lin->scale; k4a.accumulate = acc;
+  k4a.keep = (bf && dX && plan_tiled(y.gd)) ? (uint32_t*)(w + y.keep) : nullptr;
+  k4a.kw = y.kw;
   j.k4_flops = 2.0 * T * K * r;
   j.k4_bytes = 4.0 * (T * K + T * r + 2 * r * K);
   // Gradient splits over token ranges: fixed-order reduction jobs.
@@ -1039,6 +1049,8 @@ void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
   const int64_t T = jb.T, K = jb.K, N = jb.N, r = jb.r;
   const bool bf = bf16_ops(lin->w_dtype);
   launch_bwd_k3(jb, st);
+  // k4 first: it leaves the dropout keep bits that the bf16 dX product reads.
+  launch_bwd_k4(jb, st);
   if (jb.dX) {
     if (bf) {
       GemmBf16Args a;
@@ -1064,7 +1076,6 @@ void launch_bwd_plain(const BwdJob& jb, hipStream_t st) {
       launch_gemm_f32(y.gd, false, a, st);
     }
   }
-  launch_bwd_k4(jb, st);
 }
 
 // Linears of a group read one X: equal token count and input width.  Each
@@ -1378,6 +1389,7 @@ int lora_backward_slots(int n, const lora_linear* lins, const float* const* X,
     return hip_status();
   }
   for (int i = 0; i < n; ++i) launch_bwd_k3(jobs[i], st);
+  for (int i = 0; i < n; ++i) launch_bwd_k4(jobs[i], st);   // keep bits before dX
   if (want_dx) {
     GemmBf16Args a;
     memset(&a, 0, sizeof(a));
@@ -1390,7 +1402,6 @@ int lora_backward_slots(int n, const lora_linear* lins, const float* const* X,
     a.part = z.gd.k.n > 1 ? (float*)((char*)ws + off + z.gdpart) : nullptr;
     launch_gemm_bf16(z.gd, false, a, st);
   }
-  for (int i = 0; i < n; ++i) launch_bwd_k4(jobs[i], st);
   return hip_status();
 }
 

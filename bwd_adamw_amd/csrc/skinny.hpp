@@ -747,6 +747,11 @@ struct K4Args {
   float* dA;
   float scale;
   int accumulate;
+  // With dropout on: the keep bits of the mask, [T, kw] 32-bit words (bit b
+  // of word w is column 32 w + b), for the dX product after this one; or
+  // NULL.  kw is a multiple of 4.
+  uint32_t* keep;
+  int64_t kw;
 };
 
 template <int RP>
@@ -819,10 +824,25 @@ LORA_DEV void k4_block(const K4Args& p, float* smem, int64_t bx, int by) {
       int64_t t;
       const bool ok = x_ok(q, t0, t);
       f32x4 v = ok ? S.x[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      uint32_t nib = 0;
       if (ok && drop.on) {
         const uint64_t rk = drop_row(drop, t);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= drop_mul(drop, rk, kcol + e);
+        for (int e = 0; e < 4; ++e) {
+          const bool kp = drop_keep(drop, rk, kcol + e);
+          v[e] *= kp ? drop.keep : 0.0f;
+          nib |= (uint32_t)kp << e;
+        }
+      }
+      if (p.keep != nullptr && drop.on) {
+        // the eight lanes of a 32-column word (same row) OR their nibbles:
+        // DPP quad permutes (lane ^ 1, lane ^ 2), then the half-row mirror
+        // (lane i and 7 - i of each eight, one in each quad)
+        int w = (int)(nib << (4 * (c4 & 7)));
+        w |= __builtin_amdgcn_mov_dpp(w, 0xB1, 0xf, 0xf, true);
+        w |= __builtin_amdgcn_mov_dpp(w, 0x4E, 0xf, 0xf, true);
+        w |= __builtin_amdgcn_mov_dpp(w, 0x141, 0xf, 0xf, true);
+        if ((c4 & 7) == 0 && t < te && kcol < K) p.keep[t * p.kw + (kcol >> 5)] = (uint32_t)w;
       }
       *reinterpret_cast<f32x4*>(&Xs[((tid >> 4) + 16 * q) * SK_LD + 4 * c4]) = v;
     }

@@ -1452,6 +1452,51 @@ def test_direct_operand_stacked_slots_match_oracle(bf16_config_5):
     test_slots_match_oracle(("direct-pair-stacked-dora", 256, 640, 1024, 32, 2, 0.1, True))
 
 
+def _pinned(cfg, fn):
+    L.lora_set_bf16_config(cfg)
+    try:
+        return fn()
+    finally:
+        L.lora_set_bf16_config(-1)
+
+
+MASK_BIT_CASES = [
+    # name, T, K, N, r (the dX product: K output columns, contraction N)
+    ("ragged-cols", 96, 600, 1088, 16),       # last keep word partial; waves past the columns
+    ("ragged-rows", 288, 1000, 640, 32),      # a tile row past the last token
+    ("split-contraction", 256, 2560, 512, 64),
+]
+
+
+@pytest.mark.parametrize("case", MASK_BIT_CASES, ids=[c[0] for c in MASK_BIT_CASES])
+def test_direct_dx_stored_keep_bits_match_hashed_mask(case):
+    """dX on the direct-operand loop applies the LoRA term's dropout mask
+    from the keep bits that k4 stores; configuration 1 hashes the mask
+    itself.  The two agree up to the frozen product's summation order: one
+    wrong bit would move an element by a whole LoRA term, far above 1e-5."""
+    name, T, K, N, r = case
+    _say("keep bits", name)
+    c = _linear_case(T, K, N, r, "bf16", seed=zlib.crc32(name.encode()) % 1000, dy_std=1e-2, b_std=0.05)
+    dk = (77, 5, 2, 1, 3)
+    a = _pinned(1, lambda: _run_gpu(c, 2.0, 0.3, dk, False))
+    b = _pinned(5, lambda: _run_gpu(c, 2.0, 0.3, dk, False))
+    for n in ("dX", "dA", "dB"):
+        assert torch.isfinite(b[n]).all(), n
+        e = rel_err(b[n], a[n])
+        _say(f"  {n}: rel diff {e:.2e}")
+        assert e <= 1e-5, (n, e)
+
+
+def test_direct_dx_stored_keep_bits_match_hashed_mask_stacked():
+    """The same for two stacked slots (each slot's bits, own dropout keys)."""
+    cs = _slot_cases(256, 640, 1024, 32, 2, seed=83)
+    a, _, _ = _pinned(1, lambda: _run_slots(cs, 2.0, 0.3, together=True))
+    b, _, _ = _pinned(5, lambda: _run_slots(cs, 2.0, 0.3, together=True))
+    for i in range(2):
+        assert torch.isfinite(b["dX"][i]).all(), i
+        assert rel_err(b["dX"][i], a["dX"][i]) <= 1e-5, i
+
+
 @pytest.mark.parametrize("T", [256, 100])
 def test_slots_equal_separate_calls(T):
     """Stacked (T a multiple of 256) slot calls agree with separate calls up
