@@ -70,8 +70,9 @@ struct Bf16Slot {
   float* C2;               // fwd DoRA: Z, or NULL
   const float* cn;         // fwd DoRA column scale cn/cd, or NULL
   const float* cd;
-  const uint32_t* keep;    // dx: the mask's keep bits [slot rows, kw] (k4 writes
-  int64_t kw;              // them), or NULL: the mask is hashed here
+  const uint32_t* keep;    // dx: the mask's keep bits (k4 writes them; word w of
+                           // slot row t at keep[w * rows + t]), or NULL: the
+                           // mask is hashed here
 };
 
 struct GemmBf16Args {
@@ -103,7 +104,7 @@ LORA_DEV Bf16Slot bf16_slot(const GemmBf16Args& p, int slot) {
   LORA_SEL(xa.p) LORA_SEL(xa.stride) LORA_SEL(xa.nparts) LORA_SEL(xa.out)
   LORA_SEL(XB) LORA_SEL(xs)
   LORA_SEL(drop.base) LORA_SEL(drop.thr) LORA_SEL(drop.keep) LORA_SEL(drop.on)
-  LORA_SEL(C) LORA_SEL(C2) LORA_SEL(cn) LORA_SEL(cd) LORA_SEL(keep) LORA_SEL(kw)
+  LORA_SEL(C) LORA_SEL(C2) LORA_SEL(cn) LORA_SEL(cd) LORA_SEL(keep)
 #undef LORA_SEL
   return so;
 }
@@ -439,8 +440,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   // its own eight values are the m-side operand, and the W-side operand is
   // the constant 0/1 matrix P_u that maps slot 8h + e to that n.  d goes in
   // as bf16 hi and lo parts (hi + lo equals d to about 2^-18 relative).
-  auto compute_masked = [&](const uint16_t* Ab, const uint16_t* Bb, DropParams dp, const uint32_t* keep,
-                            int64_t kw) {
+  auto compute_masked = [&](const uint16_t* Ab, const uint16_t* Bb, DropParams dp, const uint32_t* keep) {
     constexpr int half = LBK / 2, NS = LBK / 16;
     // Opaque per call: the multipliers and the lane's indices do not depend
     // on the rank chunk, and hoisted out of the chunk loop (or above the main
@@ -456,17 +456,21 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
         const int n_lo = 16 * u + 8 * (e >> 2) + 4 * h + (e & 3);
         P[u][e / 2] = (r32 == n_lo ? 0x3f80u : 0u) | (r32 == n_lo + 1 ? 0x3f800000u : 0u);
       }
-    // Stored keep bits: row m's words for the wave's 128 columns (j = 0..3),
-    // one 16-byte load per row block, all issued first.  A wave whose columns
-    // start past Nc (ragged last tile) reads none; its results are not stored.
-    u32x4 kwd[MI];
+    // Stored keep bits: row m's word for each 32 columns j of the wave (a
+    // wave's load is 32 consecutive rows of one word), all issued first.
+    // Words past Nc are not read; their columns are not stored.
+    uint32_t kwd[MI][NI];
     if (dp.on && keep != nullptr) {
-      const bool cok = n0 + wn0 < p.Nc;
+      const int64_t rows = p.nslot > 1 ? p.slot_rows : p.M;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int64_t m = m0 + wm0 + i * 32 + r32;
-        const bool ok = cok && m < p.M;
-        kwd[i] = *reinterpret_cast<const u32x4*>(keep + (ok ? (m - moff) * kw + ((n0 + wn0) >> 5) : 0));
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int64_t c = n0 + wn0 + 32 * j;
+          const bool ok = c < p.Nc && m < p.M;
+          kwd[i][j] = keep[ok ? (c >> 5) * rows + (m - moff) : 0];
+        }
       }
     }
 #pragma unroll
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       }
       __syncthreads();
       if constexpr (decltype(MASKED)::value)
-        compute_masked(La, Lb, so.drop, so.keep, so.kw);
+        compute_masked(La, Lb, so.drop, so.keep);
       else
         compute(La, Lb, std::integral_constant<int, LROW>{}, std::integral_constant<int, LBK / 2>{},
                 std::integral_constant<int, LBK / 16>{}, std::false_type{});

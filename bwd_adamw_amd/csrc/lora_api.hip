@@ -325,8 +325,7 @@ struct Layout {
   bool vreduce;        // V partials summed by a separate launch
   size_t upart, xbf, gfpart;                          // forward
   size_t vpart, v, dbpart, dmpart, gbf, gdpart, dapart;   // backward
-  size_t keep;         // the dropout mask's keep bits, [T, kw] words (k4 -> dX)
-  int64_t kw;
+  size_t keep;         // the dropout mask's keep bits, ceil(K/32) x T words (k4 -> dX)
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -385,8 +384,7 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
   y.dapart = carve(off, y.k4.n > 1 ? sizeof(float) * y.k4.n * r * K : 0);
   // dX on the direct-operand loop takes the LoRA term's mask as bits that
   // k4 (which hashes every element of X anyway) leaves behind.
-  y.kw = rup(cdiv(K, 32), 4);
-  y.keep = carve(off, (bf && plan_tiled(y.gd)) ? sizeof(uint32_t) * T * y.kw : 0);
+  y.keep = carve(off, (bf && plan_tiled(y.gd)) ? sizeof(uint32_t) * T * cdiv(K, 32) : 0);
   y.bwd_bytes = off;
   return y;
 }
@@ -798,7 +796,6 @@ Bf16Slot bf16_dx_slot(const BwdJob& j) {
   so.drop = j.d;
   so.C = j.dX;
   so.keep = j.k4a.keep;
-  so.kw = j.k4a.kw;
   return so;
 }
 
@@ -860,7 +857,6 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   k4a.drop = j.d; k4a.tsplit = y.k4.len; k4a.nts = y.k4.n; k4a.dApart = dApart; k4a.dA = dA;
   k4a.scale = lin->scale; k4a.accumulate = acc;
   k4a.keep = (bf && dX && plan_tiled(y.gd)) ? (uint32_t*)(w + y.keep) : nullptr;
-  k4a.kw = y.kw;
   j.k4_flops = 2.0 * T * K * r;
   j.k4_bytes = 4.0 * (T * K + T * r + 2 * r * K);
   // Gradient splits over token ranges: fixed-order reduction jobs.

@@ -747,11 +747,10 @@ struct K4Args {
   float* dA;
   float scale;
   int accumulate;
-  // With dropout on: the keep bits of the mask, [T, kw] 32-bit words (bit b
-  // of word w is column 32 w + b), for the dX product after this one; or
-  // NULL.  kw is a multiple of 4.
+  // With dropout on: the keep bits of the mask for the dX product after
+  // this one, or NULL: 32-bit words, word w of token t at keep[w * T + t]
+  // (bit b is column 32 w + b), so a block's rows of one word are contiguous.
   uint32_t* keep;
-  int64_t kw;
 };
 
 template <int RP>
@@ -842,7 +841,7 @@ LORA_DEV void k4_block(const K4Args& p, float* smem, int64_t bx, int by) {
         w |= __builtin_amdgcn_mov_dpp(w, 0xB1, 0xf, 0xf, true);
         w |= __builtin_amdgcn_mov_dpp(w, 0x4E, 0xf, 0xf, true);
         w |= __builtin_amdgcn_mov_dpp(w, 0x141, 0xf, 0xf, true);
-        if ((c4 & 7) == 0 && t < te && kcol < K) p.keep[t * p.kw + (kcol >> 5)] = (uint32_t)w;
+        if ((c4 & 7) == 0 && t < te && kcol < K) p.keep[(kcol >> 5) * T + t] = (uint32_t)w;
       }
       *reinterpret_cast<f32x4*>(&Xs[((tid >> 4) + 16 * q) * SK_LD + 4 * c4]) = v;
     }
