@@ -793,8 +793,8 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     // sub-step s of step k + 1 (used a whole K-step later), W loads 2s and
     // 2s + 1 for step k + 3, and the sixteen MFMAs of sub-step s.  The
     // barrier waits for this wave's loads of stage k + 1 (issued in step
-    // k - 2): at most 42 loads were issued after them (step k - 1's 24, six
-    // per phase, and step k's first three phases' 18).
+    // k - 2): at most 7 (MI + 2) loads were issued after them (MI + 2 per
+    // phase, step k - 1's four phases and step k's first three).
     using Seq = std::make_integer_sequence<int, MI * NI>;
     u32x4 Ar[2][MI][KS];
     auto step = [&](int64_t k, u32x4 (&Rc)[MI][KS], u32x4 (&Rn)[MI][KS]) {
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         __builtin_amdgcn_sched_barrier(0);
-        if (s == KS - 1) asm volatile("s_waitcnt vmcnt(42) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s == KS - 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(7 * (MI + 2)) : "memory");
         rdb(Bf[(s + 1) & 1], s == KS - 1 ? nx1 : cur, (s + 1) % KS);
         lda_sub(Rn, s, k + 1);
         dma(2 * s, k + 3, nx3);
@@ -812,7 +812,8 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       }
     };
     // Issue order (fixed by the scheduling barriers): W stages 0, 1 and 2,
-    // the operand's step 0; stage 0 is in once 32 later loads may remain.
+    // the operand's step 0; stage 0 is in once 16 + MI KS later loads may
+    // remain.
 #pragma unroll
     for (int q = 0; q < 8; ++q) dma(q, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -825,7 +826,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
 #pragma unroll
     for (int ss = 0; ss < KS; ++ss) lda_sub(Ar[0], ss, 0);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(16 + MI * KS) : "memory");
     rdb(Bf[0], 0, 0);
     int64_t k = 0;
     for (; k + 2 <= nk; k += 2) {
