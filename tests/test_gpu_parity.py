@@ -200,6 +200,7 @@ DIRECT_CASES = [
     ("direct-dx-ragged-cols", 96, 600, 1088, 16, 2.0, 0.1, False),
     ("direct-split-contraction", 256, 2560, 512, 64, 1.0, 0.1, True),
     ("direct-whole-tiles", 512, 1024, 768, 64, 1.0, 0.0, False),
+    ("direct-rank-128", 128, 640, 1088, 128, 1.0, 0.2, True),   # LoRA term in two rank chunks
 ]
 
 
@@ -1465,6 +1466,7 @@ MASK_BIT_CASES = [
     ("ragged-cols", 96, 600, 1088, 16),       # last keep word partial; waves past the columns
     ("ragged-rows", 288, 1000, 640, 32),      # a tile row past the last token
     ("split-contraction", 256, 2560, 512, 64),
+    ("rank-128", 128, 640, 1088, 128),        # the mask applied to each of two rank chunks
 ]
 
 
