@@ -485,8 +485,12 @@ constexpr int K3R_LD = 68;   // row stride (floats) of the g and B^T tiles
 template <int RP, int SPB>
 constexpr int k3r_lds_floats() { return 64 * K3R_LD + 64 * (RP + 4) + SPB * RP * K3R_LD; }
 
+// Two waves per SIMD (256 registers each), except the DoRA instances with two
+// strips per block: their Z tiles in flight need more, and at two waves they
+// spilled about 90 registers; at one wave they fit (with AGPRs) and run about
+// a fifth faster on [2048, 9728, 64] despite the lower occupancy.
 template <int RP, bool ZT, int SPB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZT && SPB == 2 ? 1 : 2)))
 void k3r_kernel(K3Args p) {
   static_assert(RP == 32 || RP == 64, "rank 32 or 64");
   static_assert(SPB == 1 || SPB == 2, "one or two strips per block");
