@@ -431,6 +431,7 @@ int check_linear(const lora_linear* L) {
   if (!L->W || !L->A || !L->B) return LORA_E_INVALID;
   if (!al16(L->W) || !al16(L->A) || !al16(L->B)) return LORA_E_ALIGN;
   if ((L->dora_mag == nullptr) != (L->dora_norm == nullptr)) return LORA_E_INVALID;
+  if (L->dora_from_y && !L->dora_mag) return LORA_E_INVALID;
   if ((L->dora_mag && !al16(L->dora_mag)) || (L->dora_norm && !al16(L->dora_norm)))
     return LORA_E_ALIGN;
   if (!std::isfinite(L->scale)) return LORA_E_INVALID;
@@ -845,6 +846,8 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   K3Args& ka = j.ka;
   ka.dY = dY; ka.T = T; ka.N = N; ka.B = lin->B; ka.U = U; ka.r = r;
   ka.mag = lin->dora_mag; ka.nrm = lin->dora_norm; ka.Z = Zin;
+  // Z may hold the forward's Y (dora_from_y): sum_t dY Y / mag is the same dm.
+  ka.dmdiv = lin->dora_from_y ? lin->dora_mag : lin->dora_norm;
   ka.tsplit = y.k3.len; ka.nstrip = y.strips; ka.spb = y.k3spb; ka.nts = y.k3.n; ka.o = o;
   j.k3_flops = 4.0 * T * N * r;
   j.k3_bytes = 4.0 * (T * N + T * r + 2 * N * r) + (Zin ? 4.0 * T * N : 0.0) +
@@ -863,7 +866,7 @@ int prepare_bwd(const lora_linear* lin, const float* X, const float* dY, const f
   j.nj = 0;
   if (y.k3.n > 1) {
     j.jobs[j.nj++] = {o.dBpart, dB, nullptr, N * r, 1, y.k3.n, acc, lin->scale};
-    if (dMag) j.jobs[j.nj++] = {o.dmpart, dMag, lin->dora_norm, N, N, y.k3.n, acc, 1.0f};
+    if (dMag) j.jobs[j.nj++] = {o.dmpart, dMag, ka.dmdiv, N, N, y.k3.n, acc, 1.0f};
   }
   j.has_ja = y.k4.n > 1;
   if (j.has_ja) j.ja = {dApart, dA, nullptr, r * K, 1, y.k4.n, acc, lin->scale};

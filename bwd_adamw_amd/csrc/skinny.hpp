@@ -220,6 +220,7 @@ struct K3Args {
   int64_t r;
   const float* mag;
   const float* nrm;
+  const float* dmdiv;   // dm's divisor: nrm, or mag when Z holds the forward's Y
   const float* Z;
   int64_t tsplit;
   int64_t nstrip;   // 64-column strips of N
@@ -423,7 +424,7 @@ LORA_DEV void k3_block(const K3Args& p, float* smem, int64_t bx, int by) {
         float s = 0.f;
         for (int g = 0; g < 16; ++g) s += red[g][tid];
         if (bdirect) {
-          s /= nrm[n0 + tid];
+          s /= p.dmdiv[n0 + tid];
           o.dm[n0 + tid] = o.accumulate ? o.dm[n0 + tid] + s : s;
         } else {
           o.dmpart[(int64_t)by * N + n0 + tid] = s;
@@ -722,7 +723,7 @@ void k3r_kernel(K3Args p) {
         float sum = 0.f;
         for (int g = 0; g < 16; ++g) sum += red[g][tid];
         if (bdirect) {
-          sum /= p.nrm[n0 + tid];
+          sum /= p.dmdiv[n0 + tid];
           o.dm[n0 + tid] = o.accumulate ? o.dm[n0 + tid] + sum : sum;
         } else {
           o.dmpart[(int64_t)by * N + n0 + tid] = sum;

@@ -66,7 +66,7 @@ class LoraLinear(C.Structure):
     _fields_ = [("tokens", C.c_int64), ("in_dim", C.c_int64), ("out_dim", C.c_int64),
                 ("rank", C.c_int64), ("w_dtype", C.c_int32), ("scale", C.c_float),
                 ("W", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p),
-                ("dora_mag", C.c_void_p), ("dora_norm", C.c_void_p)]
+                ("dora_mag", C.c_void_p), ("dora_norm", C.c_void_p), ("dora_from_y", C.c_int32)]
 
 
 class LoraProfileEntry(C.Structure):
@@ -214,9 +214,12 @@ def qweight_pack(fmt: str, out_dim: int, in_dim: int, planes: dict, device="cuda
     return QWeight(fmt, out_dim, in_dim, buf)
 
 
-def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None) -> LoraLinear:
+def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None,
+                dora_from_y=False) -> LoraLinear:
     """Descriptor of one adapted linear: W [N,K] (float32 or bfloat16, or a
-    QWeight), A [r,K], B [N,r] float32, optional DoRA magnitude and norm [N]."""
+    QWeight), A [r,K], B [N,r] float32, optional DoRA magnitude and norm [N].
+    dora_from_y (DoRA only): the backward takes the forward's Y where it
+    would take Z, so the forward need not write Z."""
     if isinstance(W, QWeight):
         wd = W.code
     elif W.dtype in (torch.float32, torch.bfloat16):
@@ -235,7 +238,7 @@ def make_linear(W, A, B, scale, tokens, dora_mag=None, dora_norm=None) -> LoraLi
     wptr = _ptr(W.buf, "W", torch.uint8) if isinstance(W, QWeight) else _ptr(W, "W", None)
     return LoraLinear(int(tokens), int(K), int(N), int(r), wd, float(scale), wptr,
                       _ptr(A, "A"), _ptr(B, "B"), _ptr(dora_mag, "dora_mag"),
-                      _ptr(dora_norm, "dora_norm"))
+                      _ptr(dora_norm, "dora_norm"), 1 if dora_from_y else 0)
 
 
 def make_dropout(seed, step, ordinal, layer, proj, p) -> LoraDropout:
@@ -372,6 +375,13 @@ class GroupCall:
         self.arr = _linears(self.lins)
         self.Y, self.U = _ptrs(Y, "Y", lins), _ptrs(U, "U", lins)
         self.Z = _ptrs(Z, "Z", lins, True)
+        # DoRA linears with dora_from_y: the forward writes no Z and the
+        # backward reads Y in its place.
+        self.from_y = any(l.dora_from_y for l in lins)
+        if self.from_y and not all(l.dora_from_y for l in lins):
+            raise ValueError("dora_from_y must be set for all linears of a group call or none")
+        self.Zf = None if self.from_y else self.Z
+        self.Zb = self.Y if self.from_y else self.Z
         self.dX = _ptrs(dX, "dX", lins, True)
         self.dA = None if dA is None else _ptrs(dA, "dA", lins)
         self.dB = None if dB is None else _ptrs(dB, "dB", lins)
@@ -404,7 +414,7 @@ class GroupCall:
         return drops if drops is None or isinstance(drops, C.Array) else _drops(drops, self.n)
 
     def forward(self, X, drops=None):
-        rc = lib().lora_forward_group(self.n, self.arr, self._x_ptr(X), self.Y, self.U, self.Z,
+        rc = lib().lora_forward_group(self.n, self.arr, self._x_ptr(X), self.Y, self.U, self.Zf,
                                       self._d(drops), self.ws, self.ws_bytes, self.stream)
         _check("lora_forward_group", rc)
 
@@ -412,7 +422,7 @@ class GroupCall:
         if self.dA is None or self.dB is None:
             raise ValueError("this GroupCall was prepared without gradients")
         rc = lib().lora_backward_group(self.n, self.arr, self._x_ptr(X), self._dy_ptrs(dY),
-                                       self.U, self.Z, self.dX, self.dA, self.dB, self.dMag,
+                                       self.U, self.Zb, self.dX, self.dA, self.dB, self.dMag,
                                        1 if accumulate else 0, self._d(drops), self.ws,
                                        self.ws_bytes, self.stream)
         _check("lora_backward_group", rc)

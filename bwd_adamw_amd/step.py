@@ -154,19 +154,18 @@ class Trainer:
             for k in model.keys:
                 ws = max(ws, L.lora_slots_workspace_bytes(
                     [self._linear(k, None, dora=cfg.dora)] * self.nslots))
-        # Activations per slot (slot 0's are also U, Z, Y, dX).
+        # Activations per slot (slot 0's are also U, Y, dX).  DoRA keeps no Z:
+        # its linears take the forward's Y in the backward (dora_from_y).
         self.acts = []
         for _ in range(self.nslots if self.stack_slots else 1):
-            a = {"U": {}, "Z": {}, "Y": {}, "dX": {}}
+            a = {"U": {}, "Y": {}, "dX": {}}
             for key in model.keys:
                 K, N = model.shape[key]
                 a["U"][key] = torch.empty(self.T, r, **f32)
                 a["Y"][key] = torch.empty(self.T, N, **f32)
                 a["dX"][key] = torch.empty(self.T, K, **f32)
-                if cfg.dora:
-                    a["Z"][key] = torch.empty(self.T, N, **f32)
             self.acts.append(a)
-        self.U, self.Z, self.Y, self.dX = (self.acts[0][n] for n in ("U", "Z", "Y", "dX"))
+        self.U, self.Y, self.dX = (self.acts[0][n] for n in ("U", "Y", "dX"))
         self.ws = torch.empty(max(ws, 256), device=device, dtype=torch.uint8)
         # Streams beyond the current one (default priority), each with a
         # workspace; no more streams than units to spread (layer groups; layers
@@ -194,7 +193,8 @@ class Trainer:
                                 aligned if dora else None, aligned if dora else None)
         mag = slot.mag.get(key) if dora else None
         nrm = slot.norm.get(key) if dora else None
-        return L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T, mag, nrm)
+        return L.make_linear(W, slot.A[key], slot.B[key], self.scale, self.T, mag, nrm,
+                             dora_from_y=dora)
 
     def init_dora(self, slot: Slot):
         """Magnitude = ||W_i|| rows, then the detached norms of W + s B A."""
@@ -272,7 +272,7 @@ class Trainer:
             cfg = self.cfg
             call = L.GroupCall([self._linear(k, slot, dora=cfg.dora) for k in keys],
                                [self.Y[k] for k in keys], [self.U[k] for k in keys],
-                               [self.Z[k] for k in keys] if cfg.dora else None,
+                               None,   # DoRA: the backward reads Y (dora_from_y)
                                [self.dX[k] for k in keys], [slot.gA[k] for k in keys],
                                [slot.gB[k] for k in keys],
                                [slot.gmag[k] for k in keys] if cfg.dora else None, ws, stream)
@@ -324,14 +324,13 @@ class Trainer:
                 lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
                 L.lora_forward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
                                      [a["Y"][key] for a in acts], [a["U"][key] for a in acts],
-                                     [a["Z"][key] for a in acts] if cfg.dora else None,
-                                     drops(key), wss[on[key]], streams[on[key]])
+                                     None, drops(key), wss[on[key]], streams[on[key]])
             for key in reversed(self.model.keys):
                 lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
                 L.lora_backward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
                                       [c[g][key][1] for c in chunks_per_slot],
                                       [a["U"][key] for a in acts],
-                                      [a["Z"][key] for a in acts] if cfg.dora else None,
+                                      [a["Y"][key] for a in acts] if cfg.dora else None,
                                       [a["dX"][key] for a in acts], [sl.gA[key] for sl in slots],
                                       [sl.gB[key] for sl in slots],
                                       [sl.gmag[key] for sl in slots] if cfg.dora else None,

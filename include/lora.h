@@ -123,6 +123,9 @@ typedef struct lora_linear {
   const float* B;           /* [N,r]                                       */
   const float* dora_mag;    /* [N] or NULL                                 */
   const float* dora_norm;   /* [N] or NULL                                 */
+  int32_t dora_from_y;      /* DoRA only, else 0: the backward's Z argument
+                               is the forward's Y (below); every dora_mag
+                               entry must then be nonzero                   */
 } lora_linear;
 
 /* Layout of a block-quantized W [out_dim, in_dim] in one buffer: the planes
@@ -160,8 +163,10 @@ size_t lora_workspace_bytes(const lora_linear* lin);
  *   U = X~ A^T  [T,r]  (saved for the backward)
  *   Z = X W^T + scale * U B^T  [T,N]
  *   Y = Z, or Y = (dora_mag/dora_norm) * Z per column for DoRA.
- * Z may be NULL; DoRA callers pass it (the backward needs it).  Y and U are
- * overwritten.  `drop` may be NULL.  ws must hold lora_workspace_bytes(lin). */
+ * Z may be NULL.  A DoRA backward needs Z, or, with lin->dora_from_y set,
+ * Y in its place, in which case the forward need not write Z (half of a DoRA
+ * forward's output traffic).  Y and U are overwritten.  `drop` may be NULL.
+ * ws must hold lora_workspace_bytes(lin). */
 int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U,
                  float* Z, const lora_dropout* drop, void* ws, size_t ws_bytes,
                  void* stream);
@@ -177,7 +182,9 @@ int lora_forward(const lora_linear* lin, const float* X, float* Y, float* U,
  * accumulate != 0 adds into dA/dB/dMag (gradient accumulation over the
  * chunks of one update); accumulate == 0 overwrites them (first chunk).
  * W is read in its native [N,K] layout.  dX may be NULL (not computed).
- * U is the forward's U of the same chunk; Z is required when dMag is given.
+ * U is the forward's U of the same chunk; Z is required when dMag is given:
+ * the forward's Z, or with lin->dora_from_y its Y, from which
+ *   dMag (+)= sum_t dY * Y / dora_mag   (the same sum: Y = Z dora_mag/dora_norm).
  * The mask is recomputed from `drop`, which must equal the forward's. */
 int lora_backward(const lora_linear* lin, const float* X, const float* dY,
                   const float* U, const float* Z, float* dX, float* dA,

@@ -1453,6 +1453,92 @@ def test_direct_operand_stacked_slots_match_oracle(bf16_config_5):
     test_slots_match_oracle(("direct-pair-stacked-dora", 256, 640, 1024, 32, 2, 0.1, True))
 
 
+FROM_Y_CASES = [
+    # name, T, K, N, r, w dtype, dropout
+    ("bf16-direct", 256, 640, 1024, 32, "bf16", 0.1),
+    ("bf16-ragged", 96, 600, 1000, 16, "bf16", 0.1),
+    ("f32-ragged", 100, 264, 136, 8, "f32", 0.0),
+]
+
+
+@pytest.mark.parametrize("case", FROM_Y_CASES, ids=[c[0] for c in FROM_Y_CASES])
+def test_dora_backward_from_y(case):
+    """dora_from_y: the forward writes no Z and the backward takes the
+    forward's Y in its place (dm = sum_t dY Y / mag).  Every output matches
+    the oracle, and dm matches the Z-mode call to float32 rounding."""
+    name, T, K, N, r, wd_, p = case
+    _say("dora from y", name)
+    c = _linear_case(T, K, N, r, wd_, seed=zlib.crc32(name.encode()) % 1000, dy_std=1e-2, b_std=0.05)
+    s, dk = 2.0, (99, 1, 2, 3, 4)
+    z = _run_gpu(c, s, p, dk, True)            # Z mode: mag, norm, and the reference run
+    g = z["g"]
+    lin = L.make_linear(g["Wq"], g["A"], g["B"], s, T, z["mag"], z["norm"], dora_from_y=True)
+    ws = torch.empty(L.lora_workspace_bytes(lin), device=DEV, dtype=torch.uint8)
+    drop = L.make_dropout(*dk, p) if p > 0 else None
+    nanf = float("nan")
+    Y, U = torch.full((T, N), nanf, device=DEV), torch.full((T, r), nanf, device=DEV)
+    L.lora_forward(lin, g["X"], Y, U, None, drop, ws)
+    dX, dA = torch.full((T, K), nanf, device=DEV), torch.full((r, K), nanf, device=DEV)
+    dB, dm = torch.full((N, r), nanf, device=DEV), torch.full((N,), nanf, device=DEV)
+    L.lora_backward(lin, g["X"], g["dY"], U, Y, dX, dA, dB, dm, False, drop, ws)
+    torch.cuda.synchronize()
+    got = dict(Y=Y, U=U, dX=dX, dA=dA, dB=dB, dmag=dm)
+    mag, nrm = _dora_vectors(z, c, s)
+    ref = _oracle(c, s, p, dk, mag, nrm)
+    for n in got:
+        assert torch.isfinite(got[n]).all(), n
+        e = rel_err(got[n], ref[n])
+        _say(f"  {n}: rel err {e:.3e}")
+        assert e <= TOL[wd_], (n, e)
+    assert rel_err(dm, z["dmag"]) <= 1e-5
+
+
+def test_dora_backward_from_y_stacked_slots():
+    """The same through the stacked slot calls (each slot's own mag)."""
+    cs = _slot_cases(256, 640, 1024, 32, 2, seed=91)
+    gs = [_gpu(c) for c in cs]
+    for g in gs[1:]:
+        g["Wq"], g["W"] = gs[0]["Wq"], gs[0]["W"]
+    T, K, N, r = 256, 640, 1024, 32
+    mags = [torch.rand(N, device=DEV) + 0.5 for _ in gs]
+    nrms = [torch.empty(N, device=DEV) for _ in gs]
+    for g, nr in zip(gs, nrms):
+        L.lora_dora_row_norms(L.make_linear(g["Wq"], g["A"], g["B"], 2.0, T), nr)
+    out = {}
+    for from_y in (False, True):
+        lins = [L.make_linear(g["Wq"], g["A"], g["B"], 2.0, T, m, nr, dora_from_y=from_y)
+                for g, m, nr in zip(gs, mags, nrms)]
+        ws = torch.empty(L.lora_slots_workspace_bytes(lins), device=DEV, dtype=torch.uint8)
+        drops = [L.make_dropout(5 + i, 1, 0, 2, 3, 0.1) for i in range(2)]
+        Y = [torch.empty(T, N, device=DEV) for _ in gs]
+        U = [torch.empty(T, r, device=DEV) for _ in gs]
+        Z = None if from_y else [torch.empty(T, N, device=DEV) for _ in gs]
+        L.lora_forward_slots(lins, [g["X"] for g in gs], Y, U, Z, drops, ws)
+        dX = [torch.empty(T, K, device=DEV) for _ in gs]
+        dA = [torch.empty(r, K, device=DEV) for _ in gs]
+        dB = [torch.empty(N, r, device=DEV) for _ in gs]
+        dm = [torch.empty(N, device=DEV) for _ in gs]
+        L.lora_backward_slots(lins, [g["X"] for g in gs], [g["dY"] for g in gs], U, Y if from_y else Z,
+                              dX, dA, dB, dm, accumulate=False, drops=drops, ws=ws)
+        torch.cuda.synchronize()
+        out[from_y] = dict(Y=Y, dX=dX, dA=dA, dB=dB, dm=dm)
+    for n in ("Y", "dX", "dA", "dB"):
+        for i in range(2):
+            assert torch.equal(out[True][n][i], out[False][n][i]), (n, i)
+    for i in range(2):
+        assert rel_err(out[True]["dm"][i], out[False]["dm"][i]) <= 1e-5, i
+
+
+def test_dora_from_y_needs_dora():
+    c = _gpu(_linear_case(64, 64, 64, 4, "f32", seed=3))
+    lin = L.make_linear(c["Wq"], c["A"], c["B"], 1.0, 64, dora_from_y=True)
+    ws = torch.empty(max(L.lora_workspace_bytes(lin), 256), device=DEV, dtype=torch.uint8)
+    Y, U = torch.zeros(64, 64, device=DEV), torch.zeros(64, 4, device=DEV)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_forward(lin, c["X"], Y, U, None, None, ws)
+    assert e.value.status == -1   # LORA_E_INVALID
+
+
 def _pinned(cfg, fn):
     L.lora_set_bf16_config(cfg)
     try:
