@@ -419,10 +419,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-          // dX computes its tile transposed (epilogue below); the forward
-          // keeps rows across lanes so that its stores are whole lines.
-          if constexpr (FWD) acc[i][j] = mfma32x32x16_bf16(av[i], bv[j], acc[i][j]);
-          else acc[i][j] = mfma32x32x16_bf16(bv[j], av[i], acc[i][j]);
+          // Both directions compute the tile transposed (W-side operand
+          // first): each lane then holds four consecutive output columns of
+          // one row per accumulator group (epilogue below).
+          acc[i][j] = mfma32x32x16_bf16(bv[j], av[i], acc[i][j]);
         }
     }
   };
@@ -784,8 +784,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-          if constexpr (FWD) acc[i][j] = mfma32x32x16_bf16(R[i][s], F[j], acc[i][j]);
-          else acc[i][j] = mfma32x32x16_bf16(F[j], R[i][s], acc[i][j]);
+          acc[i][j] = mfma32x32x16_bf16(F[j], R[i][s], acc[i][j]);
         }
     };
     // Phase s of K-step k: W fragments of sub-step s + 1 (the last phase:
@@ -877,35 +876,11 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
   if (!FWD && AD && lora) lora_contraction(std::true_type{});
 
   const Bf16Slot so = bf16_slot(p, slot);
-  if constexpr (FWD) {
-    // Lane l holds column n = .. + l%32 of 16 rows: each store instruction
-    // writes whole 128-byte rows of the tile.
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int64_t gn = n0 + wn0 + j * 32 + l32;
-        if (gn >= p.Nc) continue;
-        const float c = (p.nsplit == 1 && so.cn) ? so.cn[gn] / so.cd[gn] : 1.0f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t gm = m0 + wm0 + i * 32 + row32(v, lane);
-          if (gm >= p.M) continue;
-          const float x = acc[i][j][v];
-          if (p.nsplit == 1) {
-            so.C[(gm - moff) * p.Nc + gn] = x * c;
-            if (so.C2) so.C2[(gm - moff) * p.Nc + gn] = x;
-          } else {
-            p.part[((int64_t)split * p.M + gm) * p.Nc + gn] = x;
-          }
-        }
-      }
-    return;
-  }
-  // dX: the MFMA computes the tile transposed (W-side operand first), so lane
-  // l holds output row m = .. + l%32 and, per group of four accumulators,
-  // four consecutive columns: every store is a 16-byte vector, and the
-  // dropout mask of the LoRA term needs one row key per row.
+  // The MFMA computes the tile transposed (W-side operand first), so lane l
+  // holds output row m = .. + l%32 and, per group of four accumulators, four
+  // consecutive columns: every store is a 16-byte vector (the forward's Y, Z
+  // and split partials as much as dX), and dX's dropout mask of the LoRA term
+  // needs one row key per row.
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int64_t gm = m0 + wm0 + i * 32 + l32;
@@ -914,7 +889,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(GemmBf16Args p) {
     for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int64_t gn = n0 + wn0 + j * 32 + row32(4 * v4, lane);   // Nc is a multiple of 8
+        const int64_t gn = n0 + wn0 + j * 32 + row32(4 * v4, lane);   // Nc is a multiple of 4
         if (gn >= p.Nc) continue;
         f32x4 x = {acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
                    acc[i][j][4 * v4 + 3]};
