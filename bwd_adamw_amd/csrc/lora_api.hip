@@ -356,7 +356,15 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
     y.k3spb = 1;
     y.k3nvp = y.strips;
   } else {
-    const K3Plan kp = plan_k3(T, N, r, y.strips, 512);
+    K3Plan kp = plan_k3(T, N, r, y.strips, 512);
+    // DoRA's two-strip k3r blocks carry Z tiles and run one per CU (one wave
+    // per SIMD): their rows are split so that the blocks fill one round of
+    // the CUs. The plan's two blocks per CU would leave a few blocks for a
+    // third round, and fewer row ranges also mean fewer dB partials.
+    if (kp.spb == 2 && L->dora_mag != nullptr && T % SK_T == 0 && kp.nvp <= kCUs) {
+      const int64_t len = rup(cdiv(T, clampi(kCUs / kp.nvp, 1, T / SK_T)), SK_T);
+      kp.rows = {len, (int)cdiv(T, len)};
+    }
     y.k3 = kp.rows;
     y.k3spb = kp.spb;
     y.k3nvp = kp.nvp;
