@@ -314,18 +314,32 @@ class Trainer:
         G = len(chunks_per_slot[0])
         streams, wss = self._fork()
         layers = sorted({k[0] for k in self.model.keys})
-        on = {k: layers.index(k[0]) % len(streams) for k in self.model.keys}
+        ns = len(streams)
+        on = {k: layers.index(k[0]) % ns for k in self.model.keys}
+        # Each stream takes its linears in model order, started at a point
+        # q/ns of the way through its list: with every stream on the same
+        # shapes at the same time, the four run their frozen products
+        # together and their rank-side kernels together; offset, one
+        # stream's products overlap another's memory-bound kernels.  Every
+        # linear has its own inputs, so the order changes no result.
+        lists = []
+        for q in range(ns):
+            mine = [k for k in self.model.keys if on[k] == q]
+            r = (q * len(mine)) // ns
+            lists.append(mine[r:] + mine[:r])
+        # issued round robin over the streams, so that each gets work early
+        order = [ls[i] for i in range(max(map(len, lists))) for ls in lists if i < len(ls)]
         for g in range(G):
             def drops(key):
                 if p <= 0:
                     return None
                 return [L.make_dropout(sl.seed, sl.k, g, key[0], key[1], p) for sl in slots]
-            for key in self.model.keys:
+            for key in order:
                 lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
                 L.lora_forward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
                                      [a["Y"][key] for a in acts], [a["U"][key] for a in acts],
                                      None, drops(key), wss[on[key]], streams[on[key]])
-            for key in reversed(self.model.keys):
+            for key in reversed(order):
                 lins = [self._linear(key, sl, dora=cfg.dora) for sl in slots]
                 L.lora_backward_slots(lins, [c[g][key][0] for c in chunks_per_slot],
                                       [c[g][key][1] for c in chunks_per_slot],
