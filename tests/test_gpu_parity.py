@@ -399,11 +399,14 @@ def test_full_size_linear(wl, pi):
     _check_full(got, ref, TOL[cfg.w_dtype], cfg.dora)
 
 
-@pytest.mark.parametrize("pi", [4, 6], ids=["wgate", "wdown"])
-def test_full_size_stacked_slots(pi):
+@pytest.mark.parametrize("pi,from_y", [(4, False), (6, False), (4, True)],
+                         ids=["wgate", "wdown", "wgate-from-y"])
+def test_full_size_stacked_slots(pi, from_y):
     """The DoRA workload's two slots at full size in the launch plan the
     bench times (one product over both slots' 2 x 2048 stacked rows per
-    direction); each slot against the oracle over every output."""
+    direction); each slot against the oracle over every output.  from_y:
+    as the trainer runs it, the forward writes Y only and the backward's
+    magnitude gradient reads Y."""
     cfg = WL.get_config(5)
     proj = cfg.projections[pi]
     _say("full-size stacked slots", cfg.name, proj.name)
@@ -421,15 +424,18 @@ def test_full_size_stacked_slots(pi):
     nrms = [torch.empty(N, device=DEV) for _ in cs]
     for c, n in zip(cs, nrms):
         L.lora_dora_row_norms(L.make_linear(c["Wq"], c["A"], c["B"], s, T), n)
-    lins = [L.make_linear(c["Wq"], c["A"], c["B"], s, T, m, n) for c, m, n in zip(cs, mags, nrms)]
+    lins = [L.make_linear(c["Wq"], c["A"], c["B"], s, T, m, n, dora_from_y=from_y)
+            for c, m, n in zip(cs, mags, nrms)]
     shapes = dict(Y=(T, N), U=(T, cfg.rank), dX=(T, proj.in_dim), dA=(cfg.rank, proj.in_dim),
                   dB=(N, cfg.rank), Z=(T, N), dmag=(N,))
     out = {k: [torch.full(v, float("nan"), device=DEV) for _ in cs] for k, v in shapes.items()}
     ws = torch.empty(L.lora_slots_workspace_bytes(lins), device=DEV, dtype=torch.uint8)
     dks = [(cfg.seeds[i], 0, 0, 0, proj.ordinal) for i in range(2)]
     drops = [L.make_dropout(*k, cfg.dropout) for k in dks]
-    L.lora_forward_slots(lins, [c["X"] for c in cs], out["Y"], out["U"], out["Z"], drops, ws)
-    L.lora_backward_slots(lins, [c["X"] for c in cs], [c["dY"] for c in cs], out["U"], out["Z"],
+    L.lora_forward_slots(lins, [c["X"] for c in cs], out["Y"], out["U"],
+                         None if from_y else out["Z"], drops, ws)
+    L.lora_backward_slots(lins, [c["X"] for c in cs], [c["dY"] for c in cs], out["U"],
+                          out["Y"] if from_y else out["Z"],
                           out["dX"], out["dA"], out["dB"], out["dmag"], drops=drops, ws=ws)
     torch.cuda.synchronize()
     for i, c in enumerate(cs):
@@ -437,7 +443,11 @@ def test_full_size_stacked_slots(pi):
         nrm = O.dora_row_norms(np64(c["W"]), np64(c["A"]), np64(c["B"]), s)
         assert rel_err(nrms[i], nrm) <= 1e-5
         ref = _oracle(c, s, cfg.dropout, dks[i], np64(mags[i]), nrm)
-        _check_full(got, ref, TOL["bf16"], True)
+        if from_y:
+            assert torch.isnan(got["Z"]).all(), "the forward wrote Z"
+            _check_full(got, ref, TOL["bf16"], False, names=("Y", "U", "dX", "dA", "dB", "dmag"))
+        else:
+            _check_full(got, ref, TOL["bf16"], True)
 
 
 @pytest.mark.parametrize("fmt,pi", [("q4_k", 4), ("q6_k", 6), ("q8_0", 0)],
