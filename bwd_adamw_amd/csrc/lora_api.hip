@@ -358,12 +358,17 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
   } else {
     K3Plan kp = plan_k3(T, N, r, y.strips, 512);
     // DoRA's two-strip k3r blocks carry Z tiles and run one per CU (one wave
-    // per SIMD): their rows are split so that the blocks fill one round of
-    // the CUs. The plan's two blocks per CU would leave a few blocks for a
-    // third round, and fewer row ranges also mean fewer dB partials.
-    if (kp.spb == 2 && L->dora_mag != nullptr && T % SK_T == 0 && kp.nvp <= kCUs) {
-      const int64_t len = rup(cdiv(T, clampi(kCUs / kp.nvp, 1, T / SK_T)), SK_T);
-      kp.rows = {len, (int)cdiv(T, len)};
+    // per SIMD). Their rows are split so that the blocks fill one round of
+    // the CUs: the plan's two blocks per CU would leave a few blocks for a
+    // third round, and fewer row ranges also mean fewer dB partials. Where
+    // the plan keeps one strip per block, two strips per block on such a
+    // grid halve the V partials (written here, summed by the reduction)
+    // whenever each block still gets at least three 64-row stages.
+    const int64_t nvp2 = cdiv(y.strips, 2);
+    if (L->dora_mag != nullptr && (rpad == 32 || rpad == 64) && T % SK_T == 0 && N % SK_C == 0 &&
+        kp.spb <= 2 && y.strips >= 2 && nvp2 <= kCUs) {
+      const int64_t len = rup(cdiv(T, clampi(kCUs / nvp2, 1, T / SK_T)), SK_T);
+      if (kp.spb == 2 || len >= 3 * SK_T) kp = {{len, (int)cdiv(T, len)}, 2, nvp2};
     }
     y.k3 = kp.rows;
     y.k3spb = kp.spb;
