@@ -399,8 +399,8 @@ def test_full_size_linear(wl, pi):
     _check_full(got, ref, TOL[cfg.w_dtype], cfg.dora)
 
 
-@pytest.mark.parametrize("pi,from_y", [(4, False), (6, False), (4, True)],
-                         ids=["wgate", "wdown", "wgate-from-y"])
+@pytest.mark.parametrize("pi,from_y", [(4, False), (6, False), (4, True), (0, True), (1, True)],
+                         ids=["wgate", "wdown", "wgate-from-y", "wq-from-y", "wk-from-y"])
 def test_full_size_stacked_slots(pi, from_y):
     """The DoRA workload's two slots at full size in the launch plan the
     bench times (one product over both slots' 2 x 2048 stacked rows per
