@@ -364,11 +364,16 @@ Layout make_layout(const lora_linear* L, int stack = 1) {
     // the plan keeps one strip per block, two strips per block on such a
     // grid halve the V partials (written here, summed by the reduction)
     // whenever each block still gets at least three 64-row stages.
+    // Four strips per block (strip counts that are a multiple of four) halve
+    // the V partials again where the blocks still get three stages.
     const int64_t nvp2 = cdiv(y.strips, 2);
     if (L->dora_mag != nullptr && (rpad == 32 || rpad == 64) && T % SK_T == 0 && N % SK_C == 0 &&
         kp.spb <= 2 && y.strips >= 2 && nvp2 <= kCUs) {
-      const int64_t len = rup(cdiv(T, clampi(kCUs / nvp2, 1, T / SK_T)), SK_T);
+      auto one_round = [&](int64_t nvp) { return rup(cdiv(T, clampi(kCUs / nvp, 1, T / SK_T)), SK_T); };
+      const int64_t len = one_round(nvp2);
       if (kp.spb == 2 || len >= 3 * SK_T) kp = {{len, (int)cdiv(T, len)}, 2, nvp2};
+      const int64_t nvp4 = y.strips / 4, len4 = y.strips % 4 == 0 ? one_round(nvp4) : 0;
+      if (kp.spb == 2 && len4 >= 3 * SK_T) kp = {{len4, (int)cdiv(T, len4)}, 4, nvp4};
     }
     y.k3 = kp.rows;
     y.k3spb = kp.spb;
@@ -1017,16 +1022,18 @@ void launch_bwd_k3(const BwdJob& jb, hipStream_t st) {
   {
     prof::Scope ps("k3_v_db", T, N, r, jb.k3_flops, jb.k3_bytes);
     const dim3 grid((unsigned)y.k3nvp, (unsigned)y.k3.n);
-    // Whole 64 x 64 tiles at rank 32 or 64 with at most two strips per
-    // block: the row-major variant (same outputs, V partials written once).
+    // Whole 64 x 64 tiles at rank 32 or 64 with one or two strips per
+    // block, or four when every block gets four: the row-major variant (same
+    // outputs, V partials written once).
     const bool whole = (jb.rp == 32 || jb.rp == 64) && T % SK_T == 0 && N % SK_C == 0 &&
-                       y.k3.len % SK_T == 0 && y.k3spb <= 2;
+                       y.k3.len % SK_T == 0 && (y.k3spb <= 2 || (y.k3spb == 4 && y.strips % 4 == 0));
     const bool z = jb.ka.Z != nullptr;
     if (whole) {
 #define LORA_K3R(RP_, ZT_, SPB_) \
   if (jb.rp == RP_ && z == ZT_ && y.k3spb == SPB_) launch(k3r_kernel<RP_, ZT_, SPB_>, grid, st, ps, jb.ka);
       LORA_K3R(32, false, 1) LORA_K3R(32, false, 2) LORA_K3R(32, true, 1) LORA_K3R(32, true, 2)
       LORA_K3R(64, false, 1) LORA_K3R(64, false, 2) LORA_K3R(64, true, 1) LORA_K3R(64, true, 2)
+      LORA_K3R(32, false, 4) LORA_K3R(32, true, 4) LORA_K3R(64, false, 4) LORA_K3R(64, true, 4)
 #undef LORA_K3R
     } else if (z) {
       LORA_RP_DISPATCH(jb.rp, launch(k3_kernel<RP, true>, grid, st, ps, jb.ka));

@@ -466,7 +466,7 @@ void k3_kernel(K3Args p) {
 
 // ---------------------------------------------------------------------------
 // k3r: the same pass as k3 for whole tiles (T and N multiples of 64, tsplit
-// a multiple of 64, rank padded to RP = 32 or 64, at most SPB = 2 strips per
+// a multiple of 64, rank padded to RP = 32 or 64, SPB = 1, 2 or 4 strips per
 // block), in row-major tile order: for each 64-row stage the block visits
 // its strips one after another, so the stage's V rows are summed over the
 // block's strips in registers and written once (no read-modify-write of the
@@ -489,12 +489,14 @@ constexpr int k3r_lds_floats() { return 64 * K3R_LD + 64 * (RP + 4) + SPB * RP *
 // Two waves per SIMD (256 registers each), except the DoRA instances with two
 // strips per block: their Z tiles in flight need more, and at two waves they
 // spilled about 90 registers; at one wave they fit (with AGPRs) and run about
-// a fifth faster on [2048, 9728, 64] despite the lower occupancy.
+// a fifth faster on [2048, 9728, 64] despite the lower occupancy.  Four
+// strips per block (the host groups four only when every block gets four)
+// hold four dB tiles and always run at one wave per SIMD.
 template <int RP, bool ZT, int SPB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZT && SPB == 2 ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((ZT && SPB == 2) || SPB == 4 ? 1 : 2)))
 void k3r_kernel(K3Args p) {
   static_assert(RP == 32 || RP == 64, "rank 32 or 64");
-  static_assert(SPB == 1 || SPB == 2, "one or two strips per block");
+  static_assert(SPB == 1 || SPB == 2 || SPB == 4, "one, two or four strips per block");
   constexpr int LDU = RP + 4;
   constexpr bool BOTH = RP == 64;
   __shared__ __attribute__((aligned(16))) float smem[k3r_lds_floats<RP, SPB>()];
@@ -680,7 +682,14 @@ void k3r_kernel(K3Args p) {
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  if (SPB == 2 && ns == 2) {
+  if (SPB == 4 && ns == 4) {
+    for (int idx = 0; idx < ntot; idx += 4) {
+      step(I0{}, std::false_type{}, idx, R[0], R[1]);
+      step(I1{}, std::false_type{}, idx + 1, R[1], R[0]);
+      step(std::integral_constant<int, SPB / 2>{}, std::false_type{}, idx + 2, R[0], R[1]);
+      step(std::integral_constant<int, SPB - 1>{}, std::true_type{}, idx + 3, R[1], R[0]);
+    }
+  } else if (SPB == 2 && ns == 2) {
     for (int idx = 0; idx < ntot; idx += 2) {
       step(I0{}, std::false_type{}, idx, R[0], R[1]);
       step(std::integral_constant<int, SPB - 1>{}, std::true_type{}, idx + 1, R[1], R[0]);
